@@ -1,0 +1,183 @@
+"""CPU oracle for the NVFP4 sparse-MoE decode step (Python side).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg import this package; the product package
+never does, and the oracle imports nothing from it.  The arithmetic lives in
+``oracle.c`` (double precision, plain loops); this file only marshals numpy
+arrays through ctypes.  ``oracle/model.py`` composes the steps into a layer, a
+stack and the head.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import NamedTuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liboracle.so")
+SRC_PATH = os.path.join(HERE, "oracle.c")
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+def build(force: bool = False) -> str:
+    if force or not os.path.exists(LIB_PATH):
+        subprocess.run(["gcc", "-O2", "-fPIC", "-shared", SRC_PATH, "-o", LIB_PATH, "-lm", "-lpthread"], check=True)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(LIB_PATH)
+        L.oracle_e2m1_value.argtypes = [ctypes.c_int]
+        L.oracle_e2m1_value.restype = ctypes.c_double
+        L.oracle_e4m3_value.argtypes = [ctypes.c_int]
+        L.oracle_e4m3_value.restype = ctypes.c_double
+        L.oracle_e2m1_encode.argtypes = [ctypes.c_double]
+        L.oracle_e2m1_encode.restype = ctypes.c_int
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_double]
+        L.oracle_e4m3_encode.restype = ctypes.c_int
+        L.oracle_nvfp4_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P]
+        L.oracle_nvfp4_quantize.restype = None
+        L.oracle_nvfp4_dequantize.argtypes = [_P, _P, ctypes.c_float, _I64, _I64, _P]
+        L.oracle_nvfp4_dequantize.restype = None
+        L.oracle_nvfp4_gemv.argtypes = [_P, _P, ctypes.c_float, _I64, _I64, _P, _P, ctypes.c_int]
+        L.oracle_nvfp4_gemv.restype = None
+        L.oracle_f32_gemv.argtypes = [_P, _I64, _I64, _P, _P, ctypes.c_int]
+        L.oracle_f32_gemv.restype = None
+        L.oracle_topk_softmax.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P, _P, _P]
+        L.oracle_topk_softmax.restype = None
+        L.oracle_rms_inv.argtypes = [_P, _I64, ctypes.c_double]
+        L.oracle_rms_inv.restype = ctypes.c_double
+        L.oracle_swiglu_expert.argtypes = [_P, _P, ctypes.c_float, _P, _P, ctypes.c_float, _P, _P, ctypes.c_float,
+                                           _I64, _I64, _P, _P, _P, ctypes.c_int]
+        L.oracle_swiglu_expert.restype = None
+        L.oracle_argmax.argtypes = [_P, _I64, _P]
+        L.oracle_argmax.restype = _I64
+        _lib = L
+    return _lib
+
+
+def default_threads() -> int:
+    env = os.environ.get("ORACLE_THREADS")
+    if env:
+        return max(1, int(env))
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+class NVFP4(NamedTuple):
+    """An NVFP4 matrix in the interchange layout: codes [rows][cols/2] (element
+    2j in the low nibble of byte j), E4M3 scales [rows][cols/16], fp32 S."""
+    codes: np.ndarray
+    scales: np.ndarray
+    tscale: float
+    rows: int
+    cols: int
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ------------------------------------------------------------------- codec --
+def e2m1_value(code: int) -> float:
+    return lib().oracle_e2m1_value(code)
+
+
+def e4m3_value(code: int) -> float:
+    return lib().oracle_e4m3_value(code)
+
+
+def e2m1_encode(v: float) -> int:
+    return lib().oracle_e2m1_encode(v)
+
+
+def e4m3_encode(r: float) -> int:
+    return lib().oracle_e4m3_encode(r)
+
+
+def quantize(w: np.ndarray) -> NVFP4:
+    w = _c(w, np.float32)
+    rows, cols = w.shape
+    assert cols % 16 == 0
+    codes = np.empty((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 16), np.uint8)
+    S = np.zeros(1, np.float32)
+    lib().oracle_nvfp4_quantize(w.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data, S.ctypes.data)
+    return NVFP4(codes, scales, float(S[0]), rows, cols)
+
+
+def dequantize(q: NVFP4) -> np.ndarray:
+    out = np.empty((q.rows, q.cols), np.float32)
+    codes, scales = _c(q.codes, np.uint8), _c(q.scales, np.uint8)
+    lib().oracle_nvfp4_dequantize(codes.ctypes.data, scales.ctypes.data, q.tscale, q.rows, q.cols, out.ctypes.data)
+    return out
+
+
+# ---------------------------------------------------------------- products --
+def nvfp4_gemv(q: NVFP4, x: np.ndarray, nthreads: int | None = None) -> np.ndarray:
+    x = _c(x, np.float64)
+    assert x.shape == (q.cols,)
+    y = np.empty(q.rows, np.float64)
+    codes, scales = _c(q.codes, np.uint8), _c(q.scales, np.uint8)
+    lib().oracle_nvfp4_gemv(codes.ctypes.data, scales.ctypes.data, q.tscale, q.rows, q.cols, x.ctypes.data,
+                            y.ctypes.data, nthreads or default_threads())
+    return y
+
+
+def f32_gemv(w: np.ndarray, x: np.ndarray, nthreads: int | None = None) -> np.ndarray:
+    w = _c(w, np.float32)
+    x = _c(x, np.float64)
+    rows, cols = w.shape
+    assert x.shape == (cols,)
+    y = np.empty(rows, np.float64)
+    lib().oracle_f32_gemv(w.ctypes.data, rows, cols, x.ctypes.data, y.ctypes.data, nthreads or default_threads())
+    return y
+
+
+def topk_softmax(logits: np.ndarray, k: int):
+    """-> (idx int32[k] ordered by (logit desc, index asc), w float64[k], gap)"""
+    logits = _c(logits, np.float64)
+    idx = np.empty(k, np.int32)
+    w = np.empty(k, np.float64)
+    gap = np.zeros(1, np.float64)
+    lib().oracle_topk_softmax(logits.ctypes.data, logits.size, k, idx.ctypes.data, w.ctypes.data, gap.ctypes.data)
+    return idx, w, float(gap[0])
+
+
+def rms_inv(h: np.ndarray, eps: float) -> float:
+    h = _c(h, np.float64)
+    return lib().oracle_rms_inv(h.ctypes.data, h.size, eps)
+
+
+def swiglu_expert(gate: NVFP4, up: NVFP4, down: NVFP4, u: np.ndarray, nthreads: int | None = None,
+                  return_hidden: bool = False):
+    H, I = gate.cols, gate.rows
+    assert up.rows == I and up.cols == H and down.rows == H and down.cols == I
+    u = _c(u, np.float64)
+    y = np.empty(H, np.float64)
+    h = np.empty(I, np.float64)
+    args, keep = [], []
+    for q in (gate, up, down):
+        codes, scales = _c(q.codes, np.uint8), _c(q.scales, np.uint8)
+        keep += [codes, scales]
+        args += [codes.ctypes.data, scales.ctypes.data, q.tscale]
+    lib().oracle_swiglu_expert(*args, H, I, u.ctypes.data, y.ctypes.data, h.ctypes.data, nthreads or default_threads())
+    return (y, h) if return_hidden else y
+
+
+def argmax(v: np.ndarray):
+    """-> (first index of the maximum, max minus second largest)"""
+    v = _c(v, np.float64)
+    gap = np.zeros(1, np.float64)
+    i = lib().oracle_argmax(v.ctypes.data, v.size, gap.ctypes.data)
+    return int(i), float(gap[0])

@@ -1,0 +1,278 @@
+/*
+ * oracle.c -- plain, slow CPU reference for the NVFP4 sparse-MoE decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, loads or
+ * calls this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline do.  It shares no source, header, table or helper with the HIP
+ * path.  All arithmetic is double precision over the exactly defined fp32
+ * dequantised weights, in the order the definitions below state.
+ *
+ * Sources (page titles as published; sections named):
+ *  [P3] "Flint: 125 tokens a second is what 2.5B active parameters buy at
+ *       273 GB/s" -- "The shape, read from the headers" (hidden 2,048; 256
+ *       routed experts of width 512, 6 chosen per token, one shared expert of
+ *       width 1,024; vocabulary 150,144; three matrices per expert), "Why
+ *       active parameters set the speed" (4-bit output head, 1,024 B of codes
+ *       per 2,048-wide row) and "Checking 125 tokens a second" (NVFP4 stores
+ *       4-bit values with one 8-bit scale per 16 values).
+ *  [P2] "Recursive Releases Flint, a 40B MoE Coding Model That Runs Locally at
+ *       125 Tokens per Second" -- "How does Flint's architecture work?" (a
+ *       router picks 6 of 256 experts, plus one always-active shared expert).
+ *  [P1] "Flint-40B-A2B: AI-Built MoE Coding Model Hits 125 tok/s on MacBook
+ *       Pro" -- "Quantization with Offline Distillation" (the output layer is
+ *       NVFP4 too).
+ * Where the pages leave a step open (the value encodings, the per-tensor
+ * scale, rounding, the routing weights, the SwiGLU form, the norm) the
+ * plainest reading is taken; each one is stated at the function that uses it.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- codec -- */
+
+/* E2M1 (1 sign, 2 exponent bits with bias 1, 1 mantissa bit; no Inf/NaN),
+ * decoded from its bit fields: e = 0 is subnormal, m * 2^-1; otherwise
+ * 2^(e-1) * (1 + m/2). */
+double oracle_e2m1_value(int code) {
+  int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+  return s ? -mag : mag;
+}
+
+/* OCP FP8 E4M3FN (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * Inf; S.1111.111 is NaN).  Normal 2^(e-7) (1 + m/8), subnormal 2^-6 (m/8). */
+double oracle_e4m3_value(int code) {
+  int s = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  double mag = (e == 0) ? ldexp(m / 8.0, -6) : ldexp(1.0 + m / 8.0, e - 7);
+  return s ? -mag : mag;
+}
+
+/* Round-to-nearest-even by exhaustive search over the representable
+ * magnitudes: the nearest value wins; of two equally near, the one whose code
+ * is even (last mantissa bit 0).  Beyond the largest magnitude the search
+ * returns the largest, i.e. saturation. */
+int oracle_e2m1_encode(double v) {
+  double a = fabs(v);
+  if (a >= 6.0) return 7 | (signbit(v) ? 8 : 0); /* saturate (distances to a huge |v| all round equal) */
+  int best = 0;
+  double bd = INFINITY;
+  for (int c = 0; c < 8; ++c) {
+    double d = fabs(oracle_e2m1_value(c) - a);
+    if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) { bd = d; best = c; }
+  }
+  return best | (signbit(v) ? 8 : 0);
+}
+
+/* r >= 0 (a block scale); non-negative finite E4M3 codes 0x00..0x7E. */
+int oracle_e4m3_encode(double r) {
+  if (r >= 448.0) return 0x7E; /* saturate */
+  int best = 0;
+  double bd = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    double d = fabs(oracle_e4m3_value(c) - r);
+    if (d < bd || (d == bd && (c & 1) == 0 && (best & 1) == 1)) { bd = d; best = c; }
+  }
+  return best;
+}
+
+/* ------------------------------------------------------------- quantise -- */
+
+/* NVFP4 quantisation of one matrix W [rows][cols] (cols a multiple of 16;
+ * blocks of 16 run along cols, the reduction axis) into
+ *   codes  [rows][cols/2]  element 2j in the low nibble of byte j,
+ *   scales [rows][cols/16] one E4M3 code per block,
+ *   tscale               one fp32 per-tensor scale S.
+ * [P3 "Checking 125 tokens a second": 4-bit values, one 8-bit scale per 16.]
+ * Readings taken here: S = fl32(amax / (6 * 448)), so that the largest block
+ * scale lands on E4M3's largest finite value; block scale = E4M3-RNE of
+ * blockmax / (6 S); element code = E2M1-RNE of w / (d S); a block whose scale
+ * decodes to 0 stores all-zero codes; all ratios in double. */
+void oracle_nvfp4_quantize(const float* w, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                           float* tscale) {
+  double amax = 0.0;
+  for (int64_t i = 0; i < rows * cols; ++i) {
+    double a = fabs((double)w[i]);
+    if (a > amax) amax = a;
+  }
+  float S = (float)(amax / 2688.0);
+  *tscale = S;
+  int64_t nb = cols / 16;
+  memset(codes, 0, (size_t)(rows * cols / 2));
+  memset(scales, 0, (size_t)(rows * nb));
+  if (S == 0.0f) return;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const float* blk = w + r * cols + b * 16;
+      double bm = 0.0;
+      for (int i = 0; i < 16; ++i) {
+        double a = fabs((double)blk[i]);
+        if (a > bm) bm = a;
+      }
+      int sc = oracle_e4m3_encode(bm / (6.0 * (double)S));
+      scales[r * nb + b] = (uint8_t)sc;
+      double d = oracle_e4m3_value(sc);
+      if (d == 0.0) continue;
+      for (int i = 0; i < 16; ++i) {
+        int c = oracle_e2m1_encode((double)blk[i] / (d * (double)S));
+        int64_t k = b * 16 + i;
+        uint8_t* byte = &codes[r * (cols / 2) + k / 2];
+        *byte |= (uint8_t)((k & 1) ? (c << 4) : c);
+      }
+    }
+  }
+}
+
+/* w = fl32((e2m1(c) * d) * S): c*d is exact, then one rounding to fp32. */
+static inline float deq(const uint8_t* codes, const uint8_t* scales, float S, int64_t cols, int64_t r, int64_t k) {
+  uint8_t byte = codes[r * (cols / 2) + k / 2];
+  int c = (k & 1) ? (byte >> 4) : (byte & 15);
+  double d = oracle_e4m3_value(scales[r * (cols / 16) + k / 16]);
+  return (float)((oracle_e2m1_value(c) * d) * (double)S);
+}
+
+void oracle_nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, float tscale, int64_t rows,
+                             int64_t cols, float* out) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t k = 0; k < cols; ++k) out[r * cols + k] = deq(codes, scales, tscale, cols, r, k);
+}
+
+/* ------------------------------------------------------------- products -- */
+
+typedef struct {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  float S;
+  const float* wf32; /* when non-NULL: an unquantised fp32 matrix */
+  int64_t rows, cols, r0, r1;
+  const double* x;
+  double* y;
+} gemv_job;
+
+static void* gemv_rows(void* p) {
+  gemv_job* j = (gemv_job*)p;
+  for (int64_t r = j->r0; r < j->r1; ++r) {
+    double acc = 0.0;
+    if (j->wf32) {
+      for (int64_t k = 0; k < j->cols; ++k) acc += (double)j->wf32[r * j->cols + k] * j->x[k];
+    } else {
+      for (int64_t k = 0; k < j->cols; ++k) acc += (double)deq(j->codes, j->scales, j->S, j->cols, r, k) * j->x[k];
+    }
+    j->y[r] = acc;
+  }
+  return NULL;
+}
+
+static void gemv_any(const uint8_t* codes, const uint8_t* scales, float S, const float* wf32, int64_t rows,
+                     int64_t cols, const double* x, double* y, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 64) nthreads = 64;
+  if (rows < 64) nthreads = 1;
+  gemv_job jobs[64];
+  pthread_t th[64];
+  int64_t chunk = (rows + nthreads - 1) / nthreads;
+  int used = 0;
+  for (int t = 0; t < nthreads; ++t) {
+    int64_t r0 = t * chunk, r1 = r0 + chunk < rows ? r0 + chunk : rows;
+    if (r0 >= rows) break;
+    jobs[t] = (gemv_job){codes, scales, S, wf32, rows, cols, r0, r1, x, y};
+    used++;
+  }
+  if (used == 1) { gemv_rows(&jobs[0]); return; }
+  for (int t = 0; t < used; ++t) pthread_create(&th[t], NULL, gemv_rows, &jobs[t]);
+  for (int t = 0; t < used; ++t) pthread_join(th[t], NULL);
+}
+
+/* y = deq(W) x in double; each row's sum runs k = 0..cols-1 in order, so the
+ * result does not depend on the thread count. */
+void oracle_nvfp4_gemv(const uint8_t* codes, const uint8_t* scales, float tscale, int64_t rows, int64_t cols,
+                       const double* x, double* y, int nthreads) {
+  gemv_any(codes, scales, tscale, NULL, rows, cols, x, y, nthreads);
+}
+
+/* y = W x for an unquantised fp32 matrix (the router). */
+void oracle_f32_gemv(const float* w, int64_t rows, int64_t cols, const double* x, double* y, int nthreads) {
+  gemv_any(NULL, NULL, 0.0f, w, rows, cols, x, y, nthreads);
+}
+
+/* -------------------------------------------------------------- routing -- */
+
+static const double* g_sort_keys;
+static int by_logit_desc_then_index(const void* a, const void* b) {
+  int i = *(const int*)a, j = *(const int*)b;
+  double li = g_sort_keys[i], lj = g_sort_keys[j];
+  if (li > lj) return -1;
+  if (li < lj) return 1;
+  return (i > j) - (i < j);
+}
+
+/* Top-k routing [P2 "How does Flint's architecture work?": the router selects
+ * 6 experts per token].  Selection: full sort by (logit descending, index
+ * ascending), first k.  Weights (reading): softmax over all E logits, then
+ * renormalised over the chosen k.  gap = k-th minus (k+1)-th largest logit
+ * (INFINITY when E == k).  Not thread-safe (uses a static sort key). */
+void oracle_topk_softmax(const double* logits, int E, int k, int32_t* idx, double* w, double* gap) {
+  int* order = (int*)malloc(sizeof(int) * (size_t)E);
+  for (int e = 0; e < E; ++e) order[e] = e;
+  g_sort_keys = logits;
+  qsort(order, (size_t)E, sizeof(int), by_logit_desc_then_index);
+  double mx = logits[order[0]];
+  double z = 0.0;
+  for (int e = 0; e < E; ++e) z += exp(logits[e] - mx);
+  double sel = 0.0;
+  for (int i = 0; i < k; ++i) sel += exp(logits[order[i]] - mx) / z;
+  for (int i = 0; i < k; ++i) {
+    idx[i] = order[i];
+    w[i] = (exp(logits[order[i]] - mx) / z) / sel;
+  }
+  *gap = (E > k) ? logits[order[k - 1]] - logits[order[k]] : INFINITY;
+  free(order);
+}
+
+/* RMSNorm scale with unit gain (reading: eps inside the root):
+ * 1 / sqrt(mean(h^2) + eps). */
+double oracle_rms_inv(const double* h, int64_t n, double eps) {
+  double s = 0.0;
+  for (int64_t i = 0; i < n; ++i) s += h[i] * h[i];
+  return 1.0 / sqrt(s / (double)n + eps);
+}
+
+/* --------------------------------------------------------------- expert -- */
+
+/* One SwiGLU expert [P3 "The shape, read from the headers": three matrices
+ * per expert].  Reading: the first matrix (gate) goes through SiLU, the
+ * second (up) is linear, the third (down) maps back to the hidden size:
+ *   g = Wg u, a = Wu u, h = g / (1 + e^-g) * a, y = Wd h.
+ * Wg, Wu are [I][H]; Wd is [H][I]; all NVFP4. */
+void oracle_swiglu_expert(const uint8_t* gc, const uint8_t* gs, float gS, const uint8_t* uc, const uint8_t* us,
+                          float uS, const uint8_t* dc, const uint8_t* ds, float dS, int64_t H, int64_t I,
+                          const double* u, double* y, double* h_out, int nthreads) {
+  double* g = (double*)malloc(sizeof(double) * (size_t)I);
+  double* a = (double*)malloc(sizeof(double) * (size_t)I);
+  double* h = (double*)malloc(sizeof(double) * (size_t)I);
+  oracle_nvfp4_gemv(gc, gs, gS, I, H, u, g, nthreads);
+  oracle_nvfp4_gemv(uc, us, uS, I, H, u, a, nthreads);
+  for (int64_t i = 0; i < I; ++i) h[i] = g[i] / (1.0 + exp(-g[i])) * a[i];
+  oracle_nvfp4_gemv(dc, ds, dS, H, I, h, y, nthreads);
+  if (h_out) memcpy(h_out, h, sizeof(double) * (size_t)I);
+  free(g);
+  free(a);
+  free(h);
+}
+
+/* --------------------------------------------------------------- argmax -- */
+
+/* First index of the largest value; gap = largest minus second largest. */
+int64_t oracle_argmax(const double* v, int64_t n, double* gap) {
+  int64_t best = 0;
+  for (int64_t i = 1; i < n; ++i)
+    if (v[i] > v[best]) best = i;
+  double second = -INFINITY;
+  for (int64_t i = 0; i < n; ++i)
+    if (i != best && v[i] > second) second = v[i];
+  if (gap) *gap = v[best] - second;
+  return best;
+}

@@ -1,0 +1,141 @@
+"""Seeded synthetic inputs shared by the GPU tests/benchmark and the CPU oracle.
+
+This module only draws Gaussian numbers and names the streams they come
+from; it holds none of the NVFP4 method's arithmetic.  The host generator is
+``synth.c`` (Philox4x32-10 + Box-Muller, IEEE-only arithmetic, bit-identical on
+every host); ``synth_dev.hip`` is the same definition for the GPU, used to fill
+device buffers quickly and tested bit-for-bit against the host generator.
+
+Stream naming.  Every tensor of the workloads is the stream
+``(seed, kind << 16 | expert)`` of the generator, element ``i`` being the
+row-major flat index, so that any single expert matrix can be drawn on its own.
+Weights are N(0, 0.02) (0.02 is the standard deviation), tokens N(0, 1).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsynth.so")
+SRC_PATH = os.path.join(HERE, "synth.c")
+
+# stream kinds
+ROUTER, GATE, UP, DOWN, SHARED_GATE, SHARED_UP, SHARED_DOWN, HEAD, TOKEN = range(1, 10)
+WEIGHT_STD = 0.02
+
+# seeds of the stacked workload: layer l uses weight seed l, the head 1000,
+# decode token t seed 10000 + t, batched step s slot j seed 20000 + B*s + j
+HEAD_SEED = 1000
+TOKEN_SEED0 = 10000
+BATCH_SEED0 = 20000
+
+
+def build_host_lib(force: bool = False) -> str:
+    if force or not os.path.exists(LIB_PATH):
+        cmd = ["gcc", "-O3", "-mavx2", "-ffp-contract=off", "-fno-math-errno", "-fPIC", "-shared",
+               SRC_PATH, "-o", LIB_PATH, "-lpthread", "-lm"]
+        subprocess.run(cmd, check=True)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build_host_lib()
+        L = ctypes.CDLL(LIB_PATH)
+        L.synth_normal_f32.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int64,
+                                       ctypes.c_float, ctypes.c_float, ctypes.c_void_p, ctypes.c_int]
+        L.synth_normal_f32.restype = None
+        L.synth_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+        L.synth_philox4x32_10.restype = None
+        _lib = L
+    return _lib
+
+
+def philox4x32_10(ctr, key):
+    c = np.asarray(ctr, dtype=np.uint32)
+    k = np.asarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib().synth_philox4x32_10(c.ctypes.data, k.ctypes.data, out.ctypes.data)
+    return out
+
+
+def stream_id(kind: int, expert: int = 0) -> int:
+    assert 0 <= expert < 65536
+    return (kind << 16) | expert
+
+
+def normal(seed: int, stream: int, n: int, mean: float = 0.0, std: float = 1.0, offset: int = 0,
+           out: np.ndarray | None = None, nthreads: int = 0) -> np.ndarray:
+    """n float32 draws of N(mean, std^2): elements offset..offset+n-1 of (seed, stream)."""
+    if out is None:
+        out = np.empty(n, dtype=np.float32)
+    assert out.dtype == np.float32 and out.flags.c_contiguous and out.size >= n
+    lib().synth_normal_f32(seed & 0xFFFFFFFF, stream & 0xFFFFFFFF, offset, n, mean, std, out.ctypes.data, nthreads)
+    return out
+
+
+@dataclass(frozen=True)
+class MoEDims:
+    hidden: int = 2048
+    n_experts: int = 256
+    expert_width: int = 512
+    top_k: int = 6
+    shared_width: int = 1024
+
+
+@dataclass(frozen=True)
+class Workload:
+    """A named workload: sizes and seeds (no method arithmetic)."""
+    name: str
+    dims: MoEDims
+    vocab: int = 150144
+    layers: int = 1
+    weight_seed: int = 0
+    head_seed: int = HEAD_SEED
+    token_seed: int = 0
+
+
+# the workloads this repository measures and tests
+MOE_LAYER_E32 = Workload("moe_layer_e32", MoEDims(n_experts=32))
+MOE_LAYER_E256 = Workload("moe_layer_e256", MoEDims())
+LMHEAD = Workload("lmhead_v150144", MoEDims(), vocab=150144)
+STACK47 = Workload("stack47_lmhead", MoEDims(), vocab=150144, layers=47, token_seed=TOKEN_SEED0)
+STACK47_BATCHED = Workload("stack47_lmhead_batched", MoEDims(), vocab=150144, layers=47, token_seed=BATCH_SEED0)
+
+
+def router_f32(seed: int, dims: MoEDims) -> np.ndarray:
+    return normal(seed, stream_id(ROUTER), dims.n_experts * dims.hidden, std=WEIGHT_STD).reshape(
+        dims.n_experts, dims.hidden)
+
+
+def expert_f32(seed: int, dims: MoEDims, kind: int, expert: int) -> np.ndarray:
+    """One routed expert matrix: gate/up [I][H], down [H][I]."""
+    H, I = dims.hidden, dims.expert_width
+    shape = (H, I) if kind == DOWN else (I, H)
+    return normal(seed, stream_id(kind, expert), H * I, std=WEIGHT_STD).reshape(shape)
+
+
+def shared_f32(seed: int, dims: MoEDims, kind: int) -> np.ndarray:
+    """Shared expert matrix: gate/up [Is][H], down [H][Is]."""
+    H, Is = dims.hidden, dims.shared_width
+    shape = (H, Is) if kind == SHARED_DOWN else (Is, H)
+    return normal(seed, stream_id(kind), H * Is, std=WEIGHT_STD).reshape(shape)
+
+
+def head_f32(seed: int, vocab: int, hidden: int, row0: int = 0, rows: int | None = None) -> np.ndarray:
+    """Rows row0..row0+rows-1 of the output head [vocab][hidden]."""
+    rows = vocab - row0 if rows is None else rows
+    return normal(seed, stream_id(HEAD), rows * hidden, std=WEIGHT_STD, offset=row0 * hidden).reshape(rows, hidden)
+
+
+def token_f32(seed: int, hidden: int) -> np.ndarray:
+    return normal(seed, stream_id(TOKEN), hidden, std=1.0)
