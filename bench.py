@@ -1,0 +1,155 @@
+"""Decode throughput of the 47-layer NVFP4 MoE stack + NVFP4 lm_head at batch 1.
+
+One step = one token through all 47 MoE layers (router top-6 of 256 + shared
+expert, NVFP4 experts) and the 150,144-row NVFP4 head with argmax, on seeded
+synthetic weights resident in HBM.  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(layers_sampled: int = 8) -> dict:
+    """The oracle (plain fp64 CPU code) on a bounded sample of the same
+    workload: one token through the first `layers_sampled` layers plus the
+    full head, weights prepared beforehand; scaled to 47 layers."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from oracle.model import SyntheticWeights, moe_layer
+
+    dims = synth.MoEDims()
+    W = SyntheticWeights(dims, vocab=150144)
+    x = synth.token_f32(synth.TOKEN_SEED0, dims.hidden).astype(np.float64)
+
+    def run():
+        h = x.copy()
+        t_layers = 0.0
+        for l in range(layers_sampled):
+            u = h * oracle.rms_inv(h, 1e-6)
+            t0 = time.perf_counter()
+            r = moe_layer(W, l, u)
+            t_layers += time.perf_counter() - t0
+            h = h + r.y
+        z = h * oracle.rms_inv(h, 1e-6)
+        head = W.head()
+        t0 = time.perf_counter()
+        logits = oracle.nvfp4_gemv(head, z)
+        oracle.argmax(logits)
+        return t_layers, time.perf_counter() - t0
+
+    run()                      # prepares (quantises) every tensor the token touches
+    t_layers, t_head = run()   # timed: pure oracle compute
+    per_token = t_layers * 47.0 / layers_sampled + t_head
+    return {"value": 1.0 / per_token, "unit": "tok/s", "cores": oracle.default_threads(), "kind": "oracle",
+            "sample": f"1 token through {layers_sampled} of 47 layers (scaled x47/{layers_sampled}) + full head; "
+                      f"layers {t_layers:.2f}s, head {t_head:.2f}s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=47)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (batch-1 decode; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import synth
+    from nvfp4_bit_projection_amd import bytes_model as bm
+    from nvfp4_bit_projection_amd import flint, workload
+
+    torch.cuda.set_device(0)
+    dims = synth.MoEDims()
+    L, V = args.layers, 150144
+    t0 = time.time()
+    tmp = torch.empty(dims.n_experts * dims.expert_width * dims.hidden, dtype=torch.float32, device="cuda")
+    layers = []
+    for l in range(L):
+        layers.append(workload.build_layer(dims, seed=l, tmp=tmp))
+    head = workload.build_head(V, dims.hidden, tmp=None)
+    del tmp
+    torch.cuda.synchronize()
+    log(f"weights ready in {time.time() - t0:.1f}s ({torch.cuda.memory_allocated() / 1e9:.1f} GB)")
+    d = flint.dims_struct(dims.hidden, dims.n_experts, dims.expert_width, dims.top_k, dims.shared_width)
+    stack = flint.Stack(d, layers, head, V)
+    T = args.warmup + args.steps
+    x = workload.tokens([synth.TOKEN_SEED0 + t for t in range(T)], dims.hidden)
+    argmax = torch.empty(T, dtype=torch.int32, device="cuda")
+    logits = torch.empty((1, V), dtype=torch.float32, device="cuda")
+
+    def step(t):
+        stack.decode(x[t:t + 1], logits=logits, argmax=argmax[t:t + 1])
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record()
+    for t in range(args.warmup, T):
+        step(t)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1)
+    ms_per_step = ms / args.steps
+    tok_s = 1000.0 / ms_per_step
+    shape = bm.LayerShape()
+    token_bytes = bm.token_bytes(shape, L, V)
+    gbs = token_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"{args.steps} tokens in {ms:.1f} ms (wall {wall * 1e3:.1f} ms): {tok_s:.1f} tok/s, {gbs:.1f} GB/s")
+
+    result = {
+        "metric": "decode tok/s (47-layer NVFP4 MoE+lm_head, batch 1) and achieved HBM GB/s vs peak",
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "stack47_lmhead_b1", "layers": L, "hidden": 2048, "experts": 256, "top_k": 6,
+                   "expert_width": 512, "shared_width": 1024, "vocab": V, "batch": 1,
+                   "weights": "nvfp4 e2m1 + e4m3/16 + fp32 tensor scale; fp32 router"},
+        "achieved_gbs": round(gbs, 1),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "whole decode step (all kernels of one token)",
+                     "bytes_per_launch": token_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

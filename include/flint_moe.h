@@ -1,0 +1,205 @@
+/*
+ * flint_moe.h -- C ABI of the NVFP4 sparse-MoE decode library for AMD MI355X
+ * (gfx950): router top-k, NVFP4 expert projections with SwiGLU and weighted
+ * combine, the NVFP4 output head with argmax, and the whole layer stack.
+ *
+ * The method follows these pages (titles as published, sections named):
+ *  [P3] "Flint: 125 tokens a second is what 2.5B active parameters buy at
+ *       273 GB/s" -- "The shape, read from the headers": hidden size 2,048;
+ *       47 MoE layers, each with 256 routed experts of width 512 of which 6
+ *       are selected per token, plus a shared expert of width 1,024; three
+ *       matrices per expert; untied output head over a 150,144-entry
+ *       vocabulary.  "Why active parameters set the speed": batch-1 decode
+ *       reads every touched weight once per token, so weight bytes set the
+ *       speed; the output head is 4-bit.  "Checking 125 tokens a second":
+ *       NVFP4 holds 4-bit values with one 8-bit scale per 16 values.
+ *  [P2] "Recursive Releases Flint, a 40B MoE Coding Model That Runs Locally
+ *       at 125 Tokens per Second" -- "How does Flint's architecture work?":
+ *       the router selects 6 experts per token, plus 1 always-active shared
+ *       expert.
+ *  [P1] "Flint-40B-A2B: AI-Built MoE Coding Model Hits 125 tok/s on MacBook
+ *       Pro" -- "Quantization with Offline Distillation": the output layer is
+ *       quantised to NVFP4 as well.
+ *
+ * Conventions for every call below
+ *  - Pointers are DEVICE pointers unless marked [host].  The caller owns every
+ *    buffer (weights, activations, outputs, workspace, plan); the library
+ *    allocates nothing and keeps no per-call state.
+ *  - A call validates its arguments on the host first.  On any non-zero
+ *    status nothing has been enqueued and nothing written.  FLINT_OK means
+ *    "enqueued on `stream`" (a hipStream_t; NULL is the default stream);
+ *    results are ready after the caller synchronises with that stream.
+ *  - Workspaces: size from flint_workspace_bytes(); they must be zero-filled
+ *    once before first use (e.g. allocated with torch.zeros) and every
+ *    completed call leaves them zero-filled again.  Calls that may run at the
+ *    same time need distinct workspaces.
+ *  - Alignment: weight codes/scales rows and activation vectors must be
+ *    16-byte aligned (128-bit loads).
+ *  - Inputs must be finite; NaN/Inf inputs give unspecified results.
+ *
+ * NVFP4 matrix W [rows][cols] (the interchange layout; cols is the reduction
+ * axis and a multiple of 32):
+ *    codes  uint8 [rows][cols/2]   E2M1 codes, element 2j in the LOW nibble of
+ *                                  byte j, element 2j+1 in the high nibble;
+ *    scales uint8 [rows][cols/16]  OCP E4M3FN scale of elements 16b..16b+15;
+ *    tscale float [1]              per-tensor fp32 scale S.
+ *  Dequantised value: fl32((e2m1(code) * e4m3(scale)) * S), the first product
+ *  exact.  Each routed expert matrix (gate, up, down of every expert), each
+ *  shared-expert matrix and the head is its own tensor with its own S.
+ */
+#ifndef FLINT_MOE_H
+#define FLINT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define FLINT_OK 0
+#define FLINT_E_NULL (-1)        /* a required pointer is NULL */
+#define FLINT_E_DIMS (-2)        /* a size is out of range */
+#define FLINT_E_ALIGN (-3)       /* a pointer is not 16-byte aligned */
+#define FLINT_E_WORKSPACE (-4)   /* workspace or plan buffer too small */
+#define FLINT_E_DEVICE (-5)      /* current device is not gfx950 */
+#define FLINT_E_HIP (-6)         /* a HIP call failed; see flint_last_hip_error() */
+#define FLINT_E_INTERNAL (-7)    /* a device-side wait gave up (watchdog) in an earlier call */
+#define FLINT_E_UNSUPPORTED (-8) /* valid sizes this build has no kernel for */
+
+/* MoE layer sizes.  Supported: hidden == 2048; 1 <= top_k <= 8;
+ * top_k <= n_experts <= 256; expert_width and shared_width multiples of 32,
+ * 32..2048 each. */
+typedef struct {
+  int32_t hidden;       /* H: 2048 */
+  int32_t n_experts;    /* E: 256 (32 in the reduced layer) */
+  int32_t expert_width; /* I: 512 */
+  int32_t top_k;        /* k: 6 */
+  int32_t shared_width; /* Is: 1024 */
+} flint_moe_dims;
+
+/* one NVFP4 matrix (device pointers; tscale points at one float) */
+typedef struct {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* tscale;
+} flint_nvfp4;
+
+/* one MoE layer.  Routed experts are stacked along the first axis:
+ *   router        float [E][H]            unquantised
+ *   gate/up codes uint8 [E][I][H/2], scales [E][I][H/16]
+ *   down codes    uint8 [E][H][I/2], scales [E][H][I/16]
+ *   expert_tscales float [E][3]           S of gate, up, down of each expert
+ *   shared_gate/up [Is][H], shared_down [H][Is]                              */
+typedef struct {
+  const float* router;
+  const uint8_t* gate_codes;
+  const uint8_t* gate_scales;
+  const uint8_t* up_codes;
+  const uint8_t* up_scales;
+  const uint8_t* down_codes;
+  const uint8_t* down_scales;
+  const float* expert_tscales;
+  flint_nvfp4 shared_gate;
+  flint_nvfp4 shared_up;
+  flint_nvfp4 shared_down;
+} flint_moe_layer;
+
+/* operation ids for flint_workspace_bytes */
+#define FLINT_OP_ROUTE 1
+#define FLINT_OP_DECODE 2
+#define FLINT_OP_LMHEAD 3
+#define FLINT_OP_STACK 4
+#define FLINT_OP_QUANTIZE 5
+
+/* Bytes of workspace `op` needs for batch B (tokens), vocabulary `vocab`
+ * (lmhead/stack) and L layers (stack); 0 if the arguments are invalid. */
+size_t flint_workspace_bytes(int32_t op, const flint_moe_dims* dims /*[host], may be NULL for LMHEAD/QUANTIZE*/,
+                             int32_t B, int32_t vocab, int32_t L);
+
+/* Router and top-k [P2 "How does Flint's architecture work?"; P3 "The shape,
+ * read from the headers"]: for each of B tokens x_b (float [B][H]):
+ *   logits_e = sum_k router[e][k] * x_b[k]   (fp32 router, fp32 arithmetic);
+ *   topk_idx[b][0..k) = the k largest logits, ordered by (logit descending,
+ *                       expert index ascending);
+ *   topk_w[b][i] = exp(l_i - l_0) / sum_j exp(l_j - l_0) over the chosen k
+ *                  (the softmax over all E renormalised to the chosen set).
+ * logits_opt (float [B][E]) receives the logits when non-NULL. */
+int32_t flint_moe_route(const flint_moe_dims* dims /*[host]*/, const float* router, const float* x, int32_t B,
+                        int32_t* topk_idx, float* topk_w, float* logits_opt, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/* One MoE layer for B tokens (float [B][H]), no norm and no residual:
+ *   y_b = sum_i topk_w[b][i] * E_{topk_idx[b][i]}(x_b) + Shared(x_b),
+ * where each expert is SwiGLU: E(x) = Wdown (silu(Wgate x) * (Wup x)), silu
+ * on the first (gate) matrix, all three matrices NVFP4 [P3 "The shape, read
+ * from the headers": three matrices per expert].  The shared expert has
+ * weight 1.  topk_idx_opt / topk_w_opt (int32/float [B][k]) receive the
+ * routing when non-NULL.  y is float [B][H]. */
+int32_t flint_moe_decode(const flint_moe_dims* dims /*[host]*/, const flint_moe_layer* layer /*[host]*/,
+                         const float* x, int32_t B, float* y, int32_t* topk_idx_opt, float* topk_w_opt, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* NVFP4 output head [P1 "Quantization with Offline Distillation"; P3 "Why
+ * active parameters set the speed"]: logits[b][v] = sum_k Wdeq[v][k] x[b][k]
+ * for head W [vocab][hidden], x float [B][hidden]; argmax[b] = first index
+ * of the largest logit (int32).  hidden must be 2048; vocab >= 1. */
+int32_t flint_lmhead_gemv(const flint_nvfp4* head /*[host]*/, int32_t vocab, int32_t hidden, const float* x, int32_t B,
+                          float* logits, int32_t* argmax, void* ws, size_t ws_bytes, void* stream);
+
+/* Decode stack [P2 "How does Flint's architecture work?": 47 MoE layers; P3
+ * "The shape, read from the headers": norms in the body].  For each of T
+ * tokens, strictly one after the other (batch 1: token t+1 starts after
+ * token t has produced its argmax):
+ *   h_0 = x_t;  h_{l+1} = h_l + MoE_l(h_l / sqrt(mean(h_l^2) + eps))  (l < L);
+ *   logits_t = Head(h_L / sqrt(mean(h_L^2) + eps));  argmax_t.
+ *
+ * flint_stack_prepare copies the layers' pointer table into `table`, a device
+ * buffer of flint_stack_table_bytes(L) bytes, and fills the host-side plan.
+ * The plan keeps `layers` (the caller's host array) and `table`; both, and
+ * every weight they point at, must stay valid while calls that use the plan
+ * run.  flint_stack_decode: x float [T][H]; logits float [T][vocab] (may be
+ * NULL: only argmax is written); argmax int32 [T]; routes_opt int32
+ * [T][L][k] receives every layer's chosen experts (ordered by logit
+ * descending) when non-NULL. */
+typedef struct {
+  flint_moe_dims dims;
+  int32_t n_layers;
+  int32_t vocab;
+  flint_nvfp4 head;
+  const flint_moe_layer* layers; /* [host] caller's array of n_layers */
+  const void* table;             /* device copy of the layer table */
+} flint_stack_plan;
+
+size_t flint_stack_table_bytes(int32_t L);
+int32_t flint_stack_prepare(const flint_moe_dims* dims /*[host]*/, const flint_moe_layer* layers /*[host] array of L*/,
+                            int32_t L, const flint_nvfp4* head /*[host]*/, int32_t vocab, void* table,
+                            size_t table_bytes, flint_stack_plan* plan /*[host], out*/, void* stream);
+int32_t flint_stack_decode(const flint_stack_plan* plan /*[host]*/, const float* x, int32_t T, float eps, float* logits,
+                           int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes, void* stream);
+
+/* NVFP4 quantiser (device): quantises n_mats independent matrices stacked in
+ * w (float [n_mats][rows][cols], cols a multiple of 32) into codes
+ * [n_mats][rows][cols/2], scales [n_mats][rows][cols/16] and tscales
+ * [n_mats].  Per matrix: S = fl32(max|w| / 2688); block scale = E4M3
+ * round-to-nearest-even of blockmax / (6 S), saturating at 448; code = E2M1
+ * round-to-nearest-even of w / (d S), saturating at 6, sign kept (also for
+ * values that round to zero); a block whose scale is 0 gets all-zero codes;
+ * an all-zero matrix gets S = 0.  Ratios are computed in double precision.
+ * [P3 "Checking 125 tokens a second": 4-bit values, one 8-bit scale per 16.] */
+int32_t flint_nvfp4_quantize(const float* w, int64_t n_mats, int64_t rows, int64_t cols, uint8_t* codes,
+                             uint8_t* scales, float* tscales, void* ws, size_t ws_bytes, void* stream);
+
+/* Dequantise an NVFP4 matrix to float [rows][cols] (the exact values above). */
+int32_t flint_nvfp4_dequantize(const flint_nvfp4* w /*[host]*/, int64_t rows, int64_t cols, float* out, void* stream);
+
+/* Human-readable status; the last hipError_t seen by a failing call (0 if none). */
+const char* flint_status_str(int32_t status);
+int32_t flint_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLINT_MOE_H */

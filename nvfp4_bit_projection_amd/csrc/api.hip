@@ -1,0 +1,281 @@
+// api.hip -- the C ABI (include/flint_moe.h): argument validation, workspace
+// carving and kernel launches.  Every check runs on the host before anything
+// is enqueued, so a failing call leaves all buffers untouched.
+#include <atomic>
+#include <string.h>
+
+#include "flint_internal.h"
+
+using namespace flint;
+
+namespace {
+
+std::atomic<int32_t> g_last_hip_error{0};
+std::atomic<int32_t> g_device_ok[64];  // 0 unknown, 1 gfx950, -1 other
+
+int32_t hip_fail(hipError_t e) {
+  g_last_hip_error.store((int32_t)e);
+  return FLINT_E_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int32_t check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= 64) return FLINT_E_DEVICE;
+  int st = g_device_ok[dev].load();
+  if (st == 0) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    st = (strncmp(p.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_device_ok[dev].store(st);
+  }
+  return st == 1 ? FLINT_OK : FLINT_E_DEVICE;
+}
+
+int32_t check_dims(const flint_moe_dims* d) {
+  if (!d) return FLINT_E_NULL;
+  if (d->hidden < 32 || d->hidden % 32 || d->top_k < 1 || d->top_k > kMaxTopK || d->n_experts < d->top_k ||
+      d->n_experts > kMaxExperts || d->expert_width < 32 || d->expert_width % 32 || d->expert_width > 2048 ||
+      d->shared_width < 32 || d->shared_width % 32 || d->shared_width > 2048)
+    return FLINT_E_DIMS;
+  if (d->hidden != kHidden) return FLINT_E_UNSUPPORTED;
+  if (d->top_k * d->expert_width + d->shared_width > kMaxKdown) return FLINT_E_UNSUPPORTED;
+  return FLINT_OK;
+}
+
+int32_t check_nvfp4(const flint_nvfp4* q) {
+  if (!q || !q->codes || !q->scales || !q->tscale) return FLINT_E_NULL;
+  if (!aligned16(q->codes) || !aligned4(q->scales) || !aligned4(q->tscale)) return FLINT_E_ALIGN;
+  return FLINT_OK;
+}
+
+int32_t check_layer(const flint_moe_layer* L) {
+  if (!L) return FLINT_E_NULL;
+  if (!L->router || !L->gate_codes || !L->gate_scales || !L->up_codes || !L->up_scales || !L->down_codes ||
+      !L->down_scales || !L->expert_tscales)
+    return FLINT_E_NULL;
+  if (!aligned16(L->router) || !aligned16(L->gate_codes) || !aligned16(L->up_codes) || !aligned16(L->down_codes) ||
+      !aligned4(L->gate_scales) || !aligned4(L->up_scales) || !aligned4(L->down_scales) || !aligned4(L->expert_tscales))
+    return FLINT_E_ALIGN;
+  int32_t st;
+  if ((st = check_nvfp4(&L->shared_gate)) || (st = check_nvfp4(&L->shared_up)) || (st = check_nvfp4(&L->shared_down)))
+    return st;
+  return FLINT_OK;
+}
+
+template <typename T>
+T* carve(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+}  // namespace
+
+extern "C" {
+
+const char* flint_status_str(int32_t s) {
+  switch (s) {
+    case FLINT_OK: return "ok";
+    case FLINT_E_NULL: return "a required pointer is NULL";
+    case FLINT_E_DIMS: return "a size is out of range";
+    case FLINT_E_ALIGN: return "a pointer is not 16-byte aligned";
+    case FLINT_E_WORKSPACE: return "workspace or table buffer too small";
+    case FLINT_E_DEVICE: return "current device is not gfx950";
+    case FLINT_E_HIP: return "a HIP call failed";
+    case FLINT_E_INTERNAL: return "a device-side wait gave up in an earlier call";
+    case FLINT_E_UNSUPPORTED: return "sizes not supported by this build";
+    default: return "unknown status";
+  }
+}
+
+int32_t flint_last_hip_error(void) { return g_last_hip_error.load(); }
+
+size_t flint_workspace_bytes(int32_t op, const flint_moe_dims* dims, int32_t B, int32_t vocab, int32_t L) {
+  (void)L;
+  if (B < 1) return 0;
+  switch (op) {
+    case FLINT_OP_ROUTE:
+      if (check_dims(dims) != FLINT_OK) return 0;
+      return RouteWs(dims->n_experts, B).total;
+    case FLINT_OP_DECODE:
+      if (check_dims(dims) != FLINT_OK) return 0;
+      return DecodeWs(*dims, B).total;
+    case FLINT_OP_LMHEAD:
+      if (vocab < 1) return 0;
+      return HeadWs(B).total;
+    case FLINT_OP_STACK:
+      if (check_dims(dims) != FLINT_OK || vocab < 1) return 0;
+      return StackWs(*dims, vocab).total;
+    case FLINT_OP_QUANTIZE:  // B = number of matrices
+      return align_up(4 * (size_t)B, 256);
+    default:
+      return 0;
+  }
+}
+
+int32_t flint_moe_route(const flint_moe_dims* dims, const float* router, const float* x, int32_t B, int32_t* topk_idx,
+                        float* topk_w, float* logits_opt, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st;
+  if ((st = check_dims(dims))) return st;
+  if (!router || !x || !topk_idx || !topk_w || !ws) return FLINT_E_NULL;
+  if (B < 1) return FLINT_E_DIMS;
+  if (!aligned16(router) || !aligned16(x) || !aligned4(topk_idx) || !aligned4(topk_w) || !aligned16(ws) ||
+      (logits_opt && !aligned4(logits_opt)))
+    return FLINT_E_ALIGN;
+  RouteWs rw(dims->n_experts, B);
+  if (ws_bytes < rw.total) return FLINT_E_WORKSPACE;
+  if ((st = check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  float* logits = logits_opt ? logits_opt : carve<float>(ws, rw.logits);
+  hipError_t e = launch_route(*dims, router, x, B, -1.0f, logits, topk_idx, topk_w, carve<uint32_t>(ws, rw.tickets), s);
+  return e == hipSuccess ? FLINT_OK : hip_fail(e);
+}
+
+static int32_t decode_impl(const flint_moe_dims& d, const flint_moe_layer& L, const float* x, int B, float norm_eps,
+                           float* y, bool add_to_y, int32_t* idx, float* w, void* ws, hipStream_t s) {
+  DecodeWs dw(d, B);
+  RouteWs rw(d.n_experts, B);
+  char* base = static_cast<char*>(ws);
+  float* logits = carve<float>(base + dw.route, rw.logits);
+  uint32_t* tickets = carve<uint32_t>(base + dw.route, rw.tickets);
+  float* hact = carve<float>(ws, dw.hact);
+  hipError_t e = launch_route(d, L.router, x, B, norm_eps, logits, idx, w, tickets, s);
+  if (e == hipSuccess) e = launch_gateup(d, L, x, B, norm_eps, idx, hact, s);
+  if (e == hipSuccess) e = launch_down(d, L, idx, w, hact, B, y, add_to_y, s);
+  return e == hipSuccess ? FLINT_OK : hip_fail(e);
+}
+
+int32_t flint_moe_decode(const flint_moe_dims* dims, const flint_moe_layer* layer, const float* x, int32_t B, float* y,
+                         int32_t* topk_idx_opt, float* topk_w_opt, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st;
+  if ((st = check_dims(dims))) return st;
+  if ((st = check_layer(layer))) return st;
+  if (!x || !y || !ws) return FLINT_E_NULL;
+  if (B < 1) return FLINT_E_DIMS;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(ws) || (topk_idx_opt && !aligned4(topk_idx_opt)) ||
+      (topk_w_opt && !aligned4(topk_w_opt)))
+    return FLINT_E_ALIGN;
+  DecodeWs dw(*dims, B);
+  if (ws_bytes < dw.total) return FLINT_E_WORKSPACE;
+  if ((st = check_device())) return st;
+  int32_t* idx = topk_idx_opt ? topk_idx_opt : carve<int32_t>(ws, dw.idx);
+  float* w = topk_w_opt ? topk_w_opt : carve<float>(ws, dw.wts);
+  return decode_impl(*dims, *layer, x, B, -1.0f, y, false, idx, w, ws, (hipStream_t)stream);
+}
+
+int32_t flint_lmhead_gemv(const flint_nvfp4* head, int32_t vocab, int32_t hidden, const float* x, int32_t B,
+                          float* logits, int32_t* argmax, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st;
+  if ((st = check_nvfp4(head))) return st;
+  if (!x || !logits || !argmax || !ws) return FLINT_E_NULL;
+  if (vocab < 1 || B < 1 || hidden < 32 || hidden % 32) return FLINT_E_DIMS;
+  if (hidden != kHidden) return FLINT_E_UNSUPPORTED;
+  if (!aligned16(x) || !aligned4(logits) || !aligned4(argmax) || !aligned16(ws)) return FLINT_E_ALIGN;
+  HeadWs hw(B);
+  if (ws_bytes < hw.total) return FLINT_E_WORKSPACE;
+  if ((st = check_device())) return st;
+  hipError_t e = launch_lmhead(*head, vocab, x, B, -1.0f, logits, argmax, carve<HeadPartial>(ws, hw.partials),
+                               carve<uint32_t>(ws, hw.tickets), (hipStream_t)stream);
+  return e == hipSuccess ? FLINT_OK : hip_fail(e);
+}
+
+size_t flint_stack_table_bytes(int32_t L) { return L < 1 ? 0 : stack_table_bytes(L); }
+
+int32_t flint_stack_prepare(const flint_moe_dims* dims, const flint_moe_layer* layers, int32_t L,
+                            const flint_nvfp4* head, int32_t vocab, void* table, size_t table_bytes,
+                            flint_stack_plan* plan, void* stream) {
+  int32_t st;
+  if ((st = check_dims(dims))) return st;
+  if (!layers || !head || !table || !plan) return FLINT_E_NULL;
+  if (L < 1 || vocab < 1) return FLINT_E_DIMS;
+  for (int l = 0; l < L; ++l)
+    if ((st = check_layer(&layers[l]))) return st;
+  if ((st = check_nvfp4(head))) return st;
+  if (!aligned16(table)) return FLINT_E_ALIGN;
+  if (table_bytes < stack_table_bytes(L)) return FLINT_E_WORKSPACE;
+  if ((st = check_device())) return st;
+  // build the table on the host, then one copy; the copy completes before
+  // this call returns, so the host buffer may be freed right after.
+  const size_t nb = stack_table_bytes(L);
+  char* host = new char[nb];
+  StackTable* t = reinterpret_cast<StackTable*>(host);
+  t->head = *head;
+  memcpy(t->layers, layers, sizeof(flint_moe_layer) * (size_t)L);
+  hipError_t e = hipMemcpyAsync(table, host, nb, hipMemcpyHostToDevice, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  delete[] host;
+  if (e != hipSuccess) return hip_fail(e);
+  plan->dims = *dims;
+  plan->n_layers = L;
+  plan->vocab = vocab;
+  plan->head = *head;
+  plan->layers = layers;
+  plan->table = table;
+  return FLINT_OK;
+}
+
+int32_t flint_stack_decode(const flint_stack_plan* plan, const float* x, int32_t T, float eps, float* logits,
+                           int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st;
+  if (!plan || !x || !argmax || !ws) return FLINT_E_NULL;
+  if ((st = check_dims(&plan->dims))) return st;
+  if (!plan->layers || !plan->table) return FLINT_E_NULL;
+  if (T < 1 || plan->n_layers < 1 || plan->vocab < 1 || !(eps > 0.0f)) return FLINT_E_DIMS;
+  if (!aligned16(x) || !aligned16(ws) || !aligned4(argmax) || (logits && !aligned4(logits)) ||
+      (routes_opt && !aligned4(routes_opt)))
+    return FLINT_E_ALIGN;
+  const flint_moe_dims& d = plan->dims;
+  StackWs sw(d, plan->vocab);
+  if (ws_bytes < sw.total) return FLINT_E_WORKSPACE;
+  if ((st = check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = static_cast<char*>(ws);
+  float* h = carve<float>(ws, sw.h);
+  void* dws = base + sw.decode;
+  DecodeWs dw(d, 1);
+  HeadWs hw(1);
+  const int L = plan->n_layers, k = d.top_k;
+  for (int t = 0; t < T; ++t) {
+    hipError_t e = launch_copy_f32(x + (size_t)t * kHidden, h, kHidden, s);
+    if (e != hipSuccess) return hip_fail(e);
+    for (int l = 0; l < L; ++l) {
+      int32_t* idx = routes_opt ? routes_opt + ((size_t)t * L + l) * k : carve<int32_t>(dws, dw.idx);
+      st = decode_impl(d, plan->layers[l], h, 1, eps, h, true, idx, carve<float>(dws, dw.wts), dws, s);
+      if (st) return st;
+    }
+    e = launch_lmhead(plan->head, plan->vocab, h, 1, eps, logits ? logits + (size_t)t * plan->vocab : nullptr,
+                      argmax + t, carve<HeadPartial>(base + sw.head, hw.partials),
+                      carve<uint32_t>(base + sw.head, hw.tickets), s);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return FLINT_OK;
+}
+
+int32_t flint_nvfp4_quantize(const float* w, int64_t n_mats, int64_t rows, int64_t cols, uint8_t* codes,
+                             uint8_t* scales, float* tscales, void* ws, size_t ws_bytes, void* stream) {
+  if (!w || !codes || !scales || !tscales || !ws) return FLINT_E_NULL;
+  if (n_mats < 1 || rows < 1 || cols < 32 || cols % 32) return FLINT_E_DIMS;
+  if (!aligned16(w) || !aligned16(codes) || !aligned4(scales) || !aligned4(tscales) || !aligned16(ws))
+    return FLINT_E_ALIGN;
+  if (n_mats > (int64_t)1 << 30 || ws_bytes < align_up(4 * (size_t)n_mats, 256)) return FLINT_E_WORKSPACE;
+  int32_t st;
+  if ((st = check_device())) return st;
+  hipError_t e = launch_quantize(w, n_mats, rows, cols, codes, scales, tscales, carve<uint32_t>(ws, 0),
+                                 (hipStream_t)stream);
+  return e == hipSuccess ? FLINT_OK : hip_fail(e);
+}
+
+int32_t flint_nvfp4_dequantize(const flint_nvfp4* q, int64_t rows, int64_t cols, float* out, void* stream) {
+  int32_t st;
+  if ((st = check_nvfp4(q))) return st;
+  if (!out) return FLINT_E_NULL;
+  if (rows < 1 || cols < 32 || cols % 32) return FLINT_E_DIMS;
+  if (!aligned16(out)) return FLINT_E_ALIGN;
+  if ((st = check_device())) return st;
+  hipError_t e = launch_dequantize(*q, rows, cols, out, (hipStream_t)stream);
+  return e == hipSuccess ? FLINT_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// flint_device.h -- gfx950 device building blocks shared by the kernels of this
+// library: NVFP4 decode in registers, wave reductions, cross-workgroup stores.
+//
+// NVFP4 as used here [P3 "Flint: 125 tokens a second is what 2.5B active
+// parameters buy at 273 GB/s", "Checking 125 tokens a second": 4-bit values,
+// one 8-bit scale per 16 values]: E2M1 element codes, one OCP E4M3FN scale per
+// 16 elements along the reduction axis, one fp32 scale per tensor.
+//
+// Lane layout of every NVFP4 dot product: a lane owns 32 consecutive elements
+// of a row, i.e. one 16-byte load of codes (two blocks) and one 2-byte load of
+// scales; 64 lanes cover a 2,048-wide row with a single 128-bit load each.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace flint {
+
+constexpr int kWave = 64;
+
+// OCP E4M3FN byte -> float (gfx950 converts OCP FP8 in hardware).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8(byte, 0);
+}
+
+// sum_j e2m1(code_j) * x[j] over the 8 codes of one 32-bit word (element 2i in
+// the low nibble of byte i).  The hardware conversion takes a power-of-two
+// scale; 1.0 leaves the E2M1 values unchanged.
+__device__ __forceinline__ float fp4x8_dot(uint32_t w, const float* x, float acc) {
+  auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  acc = __builtin_fmaf(v0[0], x[0], acc);
+  acc = __builtin_fmaf(v0[1], x[1], acc);
+  acc = __builtin_fmaf(v1[0], x[2], acc);
+  acc = __builtin_fmaf(v1[1], x[3], acc);
+  acc = __builtin_fmaf(v2[0], x[4], acc);
+  acc = __builtin_fmaf(v2[1], x[5], acc);
+  acc = __builtin_fmaf(v3[0], x[6], acc);
+  acc = __builtin_fmaf(v3[1], x[7], acc);
+  return acc;
+}
+
+// the 8 E2M1 values of one 32-bit word, element order as stored
+__device__ __forceinline__ void fp4x8_values(uint32_t w, float* v) {
+  auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  v[0] = v0[0]; v[1] = v0[1]; v[2] = v1[0]; v[3] = v1[1];
+  v[4] = v2[0]; v[5] = v2[1]; v[6] = v3[0]; v[7] = v3[1];
+}
+
+// One lane's share of an NVFP4 row dot product: 32 elements = codes c (two
+// 16-element blocks) with block scales sc (low byte = first block) against
+// x[0..31].  Returns d0 * dot(block0) + d1 * dot(block1) (tensor scale not
+// applied).
+__device__ __forceinline__ float nvfp4_lane_dot32(uint4 c, uint32_t sc, const float* x) {
+  float a0 = fp4x8_dot(c.x, x + 0, 0.0f);
+  a0 = fp4x8_dot(c.y, x + 8, a0);
+  float a1 = fp4x8_dot(c.z, x + 16, 0.0f);
+  a1 = fp4x8_dot(c.w, x + 24, a1);
+  return e4m3_to_f32(sc & 0xFF) * a0 + e4m3_to_f32((sc >> 8) & 0xFF) * a1;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// sum over groups of `width` consecutive lanes (width a power of two <= 64)
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// (value, index) maximum with ties to the lower index, over the wave.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float ov = __shfl_xor(v, o, kWave);
+    int oi = __shfl_xor(i, o, kWave);
+    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+  }
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// Device-scope (all XCDs) relaxed accesses: the store writes through to the
+// coherence point, the load bypasses the non-coherent per-XCD L2.
+__device__ __forceinline__ void st_dev_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev_u32(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev_f32(float* p, float v) { st_dev_u32(reinterpret_cast<uint32_t*>(p), __float_as_uint(v)); }
+__device__ __forceinline__ float ld_dev_f32(const float* p) {
+  return __uint_as_float(ld_dev_u32(reinterpret_cast<const uint32_t*>(p)));
+}
+
+}  // namespace flint

@@ -1,0 +1,96 @@
+// flint_internal.h -- host-side declarations shared by the C-ABI layer and the
+// kernel launchers: dims, workspace layout, launch entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/flint_moe.h"
+
+namespace flint {
+
+constexpr int kHidden = 2048;    // the only hidden size with kernels
+constexpr int kMaxTopK = 8;
+constexpr int kMaxExperts = 256;
+constexpr int kMaxKdown = 4096;  // top_k * expert_width + shared_width
+constexpr int kHeadBlocks = 1024;  // workgroups of the head GEMV (argmax partials)
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// argmax partial of one head workgroup
+struct HeadPartial {
+  float value;
+  int32_t index;
+};
+
+// Workspace layouts.  Every section starts on a 256-byte boundary.
+struct RouteWs {
+  size_t tickets, logits, total;
+  RouteWs(int E, int B) {
+    size_t o = 0;
+    tickets = o; o = align_up(o + 4 * (size_t)B, 256);
+    logits = o; o = align_up(o + 4 * (size_t)B * E, 256);
+    total = o;
+  }
+};
+
+struct DecodeWs {
+  size_t route, idx, wts, hact, total;
+  DecodeWs(const flint_moe_dims& d, int B) {
+    RouteWs r(d.n_experts, B);
+    size_t o = 0;
+    route = o; o = align_up(o + r.total, 256);
+    idx = o; o = align_up(o + 4 * (size_t)B * d.top_k, 256);
+    wts = o; o = align_up(o + 4 * (size_t)B * d.top_k, 256);
+    hact = o; o = align_up(o + 4 * (size_t)B * (d.top_k * d.expert_width + d.shared_width), 256);
+    total = o;
+  }
+};
+
+struct HeadWs {
+  size_t tickets, partials, total;
+  explicit HeadWs(int B) {
+    size_t o = 0;
+    tickets = o; o = align_up(o + 4 * (size_t)B, 256);
+    partials = o; o = align_up(o + sizeof(HeadPartial) * (size_t)B * kHeadBlocks, 256);
+    total = o;
+  }
+};
+
+struct StackWs {
+  size_t h, decode, head, total;
+  StackWs(const flint_moe_dims& d, int vocab) {
+    (void)vocab;
+    DecodeWs dw(d, 1);
+    HeadWs hw(1);
+    size_t o = 0;
+    h = o; o = align_up(o + 4 * (size_t)d.hidden, 256);
+    decode = o; o = align_up(o + dw.total, 256);
+    head = o; o = align_up(o + hw.total, 256);
+    total = o;
+  }
+};
+
+// Device-side table of the layer stack: the head, then the layers.
+struct StackTable {
+  flint_nvfp4 head;
+  flint_moe_layer layers[1];  // n_layers entries
+};
+inline size_t stack_table_bytes(int L) { return sizeof(StackTable) + sizeof(flint_moe_layer) * (size_t)(L > 1 ? L - 1 : 0); }
+
+// ---- kernel launchers (kernels.hip); all return the hipError_t of the launch
+hipError_t launch_route(const flint_moe_dims& d, const float* router, const float* x, int B, float norm_eps,
+                        float* logits, int32_t* idx, float* w, uint32_t* tickets, hipStream_t s);
+hipError_t launch_gateup(const flint_moe_dims& d, const flint_moe_layer& L, const float* x, int B, float norm_eps,
+                         const int32_t* idx, float* hact, hipStream_t s);
+hipError_t launch_down(const flint_moe_dims& d, const flint_moe_layer& L, const int32_t* idx, const float* w,
+                       const float* hact, int B, float* y, bool add_to_y, hipStream_t s);
+hipError_t launch_lmhead(const flint_nvfp4& head, int vocab, const float* x, int B, float norm_eps, float* logits,
+                         int32_t* argmax, HeadPartial* partials, uint32_t* tickets, hipStream_t s);
+hipError_t launch_quantize(const float* w, int64_t n_mats, int64_t rows, int64_t cols, uint8_t* codes,
+                           uint8_t* scales, float* tscales, uint32_t* amax_bits, hipStream_t s);
+hipError_t launch_dequantize(const flint_nvfp4& q, int64_t rows, int64_t cols, float* out, hipStream_t s);
+hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s);
+
+}  // namespace flint

@@ -1,0 +1,255 @@
+"""Thin Python binding of the C ABI in ``include/flint_moe.h``.
+
+Argument marshalling only: torch tensors provide device memory and the current
+HIP stream; every step of the computation runs in the HIP kernels of
+``libflint_moe.so``.  The library must have been built (``__graft_entry__.build()``
+or ``nvfp4_bit_projection_amd.build.build_library()``); importing this module
+without it raises, and there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+from .build import LIB_PATH
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+OP_ROUTE, OP_DECODE, OP_LMHEAD, OP_STACK, OP_QUANTIZE = 1, 2, 3, 4, 5
+
+
+class FlintError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({_lib.flint_status_str(status).decode()}), "
+                         f"hip error {_lib.flint_last_hip_error()}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("hidden", _I32), ("n_experts", _I32), ("expert_width", _I32), ("top_k", _I32),
+                ("shared_width", _I32)]
+
+
+class NVFP4(ctypes.Structure):
+    _fields_ = [("codes", _P), ("scales", _P), ("tscale", _P)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("router", _P), ("gate_codes", _P), ("gate_scales", _P), ("up_codes", _P), ("up_scales", _P),
+                ("down_codes", _P), ("down_scales", _P), ("expert_tscales", _P), ("shared_gate", NVFP4),
+                ("shared_up", NVFP4), ("shared_down", NVFP4)]
+
+
+class StackPlan(ctypes.Structure):
+    _fields_ = [("dims", Dims), ("n_layers", _I32), ("vocab", _I32), ("head", NVFP4), ("layers", _P),
+                ("table", _P)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH)
+    sigs = {
+        "flint_status_str": ([_I32], ctypes.c_char_p),
+        "flint_last_hip_error": ([], _I32),
+        "flint_workspace_bytes": ([_I32, ctypes.POINTER(Dims), _I32, _I32, _I32], _SZ),
+        "flint_moe_route": ([ctypes.POINTER(Dims), _P, _P, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
+        "flint_moe_decode": ([ctypes.POINTER(Dims), ctypes.POINTER(Layer), _P, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
+        "flint_lmhead_gemv": ([ctypes.POINTER(NVFP4), _I32, _I32, _P, _I32, _P, _P, _P, _SZ, _P], _I32),
+        "flint_stack_table_bytes": ([_I32], _SZ),
+        "flint_stack_prepare": ([ctypes.POINTER(Dims), ctypes.POINTER(Layer), _I32, ctypes.POINTER(NVFP4), _I32, _P,
+                                 _SZ, ctypes.POINTER(StackPlan), _P], _I32),
+        "flint_stack_decode": ([ctypes.POINTER(StackPlan), _P, _I32, ctypes.c_float, _P, _P, _P, _P, _SZ, _P], _I32),
+        "flint_nvfp4_quantize": ([_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _I32),
+        "flint_nvfp4_dequantize": ([ctypes.POINTER(NVFP4), _I64, _I64, _P, _P], _I32),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    return L
+
+
+_lib = _load()
+
+# every symbol include/flint_moe.h declares
+EXPORTED = ("flint_status_str", "flint_last_hip_error", "flint_workspace_bytes", "flint_moe_route",
+            "flint_moe_decode", "flint_lmhead_gemv", "flint_stack_table_bytes", "flint_stack_prepare",
+            "flint_stack_decode", "flint_nvfp4_quantize", "flint_nvfp4_dequantize")
+
+
+def lib():
+    return _lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise FlintError(status, what)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def dims_struct(hidden=2048, n_experts=256, expert_width=512, top_k=6, shared_width=1024) -> Dims:
+    return Dims(hidden, n_experts, expert_width, top_k, shared_width)
+
+
+def workspace_bytes(op: int, dims: Dims | None, B: int = 1, vocab: int = 0, L: int = 0) -> int:
+    return _lib.flint_workspace_bytes(op, ctypes.byref(dims) if dims is not None else None, B, vocab, L)
+
+
+def workspace(op: int, dims: Dims | None, B: int = 1, vocab: int = 0, L: int = 0, device="cuda") -> torch.Tensor:
+    n = workspace_bytes(op, dims, B, vocab, L)
+    if n == 0:
+        raise ValueError("invalid workspace request")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------ weight holders --
+@dataclass
+class NVFP4Tensor:
+    """codes uint8 [..., rows, cols/2], scales uint8 [..., rows, cols/16], tscale float32 [...]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tscale: torch.Tensor
+
+    def c(self, index: int | None = None) -> NVFP4:
+        if index is None:
+            return NVFP4(self.codes.data_ptr(), self.scales.data_ptr(), self.tscale.data_ptr())
+        return NVFP4(self.codes[index].data_ptr(), self.scales[index].data_ptr(), self.tscale[index].data_ptr())
+
+
+@dataclass
+class LayerWeights:
+    router: torch.Tensor          # float32 [E][H]
+    gate_codes: torch.Tensor      # uint8 [E][I][H/2]
+    gate_scales: torch.Tensor     # uint8 [E][I][H/16]
+    up_codes: torch.Tensor
+    up_scales: torch.Tensor
+    down_codes: torch.Tensor      # uint8 [E][H][I/2]
+    down_scales: torch.Tensor     # uint8 [E][H][I/16]
+    expert_tscales: torch.Tensor  # float32 [E][3]
+    shared_gate: NVFP4Tensor
+    shared_up: NVFP4Tensor
+    shared_down: NVFP4Tensor
+
+    def c(self) -> Layer:
+        return Layer(self.router.data_ptr(), self.gate_codes.data_ptr(), self.gate_scales.data_ptr(),
+                     self.up_codes.data_ptr(), self.up_scales.data_ptr(), self.down_codes.data_ptr(),
+                     self.down_scales.data_ptr(), self.expert_tscales.data_ptr(), self.shared_gate.c(),
+                     self.shared_up.c(), self.shared_down.c())
+
+
+# --------------------------------------------------------------- operations --
+def quantize(w: torch.Tensor) -> NVFP4Tensor:
+    """w float32 cuda [n_mats, rows, cols] (or [rows, cols]) -> NVFP4 per matrix."""
+    squeeze = w.dim() == 2
+    if squeeze:
+        w = w.unsqueeze(0)
+    n, rows, cols = w.shape
+    w = w.contiguous()
+    codes = torch.empty((n, rows, cols // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((n, rows, cols // 16), dtype=torch.uint8, device=w.device)
+    ts = torch.empty(n, dtype=torch.float32, device=w.device)
+    ws = workspace(OP_QUANTIZE, None, B=n, device=w.device)
+    _check(_lib.flint_nvfp4_quantize(w.data_ptr(), n, rows, cols, codes.data_ptr(), scales.data_ptr(),
+                                     ts.data_ptr(), ws.data_ptr(), ws.numel(), _stream()), "flint_nvfp4_quantize")
+    if squeeze:
+        return NVFP4Tensor(codes[0], scales[0], ts[:1])
+    return NVFP4Tensor(codes, scales, ts)
+
+
+def quantize_into(w: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, tscales: torch.Tensor,
+                  ws: torch.Tensor) -> None:
+    """In-place variant: w [n, rows, cols] into preallocated outputs (views allowed if contiguous)."""
+    n, rows, cols = w.shape
+    _check(_lib.flint_nvfp4_quantize(w.data_ptr(), n, rows, cols, codes.data_ptr(), scales.data_ptr(),
+                                     tscales.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
+           "flint_nvfp4_quantize")
+
+
+def dequantize(q: NVFP4Tensor, rows: int, cols: int, index: int | None = None) -> torch.Tensor:
+    out = torch.empty((rows, cols), dtype=torch.float32, device=q.codes.device)
+    s = q.c(index)
+    _check(_lib.flint_nvfp4_dequantize(ctypes.byref(s), rows, cols, out.data_ptr(), _stream()),
+           "flint_nvfp4_dequantize")
+    return out
+
+
+def route(dims: Dims, router: torch.Tensor, x: torch.Tensor, ws: torch.Tensor | None = None):
+    """x float32 [B][H] -> (idx int32 [B][k], w float32 [B][k], logits float32 [B][E])"""
+    B = x.shape[0]
+    idx = torch.empty((B, dims.top_k), dtype=torch.int32, device=x.device)
+    w = torch.empty((B, dims.top_k), dtype=torch.float32, device=x.device)
+    logits = torch.empty((B, dims.n_experts), dtype=torch.float32, device=x.device)
+    ws = workspace(OP_ROUTE, dims, B) if ws is None else ws
+    _check(_lib.flint_moe_route(ctypes.byref(dims), router.data_ptr(), x.data_ptr(), B, idx.data_ptr(), w.data_ptr(),
+                                logits.data_ptr(), ws.data_ptr(), ws.numel(), _stream()), "flint_moe_route")
+    return idx, w, logits
+
+
+def moe_decode(dims: Dims, layer: LayerWeights, x: torch.Tensor, ws: torch.Tensor | None = None):
+    """x float32 [B][H] -> (y float32 [B][H], idx [B][k], w [B][k])"""
+    B = x.shape[0]
+    y = torch.empty_like(x)
+    idx = torch.empty((B, dims.top_k), dtype=torch.int32, device=x.device)
+    w = torch.empty((B, dims.top_k), dtype=torch.float32, device=x.device)
+    ws = workspace(OP_DECODE, dims, B) if ws is None else ws
+    lc = layer.c()
+    _check(_lib.flint_moe_decode(ctypes.byref(dims), ctypes.byref(lc), x.data_ptr(), B, y.data_ptr(), idx.data_ptr(),
+                                 w.data_ptr(), ws.data_ptr(), ws.numel(), _stream()), "flint_moe_decode")
+    return y, idx, w
+
+
+def lmhead(head: NVFP4Tensor, vocab: int, x: torch.Tensor, ws: torch.Tensor | None = None,
+           logits: torch.Tensor | None = None, argmax: torch.Tensor | None = None):
+    """x float32 [B][H] -> (logits float32 [B][vocab], argmax int32 [B])"""
+    B, H = x.shape
+    logits = torch.empty((B, vocab), dtype=torch.float32, device=x.device) if logits is None else logits
+    argmax = torch.empty(B, dtype=torch.int32, device=x.device) if argmax is None else argmax
+    ws = workspace(OP_LMHEAD, None, B, vocab) if ws is None else ws
+    hc = head.c()
+    _check(_lib.flint_lmhead_gemv(ctypes.byref(hc), vocab, H, x.data_ptr(), B, logits.data_ptr(), argmax.data_ptr(),
+                                  ws.data_ptr(), ws.numel(), _stream()), "flint_lmhead_gemv")
+    return logits, argmax
+
+
+class Stack:
+    """A prepared layer stack plus head (keeps the C structs and buffers alive)."""
+
+    def __init__(self, dims: Dims, layers: list[LayerWeights], head: NVFP4Tensor, vocab: int, device="cuda"):
+        self.dims, self.vocab, self.n_layers = dims, vocab, len(layers)
+        self._layers_c = (Layer * len(layers))(*[l.c() for l in layers])
+        self._head_c = head.c()
+        self._keep = (layers, head)
+        tb = _lib.flint_stack_table_bytes(len(layers))
+        self.table = torch.zeros(tb, dtype=torch.uint8, device=device)
+        self.plan = StackPlan()
+        _check(_lib.flint_stack_prepare(ctypes.byref(dims), self._layers_c, len(layers), ctypes.byref(self._head_c),
+                                        vocab, self.table.data_ptr(), tb, ctypes.byref(self.plan), _stream()),
+               "flint_stack_prepare")
+        self.ws = workspace(OP_STACK, dims, 1, vocab, len(layers), device=device)
+
+    def decode(self, x: torch.Tensor, eps: float = 1e-6, logits: torch.Tensor | None = None,
+               argmax: torch.Tensor | None = None, routes: torch.Tensor | None = None, want_logits: bool = True):
+        """x float32 [T][H]: T tokens decoded one after the other."""
+        T = x.shape[0]
+        if want_logits and logits is None:
+            logits = torch.empty((T, self.vocab), dtype=torch.float32, device=x.device)
+        if argmax is None:
+            argmax = torch.empty(T, dtype=torch.int32, device=x.device)
+        _check(_lib.flint_stack_decode(ctypes.byref(self.plan), x.data_ptr(), T, eps, _ptr(logits), argmax.data_ptr(),
+                                       _ptr(routes), self.ws.data_ptr(), self.ws.numel(), _stream()),
+               "flint_stack_decode")
+        return logits, argmax

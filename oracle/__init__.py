@@ -46,7 +46,7 @@ def lib():
         L.oracle_e2m1_encode.restype = ctypes.c_int
         L.oracle_e4m3_encode.argtypes = [ctypes.c_double]
         L.oracle_e4m3_encode.restype = ctypes.c_int
-        L.oracle_nvfp4_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P]
+        L.oracle_nvfp4_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P, ctypes.c_int]
         L.oracle_nvfp4_quantize.restype = None
         L.oracle_nvfp4_dequantize.argtypes = [_P, _P, ctypes.c_float, _I64, _I64, _P]
         L.oracle_nvfp4_dequantize.restype = None
@@ -105,14 +105,15 @@ def e4m3_encode(r: float) -> int:
     return lib().oracle_e4m3_encode(r)
 
 
-def quantize(w: np.ndarray) -> NVFP4:
+def quantize(w: np.ndarray, nthreads: int | None = None) -> NVFP4:
     w = _c(w, np.float32)
     rows, cols = w.shape
     assert cols % 16 == 0
     codes = np.empty((rows, cols // 2), np.uint8)
     scales = np.empty((rows, cols // 16), np.uint8)
     S = np.zeros(1, np.float32)
-    lib().oracle_nvfp4_quantize(w.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data, S.ctypes.data)
+    lib().oracle_nvfp4_quantize(w.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data, S.ctypes.data,
+                                nthreads or default_threads())
     return NVFP4(codes, scales, float(S[0]), rows, cols)
 
 

@@ -81,6 +81,40 @@ int oracle_e4m3_encode(double r) {
 
 /* ------------------------------------------------------------- quantise -- */
 
+typedef struct {
+  const float* w;
+  int64_t cols, r0, r1;
+  float S;
+  uint8_t *codes, *scales;
+} quant_job;
+
+static void* quant_rows(void* p) {
+  quant_job* j = (quant_job*)p;
+  const int64_t cols = j->cols, nb = cols / 16;
+  const double S = (double)j->S;
+  for (int64_t r = j->r0; r < j->r1; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const float* blk = j->w + r * cols + b * 16;
+      double bm = 0.0;
+      for (int i = 0; i < 16; ++i) {
+        double a = fabs((double)blk[i]);
+        if (a > bm) bm = a;
+      }
+      int sc = oracle_e4m3_encode(bm / (6.0 * S));
+      j->scales[r * nb + b] = (uint8_t)sc;
+      double d = oracle_e4m3_value(sc);
+      if (d == 0.0) continue;
+      for (int i = 0; i < 16; ++i) {
+        int c = oracle_e2m1_encode((double)blk[i] / (d * S));
+        int64_t k = b * 16 + i;
+        uint8_t* byte = &j->codes[r * (cols / 2) + k / 2];
+        *byte |= (uint8_t)((k & 1) ? (c << 4) : c);
+      }
+    }
+  }
+  return NULL;
+}
+
 /* NVFP4 quantisation of one matrix W [rows][cols] (cols a multiple of 16;
  * blocks of 16 run along cols, the reduction axis) into
  *   codes  [rows][cols/2]  element 2j in the low nibble of byte j,
@@ -92,7 +126,7 @@ int oracle_e4m3_encode(double r) {
  * blockmax / (6 S); element code = E2M1-RNE of w / (d S); a block whose scale
  * decodes to 0 stores all-zero codes; all ratios in double. */
 void oracle_nvfp4_quantize(const float* w, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
-                           float* tscale) {
+                           float* tscale, int nthreads) {
   double amax = 0.0;
   for (int64_t i = 0; i < rows * cols; ++i) {
     double a = fabs((double)w[i]);
@@ -100,30 +134,26 @@ void oracle_nvfp4_quantize(const float* w, int64_t rows, int64_t cols, uint8_t* 
   }
   float S = (float)(amax / 2688.0);
   *tscale = S;
-  int64_t nb = cols / 16;
   memset(codes, 0, (size_t)(rows * cols / 2));
-  memset(scales, 0, (size_t)(rows * nb));
+  memset(scales, 0, (size_t)(rows * (cols / 16)));
   if (S == 0.0f) return;
-  for (int64_t r = 0; r < rows; ++r) {
-    for (int64_t b = 0; b < nb; ++b) {
-      const float* blk = w + r * cols + b * 16;
-      double bm = 0.0;
-      for (int i = 0; i < 16; ++i) {
-        double a = fabs((double)blk[i]);
-        if (a > bm) bm = a;
-      }
-      int sc = oracle_e4m3_encode(bm / (6.0 * (double)S));
-      scales[r * nb + b] = (uint8_t)sc;
-      double d = oracle_e4m3_value(sc);
-      if (d == 0.0) continue;
-      for (int i = 0; i < 16; ++i) {
-        int c = oracle_e2m1_encode((double)blk[i] / (d * (double)S));
-        int64_t k = b * 16 + i;
-        uint8_t* byte = &codes[r * (cols / 2) + k / 2];
-        *byte |= (uint8_t)((k & 1) ? (c << 4) : c);
-      }
-    }
+  /* rows are independent: splitting them over threads changes nothing */
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 64) nthreads = 64;
+  if (rows < 64) nthreads = 1;
+  quant_job jobs[64];
+  pthread_t th[64];
+  int64_t chunk = (rows + nthreads - 1) / nthreads;
+  int used = 0;
+  for (int t = 0; t < nthreads; ++t) {
+    int64_t r0 = t * chunk, r1 = r0 + chunk < rows ? r0 + chunk : rows;
+    if (r0 >= rows) break;
+    jobs[t] = (quant_job){w, cols, r0, r1, S, codes, scales};
+    used++;
   }
+  if (used == 1) { quant_rows(&jobs[0]); return; }
+  for (int t = 0; t < used; ++t) pthread_create(&th[t], NULL, quant_rows, &jobs[t]);
+  for (int t = 0; t < used; ++t) pthread_join(th[t], NULL);
 }
 
 /* w = fl32((e2m1(c) * d) * S): c*d is exact, then one rounding to fp32. */

@@ -23,6 +23,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsynth.so")
 SRC_PATH = os.path.join(HERE, "synth.c")
+DEV_LIB_PATH = os.path.join(HERE, "libsynth_dev.so")
+DEV_SRC_PATH = os.path.join(HERE, "synth_dev.hip")
 
 # stream kinds
 ROUTER, GATE, UP, DOWN, SHARED_GATE, SHARED_UP, SHARED_DOWN, HEAD, TOKEN = range(1, 10)
@@ -41,6 +43,49 @@ def build_host_lib(force: bool = False) -> str:
                SRC_PATH, "-o", LIB_PATH, "-lpthread", "-lm"]
         subprocess.run(cmd, check=True)
     return LIB_PATH
+
+
+def build_device_lib(force: bool = False) -> str:
+    """hipcc build of the device generator (no GPU needed to build)."""
+    if force or not os.path.exists(DEV_LIB_PATH):
+        tmp = DEV_LIB_PATH + ".tmp"
+        cmd = [os.environ.get("HIPCC", "/opt/rocm/bin/hipcc"), "--offload-arch=gfx950", "-O3", "-ffp-contract=off",
+               "-fPIC", "-shared", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", DEV_SRC_PATH,
+               "-o", tmp]
+        subprocess.run(cmd, check=True, stderr=subprocess.PIPE)
+        os.replace(tmp, DEV_LIB_PATH)
+    return DEV_LIB_PATH
+
+
+_dev_lib = None
+
+
+def dev_lib():
+    global _dev_lib
+    if _dev_lib is None:
+        if not os.path.exists(DEV_LIB_PATH):
+            raise ImportError(f"{DEV_LIB_PATH} is not built")
+        L = ctypes.CDLL(DEV_LIB_PATH)
+        L.synth_dev_normal_f32.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int64,
+                                           ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                                           ctypes.c_void_p]
+        L.synth_dev_normal_f32.restype = ctypes.c_int
+        _dev_lib = L
+    return _dev_lib
+
+
+def normal_device(seed: int, stream: int, n: int, out, mean: float = 0.0, std: float = 1.0, offset: int = 0,
+                  n_streams: int = 1, hip_stream: int | None = None):
+    """Fill the float32 device tensor `out` (n_streams * n elements) with the
+    same numbers as ``normal`` for streams stream .. stream+n_streams-1."""
+    import torch
+    assert out.dtype == torch.float32 and out.is_contiguous() and out.numel() >= n * n_streams
+    hs = torch.cuda.current_stream().cuda_stream if hip_stream is None else hip_stream
+    rc = dev_lib().synth_dev_normal_f32(seed & 0xFFFFFFFF, stream & 0xFFFFFFFF, offset, n, n_streams, mean, std,
+                                        out.data_ptr(), hs)
+    if rc:
+        raise RuntimeError(f"synth_dev_normal_f32 failed with hip error {rc}")
+    return out
 
 
 _lib = None

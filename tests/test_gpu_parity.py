@@ -1,0 +1,264 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: bit-exact for the generator, the quantiser, dequantised weights and
+routing/argmax indices; relative L2 error <= 1e-4 and max-abs error <=
+2e-3 * max|ref| for fp32 outputs.  Tokens whose oracle routing (or head)
+margin is below 1e-5 are redrawn, so that the fp32 GPU and the fp64 oracle
+must agree on every index.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle.model import SyntheticWeights, moe_layer, stack_token
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-4
+MAX_ABS = 2e-3
+MARGIN = 1e-5
+
+
+@pytest.fixture(scope="module")
+def F():
+    from nvfp4_bit_projection_amd import flint, workload
+    torch.cuda.set_device(0)
+    return flint, workload
+
+
+def assert_close(got, ref, what=""):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300)
+    mabs = np.abs(got - ref).max()
+    assert rel <= REL_L2, f"{what}: rel L2 {rel:.3e}"
+    assert mabs <= MAX_ABS * np.abs(ref).max(), f"{what}: max abs {mabs:.3e} vs {np.abs(ref).max():.3e}"
+    return rel
+
+
+def dims_struct(F, d):
+    return F[0].dims_struct(d.hidden, d.n_experts, d.expert_width, d.top_k, d.shared_width)
+
+
+# ---------------------------------------------------------------- generator --
+@pytest.mark.parametrize("seed,kind,expert,n,offset", [(0, synth.GATE, 0, 1 << 20, 0), (3, synth.TOKEN, 0, 2048, 0),
+                                                        (1000, synth.HEAD, 0, 100003, 2048 * 7 + 1),
+                                                        (46, synth.DOWN, 255, 4097, 3)])
+def test_device_generator_matches_host(F, seed, kind, expert, n, offset):
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    synth.normal_device(seed, synth.stream_id(kind, expert), n, out, std=0.02, offset=offset)
+    host = synth.normal(seed, synth.stream_id(kind, expert), n, std=0.02, offset=offset)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), host.view(np.uint32))
+
+
+def test_device_generator_multi_stream(F):
+    n, ns = 5000, 7
+    out = torch.empty(n * ns, dtype=torch.float32, device="cuda")
+    synth.normal_device(9, synth.stream_id(synth.UP, 3), n, out, std=0.02, n_streams=ns)
+    got = out.cpu().numpy().reshape(ns, n)
+    for i in range(ns):
+        assert np.array_equal(got[i], synth.normal(9, synth.stream_id(synth.UP, 3 + i), n, std=0.02))
+
+
+# ---------------------------------------------------------------- quantiser --
+def quant_cases():
+    d = synth.MoEDims()
+    rng = np.random.default_rng(0)
+    wide = (rng.standard_normal((64, 512)) * np.exp(rng.uniform(-20, 5, (64, 1)))).astype(np.float32)
+    special = synth.expert_f32(1, d, synth.UP, 2)[:40].copy()
+    special[3, 16:32] = 0.0
+    special[5, 7] = -0.0
+    special[6, 0:16] = -1e-12
+    special[6, 3] = 0.05
+    return {
+        "gate": synth.expert_f32(0, d, synth.GATE, 0),
+        "down": synth.expert_f32(0, d, synth.DOWN, 5),
+        "head_slice": synth.head_f32(synth.HEAD_SEED, 150144, 2048, row0=1000, rows=4099),
+        "wide_dynamic_range": wide,
+        "zero_blocks_neg_zero": special,
+        "all_zero": np.zeros((8, 64), np.float32),
+    }
+
+
+@pytest.mark.parametrize("name", list(quant_cases().keys()))
+def test_quantizer_bit_exact(F, name):
+    flint, _ = F
+    w = quant_cases()[name]
+    q = flint.quantize(torch.from_numpy(w).cuda())
+    ref = oracle.quantize(w)
+    torch.cuda.synchronize()
+    assert q.tscale.cpu().numpy()[0].view(np.uint32) == np.float32(ref.tscale).view(np.uint32)
+    assert np.array_equal(q.scales.cpu().numpy(), ref.scales)
+    assert np.array_equal(q.codes.cpu().numpy(), ref.codes)
+    deq = flint.dequantize(q, *w.shape)
+    assert np.array_equal(deq.cpu().numpy().view(np.uint32), oracle.dequantize(ref).view(np.uint32))
+
+
+def test_quantizer_many_matrices(F):
+    flint, _ = F
+    d = synth.MoEDims()
+    ws = [synth.expert_f32(4, d, synth.GATE, e)[:64] for e in range(5)]
+    q = flint.quantize(torch.from_numpy(np.stack(ws)).cuda())
+    for e, w in enumerate(ws):
+        ref = oracle.quantize(w)
+        assert float(q.tscale[e]) == ref.tscale
+        assert np.array_equal(q.codes[e].cpu().numpy(), ref.codes)
+        assert np.array_equal(q.scales[e].cpu().numpy(), ref.scales)
+
+
+# ----------------------------------------------------------------- routing --
+def screened_tokens(W, seed_layer, count, start, dims):
+    out = []
+    s = start
+    while len(out) < count:
+        u = synth.token_f32(s, dims.hidden).astype(np.float64)
+        logits = oracle.f32_gemv(W.router(seed_layer), u)
+        idx, w, gap = oracle.topk_softmax(logits, dims.top_k)
+        if gap >= MARGIN:
+            out.append((s, idx, w, logits))
+        s += 1
+    return out
+
+
+@pytest.mark.parametrize("E", [32, 256])
+def test_route(F, E):
+    flint, workload = F
+    d = synth.MoEDims(n_experts=E)
+    W = SyntheticWeights(d)
+    toks = screened_tokens(W, 0, 5, 0, d)
+    x = workload.tokens([t[0] for t in toks], d.hidden)
+    router = torch.from_numpy(W.router(0)).cuda()
+    idx, w, logits = flint.route(dims_struct(F, d), router, x)
+    torch.cuda.synchronize()
+    for b, (_, ridx, rw, rlog) in enumerate(toks):
+        gi = idx[b].cpu().numpy()
+        assert sorted(gi.tolist()) == sorted(ridx.tolist())
+        gw = dict(zip(gi.tolist(), w[b].cpu().numpy().tolist()))
+        for e, we in zip(ridx.tolist(), rw.tolist()):
+            assert abs(gw[e] - we) <= 1e-5
+        assert abs(sum(gw.values()) - 1.0) < 1e-5
+        assert_close(logits[b].cpu().numpy(), rlog, "router logits")
+
+
+# --------------------------------------------------------------- MoE layer --
+@pytest.mark.parametrize("E,B", [(32, 1), (32, 3), (256, 1), (256, 2)])
+def test_moe_decode(F, E, B):
+    flint, workload = F
+    d = synth.MoEDims(n_experts=E)
+    layer = workload.build_layer(d, seed=0)
+    W = SyntheticWeights(d)
+    toks = screened_tokens(W, 0, B, 100 * B, d)
+    x = workload.tokens([t[0] for t in toks], d.hidden)
+    y, idx, w = flint.moe_decode(dims_struct(F, d), layer, x)
+    torch.cuda.synchronize()
+    for b, (s, ridx, _, _) in enumerate(toks):
+        ref = moe_layer(W, 0, synth.token_f32(s, d.hidden).astype(np.float64))
+        assert sorted(idx[b].cpu().numpy().tolist()) == sorted(ref.idx.tolist())
+        assert_close(y[b].cpu().numpy(), ref.y, f"moe layer E={E} b={b}")
+
+
+def test_moe_decode_one_expert_shape_variant(F):
+    """A narrower shared expert and top-2 of 8 (ragged against the 4,096-wide
+    down-projection tiling)."""
+    flint, workload = F
+    d = synth.MoEDims(n_experts=8, expert_width=96, top_k=2, shared_width=160)
+    layer = workload.build_layer(d, seed=5)
+    W = SyntheticWeights(d)
+    toks = screened_tokens(W, 5, 2, 0, d)
+    x = workload.tokens([t[0] for t in toks], d.hidden)
+    y, idx, _ = flint.moe_decode(dims_struct(F, d), layer, x)
+    torch.cuda.synchronize()
+    for b, (s, ridx, _, _) in enumerate(toks):
+        ref = moe_layer(W, 5, synth.token_f32(s, d.hidden).astype(np.float64))
+        assert sorted(idx[b].cpu().numpy().tolist()) == sorted(ref.idx.tolist())
+        assert_close(y[b].cpu().numpy(), ref.y, "moe variant")
+
+
+# -------------------------------------------------------------------- head --
+@pytest.mark.parametrize("vocab", [1, 17, 4099, 16385])
+def test_lmhead_ragged(F, vocab):
+    flint, workload = F
+    head = workload.build_head(vocab, 2048, seed=77)
+    q = oracle.quantize(synth.head_f32(77, vocab, 2048))
+    for s in range(3):
+        x = workload.tokens([s], 2048)
+        logits, am = flint.lmhead(head, vocab, x)
+        torch.cuda.synchronize()
+        ref = oracle.nvfp4_gemv(q, synth.token_f32(s, 2048).astype(np.float64))
+        assert_close(logits[0].cpu().numpy(), ref, f"head V={vocab}")
+        i, gap = oracle.argmax(ref)
+        if gap >= MARGIN:
+            assert int(am[0]) == i
+
+
+def test_lmhead_one_hot_recovers_columns(F):
+    flint, workload = F
+    vocab = 300
+    head = workload.build_head(vocab, 2048, seed=3)
+    deq = flint.dequantize(head, vocab, 2048).cpu().numpy()
+    for k in (0, 1, 31, 32, 1000, 2047):
+        x = torch.zeros((1, 2048), dtype=torch.float32, device="cuda")
+        x[0, k] = 1.0
+        logits, _ = flint.lmhead(head, vocab, x)
+        assert np.array_equal(logits[0].cpu().numpy().view(np.uint32), deq[:, k].view(np.uint32))
+
+
+@pytest.fixture(scope="module")
+def full_head(F):
+    _, workload = F
+    V = 150144
+    head = workload.build_head(V, 2048)
+    q = oracle.quantize(synth.head_f32(synth.HEAD_SEED, V, 2048))
+    return head, q, V
+
+
+def test_lmhead_full_size(F, full_head):
+    flint, workload = F
+    head, q, V = full_head
+    found = 0
+    s = 0
+    while found < 2:
+        ref = oracle.nvfp4_gemv(q, synth.token_f32(s, 2048).astype(np.float64))
+        i, gap = oracle.argmax(ref)
+        if gap >= MARGIN:
+            logits, am = flint.lmhead(head, V, workload.tokens([s], 2048))
+            torch.cuda.synchronize()
+            assert_close(logits[0].cpu().numpy(), ref, "full head")
+            assert int(am[0]) == i
+            found += 1
+        s += 1
+
+
+# ------------------------------------------------------------------- stack --
+def stack_case(F, dims, L, vocab, n_tokens, seed0):
+    flint, workload = F
+    layers = [workload.build_layer(dims, seed=l) for l in range(L)]
+    head = workload.build_head(vocab, dims.hidden)
+    W = SyntheticWeights(dims, vocab=vocab)
+    stack = flint.Stack(dims_struct(F, dims), layers, head, vocab)
+    s, chosen, refs = seed0, [], []
+    while len(chosen) < n_tokens:
+        r = stack_token(W, synth.token_f32(s, dims.hidden), L)
+        if min(r.gaps) >= MARGIN and r.argmax_gap >= MARGIN:
+            chosen.append(s)
+            refs.append(r)
+        s += 1
+    x = workload.tokens(chosen, dims.hidden)
+    routes = torch.zeros((n_tokens, L, dims.top_k), dtype=torch.int32, device="cuda")
+    logits, am = stack.decode(x, routes=routes)
+    torch.cuda.synchronize()
+    for t, r in enumerate(refs):
+        for l in range(L):
+            assert sorted(routes[t, l].cpu().numpy().tolist()) == sorted(r.routes[l].tolist()), (t, l)
+        assert_close(logits[t].cpu().numpy(), r.logits, f"stack token {t}")
+        assert int(am[t]) == r.argmax
+
+
+def test_stack_small(F):
+    stack_case(F, synth.MoEDims(n_experts=32), L=3, vocab=4099, n_tokens=3, seed0=0)
+
+
+def test_stack_e256_four_layers(F):
+    stack_case(F, synth.MoEDims(), L=4, vocab=16385, n_tokens=2, seed0=synth.TOKEN_SEED0)

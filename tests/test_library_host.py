@@ -1,0 +1,113 @@
+"""The C-ABI library on the host: it loads, exports every symbol its header
+declares, and rejects bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flint_moe.h")
+
+
+@pytest.fixture(scope="module")
+def F():
+    from nvfp4_bit_projection_amd import build
+    if not os.path.exists(build.LIB_PATH):
+        build.build_library()
+    from nvfp4_bit_projection_amd import flint
+    return flint
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flint_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(F):
+    names = declared_functions()
+    assert len(names) >= 11
+    lib = ctypes.CDLL(F.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(F.EXPORTED) == names
+
+
+def test_status_strings(F):
+    L = F.lib()
+    for code in range(0, -9, -1):
+        assert L.flint_status_str(code) and L.flint_status_str(code) != b"unknown status"
+    assert L.flint_status_str(5) == b"unknown status"
+
+
+def test_workspace_sizes(F):
+    d = F.dims_struct()
+    assert F.workspace_bytes(F.OP_ROUTE, d, 1) > 0
+    assert F.workspace_bytes(F.OP_DECODE, d, 4) > F.workspace_bytes(F.OP_DECODE, d, 1)
+    assert F.workspace_bytes(F.OP_LMHEAD, None, 1, 150144) > 0
+    assert F.workspace_bytes(F.OP_STACK, d, 1, 150144, 47) > 0
+    assert F.workspace_bytes(F.OP_QUANTIZE, None, 256) >= 1024
+    assert F.workspace_bytes(F.OP_DECODE, d, 0) == 0
+    assert F.workspace_bytes(99, d, 1) == 0
+    bad = F.dims_struct(top_k=9)
+    assert F.workspace_bytes(F.OP_DECODE, bad, 1) == 0
+
+
+# Host-side validation runs before any HIP call, so these return their codes
+# on a machine without a GPU.  Pointers below are fake but never dereferenced.
+FAKE = 0x10000
+
+
+def test_route_rejections(F):
+    L = F.lib()
+    d = F.dims_struct()
+    r = lambda dims, router, x, B, idx, w, ws, wsb: L.flint_moe_route(
+        ctypes.byref(dims) if dims is not None else None, router, x, B, idx, w, None, ws, wsb, None)
+    need = F.workspace_bytes(F.OP_ROUTE, d, 1)
+    assert r(None, FAKE, FAKE, 1, FAKE, FAKE, FAKE, need) == -1
+    assert r(d, None, FAKE, 1, FAKE, FAKE, FAKE, need) == -1
+    assert r(d, FAKE, FAKE, 0, FAKE, FAKE, FAKE, need) == -2
+    assert r(F.dims_struct(top_k=0), FAKE, FAKE, 1, FAKE, FAKE, FAKE, need) == -2
+    assert r(F.dims_struct(n_experts=4, top_k=6), FAKE, FAKE, 1, FAKE, FAKE, FAKE, need) == -2
+    assert r(F.dims_struct(n_experts=300), FAKE, FAKE, 1, FAKE, FAKE, FAKE, need) == -2
+    assert r(F.dims_struct(hidden=1024), FAKE, FAKE, 1, FAKE, FAKE, FAKE, need) == -8
+    assert r(F.dims_struct(expert_width=1024, top_k=8), FAKE, FAKE, 1, FAKE, FAKE, FAKE, need) == -8
+    assert r(d, FAKE + 4, FAKE, 1, FAKE, FAKE, FAKE, need) == -3
+    assert r(d, FAKE, FAKE, 1, FAKE, FAKE, FAKE, need - 1) == -4
+
+
+def test_decode_and_head_rejections(F):
+    L = F.lib()
+    d = F.dims_struct()
+    lay = F.Layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, F.NVFP4(FAKE, FAKE, FAKE),
+                  F.NVFP4(FAKE, FAKE, FAKE), F.NVFP4(FAKE, FAKE, FAKE))
+    need = F.workspace_bytes(F.OP_DECODE, d, 1)
+    dec = lambda layer, wsb: L.flint_moe_decode(ctypes.byref(d), ctypes.byref(layer), FAKE, 1, FAKE, None, None,
+                                                FAKE, wsb, None)
+    assert dec(lay, need - 1) == -4
+    lay2 = F.Layer(*[getattr(lay, f) for f, _ in F.Layer._fields_])
+    lay2.down_codes = None
+    assert dec(lay2, need) == -1
+    lay3 = F.Layer(*[getattr(lay, f) for f, _ in F.Layer._fields_])
+    lay3.shared_up = F.NVFP4(FAKE + 8, FAKE, FAKE)
+    assert dec(lay3, need) == -3
+    head = F.NVFP4(FAKE, FAKE, FAKE)
+    hneed = F.workspace_bytes(F.OP_LMHEAD, None, 1, 100)
+    hd = lambda vocab, hidden, wsb: L.flint_lmhead_gemv(ctypes.byref(head), vocab, hidden, FAKE, 1, FAKE, FAKE, FAKE,
+                                                        wsb, None)
+    assert hd(0, 2048, hneed) == -2
+    assert hd(100, 2048, hneed - 1) == -4
+    assert hd(100, 1024, hneed) == -8
+    assert hd(100, 2000, hneed) == -2
+
+
+def test_quantize_and_stack_rejections(F):
+    L = F.lib()
+    q = lambda n, rows, cols, wsb: L.flint_nvfp4_quantize(FAKE, n, rows, cols, FAKE, FAKE, FAKE, FAKE, wsb, None)
+    assert q(1, 4, 48, 256) == -2
+    assert q(0, 4, 64, 256) == -2
+    assert q(300, 4, 64, 256) == -4
+    plan = F.StackPlan()
+    assert L.flint_stack_decode(ctypes.byref(plan), FAKE, 1, 1e-6, None, FAKE, None, FAKE, 1 << 20, None) in (-1, -2)
+    assert L.flint_stack_table_bytes(0) == 0 and L.flint_stack_table_bytes(47) > 47 * ctypes.sizeof(F.Layer)
