@@ -170,7 +170,18 @@ typedef struct {
   flint_nvfp4 head;
   const flint_moe_layer* layers; /* [host] caller's array of n_layers */
   const void* table;             /* device copy of the layer table */
+  int32_t schedule;              /* FLINT_SCHEDULE_*; prepare sets AUTO */
 } flint_stack_plan;
+
+/* Schedules of flint_stack_decode.  PERSISTENT: one cooperative launch that
+ * runs every token, layer and the head (needs expert_width and shared_width
+ * multiples of 256, top_k*expert_width/8 + shared_width/8 == 512,
+ * shared_width <= 1024, an even n_experts); KERNELS: three kernels per layer
+ * and one for the head, any supported sizes; AUTO: PERSISTENT when the sizes
+ * allow it. */
+#define FLINT_SCHEDULE_AUTO 0
+#define FLINT_SCHEDULE_KERNELS 1
+#define FLINT_SCHEDULE_PERSISTENT 2
 
 size_t flint_stack_table_bytes(int32_t L);
 int32_t flint_stack_prepare(const flint_moe_dims* dims /*[host]*/, const flint_moe_layer* layers /*[host] array of L*/,
@@ -178,6 +189,30 @@ int32_t flint_stack_prepare(const flint_moe_dims* dims /*[host]*/, const flint_m
                             size_t table_bytes, flint_stack_plan* plan /*[host], out*/, void* stream);
 int32_t flint_stack_decode(const flint_stack_plan* plan /*[host]*/, const float* x, int32_t T, float eps, float* logits,
                            int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes, void* stream);
+
+/* Profiling variant of flint_stack_decode for the persistent schedule: also
+ * writes, for the first token, device wall-clock stamps (100 MHz ticks) of
+ * the phase boundaries of two workgroups (one on the first XCD, one on the
+ * last) into trace, int64 [2][L+1][10], followed by the stamps of layer 1 of
+ * all 256 workgroups, int64 [256][10]: per layer l the stamps at the start
+ * of the layer, after the norm, after the router/shared rows, after the
+ * logits arrive, after top-k, after the routed rows, after the hidden slice
+ * arrives, after the partial output, after the partials arrive and after the
+ * new residual arrives; row L holds the head start, the head end and the
+ * token's end.  Returns FLINT_E_UNSUPPORTED for the kernel-sequence
+ * schedule. */
+int32_t flint_stack_decode_traced(const flint_stack_plan* plan /*[host]*/, const float* x, int32_t T, float eps,
+                                  float* logits, int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes,
+                                  int64_t* trace, void* stream);
+
+/* Stack workspace contract: zero-filled before the first call; afterwards it
+ * carries the persistent schedule's epoch counter and must not be changed
+ * between calls.  Every wait inside the persistent kernel is bounded; if one
+ * gives up (a fault elsewhere), the kernel raises a flag in the workspace and
+ * returns, and later calls on that workspace do nothing until it is zeroed
+ * again.  flint_stack_error synchronously copies that flag to *error [host]
+ * (0: none). */
+int32_t flint_stack_error(const void* ws, size_t ws_bytes, int32_t* error /*[host]*/);
 
 /* NVFP4 quantiser (device): quantises n_mats independent matrices stacked in
  * w (float [n_mats][rows][cols], cols a multiple of 32) into codes

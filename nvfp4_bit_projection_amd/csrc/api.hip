@@ -213,24 +213,34 @@ int32_t flint_stack_prepare(const flint_moe_dims* dims, const flint_moe_layer* l
   plan->head = *head;
   plan->layers = layers;
   plan->table = table;
+  plan->schedule = FLINT_SCHEDULE_AUTO;
   return FLINT_OK;
 }
 
-int32_t flint_stack_decode(const flint_stack_plan* plan, const float* x, int32_t T, float eps, float* logits,
-                           int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes, void* stream) {
+static int32_t stack_decode_impl(const flint_stack_plan* plan, const float* x, int32_t T, float eps, float* logits,
+                                 int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes, int64_t* trace,
+                                 void* stream) {
   int32_t st;
   if (!plan || !x || !argmax || !ws) return FLINT_E_NULL;
   if ((st = check_dims(&plan->dims))) return st;
   if (!plan->layers || !plan->table) return FLINT_E_NULL;
-  if (T < 1 || plan->n_layers < 1 || plan->vocab < 1 || !(eps > 0.0f)) return FLINT_E_DIMS;
+  if (T < 1 || plan->n_layers < 1 || plan->vocab < 1 || !(eps > 0.0f) || plan->schedule < 0 || plan->schedule > 2)
+    return FLINT_E_DIMS;
   if (!aligned16(x) || !aligned16(ws) || !aligned4(argmax) || (logits && !aligned4(logits)) ||
       (routes_opt && !aligned4(routes_opt)))
     return FLINT_E_ALIGN;
   const flint_moe_dims& d = plan->dims;
   StackWs sw(d, plan->vocab);
   if (ws_bytes < sw.total) return FLINT_E_WORKSPACE;
+  const bool persistent_ok = stack_persistent_supported(d);
+  if (plan->schedule == FLINT_SCHEDULE_PERSISTENT && !persistent_ok) return FLINT_E_UNSUPPORTED;
   if ((st = check_device())) return st;
   hipStream_t s = (hipStream_t)stream;
+  if (persistent_ok && plan->schedule != FLINT_SCHEDULE_KERNELS) {
+    hipError_t e = launch_stack_persistent(d, plan->n_layers, plan->vocab, plan->table, x, T, eps, logits, argmax,
+                                           routes_opt, static_cast<char*>(ws) + sw.persist, trace, s);
+    return e == hipSuccess ? FLINT_OK : hip_fail(e);
+  }
   char* base = static_cast<char*>(ws);
   float* h = carve<float>(ws, sw.h);
   void* dws = base + sw.decode;
@@ -251,6 +261,28 @@ int32_t flint_stack_decode(const flint_stack_plan* plan, const float* x, int32_t
     if (e != hipSuccess) return hip_fail(e);
   }
   return FLINT_OK;
+}
+
+int32_t flint_stack_decode(const flint_stack_plan* plan, const float* x, int32_t T, float eps, float* logits,
+                           int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes, void* stream) {
+  return stack_decode_impl(plan, x, T, eps, logits, argmax, routes_opt, ws, ws_bytes, nullptr, stream);
+}
+
+int32_t flint_stack_decode_traced(const flint_stack_plan* plan, const float* x, int32_t T, float eps, float* logits,
+                                  int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes, int64_t* trace,
+                                  void* stream) {
+  if (!trace) return FLINT_E_NULL;
+  if (!aligned16(trace)) return FLINT_E_ALIGN;
+  if (plan && plan->schedule == FLINT_SCHEDULE_KERNELS) return FLINT_E_UNSUPPORTED;
+  if (plan && !stack_persistent_supported(plan->dims)) return FLINT_E_UNSUPPORTED;
+  return stack_decode_impl(plan, x, T, eps, logits, argmax, routes_opt, ws, ws_bytes, trace, stream);
+}
+
+int32_t flint_stack_error(const void* ws, size_t ws_bytes, int32_t* error) {
+  if (!ws || !error) return FLINT_E_NULL;
+  if (ws_bytes < 256) return FLINT_E_WORKSPACE;
+  hipError_t e = read_stack_error(ws, error);
+  return e == hipSuccess ? FLINT_OK : hip_fail(e);
 }
 
 int32_t flint_nvfp4_quantize(const float* w, int64_t n_mats, int64_t rows, int64_t cols, uint8_t* codes,

@@ -18,6 +18,31 @@ namespace flint {
 
 constexpr int kWave = 64;
 
+// Buffer loads: a uniform resource per matrix plus a per-lane byte offset.
+// Unlike generic (flat) loads of pointers read from a device-side table they
+// count only against the vector-memory wait counter, so LDS accesses and
+// barriers do not wait for weight loads in flight.  Sizes above 2 GiB are not
+// used by these kernels.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0,
+                                           (int)(bytes < 0x7FFFFFFFull ? bytes : 0x7FFFFFFFull), 0x00020000);
+}
+__device__ __forceinline__ uint4 bload_u4(rsrc_t r, uint32_t off) {
+  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t bload_u16(rsrc_t r, uint32_t off) {
+  return (uint32_t)(unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+__device__ __forceinline__ float4 bload_f4(rsrc_t r, uint32_t off) {
+  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+}
+__device__ __forceinline__ float bload_f32(rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 // OCP E4M3FN byte -> float (gfx950 converts OCP FP8 in hardware).
 __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
   return __builtin_amdgcn_cvt_f32_fp8(byte, 0);
@@ -64,18 +89,67 @@ __device__ __forceinline__ float nvfp4_lane_dot32(uint4 c, uint32_t sc, const fl
   return e4m3_to_f32(sc & 0xFF) * a0 + e4m3_to_f32((sc >> 8) & 0xFF) * a1;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+// Cross-lane steps with DPP (data-parallel primitives: register-to-register
+// moves inside a 16-lane row), a few cycles each, instead of LDS round trips.
+// Every lane of the wave must be active.
+template <int ctrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
+}
+template <int ctrl>
+__device__ __forceinline__ int dpp_i32(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, ctrl, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+
+// sum over each row of 16 lanes, result in every lane of the row
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
   return v;
+}
+__device__ __forceinline__ float lane_f32(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// sum over the wave, result (uniform) in every lane
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return ((lane_f32(v, 0) + lane_f32(v, 16)) + lane_f32(v, 32)) + lane_f32(v, 48);
 }
 
 // sum over groups of `width` consecutive lanes (width a power of two <= 64)
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {
+  if constexpr (width == 16) {
+    return row16_sum(v);
+  } else {
 #pragma unroll
-  for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+    for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+  }
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
+}
+
+__device__ __forceinline__ int wave_min_dpp(int v) {
+  v = min(v, dpp_i32<kDppXor1>(v));
+  v = min(v, dpp_i32<kDppXor2>(v));
+  v = min(v, dpp_i32<kDppHalfMirror>(v));
+  v = min(v, dpp_i32<kDppMirror>(v));
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -58,13 +58,20 @@ struct HeadWs {
   }
 };
 
+// persistent decode (stack.hip)
+bool stack_persistent_supported(const flint_moe_dims& d);
+size_t stack_persistent_ws_bytes();
+
+// Stack workspace: the persistent kernel's exchange area first (its control
+// words at offset 0), then the buffers of the kernel-sequence schedule.
 struct StackWs {
-  size_t h, decode, head, total;
+  size_t persist, h, decode, head, total;
   StackWs(const flint_moe_dims& d, int vocab) {
     (void)vocab;
     DecodeWs dw(d, 1);
     HeadWs hw(1);
     size_t o = 0;
+    persist = o; o = align_up(o + stack_persistent_ws_bytes(), 256);
     h = o; o = align_up(o + 4 * (size_t)d.hidden, 256);
     decode = o; o = align_up(o + dw.total, 256);
     head = o; o = align_up(o + hw.total, 256);
@@ -92,5 +99,9 @@ hipError_t launch_quantize(const float* w, int64_t n_mats, int64_t rows, int64_t
                            uint8_t* scales, float* tscales, uint32_t* amax_bits, hipStream_t s);
 hipError_t launch_dequantize(const flint_nvfp4& q, int64_t rows, int64_t cols, float* out, hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s);
+hipError_t launch_stack_persistent(const flint_moe_dims& d, int L, int vocab, const void* table, const float* x,
+                                   int T, float eps, float* logits, int32_t* argmax, int32_t* routes, void* ws,
+                                   int64_t* trace, hipStream_t s);
+hipError_t read_stack_error(const void* ws, int32_t* out);
 
 }  // namespace flint

@@ -48,7 +48,10 @@ class Layer(ctypes.Structure):
 
 class StackPlan(ctypes.Structure):
     _fields_ = [("dims", Dims), ("n_layers", _I32), ("vocab", _I32), ("head", NVFP4), ("layers", _P),
-                ("table", _P)]
+                ("table", _P), ("schedule", _I32)]
+
+
+SCHEDULE_AUTO, SCHEDULE_KERNELS, SCHEDULE_PERSISTENT = 0, 1, 2
 
 
 def _load():
@@ -66,6 +69,9 @@ def _load():
         "flint_stack_prepare": ([ctypes.POINTER(Dims), ctypes.POINTER(Layer), _I32, ctypes.POINTER(NVFP4), _I32, _P,
                                  _SZ, ctypes.POINTER(StackPlan), _P], _I32),
         "flint_stack_decode": ([ctypes.POINTER(StackPlan), _P, _I32, ctypes.c_float, _P, _P, _P, _P, _SZ, _P], _I32),
+        "flint_stack_decode_traced": ([ctypes.POINTER(StackPlan), _P, _I32, ctypes.c_float, _P, _P, _P, _P, _SZ, _P,
+                                       _P], _I32),
+        "flint_stack_error": ([_P, _SZ, ctypes.POINTER(_I32)], _I32),
         "flint_nvfp4_quantize": ([_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _I32),
         "flint_nvfp4_dequantize": ([ctypes.POINTER(NVFP4), _I64, _I64, _P, _P], _I32),
     }
@@ -81,7 +87,7 @@ _lib = _load()
 # every symbol include/flint_moe.h declares
 EXPORTED = ("flint_status_str", "flint_last_hip_error", "flint_workspace_bytes", "flint_moe_route",
             "flint_moe_decode", "flint_lmhead_gemv", "flint_stack_table_bytes", "flint_stack_prepare",
-            "flint_stack_decode", "flint_nvfp4_quantize", "flint_nvfp4_dequantize")
+            "flint_stack_decode", "flint_stack_decode_traced", "flint_stack_error", "flint_nvfp4_quantize", "flint_nvfp4_dequantize")
 
 
 def lib():
@@ -228,7 +234,8 @@ def lmhead(head: NVFP4Tensor, vocab: int, x: torch.Tensor, ws: torch.Tensor | No
 class Stack:
     """A prepared layer stack plus head (keeps the C structs and buffers alive)."""
 
-    def __init__(self, dims: Dims, layers: list[LayerWeights], head: NVFP4Tensor, vocab: int, device="cuda"):
+    def __init__(self, dims: Dims, layers: list[LayerWeights], head: NVFP4Tensor, vocab: int, device="cuda",
+                 schedule: int = SCHEDULE_AUTO):
         self.dims, self.vocab, self.n_layers = dims, vocab, len(layers)
         self._layers_c = (Layer * len(layers))(*[l.c() for l in layers])
         self._head_c = head.c()
@@ -239,7 +246,25 @@ class Stack:
         _check(_lib.flint_stack_prepare(ctypes.byref(dims), self._layers_c, len(layers), ctypes.byref(self._head_c),
                                         vocab, self.table.data_ptr(), tb, ctypes.byref(self.plan), _stream()),
                "flint_stack_prepare")
+        self.plan.schedule = schedule
         self.ws = workspace(OP_STACK, dims, 1, vocab, len(layers), device=device)
+
+    def decode_traced(self, x: torch.Tensor, eps: float = 1e-6):
+        """Persistent schedule with phase stamps of the first token:
+        -> (argmax, trace int64 [2][L+1][10] ++ [256][10] in 100 MHz ticks, flat)"""
+        T = x.shape[0]
+        argmax = torch.empty(T, dtype=torch.int32, device=x.device)
+        trace = torch.zeros(2 * (self.n_layers + 1) * 10 + 256 * 10, dtype=torch.int64, device=x.device)
+        _check(_lib.flint_stack_decode_traced(ctypes.byref(self.plan), x.data_ptr(), T, eps, None, argmax.data_ptr(),
+                                              None, self.ws.data_ptr(), self.ws.numel(), trace.data_ptr(), _stream()),
+               "flint_stack_decode_traced")
+        return argmax, trace
+
+    def error(self) -> int:
+        """The persistent schedule's watchdog flag (0: none); synchronises."""
+        e = _I32(0)
+        _check(_lib.flint_stack_error(self.ws.data_ptr(), self.ws.numel(), ctypes.byref(e)), "flint_stack_error")
+        return e.value
 
     def decode(self, x: torch.Tensor, eps: float = 1e-6, logits: torch.Tensor | None = None,
                argmax: torch.Tensor | None = None, routes: torch.Tensor | None = None, want_logits: bool = True):
