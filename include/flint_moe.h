@@ -193,14 +193,17 @@ int32_t flint_stack_decode(const flint_stack_plan* plan /*[host]*/, const float*
 /* Profiling variant of flint_stack_decode for the persistent schedule: also
  * writes, for the first token, device wall-clock stamps (100 MHz ticks) of
  * the phase boundaries of two workgroups (one on the first XCD, one on the
- * last) into trace, int64 [2][L+1][10], followed by the stamps of layer 1 of
- * all 256 workgroups, int64 [256][10]: per layer l the stamps at the start
- * of the layer, after the norm, after the router/shared rows, after the
- * logits arrive, after top-k, after the routed rows, after the hidden slice
- * arrives, after the partial output, after the partials arrive and after the
- * new residual arrives; row L holds the head start, the head end and the
- * token's end.  Returns FLINT_E_UNSUPPORTED for the kernel-sequence
- * schedule. */
+ * last) into trace, int64 [2][L+1][16], followed by the stamps of layer 1 of
+ * all 256 workgroups, int64 [256][16].  Per layer l, seen by the first
+ * polling wave: 0 layer start, 1 norm done, 2 router/shared rows done,
+ * 3 logits arrived, 4 top-k done, 5 routed rows done, 6 hidden slice arrived,
+ * 7 partial output done, 8 partials arrived, 9 new residual arrived; seen by
+ * the first loading wave: 10 its router rows present, 11 router/shared
+ * results stored, 12 next layer's rows requested, 13 its routed pair stored,
+ * 14 its partial outputs stored; 15: the first polling wave's routed pairs
+ * stored.  Row L holds the head start, the head end and the token's end.
+ * Returns FLINT_E_UNSUPPORTED for the kernel-sequence schedule and for more
+ * than 64 layers. */
 int32_t flint_stack_decode_traced(const flint_stack_plan* plan /*[host]*/, const float* x, int32_t T, float eps,
                                   float* logits, int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes,
                                   int64_t* trace, void* stream);

@@ -232,7 +232,7 @@ static int32_t stack_decode_impl(const flint_stack_plan* plan, const float* x, i
   const flint_moe_dims& d = plan->dims;
   StackWs sw(d, plan->vocab);
   if (ws_bytes < sw.total) return FLINT_E_WORKSPACE;
-  const bool persistent_ok = stack_persistent_supported(d);
+  const bool persistent_ok = stack_persistent_supported(d, plan->n_layers);
   if (plan->schedule == FLINT_SCHEDULE_PERSISTENT && !persistent_ok) return FLINT_E_UNSUPPORTED;
   if ((st = check_device())) return st;
   hipStream_t s = (hipStream_t)stream;
@@ -274,7 +274,7 @@ int32_t flint_stack_decode_traced(const flint_stack_plan* plan, const float* x, 
   if (!trace) return FLINT_E_NULL;
   if (!aligned16(trace)) return FLINT_E_ALIGN;
   if (plan && plan->schedule == FLINT_SCHEDULE_KERNELS) return FLINT_E_UNSUPPORTED;
-  if (plan && !stack_persistent_supported(plan->dims)) return FLINT_E_UNSUPPORTED;
+  if (plan && !stack_persistent_supported(plan->dims, plan->n_layers)) return FLINT_E_UNSUPPORTED;
   return stack_decode_impl(plan, x, T, eps, logits, argmax, routes_opt, ws, ws_bytes, trace, stream);
 }
 

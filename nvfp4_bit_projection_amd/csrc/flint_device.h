@@ -117,10 +117,19 @@ __device__ __forceinline__ float lane_f32(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-// sum over the wave, result (uniform) in every lane
+// Row broadcasts (GFX9 DPP): lane 15 of each row to the next row, and lane
+// 31 to rows 2 and 3; rows outside the row mask keep `old`.
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+// sum over the wave, result (uniform) in every lane: row sums, then row 1 +=
+// row 0 and row 3 += row 2, then row 3 += row 1; lane 63 holds
+// (r0 + r1) + (r2 + r3)
 __device__ __forceinline__ float wave_sum(float v) {
   v = row16_sum(v);
-  return ((lane_f32(v, 0) + lane_f32(v, 16)) + lane_f32(v, 32)) + lane_f32(v, 48);
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowBcast15, 0xA, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kDppRowBcast31, 0xC, 0xF, false));
+  return lane_f32(v, 63);
 }
 
 // sum over groups of `width` consecutive lanes (width a power of two <= 64)
@@ -135,21 +144,49 @@ __device__ __forceinline__ float group_sum(float v) {
   }
 }
 
+// maximum over the wave, result (uniform) in every lane
 __device__ __forceinline__ float wave_max_dpp(float v) {
   v = fmaxf(v, dpp_f32<kDppXor1>(v));
   v = fmaxf(v, dpp_f32<kDppXor2>(v));
   v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
   v = fmaxf(v, dpp_f32<kDppMirror>(v));
-  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), kDppRowBcast15,
+                                                           0xA, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), kDppRowBcast31,
+                                                           0xC, 0xF, false)));
+  return lane_f32(v, 63);
 }
 
+// Order-preserving int32 key of a float (not NaN): flipping the magnitude
+// bits of negative values makes signed integer order match float order.  The
+// map is its own inverse.
+__device__ __forceinline__ int ord_key(float f) {
+  const int b = __float_as_int(f);
+  return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float ord_key_value(int key) { return __int_as_float(key ^ ((key >> 31) & 0x7FFFFFFF)); }
+
+// maximum over the wave of an int, result (uniform) in every lane; every
+// step is one fused DPP max
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = max(v, __builtin_amdgcn_mov_dpp(v, kDppXor1, 0xF, 0xF, true));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, kDppXor2, 0xF, 0xF, true));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, kDppHalfMirror, 0xF, 0xF, true));
+  v = max(v, __builtin_amdgcn_mov_dpp(v, kDppMirror, 0xF, 0xF, true));
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, kDppRowBcast15, 0xA, 0xF, false));
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, kDppRowBcast31, 0xC, 0xF, false));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// minimum over the wave, result (uniform) in every lane
 __device__ __forceinline__ int wave_min_dpp(int v) {
   v = min(v, dpp_i32<kDppXor1>(v));
   v = min(v, dpp_i32<kDppXor2>(v));
   v = min(v, dpp_i32<kDppHalfMirror>(v));
   v = min(v, dpp_i32<kDppMirror>(v));
-  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, kDppRowBcast15, 0xA, 0xF, false));
+  v = min(v, __builtin_amdgcn_update_dpp(v, v, kDppRowBcast31, 0xC, 0xF, false));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 __device__ __forceinline__ float wave_max(float v) {

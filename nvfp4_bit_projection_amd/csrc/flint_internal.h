@@ -59,7 +59,8 @@ struct HeadWs {
 };
 
 // persistent decode (stack.hip)
-bool stack_persistent_supported(const flint_moe_dims& d);
+constexpr int kMaxStackLayers = 64;  // layers the persistent schedule takes
+bool stack_persistent_supported(const flint_moe_dims& d, int L);
 size_t stack_persistent_ws_bytes();
 
 // Stack workspace: the persistent kernel's exchange area first (its control

@@ -53,8 +53,8 @@ constexpr int kSliceK = 512;            // k * (I/8) + Is/8: one group's slice o
 constexpr int kHeadRowsPerWave = 8;
 constexpr int kCommWaves = 4;                      // waves that poll the exchanges
 constexpr int kCommThreads = kCommWaves * 64;
-constexpr int kGateUpPerWave = 3;                  // routed gate/up pairs per communication wave
-constexpr int kDownPasses = 4;                     // 4-row passes of a load wave in phase C
+constexpr int kGateUpComm = 2;                     // routed gate/up pairs per communication wave
+constexpr int kDownPasses = 2;                     // 4-row down-projection passes of every wave
 constexpr uint32_t kSpinLimit = 1u << 22;
 #ifndef FLINT_POLL_SLEEP
 #define FLINT_POLL_SLEEP 2
@@ -87,11 +87,38 @@ struct StackParams {
   int64_t* trace;  // optional [2][L+1][kTracePoints] phase timestamps of workgroups 0 and 255
 };
 
-constexpr int kTracePoints = 10;
+constexpr int kTracePoints = 16;
+constexpr int kTraceMaxLayers = kMaxStackLayers;
 
+// Exchange scopes.  Values that cross XCDs are stored with device-scope
+// stores (written through to the coherence point beyond the per-XCD L2) and
+// polled with device-scope loads.  Values exchanged inside one XCD stay in
+// its shared L2: plain stores (the per-CU vector cache is write-through) and
+// loads that miss the per-CU cache (SC0) and stream (NT) -- about 30% less
+// latency per round trip.  The kernel checks at start that workgroup b runs
+// on XCD b % 8, which the in-XCD exchanges rely on.
+enum class Scope { kXcd, kDevice };
+template <Scope sc>
 __device__ __forceinline__ void put_pair(uint64_t* p, float v, uint32_t ep) {
-  __hip_atomic_store(p, (uint64_t)__float_as_uint(v) | ((uint64_t)ep << 32), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t x = (uint64_t)__float_as_uint(v) | ((uint64_t)ep << 32);
+  if constexpr (sc == Scope::kDevice)
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+template <Scope sc>
+constexpr int poll_aux() { return sc == Scope::kDevice ? 16 /* SC1 */ : 3 /* SC0 | NT */; }
+__device__ __forceinline__ uint32_t xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20); }
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its global loads and stores (the exchanges carry their
+// own epochs, and loads issued ahead of time stay in flight across it).
+// The signal fences keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void wg_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 struct WaitCtx {
@@ -99,31 +126,54 @@ struct WaitCtx {
   int* bad;  // LDS flag
 };
 
-// Wait until pairs [0, n) (n even) of buf carry epoch ep; values -> dst.
-// Pair i goes to dst[i]; for a strided source use wait_pairs_rows.
-__device__ __forceinline__ void wait_pairs(const uint64_t* buf, int n, uint32_t ep, float* dst, const WaitCtx& w,
-                                           bool pad = false) {
-  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t*>(buf), 0, n * 8, 0x00020000);
-  for (int c = threadIdx.x; threadIdx.x < kCommThreads && c < n / 2; c += kCommThreads) {
-    uint32_t spins = 0;
-    while (true) {
-      auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, c * 16, 0, 16);
-      if (v[1] == ep && v[3] == ep) {
-        const int d = pad ? padded(2 * c) : 2 * c;  // 2c, 2c+1 share a row
-        dst[d] = __uint_as_float(v[0]);
-        dst[d + 1] = __uint_as_float(v[2]);
-        break;
-      }
-      ++spins;
-      if (spins > kSpinLimit || ((spins & 1023) == 0 && ld_dev_u32(w.err))) {
-        atomicOr(w.err, 1u);
-        *w.bad = 1;
-        break;
-      }
-      poll_backoff();
-    }
+// Raise the error flag after a wait timed out (or another workgroup raised it).
+__device__ __forceinline__ bool poll_gave_up(uint32_t& spins, const WaitCtx& w) {
+  ++spins;
+  if (spins > kSpinLimit || ((spins & 1023) == 0 && ld_dev_u32(w.err))) {
+    atomicOr(w.err, 1u);
+    *w.bad = 1;
+    return true;
   }
-  __syncthreads();
+  poll_backoff();
+  return false;
+}
+
+// Poll until pairs [0, n) (n even, n <= 8 * kCommThreads) of buf carry epoch
+// ep; values -> dst (pair i to dst[i], or to its padded row position).  Called
+// by the communication waves only; each thread owns up to four 128-bit
+// chunks and keeps all of its outstanding chunks in flight at once.
+template <Scope sc>
+__device__ __forceinline__ void poll_pairs(const uint64_t* buf, int n, uint32_t ep, float* dst, const WaitCtx& w,
+                                           bool pad = false) {
+  constexpr int kMaxPer = 4;
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t*>(buf), 0, n * 8, 0x00020000);
+  const int t = threadIdx.x;
+  uint32_t pending = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i)
+    if (t + i * kCommThreads < n / 2) pending |= 1u << i;
+  uint32_t spins = 0;
+  while (pending) {
+    uint32_t v[kMaxPer][4];
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      if (pending & (1u << i)) {
+        auto x = __builtin_amdgcn_raw_buffer_load_b128(rs, (t + i * kCommThreads) * 16, 0, poll_aux<sc>());
+        v[i][0] = x[0]; v[i][1] = x[1]; v[i][2] = x[2]; v[i][3] = x[3];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      if ((pending & (1u << i)) && v[i][1] == ep && v[i][3] == ep) {
+        const int c = t + i * kCommThreads;
+        const int d = pad ? padded(2 * c) : 2 * c;  // 2c, 2c+1 share a row
+        dst[d] = __uint_as_float(v[i][0]);
+        dst[d + 1] = __uint_as_float(v[i][2]);
+        pending &= ~(1u << i);
+      }
+    }
+    if (!pending || poll_gave_up(spins, w)) break;
+  }
 }
 
 __device__ __forceinline__ void lds_x32(const float* src, float* xv) {
@@ -135,109 +185,175 @@ __device__ __forceinline__ void lds_x32(const float* src, float* xv) {
   }
 }
 
-// RMSNorm scale of sh_h (kHidden values) -> sh_u = s * sh_h
-__device__ __forceinline__ void rms_to_u(const float* sh_h, float* sh_u, float* sh_red, float eps) {
+// RMSNorm scale of h (kHidden values) -> u = s * h (padded rows); two barriers
+__device__ __forceinline__ void rms_to_u(const float* h, float* u, float* red, float eps) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   float v[kHidden / kStackThreads];
   float ss = 0.0f;
 #pragma unroll
   for (int i = 0; i < kHidden / kStackThreads; ++i) {
-    v[i] = sh_h[t + i * kStackThreads];
+    v[i] = h[t + i * kStackThreads];
     ss = __builtin_fmaf(v[i], v[i], ss);
   }
   ss = wave_sum(ss);
-  if (lane == 0) sh_red[w] = ss;
-  __syncthreads();
+  if (lane == 0) red[w] = ss;
+  wg_barrier();
   float tot = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kStackWaves; ++i) tot += sh_red[i];
+  for (int i = 0; i < kStackWaves; ++i) tot += red[i];
   const float s = 1.0f / sqrtf(tot * (1.0f / kHidden) + eps);
 #pragma unroll
-  for (int i = 0; i < kHidden / kStackThreads; ++i) sh_u[padded(t + i * kStackThreads)] = v[i] * s;
-  __syncthreads();
+  for (int i = 0; i < kHidden / kStackThreads; ++i) u[padded(t + i * kStackThreads)] = v[i] * s;
+  wg_barrier();
 }
 
-__device__ __forceinline__ void load_f32x32(rsrc_t r, uint32_t off, float* v) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float4 a = bload_f4(r, off + 16 * i);
-    v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
-  }
+// The layer table (device pointers) is copied to LDS at the start, so that a
+// pointer costs an LDS read rather than a scalar-cache miss on the way to a
+// dependent load.  Word indices of one layer's entry:
+enum LayerWord {
+  kWRouter, kWGateC, kWGateS, kWUpC, kWUpS, kWDownC, kWDownS, kWExpTs,
+  kWSgC, kWSgS, kWSgT, kWSuC, kWSuS, kWSuT, kWSdC, kWSdS, kWSdT, kLayerWords
+};
+static_assert(sizeof(flint_moe_layer) == kLayerWords * sizeof(uint64_t), "layer entry is a pointer array");
+static_assert(sizeof(flint_nvfp4) == 3 * sizeof(uint64_t), "head entry is a pointer array");
+
+struct StackLds {
+  float h[kHidden];                                  // residual stream
+  float u[kHidden / 32 * kRowPad];                   // normalised residual, padded rows
+  float logit[kMaxExperts];
+  float hs[kSliceK / 32 * kRowPad];                  // this group's hidden slice, padded rows
+  float part[kGroups * 64];                          // the 8 partial outputs of this workgroup's rows
+  float hp[2 * kStackWGs];                           // head partials (max, index)
+  float red[kStackWaves];
+  float w[kMaxTopK];
+  int32_t idx[kMaxTopK];
+  int32_t cand_k[kCommWaves * kMaxTopK];  // top-k candidates (keys) of each communication wave
+  int32_t cand_i[kCommWaves * kMaxTopK];
+  float bv[kStackWaves];
+  int32_t bi[kStackWaves];
+  int32_t bad;
+  uint64_t tab[kMaxStackLayers * kLayerWords + 3];   // layer table, then the head
+  int64_t tr[(kTraceMaxLayers + 1) * kTracePoints];  // phase stamps of the first token
+};
+
+// pointer word of the LDS table as a wave-uniform (scalar) pointer
+template <class T>
+__device__ __forceinline__ T* tab_ptr(const StackLds& S, int word) {
+  const uint64_t v = S.tab[word];
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
 }
 
-__device__ __forceinline__ float dot32(const float* a, const float* b) {
-  float acc = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) acc = __builtin_fmaf(a[i], b[i], acc);
-  return acc;
-}
+// Block and wave coordinates shared by both roles.
+struct StackCoord {
+  int t, lane, wv, g, li;
+  int L, E, I, k, Is, V;
+  int Ix, Isx, nroutedx;
+  uint32_t base;
+  bool tracing;
+};
 
-__global__ __launch_bounds__(kStackThreads, 1) void k_stack_decode(StackParams P,
-                                                                  const StackTable* __restrict__ table) {
-  __shared__ __align__(16) float sh_h[kHidden];
-  __shared__ __align__(16) float sh_u[kHidden / 32 * kRowPad];
-  __shared__ __align__(16) float sh_logit[kMaxExperts];
-  __shared__ __align__(16) float sh_hs[kSliceK / 32 * kRowPad];
-  __shared__ __align__(16) float sh_part[kGroups * 64];
-  __shared__ __align__(16) float sh_hp[2 * kStackWGs];
-  __shared__ float sh_red[kStackWaves];
-  __shared__ int32_t sh_idx[kMaxTopK];
-  __shared__ float sh_w[kMaxTopK];
-  __shared__ float sh_bv[kStackWaves];
-  __shared__ int sh_bi[kStackWaves];
-  __shared__ int sh_bad;
-
-  // the wave index is uniform across a wave: say so, so that everything
-  // derived from it (row choices, buffer resources) stays in scalar registers
-  const int t = threadIdx.x, lane = t & 63, wv = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int g = blockIdx.x % kGroups, li = blockIdx.x / kGroups;
-  const int L = P.L, E = P.E, I = P.I, k = P.k, Is = P.Is, V = P.V;
-  const int Ix = I / kGroups, Isx = Is / kGroups;  // this group's slice widths
-  const int nroutedx = k * Ix;                     // routed rows of the slice (384)
-  // Wave roles.  A wave's loads complete in issue order, so a wave polling
-  // for an exchange must not have weight loads in flight: waves 0-3 poll
-  // every exchange and compute the routed gate/up rows (whose loads they
-  // consume before polling); waves 4-7 compute the router, shared and down
-  // rows and hold the loads issued ahead of time.
-  const bool comm = wv < kCommWaves;
-  const int lw = wv - kCommWaves;
-  if (t == 0) sh_bad = 0;
-  __syncthreads();
-  WaitCtx wc{P.ctrl + 1, &sh_bad};
-  if (ld_dev_u32(P.ctrl + 1)) return;  // an earlier call gave up: do nothing
-  const uint32_t base = ld_dev_u32(P.ctrl);
-  // phase timestamps (first token only) of one workgroup on XCD 0 and one on XCD 7
-  // (workgroup-uniform pointers, written by thread 0 only)
-  int64_t* trace = nullptr;
-  if (P.trace && (blockIdx.x == 0 || blockIdx.x == kStackWGs - 1))
-    trace = P.trace + (blockIdx.x == 0 ? 0 : (size_t)(L + 1) * kTracePoints);
-  int64_t* trace_all = P.trace ? P.trace + 2 * (size_t)(L + 1) * kTracePoints +
-                                     (size_t)blockIdx.x * kTracePoints : nullptr;
-#define FLINT_TRACE(l_, i_)                                                                         \
-  do {                                                                                               \
-    if (trace && t == 0 && tok == 0) trace[(size_t)(l_) * kTracePoints + (i_)] = wall_clock64();     \
-    if (trace_all && t == 0 && tok == 0 && (l_) == 1) trace_all[(i_)] = wall_clock64();              \
+// One role's pass over all tokens.  Both roles execute the same sequence of
+// workgroup barriers (marked B1..B7 per layer, H1..H4 per token) and leave
+// at the same barrier on error; returns false then.
+//
+// Communication role (waves 0-3): polls every exchange, takes the top k, and
+// computes 2 of the 12 routed gate/up pairs per wave and workgroup.  A wave's
+// loads complete in issue order, so a wave that polls must not have weight
+// loads in flight.
+// Loading role (waves 4-7): router rows and the shared expert's gate/up
+// (phase A), one routed gate/up pair and the down-projection operands
+// (phase B), the partial outputs (phase C), the residual rows (phase D), and
+// the next layer's router and shared rows, requested ahead of time.
+template <bool kComm>
+__device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& C) {
+  const int t = C.t, lane = C.lane, wv = C.wv, g = C.g, li = C.li;
+  const int L = C.L, E = C.E, I = C.I, k = C.k, Is = C.Is, V = C.V;
+  const int Ix = C.Ix, Isx = C.Isx, nroutedx = C.nroutedx;
+  const int lw = wv - kCommWaves;  // loading-wave index (loading role)
+  WaitCtx wc{P.ctrl + 1, &S.bad};
+#define FLINT_TRACE_AT(tid_, l_, i_)                                                                 \
+  do {                                                                                                 \
+    if (C.tracing && t == (tid_) && tok == 0) S.tr[(l_) * kTracePoints + (i_)] = wall_clock64();       \
   } while (0)
+#define FLINT_TRACE(l_, i_) FLINT_TRACE_AT(0, l_, i_)
+#define FLINT_TRACE_LOAD(l_, i_) FLINT_TRACE_AT(kCommThreads, l_, i_)
 
-  // phase-A operands of a load wave: router rows ra0, ra1 and shared pair qa
-  const int ra0 = li + kGroupWGs * (2 * lw), ra1 = li + kGroupWGs * (2 * lw + 1);
+  // ---- loading role: phase-A operands, requested one layer ahead and held
+  // in registers: the first loading wave holds router row blockIdx.x (every
+  // router row is read by exactly one workgroup of the chip), every loading
+  // wave one pair qa of the shared expert and its tensor scales.
+  // Unconditional loads (a wave without a row reads row 0 and ignores it), so
+  // that no branch join forces an early wait on the data.
+  const int rrow = blockIdx.x;  // router row of this workgroup (if < E)
   const int qa = li + kGroupWGs * lw;
-  float wr0[32], wr1[32];
-  uint4 cgs, cus;
+  float4 wr[kHidden / 256];
+  uint4 cgs = make_uint4(0, 0, 0, 0), cus = make_uint4(0, 0, 0, 0);
   uint32_t sgs = 0, sus = 0;
-  bool prefetched = false;
-  // unconditional loads (a wave with no row reads row 0 and ignores it), so
-  // that no branch join forces an early wait on the data
-  auto load_phase_a = [&](const flint_moe_layer& Lx) {
-    const rsrc_t rr = make_rsrc(Lx.router, (uint64_t)E * kHidden * 4);
-    const uint32_t r0 = ra0 < E ? (uint32_t)ra0 : 0u, r1 = ra1 < E ? (uint32_t)ra1 : 0u;
-    load_f32x32(rr, (r0 * kHidden + 32 * lane) * 4, wr0);
-    load_f32x32(rr, (r1 * kHidden + 32 * lane) * 4, wr1);
+  float tgs = 0.0f, tus = 0.0f;
+  bool have_a = false;  // this layer's phase-A operands were requested earlier
+  auto load_phase_a = [&](int lx) {
+    const int w0 = lx * kLayerWords;
+    if (lw == 0) {
+      const rsrc_t rr = make_rsrc(tab_ptr<const float>(S, w0 + kWRouter), (uint64_t)E * kHidden * 4);
+      const uint32_t r0 = rrow < E ? (uint32_t)rrow : 0u;
+#pragma unroll
+      for (int i = 0; i < kHidden / 256; ++i) wr[i] = bload_f4(rr, (r0 * kHidden + 256 * i) * 4 + 16 * lane);
+    }
     const uint32_t row = (uint32_t)(g * Isx + (qa < Isx ? qa : 0));
-    cgs = bload_u4(make_rsrc(Lx.shared_gate.codes, (uint64_t)Is * kHidden / 2), row * (kHidden / 2) + 16 * lane);
-    sgs = bload_u16(make_rsrc(Lx.shared_gate.scales, (uint64_t)Is * kHidden / 16), row * (kHidden / 16) + 2 * lane);
-    cus = bload_u4(make_rsrc(Lx.shared_up.codes, (uint64_t)Is * kHidden / 2), row * (kHidden / 2) + 16 * lane);
-    sus = bload_u16(make_rsrc(Lx.shared_up.scales, (uint64_t)Is * kHidden / 16), row * (kHidden / 16) + 2 * lane);
+    const uint64_t nc = (uint64_t)Is * kHidden / 2, ns = (uint64_t)Is * kHidden / 16;
+    cgs = bload_u4(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSgC), nc), row * (kHidden / 2) + 16 * lane);
+    sgs = bload_u16(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSgS), ns), row * (kHidden / 16) + 2 * lane);
+    cus = bload_u4(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSuC), nc), row * (kHidden / 2) + 16 * lane);
+    sus = bload_u16(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSuS), ns), row * (kHidden / 16) + 2 * lane);
+    tgs = bload_f32(make_rsrc(tab_ptr<const float>(S, w0 + kWSgT), 4), 0);
+    tus = bload_f32(make_rsrc(tab_ptr<const float>(S, w0 + kWSuT), 4), 0);
+  };
+  // router row (registers) . normalised activations: lane i takes columns
+  // 256 c + 4 i .. 256 c + 4 i + 3, c = 0..7
+  auto router_dot = [&]() {
+    float4 u[kHidden / 256];
+#pragma unroll
+    for (int c = 0; c < kHidden / 256; ++c) u[c] = *reinterpret_cast<const float4*>(S.u + padded(256 * c + 4 * lane));
+    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;  // four chains for latency
+#pragma unroll
+    for (int c = 0; c < kHidden / 256; ++c) {
+      a0 = __builtin_fmaf(wr[c].x, u[c].x, a0);
+      a1 = __builtin_fmaf(wr[c].y, u[c].y, a1);
+      a2 = __builtin_fmaf(wr[c].z, u[c].z, a2);
+      a3 = __builtin_fmaf(wr[c].w, u[c].w, a3);
+    }
+    return wave_sum((a0 + a1) + (a2 + a3));
+  };
+
+  // SwiGLU of routed gate/up pair p of this group's slice: loads ...
+  struct PairOps {
+    uint4 cg, cu;
+    uint32_t sg, su;
+    float Sg, Su;
+  };
+  auto load_pair = [&](int w0, int p) {
+    const int p_ = p < nroutedx ? p : 0;
+    const int slot = p_ / Ix, rl = p_ % Ix;
+    const int e = S.idx[slot];
+    const uint32_t row = (uint32_t)(e * I + g * Ix + rl);
+    const uint64_t nc = (uint64_t)E * I * kHidden / 2, ns = (uint64_t)E * I * kHidden / 16;
+    const rsrc_t rts = make_rsrc(tab_ptr<const float>(S, w0 + kWExpTs), (uint64_t)E * 3 * 4);
+    PairOps o;
+    o.cg = bload_u4(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWGateC), nc), row * (kHidden / 2) + 16 * lane);
+    o.cu = bload_u4(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWUpC), nc), row * (kHidden / 2) + 16 * lane);
+    o.sg = bload_u16(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWGateS), ns), row * (kHidden / 16) + 2 * lane);
+    o.su = bload_u16(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWUpS), ns), row * (kHidden / 16) + 2 * lane);
+    o.Sg = bload_f32(rts, (uint32_t)(3 * e + 0) * 4);
+    o.Su = bload_f32(rts, (uint32_t)(3 * e + 1) * 4);
+    return o;
+  };
+  // ... and the SwiGLU value g(x) * u(x) with g = silu(gate . x)
+  auto pair_value = [&](const PairOps& o, const float* xv) {
+    const float gv = wave_sum(nvfp4_lane_dot32(o.cg, o.sg, xv)) * o.Sg;
+    const float av = wave_sum(nvfp4_lane_dot32(o.cu, o.su, xv)) * o.Su;
+    return silu(gv) * av;
   };
 
   const rsrc_t rx = make_rsrc(P.x, (uint64_t)P.T * kHidden * 4);
@@ -245,237 +361,246 @@ __global__ __launch_bounds__(kStackThreads, 1) void k_stack_decode(StackParams P
     // residual stream <- x_t
 #pragma unroll
     for (int i = 0; i < kHidden / kStackThreads; ++i)
-      sh_h[t + i * kStackThreads] = bload_f32(rx, (uint32_t)(tok * kHidden + t + i * kStackThreads) * 4);
-    __syncthreads();
+      S.h[t + i * kStackThreads] = bload_f32(rx, (uint32_t)(tok * kHidden + t + i * kStackThreads) * 4);
+    wg_barrier();
 
     for (int l = 0; l < L; ++l) {
-      const flint_moe_layer& Lw = table->layers[l];
+      const int w0 = l * kLayerWords;
       const int par = l & 1;
-      const uint32_t ep0 = base + 1u + (uint32_t)((tok * (L + 1) + l) * 4);
+      const uint32_t ep0 = C.base + 1u + (uint32_t)((tok * (L + 1) + l) * 4);
       uint64_t* s2 = P.s2 + ((size_t)par * kGroups + g) * kMaxExperts;
       uint64_t* s3 = P.s3 + ((size_t)par * kGroups + g) * kSliceK;
+      uint64_t* s4a = P.s4a + (size_t)par * kGroups * kHidden;
       uint64_t* s4b = P.s4b + ((size_t)par * kGroups + g) * kHidden;
 
       // ---------------------------------------------------------- phase A
       FLINT_TRACE(l, 0);
-      if (!comm && !prefetched) load_phase_a(Lw);
-      prefetched = false;
-      rms_to_u(sh_h, sh_u, sh_red, P.eps);
+      if (!kComm && !have_a) {
+        load_phase_a(l);
+      }
+      rms_to_u(S.h, S.u, S.red, P.eps);  // B1, B2
       FLINT_TRACE(l, 1);
       float xv[32];  // this lane's 32 normalised activations (phases A and B)
-      lds_x32(sh_u + kRowPad * lane, xv);
-      if (!comm) {
-        if (ra0 < E) {
-          const float acc = wave_sum(dot32(wr0, xv));
-          if (lane == 0) put_pair(&s2[ra0], acc, ep0);
-        }
-        if (ra1 < E) {
-          const float acc = wave_sum(dot32(wr1, xv));
-          if (lane == 0) put_pair(&s2[ra1], acc, ep0);
-        }
-        if (qa < Isx) {
-          const float gv = wave_sum(nvfp4_lane_dot32(cgs, sgs, xv)) *
-                           bload_f32(make_rsrc(Lw.shared_gate.tscale, 4), 0);
-          const float av = wave_sum(nvfp4_lane_dot32(cus, sus, xv)) *
-                           bload_f32(make_rsrc(Lw.shared_up.tscale, 4), 0);
-          if (lane == 0) put_pair(&s3[nroutedx + qa], silu(gv) * av, ep0 + 1);
-        }
+      lds_x32(S.u + kRowPad * lane, xv);
+      // router logit blockIdx.x, stored into the logit exchange of every group
+      if (!kComm && lw == 0 && rrow < E) {
+        const float acc = router_dot();
+        if (lane < kGroups) put_pair<Scope::kDevice>(&P.s2[((size_t)par * kGroups + lane) * kMaxExperts + rrow], acc, ep0);
       }
+      if constexpr (kComm) {
+        poll_pairs<Scope::kDevice>(s2, E, ep0, S.logit, wc);
+      } else {
+        FLINT_TRACE_LOAD(l, 8);
+        if (qa < Isx) {
+          const float gv = wave_sum(nvfp4_lane_dot32(cgs, sgs, xv)) * tgs;
+          const float av = wave_sum(nvfp4_lane_dot32(cus, sus, xv)) * tus;
+          if (lane == 0) put_pair<Scope::kXcd>(&s3[nroutedx + qa], silu(gv) * av, ep0 + 1);
+        }
+        FLINT_TRACE_LOAD(l, 9);
+        // the next layer's router and shared rows (the next token's first
+        // layer after the last one) do not depend on this token: request them
+        // now, while memory is idle during the logit exchange and top-k
+        const int next = l + 1 < L ? l + 1 : (tok + 1 < P.T ? 0 : -1);
+        __builtin_amdgcn_sched_barrier(0);
+        have_a = next >= 0;
+        if (have_a) load_phase_a(next);
+        FLINT_TRACE_LOAD(l, 10);
+      }
+      wg_barrier();  // B3: logits in LDS
+      if (S.bad) return false;
       FLINT_TRACE(l, 2);
 
       // ---------------------------------------------------------- phase B
-      wait_pairs(s2, E, ep0, sh_logit, wc);
-      if (sh_bad) return;
-      FLINT_TRACE(l, 3);
-      if (wv == 0) {
-        // top-k in one wave: each lane holds 4 logits sorted by (value desc,
-        // index asc); k rounds of a wave maximum (DPP), ties to the lowest index
-        float v[4];
-        int id[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          id[q] = lane + 64 * q;
-          v[q] = id[q] < E ? sh_logit[id[q]] : -FLT_MAX;
-          if (id[q] >= E) id[q] = INT_MAX;
-        }
-        auto cswap = [&](int a, int b) {
-          const bool sw = v[b] > v[a] || (v[b] == v[a] && id[b] < id[a]);
-          const float tv = sw ? v[b] : v[a];
-          const int ti = sw ? id[b] : id[a];
-          v[b] = sw ? v[a] : v[b];
-          id[b] = sw ? id[a] : id[b];
-          v[a] = tv;
-          id[a] = ti;
-        };
-        cswap(0, 1); cswap(2, 3); cswap(0, 2); cswap(1, 3); cswap(1, 2);
-        float first = 0.0f, z = 0.0f, my_v = 0.0f;
-        int my_i = 0;
-        for (int r = 0; r < k; ++r) {
-          const float m = wave_max_dpp(v[0]);
-          const int mi = wave_min_dpp(v[0] == m ? id[0] : INT_MAX);
-          if (r == 0) first = m;
-          z += __expf(m - first);
-          if (lane == r) { my_v = m; my_i = mi; }
-          if (id[0] == mi) {
-            v[0] = v[1]; id[0] = id[1];
-            v[1] = v[2]; id[1] = id[2];
-            v[2] = v[3]; id[2] = id[3];
-            v[3] = -FLT_MAX; id[3] = INT_MAX;
-          }
-        }
+      // top-k in two stages on order-preserving integer keys of the logits.
+      // Stage 1: communication wave w takes the top k of logits 64 w ..
+      // 64 w + 63 (one per lane); each round takes the wave maximum and, by a
+      // ballot, its lowest lane, which holds the lowest index among equal
+      // values, and knocks that lane out.  Stage 2: wave 0 does the same over
+      // the 4 k candidates, laid out by wave and then rank, so that among
+      // equal values the lowest lane again holds the lowest index.
+      auto topk_round = [&](int& key, int r, int& my_key, int& my_l) {
+        const int m = wave_max_i32(key);
+        const uint64_t at = __builtin_amdgcn_ballot_w64(key == m);
+        const int lmax = (int)__builtin_ctzll(at);
+        if (lane == r) { my_key = m; my_l = lmax; }
+        if (lane == lmax) key = INT_MIN;
+      };
+      if constexpr (kComm) {
+        const int id = 64 * wv + lane;
+        int key = id < E ? ord_key(S.logit[id]) : INT_MIN + 1;
+        int ck = INT_MIN, cl = 0;
+        for (int r = 0; r < k; ++r) topk_round(key, r, ck, cl);
         if (lane < k) {
-          sh_idx[lane] = my_i;
-          sh_w[lane] = __expf(my_v - first) / z;
+          S.cand_k[kMaxTopK * wv + lane] = ck;
+          S.cand_i[kMaxTopK * wv + lane] = 64 * wv + cl;
         }
       }
-      __syncthreads();
-      FLINT_TRACE(l, 4);
-      if (P.routes && blockIdx.x == 0 && t < k) P.routes[((size_t)tok * L + l) * k + t] = sh_idx[t];
+      wg_barrier();  // B3b: candidates in LDS
+      if constexpr (kComm) {
+        if (wv == 0) {
+          const bool valid = lane < kCommWaves * kMaxTopK && (lane % kMaxTopK) < k;
+          int key = valid ? S.cand_k[lane] : INT_MIN;
+          const int ci = valid ? S.cand_i[lane] : INT_MAX;
+          int my_key = INT_MIN, my_l = 0;
+          for (int r = 0; r < k; ++r) topk_round(key, r, my_key, my_l);
+          const int my_i = __builtin_amdgcn_ds_bpermute(my_l << 2, ci);
+          // softmax over the k chosen logits (lane r holds the r-th; the
+          // first is the largest)
+          const float my_v = ord_key_value(my_key);
+          const float first = lane_f32(my_v, 0);
+          const float e = lane < k ? __expf(my_v - first) : 0.0f;
+          const float z = lane_f32(row16_sum(e), 0);
+          if (lane < k) {
+            S.idx[lane] = my_i;
+            S.w[lane] = e / z;
+          }
+          FLINT_TRACE(l, 15);
+        }
+      }
+      wg_barrier();  // B4: top-k in LDS
+      FLINT_TRACE(l, 3);
 
-      // routed gate/up (communication waves): pairs p = li + 32 (wv + 4 pp)
-      // down-projection operands (load waves): output rows n = 64 li + 16 lw
+      // routed gate/up pairs p = li + 32 q: q = wv + 4 pp (pp < 2) for a
+      // communication wave, q = 8 + lw for a loading wave.
+      // Down-projection operands (every wave): output rows n = 64 li + 8 wv
       // + 4 pc + lane/16, 16 lanes per row, lane chunk j = 32 columns of the
-      // slice; chunks j < 12 are routed columns, the rest shared ones, both
-      // loads are issued for every lane and the right one is picked at use
+      // slice; chunks j < 12 are routed columns, the rest shared ones.  These
+      // loads are issued after the wave's gate/up loads, so the gate/up
+      // arithmetic does not wait for them, and they arrive well before the
+      // hidden slice is complete.
       const int j = lane & 15;
       const bool routed = 32 * j < nroutedx;
       const int dslot = routed ? (32 * j) / Ix : 0;
-      uint4 cd[kDownPasses];
-      uint32_t sd[kDownPasses];
+      uint4 cdr[kDownPasses], cds[kDownPasses];
+      uint32_t sdr[kDownPasses], sds[kDownPasses];
       float dts = 0.0f, sts = 0.0f, dw = 0.0f;
-      if (comm) {
-        const rsrc_t rgc = make_rsrc(Lw.gate_codes, (uint64_t)E * I * kHidden / 2);
-        const rsrc_t rgs = make_rsrc(Lw.gate_scales, (uint64_t)E * I * kHidden / 16);
-        const rsrc_t ruc = make_rsrc(Lw.up_codes, (uint64_t)E * I * kHidden / 2);
-        const rsrc_t rus = make_rsrc(Lw.up_scales, (uint64_t)E * I * kHidden / 16);
-        const rsrc_t rts = make_rsrc(Lw.expert_tscales, (uint64_t)E * 3 * 4);
-        uint4 cg[kGateUpPerWave], cu[kGateUpPerWave];
-        uint32_t sg[kGateUpPerWave], su[kGateUpPerWave];
-        float Sg[kGateUpPerWave], Su[kGateUpPerWave];
-#pragma unroll
-        for (int pp = 0; pp < kGateUpPerWave; ++pp) {
-          const int p = li + kGroupWGs * (wv + kCommWaves * pp);
-          const int p_ = p < nroutedx ? p : 0;
-          const int slot = p_ / Ix, rl = p_ % Ix;
-          const int e = sh_idx[slot];
-          const uint32_t row = (uint32_t)(e * I + g * Ix + rl);
-          cg[pp] = bload_u4(rgc, row * (kHidden / 2) + 16 * lane);
-          cu[pp] = bload_u4(ruc, row * (kHidden / 2) + 16 * lane);
-          sg[pp] = bload_u16(rgs, row * (kHidden / 16) + 2 * lane);
-          su[pp] = bload_u16(rus, row * (kHidden / 16) + 2 * lane);
-          Sg[pp] = bload_f32(rts, (uint32_t)(3 * e + 0) * 4);
-          Su[pp] = bload_f32(rts, (uint32_t)(3 * e + 1) * 4);
-        }
-#pragma unroll
-        for (int pp = 0; pp < kGateUpPerWave; ++pp) {
-          const int p = li + kGroupWGs * (wv + kCommWaves * pp);
-          if (p < nroutedx) {
-            const float gv = wave_sum(nvfp4_lane_dot32(cg[pp], sg[pp], xv)) * Sg[pp];
-            const float av = wave_sum(nvfp4_lane_dot32(cu[pp], su[pp], xv)) * Su[pp];
-            if (lane == 0) put_pair(&s3[p], silu(gv) * av, ep0 + 1);
-          }
-        }
-      } else {
-        const rsrc_t rdc = make_rsrc(Lw.down_codes, (uint64_t)E * kHidden * I / 2);
-        const rsrc_t rds = make_rsrc(Lw.down_scales, (uint64_t)E * kHidden * I / 16);
-        const rsrc_t rsdc = make_rsrc(Lw.shared_down.codes, (uint64_t)kHidden * Is / 2);
-        const rsrc_t rsds = make_rsrc(Lw.shared_down.scales, (uint64_t)kHidden * Is / 16);
+      auto load_down = [&]() {
+        const rsrc_t rdc = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWDownC), (uint64_t)E * kHidden * I / 2);
+        const rsrc_t rds = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWDownS), (uint64_t)E * kHidden * I / 16);
+        const rsrc_t rsdc = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSdC), (uint64_t)kHidden * Is / 2);
+        const rsrc_t rsds = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSdS), (uint64_t)kHidden * Is / 16);
         const int doff = routed ? (32 * j) % Ix : 0;
-        const int de = sh_idx[dslot];
+        const int de = S.idx[dslot];
         const int rcol = g * Ix + doff, scol = routed ? 0 : g * Isx + (32 * j - nroutedx);
+        // every lane issues both loads; the one that is not its own reads
+        // past the end of its buffer, which returns zeros and touches no
+        // memory, so the pair combines with an OR and no branch is needed
+        const uint32_t oob_c = (uint32_t)((uint64_t)E * kHidden * I / 2);
+        const uint32_t oob_s = (uint32_t)((uint64_t)kHidden * Is / 2);
 #pragma unroll
         for (int pc = 0; pc < kDownPasses; ++pc) {
-          const int n = 64 * li + 16 * lw + 4 * pc + (lane >> 4);
+          const int n = 64 * li + 8 * wv + 4 * pc + (lane >> 4);
           const uint32_t rrow = (uint32_t)(de * kHidden + n);
-          // lanes of routed and of shared chunks load into the same registers
-          // under their own execution masks
-          if (routed) {
-            cd[pc] = bload_u4(rdc, rrow * (I / 2) + rcol / 2);
-            sd[pc] = bload_u16(rds, rrow * (I / 16) + rcol / 16);
-          } else {
-            cd[pc] = bload_u4(rsdc, (uint32_t)(n * (Is / 2) + scol / 2));
-            sd[pc] = bload_u16(rsds, (uint32_t)(n * (Is / 16) + scol / 16));
+          cdr[pc] = bload_u4(rdc, routed ? rrow * (I / 2) + rcol / 2 : oob_c);
+          sdr[pc] = bload_u16(rds, routed ? rrow * (I / 16) + rcol / 16 : oob_c / 8);
+          cds[pc] = bload_u4(rsdc, routed ? oob_s : (uint32_t)(n * (Is / 2) + scol / 2));
+          sds[pc] = bload_u16(rsds, routed ? oob_s / 8 : (uint32_t)(n * (Is / 16) + scol / 16));
+        }
+        dts = bload_f32(make_rsrc(tab_ptr<const float>(S, w0 + kWExpTs), (uint64_t)E * 3 * 4),
+                        (uint32_t)(3 * de + 2) * 4);
+        sts = bload_f32(make_rsrc(tab_ptr<const float>(S, w0 + kWSdT), 4), 0);
+        dw = S.w[dslot];
+      };
+      if constexpr (kComm) {
+        PairOps o[kGateUpComm];
+#pragma unroll
+        for (int pp = 0; pp < kGateUpComm; ++pp) o[pp] = load_pair(w0, li + kGroupWGs * (wv + kCommWaves * pp));
+        load_down();
+#pragma unroll
+        for (int pp = 0; pp < kGateUpComm; ++pp) {
+          const int p = li + kGroupWGs * (wv + kCommWaves * pp);
+          if (p < nroutedx) {
+            const float hval = pair_value(o[pp], xv);
+            if (lane == 0) put_pair<Scope::kXcd>(&s3[p], hval, ep0 + 1);
           }
         }
-        dts = bload_f32(make_rsrc(Lw.expert_tscales, (uint64_t)E * 3 * 4), (uint32_t)(3 * de + 2) * 4);
-        sts = bload_f32(make_rsrc(Lw.shared_down.tscale, 4), 0);
-        dw = sh_w[dslot];
+        FLINT_TRACE(l, 4);
+        poll_pairs<Scope::kXcd>(s3, kSliceK, ep0 + 1, S.hs, wc, true);
+      } else {
+        FLINT_TRACE_LOAD(l, 11);
+        if (P.routes && blockIdx.x == 0 && t - kCommThreads < k)
+          P.routes[((size_t)tok * L + l) * k + (t - kCommThreads)] = S.idx[t - kCommThreads];
+        const int p = li + kGroupWGs * (2 * kCommWaves + lw);
+        const PairOps o = load_pair(w0, p);
+        load_down();
+        if (p < nroutedx) {
+          const float hval = pair_value(o, xv);
+          if (lane == 0) put_pair<Scope::kXcd>(&s3[p], hval, ep0 + 1);
+        }
+        FLINT_TRACE_LOAD(l, 12);
       }
+      wg_barrier();  // B5: hidden slice in LDS
+      if (S.bad) return false;
       FLINT_TRACE(l, 5);
 
       // ---------------------------------------------------------- phase C
-      wait_pairs(s3, kSliceK, ep0 + 1, sh_hs, wc, true);
-      if (sh_bad) return;
-      FLINT_TRACE(l, 6);
-      if (!comm) {
+      {
         float hv[32];
-        lds_x32(sh_hs + kRowPad * j, hv);
+        lds_x32(S.hs + kRowPad * j, hv);
         const float coef = routed ? dw * dts : sts;
 #pragma unroll
         for (int pc = 0; pc < kDownPasses; ++pc) {
-          const float acc = row16_sum(coef * nvfp4_lane_dot32(cd[pc], sd[pc], hv));
-          const int n = 64 * li + 16 * lw + 4 * pc + (lane >> 4);
-          if (j == 0) put_pair(&P.s4a[((size_t)par * kGroups + g) * kHidden + n], acc, ep0 + 2);
-        }
-        // the next layer's router and shared rows do not depend on this
-        // token: load them now, while the partial outputs are exchanged
-        if (l + 1 < L) {
-          __builtin_amdgcn_sched_barrier(0);  // keep these loads after the down rows
-          load_phase_a(table->layers[l + 1]);
-          prefetched = true;
+          const uint4 c = make_uint4(cdr[pc].x | cds[pc].x, cdr[pc].y | cds[pc].y, cdr[pc].z | cds[pc].z,
+                                     cdr[pc].w | cds[pc].w);
+          const float acc = row16_sum(coef * nvfp4_lane_dot32(c, sdr[pc] | sds[pc], hv));
+          const int n = 64 * li + 8 * wv + 4 * pc + (lane >> 4);
+          if (j == 0) put_pair<Scope::kDevice>(&s4a[(size_t)g * kHidden + n], acc, ep0 + 2);
         }
       }
-      FLINT_TRACE(l, 7);
-
-      // ---------------------------------------------------------- phase D
-      if (comm) {  // rows 64 li .. 64 li + 63 of every group's partial output
-        __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            P.s4a + (size_t)par * kGroups * kHidden, 0, kGroups * kHidden * 8, 0x00020000);
+      if constexpr (kComm) {
+        // rows 64 li .. 64 li + 63 of every group's partial output
+        __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(s4a, 0, kGroups * kHidden * 8, 0x00020000);
         const int gg = t >> 5, cc = t & 31;  // kCommThreads == kGroups * 32 chunks
         const int off = (gg * kHidden + 64 * li + 2 * cc) * 8;
         uint32_t spins = 0;
         while (true) {
           auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 16);
           if (v[1] == ep0 + 2 && v[3] == ep0 + 2) {
-            sh_part[gg * 64 + 2 * cc] = __uint_as_float(v[0]);
-            sh_part[gg * 64 + 2 * cc + 1] = __uint_as_float(v[2]);
+            S.part[gg * 64 + 2 * cc] = __uint_as_float(v[0]);
+            S.part[gg * 64 + 2 * cc + 1] = __uint_as_float(v[2]);
             break;
           }
-          ++spins;
-          if (spins > kSpinLimit || ((spins & 1023) == 0 && ld_dev_u32(wc.err))) {
-            atomicOr(wc.err, 1u);
-            sh_bad = 1;
-            break;
-          }
-          poll_backoff();
+          if (poll_gave_up(spins, wc)) break;
+        }
+      } else {
+        FLINT_TRACE_LOAD(l, 13);
+      }
+      wg_barrier();  // B6: partial outputs of this workgroup's rows in LDS
+      if (S.bad) return false;
+      FLINT_TRACE(l, 6);
+
+      // ---------------------------------------------------------- phase D
+      // the first loading wave adds the partials (fixed order) to its rows of
+      // the residual and publishes them; the communication waves collect the
+      // group's new residual (the rows this workgroup owns arrive only after
+      // they were read here)
+      if constexpr (kComm) {
+        poll_pairs<Scope::kXcd>(s4b, kHidden, ep0 + 3, S.h, wc);
+      } else {
+        if (lw == 0) {
+          float y = 0.0f;
+#pragma unroll
+          for (int gg = 0; gg < kGroups; ++gg) y += S.part[gg * 64 + lane];
+          put_pair<Scope::kXcd>(&s4b[64 * li + lane], S.h[64 * li + lane] + y, ep0 + 3);
+          FLINT_TRACE_LOAD(l, 14);
         }
       }
-      __syncthreads();
-      if (sh_bad) return;
-      FLINT_TRACE(l, 8);
-      if (t < 64) {
-        float y = 0.0f;
-#pragma unroll
-        for (int gg = 0; gg < kGroups; ++gg) y += sh_part[gg * 64 + t];
-        put_pair(&s4b[64 * li + t], sh_h[64 * li + t] + y, ep0 + 3);
-      }
-      __syncthreads();
-      wait_pairs(s4b, kHidden, ep0 + 3, sh_h, wc);
-      if (sh_bad) return;
-      FLINT_TRACE(l, 9);
+      wg_barrier();  // B7: new residual in LDS
+      if (S.bad) return false;
+      FLINT_TRACE(l, 7);
     }
 
     // -------------------------------------------------------------- head
     FLINT_TRACE(L, 0);
-    rms_to_u(sh_h, sh_u, sh_red, P.eps);
-    const uint32_t eph = base + 1u + (uint32_t)((tok * (L + 1) + L) * 4);
+    rms_to_u(S.h, S.u, S.red, P.eps);  // H1, H2
+    const uint32_t eph = C.base + 1u + (uint32_t)((tok * (L + 1) + L) * 4);
     {
       float xv[32];
-      lds_x32(sh_u + kRowPad * lane, xv);
-      const flint_nvfp4& Hd = table->head;
-      const float S = bload_f32(make_rsrc(Hd.tscale, 4), 0);
-      const rsrc_t rhc = make_rsrc(Hd.codes, (uint64_t)V * kHidden / 2);
-      const rsrc_t rhs = make_rsrc(Hd.scales, (uint64_t)V * kHidden / 16);
+      lds_x32(S.u + kRowPad * lane, xv);
+      const int hw = kMaxStackLayers * kLayerWords;
+      const float Sh = bload_f32(make_rsrc(tab_ptr<const float>(S, hw + 2), 4), 0);
+      const rsrc_t rhc = make_rsrc(tab_ptr<const uint8_t>(S, hw + 0), (uint64_t)V * kHidden / 2);
+      const rsrc_t rhs = make_rsrc(tab_ptr<const uint8_t>(S, hw + 1), (uint64_t)V * kHidden / 16);
       float* lg = P.logits ? P.logits + (size_t)tok * V : nullptr;
       const int gw = blockIdx.x * kStackWaves + wv, nw = kStackWGs * kStackWaves;
       float best = -FLT_MAX;
@@ -491,7 +616,7 @@ __global__ __launch_bounds__(kStackThreads, 1) void k_stack_decode(StackParams P
         }
 #pragma unroll
         for (int q = 0; q < kHeadRowsPerWave; ++q) {
-          const float v = wave_sum(nvfp4_lane_dot32(c[q], s[q], xv)) * S;
+          const float v = wave_sum(nvfp4_lane_dot32(c[q], s[q], xv)) * Sh;
           const int row = r0 + q;
           if (row < V) {
             if (lane == 0 && lg) lg[row] = v;
@@ -499,46 +624,93 @@ __global__ __launch_bounds__(kStackThreads, 1) void k_stack_decode(StackParams P
           }
         }
       }
-      if (lane == 0) { sh_bv[wv] = best; sh_bi[wv] = besti; }
-      __syncthreads();
+      if (lane == 0) { S.bv[wv] = best; S.bi[wv] = besti; }
+      wg_barrier();  // H3
       FLINT_TRACE(L, 1);
-      if (t == 0) {
-        float bv = sh_bv[0];
-        int bi = sh_bi[0];
+      if (!kComm && t == kCommThreads) {
+        float bv = S.bv[0];
+        int bi = S.bi[0];
         for (int w = 1; w < kStackWaves; ++w)
-          if (sh_bv[w] > bv || (sh_bv[w] == bv && sh_bi[w] < bi)) { bv = sh_bv[w]; bi = sh_bi[w]; }
+          if (S.bv[w] > bv || (S.bv[w] == bv && S.bi[w] < bi)) { bv = S.bv[w]; bi = S.bi[w]; }
         uint64_t* hp = P.hp + ((size_t)(tok & 1) * kStackWGs + blockIdx.x) * 2;
-        put_pair(hp, bv, eph);
-        put_pair(hp + 1, __int_as_float(bi), eph);
+        put_pair<Scope::kDevice>(hp, bv, eph);
+        put_pair<Scope::kDevice>(hp + 1, __int_as_float(bi), eph);
       }
     }
     // every workgroup waits for all head partials: the token boundary
-    wait_pairs(P.hp + (size_t)(tok & 1) * kStackWGs * 2, 2 * kStackWGs, eph, sh_hp, wc);
-    if (sh_bad) return;
+    if constexpr (kComm) poll_pairs<Scope::kDevice>(P.hp + (size_t)(tok & 1) * kStackWGs * 2, 2 * kStackWGs, eph, S.hp, wc);
+    wg_barrier();  // H4
+    if (S.bad) return false;
     FLINT_TRACE(L, 2);
-    if (wv == 0) {
+    if (kComm && wv == 0) {
       float bv = -FLT_MAX;
       int bi = INT_MAX;
       for (int i = lane; i < kStackWGs; i += 64) {
-        const float v = sh_hp[2 * i];
-        const int id = __float_as_int(sh_hp[2 * i + 1]);
+        const float v = S.hp[2 * i];
+        const int id = __float_as_int(S.hp[2 * i + 1]);
         if (v > bv || (v == bv && id < bi)) { bv = v; bi = id; }
       }
       wave_argmax(bv, bi);
       if (lane == 0 && blockIdx.x == 0) P.argmax[tok] = bi;
     }
-    __syncthreads();
+    wg_barrier();  // H5: S.hp and S.h are rewritten by the next token
   }
-  if (blockIdx.x == 0 && t == 0)
-    st_dev_u32(P.ctrl, base + (uint32_t)(P.T * (P.L + 1) * 4) + 4u);
+  return true;
 #undef FLINT_TRACE
+#undef FLINT_TRACE_LOAD
+#undef FLINT_TRACE_AT
 }
 
-bool stack_persistent_supported(const flint_moe_dims& d) {
-  return d.hidden == kHidden && d.n_experts % 2 == 0 && d.expert_width % 256 == 0 && d.shared_width % 256 == 0 &&
+__global__ __launch_bounds__(kStackThreads, 1) void k_stack_decode(StackParams P,
+                                                                  const StackTable* __restrict__ table) {
+  __shared__ StackLds S;
+  StackCoord C;
+  C.t = threadIdx.x;
+  C.lane = C.t & 63;
+  // the wave index is uniform across a wave: say so, so that the role branch
+  // and everything derived from it stay scalar
+  C.wv = __builtin_amdgcn_readfirstlane(C.t >> 6);
+  C.g = blockIdx.x % kGroups;
+  C.li = blockIdx.x / kGroups;
+  C.L = P.L; C.E = P.E; C.I = P.I; C.k = P.k; C.Is = P.Is; C.V = P.V;
+  C.Ix = C.I / kGroups;
+  C.Isx = C.Is / kGroups;
+  C.nroutedx = C.k * C.Ix;
+  C.tracing = P.trace != nullptr;
+  // layer table (and head) to LDS
+  {
+    const uint64_t* src = reinterpret_cast<const uint64_t*>(table->layers);
+    for (int i = C.t; i < C.L * kLayerWords; i += kStackThreads) S.tab[i] = src[i];
+    const uint64_t* hsrc = reinterpret_cast<const uint64_t*>(&table->head);
+    if (C.t < 3) S.tab[kMaxStackLayers * kLayerWords + C.t] = hsrc[C.t];
+  }
+  if (C.t == 0) S.bad = 0;
+  wg_barrier();
+  if (ld_dev_u32(P.ctrl + 1)) return;  // an earlier call gave up: do nothing
+  if (xcc_id() != (uint32_t)C.g) {     // the in-XCD exchanges need b -> XCD b % 8
+    if (C.t == 0) atomicOr(P.ctrl + 1, 2u);
+    return;
+  }
+  C.base = ld_dev_u32(P.ctrl);
+  const bool ok = C.wv < kCommWaves ? stack_role<true>(P, S, C) : stack_role<false>(P, S, C);
+  if (!ok) return;
+  if (C.tracing) {
+    const int L = C.L, t = C.t;
+    if (blockIdx.x == 0 || blockIdx.x == kStackWGs - 1) {
+      int64_t* dst = P.trace + (blockIdx.x == 0 ? 0 : (size_t)(L + 1) * kTracePoints);
+      for (int i = t; i < (L + 1) * kTracePoints; i += kStackThreads) dst[i] = S.tr[i];
+    }
+    if (t < kTracePoints)
+      P.trace[2 * (size_t)(L + 1) * kTracePoints + (size_t)blockIdx.x * kTracePoints + t] = S.tr[kTracePoints + t];
+  }
+  if (blockIdx.x == 0 && C.t == 0) st_dev_u32(P.ctrl, C.base + (uint32_t)(P.T * (P.L + 1) * 4) + 4u);
+}
+
+bool stack_persistent_supported(const flint_moe_dims& d, int L) {
+  return L >= 1 && L <= kMaxStackLayers && d.hidden == kHidden && d.n_experts % 2 == 0 && d.expert_width % 256 == 0 && d.shared_width % 256 == 0 &&
          d.n_experts % 8 == 0 && d.shared_width / kGroups <= 4 * kGroupWGs && d.n_experts <= kStackWaves * kGroupWGs &&
          d.top_k * (d.expert_width / kGroups) + d.shared_width / kGroups == kSliceK &&
-         d.top_k * (d.expert_width / kGroups) <= kGateUpPerWave * kCommWaves * kGroupWGs &&
+         d.top_k * (d.expert_width / kGroups) <= (kGateUpComm * kCommWaves + kStackWaves - kCommWaves) * kGroupWGs &&
          d.shared_width / kGroups <= (kStackWaves - kCommWaves) * kGroupWGs &&
          d.n_experts <= 2 * (kStackWaves - kCommWaves) * kGroupWGs;
 }

@@ -51,6 +51,7 @@ class StackPlan(ctypes.Structure):
                 ("table", _P), ("schedule", _I32)]
 
 
+TRACE_POINTS = 16  # stamps per layer of flint_stack_decode_traced
 SCHEDULE_AUTO, SCHEDULE_KERNELS, SCHEDULE_PERSISTENT = 0, 1, 2
 
 
@@ -251,10 +252,10 @@ class Stack:
 
     def decode_traced(self, x: torch.Tensor, eps: float = 1e-6):
         """Persistent schedule with phase stamps of the first token:
-        -> (argmax, trace int64 [2][L+1][10] ++ [256][10] in 100 MHz ticks, flat)"""
+        -> (argmax, trace int64 [2][L+1][16] ++ [256][16] in 100 MHz ticks, flat)"""
         T = x.shape[0]
         argmax = torch.empty(T, dtype=torch.int32, device=x.device)
-        trace = torch.zeros(2 * (self.n_layers + 1) * 10 + 256 * 10, dtype=torch.int64, device=x.device)
+        trace = torch.zeros(2 * (self.n_layers + 1) * TRACE_POINTS + 256 * TRACE_POINTS, dtype=torch.int64, device=x.device)
         _check(_lib.flint_stack_decode_traced(ctypes.byref(self.plan), x.data_ptr(), T, eps, None, argmax.data_ptr(),
                                               None, self.ws.data_ptr(), self.ws.numel(), trace.data_ptr(), _stream()),
                "flint_stack_decode_traced")
