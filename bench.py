@@ -2,15 +2,19 @@
 
 One step = one token through all 47 MoE layers (router top-6 of 256 + shared
 expert, NVFP4 experts) and the 150,144-row NVFP4 head with argmax, on seeded
-synthetic weights resident in HBM.  Prints one JSON line.
+synthetic weights resident in HBM: one call of flint_stack_decode, i.e. one
+launch of the persistent stack kernel.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+  python bench.py --copy-calib      # one 1 GiB device copy (counter calibration)
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -18,10 +22,36 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+KERNEL = "k_stack_decode"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_stack_decode_stack47_b1_traffic.md")
+KERNEL_SOURCES = ["nvfp4_bit_projection_amd/csrc/stack.hip", "nvfp4_bit_projection_amd/csrc/flint_device.h",
+                  "nvfp4_bit_projection_amd/csrc/flint_internal.h"]
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic() -> int | None:
+    """HBM bytes per launch of the stack kernel from the committed counter
+    summary, if it was taken on the current kernel source."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    src = re.search(r"source_hash:\s*([0-9a-f]+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return int(val.group(1))
 
 
 def cpu_baseline(layers_sampled: int = 8) -> dict:
@@ -62,6 +92,21 @@ def cpu_baseline(layers_sampled: int = 8) -> dict:
                       f"layers {t_layers:.2f}s, head {t_head:.2f}s"}
 
 
+def copy_calib() -> int:
+    """One device-to-device copy of 1 GiB (reads 1 GiB, writes 1 GiB): the
+    reference dispatch for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    n = (1 << 30) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copied {4 * n} bytes")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -69,11 +114,14 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--layers", type=int, default=47)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (batch-1 decode; see DESIGN.md for how it would shard)",
               file=sys.stderr)
         return 2
+    if args.copy_calib:
+        return copy_calib()
 
     import torch
 
@@ -86,9 +134,7 @@ def main() -> int:
     L, V = args.layers, 150144
     t0 = time.time()
     tmp = torch.empty(dims.n_experts * dims.expert_width * dims.hidden, dtype=torch.float32, device="cuda")
-    layers = []
-    for l in range(L):
-        layers.append(workload.build_layer(dims, seed=l, tmp=tmp))
+    layers = [workload.build_layer(dims, seed=l, tmp=tmp) for l in range(L)]
     head = workload.build_head(V, dims.hidden, tmp=None)
     del tmp
     torch.cuda.synchronize()
@@ -106,22 +152,53 @@ def main() -> int:
     for t in range(args.warmup):
         step(t)
     torch.cuda.synchronize()
+    if stack.error():
+        log("the stack kernel raised its error flag")
+        return 1
+    # every step is one launch of the stack kernel on torch's current stream;
+    # events around each launch give its duration, events around the whole
+    # loop the throughput
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     ev0.record()
-    for t in range(args.warmup, T):
+    for i, t in enumerate(range(args.warmup, T)):
+        starts[i].record()
         step(t)
+        ends[i].record()
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms = ev0.elapsed_time(ev1)
     ms_per_step = ms / args.steps
     tok_s = 1000.0 / ms_per_step
+    launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    launch_avg = sum(launch_ms) / len(launch_ms)
     shape = bm.LayerShape()
     token_bytes = bm.token_bytes(shape, L, V)
-    gbs = token_bytes / (ms_per_step * 1e-3) / 1e9
-    log(f"{args.steps} tokens in {ms:.1f} ms (wall {wall * 1e3:.1f} ms): {tok_s:.1f} tok/s, {gbs:.1f} GB/s")
+    gbs = token_bytes / (launch_avg * 1e-3) / 1e9
+    log(f"{args.steps} tokens in {ms:.1f} ms (wall {wall * 1e3:.1f} ms): {tok_s:.1f} tok/s; "
+        f"{KERNEL} launch avg {launch_avg * 1e3:.1f} us (median {launch_ms[len(launch_ms) // 2] * 1e3:.1f}), "
+        f"{gbs:.1f} GB/s")
 
+    # the same kernel taking 16 tokens per launch (inputs given up front):
+    # the launch cost spread over 16 tokens, reported for context only
+    n16 = min(16, args.steps)
+    xs = x[args.warmup:args.warmup + n16]
+    am16 = torch.empty(n16, dtype=torch.int32, device="cuda")
+    stack.decode(xs, argmax=am16, want_logits=False)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    stack.decode(xs, argmax=am16, want_logits=False)
+    e1.record()
+    torch.cuda.synchronize()
+    multi_tok_s = n16 * 1000.0 / e0.elapsed_time(e1)
+    if not torch.equal(am16, argmax[args.warmup:args.warmup + n16]):
+        log("argmax differs between one-token and multi-token launches")
+        return 1
+
+    traffic = measured_traffic()
     result = {
         "metric": "decode tok/s (47-layer NVFP4 MoE+lm_head, batch 1) and achieved HBM GB/s vs peak",
         "value": round(tok_s, 2),
@@ -138,12 +215,18 @@ def main() -> int:
         "config": {"workload": "stack47_lmhead_b1", "layers": L, "hidden": 2048, "experts": 256, "top_k": 6,
                    "expert_width": 512, "shared_width": 1024, "vocab": V, "batch": 1,
                    "weights": "nvfp4 e2m1 + e4m3/16 + fp32 tensor scale; fp32 router"},
-        "achieved_gbs": round(gbs, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "whole decode step (all kernels of one token)",
-                     "bytes_per_launch": token_bytes},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": (round(traffic / (launch_avg * 1e-3) / 1e9, 1) if traffic else None),
+                     "kernel": KERNEL, "bytes_per_launch": token_bytes,
+                     "traffic_bytes_per_launch": traffic, "launch_us": round(launch_avg * 1e3, 2)},
+        "tokens_per_launch_16": round(multi_tok_s, 2) if n16 == 16 else None,
     }
+    # release device memory before the interpreter exits (keeps profilers'
+    # teardown away from live allocations)
+    del stack, layers, head, x, xs, logits, argmax, am16, starts, ends, ev0, ev1, e0, e1
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline()

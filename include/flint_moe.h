@@ -173,7 +173,8 @@ typedef struct {
   int32_t schedule;              /* FLINT_SCHEDULE_*; prepare sets AUTO */
 } flint_stack_plan;
 
-/* Schedules of flint_stack_decode.  PERSISTENT: one cooperative launch that
+/* Schedules of flint_stack_decode.  PERSISTENT: one launch (256 workgroups,
+ * one per compute unit, all resident) that
  * runs every token, layer and the head (needs expert_width and shared_width
  * multiples of 256, top_k*expert_width/8 + shared_width/8 == 512,
  * shared_width <= 1024, an even n_experts); KERNELS: three kernels per layer

@@ -1,5 +1,5 @@
 // stack.hip -- persistent batch-1 decode of the whole MoE layer stack plus the
-// NVFP4 head, one cooperative launch per call.
+// NVFP4 head, one launch per call.
 //
 // Method [P2 "Recursive Releases Flint, a 40B MoE Coding Model That Runs
 // Locally at 125 Tokens per Second", "How does Flint's architecture work?":
@@ -11,8 +11,8 @@
 // is one fused kernel for the whole decode pass ("Custom Inference Kernels",
 // P1); this is the MI355X form of that idea.
 //
-// Geometry.  256 workgroups of 512 threads, one per compute unit, launched
-// cooperatively so all are resident.  Workgroups are dealt to the 8 XCDs
+// Geometry.  256 workgroups of 512 threads, one per compute unit, all
+// resident at once.  Workgroups are dealt to the 8 XCDs
 // round-robin, so workgroup b sits on XCD b % 8: group g = b % 8 is the 32
 // workgroups of one XCD, and li = b / 8 is the index inside the group.
 //
@@ -38,6 +38,8 @@
 // leave the kernel.
 #include <float.h>
 #include <limits.h>
+
+#include <atomic>
 
 #include "flint_device.h"
 #include "flint_internal.h"
@@ -397,13 +399,6 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
           if (lane == 0) put_pair<Scope::kXcd>(&s3[nroutedx + qa], silu(gv) * av, ep0 + 1);
         }
         FLINT_TRACE_LOAD(l, 9);
-        // the next layer's router and shared rows (the next token's first
-        // layer after the last one) do not depend on this token: request them
-        // now, while memory is idle during the logit exchange and top-k
-        const int next = l + 1 < L ? l + 1 : (tok + 1 < P.T ? 0 : -1);
-        __builtin_amdgcn_sched_barrier(0);
-        have_a = next >= 0;
-        if (have_a) load_phase_a(next);
         FLINT_TRACE_LOAD(l, 10);
       }
       wg_barrier();  // B3: logits in LDS
@@ -563,6 +558,13 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
           if (poll_gave_up(spins, wc)) break;
         }
       } else {
+        // the next layer's router and shared rows (the next token's first
+        // layer after the last one) do not depend on this token: request them
+        // now, while the partial outputs and the residual are exchanged
+        const int next = l + 1 < L ? l + 1 : (tok + 1 < P.T ? 0 : -1);
+        __builtin_amdgcn_sched_barrier(0);
+        have_a = next >= 0;
+        if (have_a) load_phase_a(next);
         FLINT_TRACE_LOAD(l, 13);
       }
       wg_barrier();  // B6: partial outputs of this workgroup's rows in LDS
@@ -741,9 +743,29 @@ hipError_t launch_stack_persistent(const flint_moe_dims& d, int L, int vocab, co
   P.s4b = reinterpret_cast<uint64_t*>(w); w += sizeof(uint64_t) * 2 * kGroups * kHidden;
   P.hp = reinterpret_cast<uint64_t*>(w);
   const StackTable* tab = P.table;
-  void* args[] = {&P, &tab};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(k_stack_decode), dim3(kStackWGs),
-                                    dim3(kStackThreads), args, 0, s);
+  // A plain launch: 256 workgroups of 512 threads, one per compute unit,
+  // all resident at once when the device is otherwise idle (checked once per
+  // device from the occupancy calculator).  If another queue holds compute
+  // units so that some workgroups cannot start, the running ones give up at
+  // their wait limit and raise the error flag, the late ones see it and
+  // return: a reported error, not a hang.
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  static std::atomic<int> resident[64];
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  int r = resident[dev].load();
+  if (r == 0) {
+    int per_cu = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stack_decode, kStackThreads, 0);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    r = per_cu * cus >= kStackWGs ? 1 : -1;
+    resident[dev].store(r);
+  }
+  if (r != 1) return hipErrorCooperativeLaunchTooLarge;
+  k_stack_decode<<<dim3(kStackWGs), dim3(kStackThreads), 0, s>>>(P, tab);
+  return hipGetLastError();
 }
 
 hipError_t read_stack_error(const void* ws, int32_t* out) {
