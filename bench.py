@@ -182,22 +182,6 @@ def main() -> int:
         f"{KERNEL} launch avg {launch_avg * 1e3:.1f} us (median {launch_ms[len(launch_ms) // 2] * 1e3:.1f}), "
         f"{gbs:.1f} GB/s")
 
-    # the same kernel taking 16 tokens per launch (inputs given up front):
-    # the launch cost spread over 16 tokens, reported for context only
-    n16 = min(16, args.steps)
-    xs = x[args.warmup:args.warmup + n16]
-    am16 = torch.empty(n16, dtype=torch.int32, device="cuda")
-    stack.decode(xs, argmax=am16, want_logits=False)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    stack.decode(xs, argmax=am16, want_logits=False)
-    e1.record()
-    torch.cuda.synchronize()
-    multi_tok_s = n16 * 1000.0 / e0.elapsed_time(e1)
-    if not torch.equal(am16, argmax[args.warmup:args.warmup + n16]):
-        log("argmax differs between one-token and multi-token launches")
-        return 1
-
     traffic = measured_traffic()
     result = {
         "metric": "decode tok/s (47-layer NVFP4 MoE+lm_head, batch 1) and achieved HBM GB/s vs peak",
@@ -220,11 +204,10 @@ def main() -> int:
                      "traffic": (round(traffic / (launch_avg * 1e-3) / 1e9, 1) if traffic else None),
                      "kernel": KERNEL, "bytes_per_launch": token_bytes,
                      "traffic_bytes_per_launch": traffic, "launch_us": round(launch_avg * 1e3, 2)},
-        "tokens_per_launch_16": round(multi_tok_s, 2) if n16 == 16 else None,
     }
     # release device memory before the interpreter exits (keeps profilers'
     # teardown away from live allocations)
-    del stack, layers, head, x, xs, logits, argmax, am16, starts, ends, ev0, ev1, e0, e1
+    del stack, layers, head, x, logits, argmax, starts, ends, ev0, ev1
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
