@@ -157,9 +157,16 @@ int32_t flint_lmhead_gemv(const flint_nvfp4* head /*[host]*/, int32_t vocab, int
  *
  * flint_stack_prepare copies the layers' pointer table into `table`, a device
  * buffer of flint_stack_table_bytes(L) bytes, and fills the host-side plan.
- * The plan keeps `layers` (the caller's host array) and `table`; both, and
- * every weight they point at, must stay valid while calls that use the plan
- * run.  flint_stack_decode: x float [T][H]; logits float [T][vocab] (may be
+ * For the persistent schedule it also repacks every layer's down projections
+ * (routed and shared) into `packed`, a device buffer of
+ * flint_stack_packed_bytes(dims, L) bytes: the columns of each down matrix
+ * cut into 8 slices (one per XCD), each slice contiguous over all rows, same
+ * codes and scales.  `packed` may be NULL (then only the kernel-sequence
+ * schedule is available); flint_stack_packed_bytes returns 0 when the sizes
+ * do not allow the persistent schedule.  Prepare synchronises `stream`.
+ * The plan keeps `layers` (the caller's host array), `table` and `packed`;
+ * they, and every weight they point at, must stay valid and unchanged while
+ * calls that use the plan run.  flint_stack_decode: x float [T][H]; logits float [T][vocab] (may be
  * NULL: only argmax is written); argmax int32 [T]; routes_opt int32
  * [T][L][k] receives every layer's chosen experts (ordered by logit
  * descending) when non-NULL. */
@@ -171,6 +178,7 @@ typedef struct {
   const flint_moe_layer* layers; /* [host] caller's array of n_layers */
   const void* table;             /* device copy of the layer table */
   int32_t schedule;              /* FLINT_SCHEDULE_*; prepare sets AUTO */
+  const void* packed;            /* repacked down projections, or NULL */
 } flint_stack_plan;
 
 /* Schedules of flint_stack_decode.  PERSISTENT: one launch (256 workgroups,
@@ -179,15 +187,17 @@ typedef struct {
  * multiples of 256, top_k*expert_width/8 + shared_width/8 == 512,
  * shared_width <= 1024, an even n_experts); KERNELS: three kernels per layer
  * and one for the head, any supported sizes; AUTO: PERSISTENT when the sizes
- * allow it. */
+ * allow it and the plan holds packed down projections. */
 #define FLINT_SCHEDULE_AUTO 0
 #define FLINT_SCHEDULE_KERNELS 1
 #define FLINT_SCHEDULE_PERSISTENT 2
 
 size_t flint_stack_table_bytes(int32_t L);
+size_t flint_stack_packed_bytes(const flint_moe_dims* dims /*[host]*/, int32_t L);
 int32_t flint_stack_prepare(const flint_moe_dims* dims /*[host]*/, const flint_moe_layer* layers /*[host] array of L*/,
                             int32_t L, const flint_nvfp4* head /*[host]*/, int32_t vocab, void* table,
-                            size_t table_bytes, flint_stack_plan* plan /*[host], out*/, void* stream);
+                            size_t table_bytes, void* packed, size_t packed_bytes,
+                            flint_stack_plan* plan /*[host], out*/, void* stream);
 int32_t flint_stack_decode(const flint_stack_plan* plan /*[host]*/, const float* x, int32_t T, float eps, float* logits,
                            int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes, void* stream);
 

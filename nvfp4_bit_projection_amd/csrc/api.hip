@@ -183,9 +183,14 @@ int32_t flint_lmhead_gemv(const flint_nvfp4* head, int32_t vocab, int32_t hidden
 
 size_t flint_stack_table_bytes(int32_t L) { return L < 1 ? 0 : stack_table_bytes(L); }
 
+size_t flint_stack_packed_bytes(const flint_moe_dims* dims, int32_t L) {
+  if (check_dims(dims) || !stack_persistent_supported(*dims, L)) return 0;
+  return PackedDown(*dims).total * (size_t)L;
+}
+
 int32_t flint_stack_prepare(const flint_moe_dims* dims, const flint_moe_layer* layers, int32_t L,
-                            const flint_nvfp4* head, int32_t vocab, void* table, size_t table_bytes,
-                            flint_stack_plan* plan, void* stream) {
+                            const flint_nvfp4* head, int32_t vocab, void* table, size_t table_bytes, void* packed,
+                            size_t packed_bytes, flint_stack_plan* plan, void* stream) {
   int32_t st;
   if ((st = check_dims(dims))) return st;
   if (!layers || !head || !table || !plan) return FLINT_E_NULL;
@@ -195,16 +200,44 @@ int32_t flint_stack_prepare(const flint_moe_dims* dims, const flint_moe_layer* l
   if ((st = check_nvfp4(head))) return st;
   if (!aligned16(table)) return FLINT_E_ALIGN;
   if (table_bytes < stack_table_bytes(L)) return FLINT_E_WORKSPACE;
+  if (packed) {
+    if (!stack_persistent_supported(*dims, L)) return FLINT_E_UNSUPPORTED;
+    if (!aligned16(packed)) return FLINT_E_ALIGN;
+    if (packed_bytes < PackedDown(*dims).total * (size_t)L) return FLINT_E_WORKSPACE;
+  }
   if ((st = check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
   // build the table on the host, then one copy; the copy completes before
-  // this call returns, so the host buffer may be freed right after.
+  // this call returns, so the host buffer may be freed right after.  With a
+  // packed buffer, the table's down-projection pointers refer to the packed
+  // (column-sliced) copies.
   const size_t nb = stack_table_bytes(L);
   char* host = new char[nb];
   StackTable* t = reinterpret_cast<StackTable*>(host);
   t->head = *head;
   memcpy(t->layers, layers, sizeof(flint_moe_layer) * (size_t)L);
-  hipError_t e = hipMemcpyAsync(table, host, nb, hipMemcpyHostToDevice, (hipStream_t)stream);
-  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  hipError_t e = hipSuccess;
+  if (packed) {
+    const PackedDown pd(*dims);
+    const int H = dims->hidden, E = dims->n_experts, I = dims->expert_width, Is = dims->shared_width;
+    for (int l = 0; l < L && e == hipSuccess; ++l) {
+      uint8_t* base = static_cast<uint8_t*>(packed) + pd.total * (size_t)l;
+      const flint_moe_layer& src = layers[l];
+      flint_moe_layer& dst = t->layers[l];
+      e = launch_slice_cols(src.down_codes, base + pd.codes, E, H, I / 2, kStackGroups, s);
+      if (e == hipSuccess) e = launch_slice_cols(src.down_scales, base + pd.scales, E, H, I / 16, kStackGroups, s);
+      if (e == hipSuccess)
+        e = launch_slice_cols(src.shared_down.codes, base + pd.shared_codes, 1, H, Is / 2, kStackGroups, s);
+      if (e == hipSuccess)
+        e = launch_slice_cols(src.shared_down.scales, base + pd.shared_scales, 1, H, Is / 16, kStackGroups, s);
+      dst.down_codes = base + pd.codes;
+      dst.down_scales = base + pd.scales;
+      dst.shared_down.codes = base + pd.shared_codes;
+      dst.shared_down.scales = base + pd.shared_scales;
+    }
+  }
+  if (e == hipSuccess) e = hipMemcpyAsync(table, host, nb, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
   delete[] host;
   if (e != hipSuccess) return hip_fail(e);
   plan->dims = *dims;
@@ -214,6 +247,7 @@ int32_t flint_stack_prepare(const flint_moe_dims* dims, const flint_moe_layer* l
   plan->layers = layers;
   plan->table = table;
   plan->schedule = FLINT_SCHEDULE_AUTO;
+  plan->packed = packed;
   return FLINT_OK;
 }
 
@@ -232,7 +266,7 @@ static int32_t stack_decode_impl(const flint_stack_plan* plan, const float* x, i
   const flint_moe_dims& d = plan->dims;
   StackWs sw(d, plan->vocab);
   if (ws_bytes < sw.total) return FLINT_E_WORKSPACE;
-  const bool persistent_ok = stack_persistent_supported(d, plan->n_layers);
+  const bool persistent_ok = plan->packed && stack_persistent_supported(d, plan->n_layers);
   if (plan->schedule == FLINT_SCHEDULE_PERSISTENT && !persistent_ok) return FLINT_E_UNSUPPORTED;
   if ((st = check_device())) return st;
   hipStream_t s = (hipStream_t)stream;
@@ -274,7 +308,7 @@ int32_t flint_stack_decode_traced(const flint_stack_plan* plan, const float* x, 
   if (!trace) return FLINT_E_NULL;
   if (!aligned16(trace)) return FLINT_E_ALIGN;
   if (plan && plan->schedule == FLINT_SCHEDULE_KERNELS) return FLINT_E_UNSUPPORTED;
-  if (plan && !stack_persistent_supported(plan->dims, plan->n_layers)) return FLINT_E_UNSUPPORTED;
+  if (plan && (!plan->packed || !stack_persistent_supported(plan->dims, plan->n_layers))) return FLINT_E_UNSUPPORTED;
   return stack_decode_impl(plan, x, T, eps, logits, argmax, routes_opt, ws, ws_bytes, trace, stream);
 }
 

@@ -60,6 +60,22 @@ struct HeadWs {
 
 // persistent decode (stack.hip)
 constexpr int kMaxStackLayers = 64;  // layers the persistent schedule takes
+constexpr int kStackGroups = 8;      // XCDs: column slices of the down projections
+// Down projections of one layer repacked for the persistent schedule: the
+// columns of each routed expert and of the shared expert cut into 8 slices,
+// each slice stored contiguously over all rows, so that the XCD that owns a
+// slice reads whole cache lines.
+struct PackedDown {
+  size_t codes, scales, shared_codes, shared_scales, total;  // byte offsets in one layer's block
+  explicit PackedDown(const flint_moe_dims& d) {
+    size_t o = 0;
+    codes = o; o = align_up(o + (size_t)d.n_experts * d.hidden * d.expert_width / 2, 256);
+    scales = o; o = align_up(o + (size_t)d.n_experts * d.hidden * d.expert_width / 16, 256);
+    shared_codes = o; o = align_up(o + (size_t)d.hidden * d.shared_width / 2, 256);
+    shared_scales = o; o = align_up(o + (size_t)d.hidden * d.shared_width / 16, 256);
+    total = o;
+  }
+};
 bool stack_persistent_supported(const flint_moe_dims& d, int L);
 size_t stack_persistent_ws_bytes();
 
@@ -100,6 +116,8 @@ hipError_t launch_quantize(const float* w, int64_t n_mats, int64_t rows, int64_t
                            uint8_t* scales, float* tscales, uint32_t* amax_bits, hipStream_t s);
 hipError_t launch_dequantize(const flint_nvfp4& q, int64_t rows, int64_t cols, float* out, hipStream_t s);
 hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s);
+hipError_t launch_slice_cols(const uint8_t* src, uint8_t* dst, int64_t outer, int rows, int rb, int G,
+                             hipStream_t s);
 hipError_t launch_stack_persistent(const flint_moe_dims& d, int L, int vocab, const void* table, const float* x,
                                    int T, float eps, float* logits, int32_t* argmax, int32_t* routes, void* ws,
                                    int64_t* trace, hipStream_t s);

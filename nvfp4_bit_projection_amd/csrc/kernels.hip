@@ -470,6 +470,32 @@ hipError_t launch_dequantize(const flint_nvfp4& q, int64_t rows, int64_t cols, f
   return hipGetLastError();
 }
 
+// Column slicing of a byte matrix for the stack schedule: src [outer][rows][rb]
+// -> dst [outer][G][rows][rb/G], 2-byte granules (rb/G even).
+__global__ void k_slice_cols(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int64_t outer, int rows,
+                             int rb, int G) {
+  const int sw = rb / G / 2;  // 2-byte words per slice row
+  const int64_t n = outer * (int64_t)G * rows * sw;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int k = (int)(i % sw);
+    int64_t r = i / sw;
+    const int row = (int)(r % rows);
+    r /= rows;
+    const int g = (int)(r % G);
+    const int64_t o = r / G;
+    dst[i] = src[((o * rows + row) * rb + (int64_t)g * (rb / G)) / 2 + k];
+  }
+}
+
+hipError_t launch_slice_cols(const uint8_t* src, uint8_t* dst, int64_t outer, int rows, int rb, int G,
+                             hipStream_t s) {
+  const int64_t words = outer * rows * (int64_t)rb / 2;
+  const int blocks = (int)((words + 255) / 256 < 4096 ? (words + 255) / 256 : 4096);
+  k_slice_cols<<<blocks, 256, 0, s>>>(reinterpret_cast<const uint16_t*>(src), reinterpret_cast<uint16_t*>(dst), outer,
+                                      rows, rb, G);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s) {
   k_copy_f32<<<(n + 255) / 256, 256, 0, s>>>(src, dst, n);
   return hipGetLastError();

@@ -474,9 +474,12 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
         const rsrc_t rds = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWDownS), (uint64_t)E * kHidden * I / 16);
         const rsrc_t rsdc = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSdC), (uint64_t)kHidden * Is / 2);
         const rsrc_t rsds = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSdS), (uint64_t)kHidden * Is / 16);
-        const int doff = routed ? (32 * j) % Ix : 0;
+        const int doff = routed ? (32 * j) % Ix : 0;  // column in the expert's slice
         const int de = S.idx[dslot];
-        const int rcol = g * Ix + doff, scol = routed ? 0 : g * Isx + (32 * j - nroutedx);
+        const int scol = routed ? 0 : 32 * j - nroutedx;  // column in the shared slice
+        // column-sliced layouts (packed at prepare time): routed [E][8][H][Ix],
+        // shared [8][H][Isx], codes 2 per byte, one scale byte per 16 columns
+        const uint32_t rslice = (uint32_t)((de * kGroups + g) * kHidden), sslice = (uint32_t)(g * kHidden);
         // every lane issues both loads; the one that is not its own reads
         // past the end of its buffer, which returns zeros and touches no
         // memory, so the pair combines with an OR and no branch is needed
@@ -485,11 +488,11 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
 #pragma unroll
         for (int pc = 0; pc < kDownPasses; ++pc) {
           const int n = 64 * li + 8 * wv + 4 * pc + (lane >> 4);
-          const uint32_t rrow = (uint32_t)(de * kHidden + n);
-          cdr[pc] = bload_u4(rdc, routed ? rrow * (I / 2) + rcol / 2 : oob_c);
-          sdr[pc] = bload_u16(rds, routed ? rrow * (I / 16) + rcol / 16 : oob_c / 8);
-          cds[pc] = bload_u4(rsdc, routed ? oob_s : (uint32_t)(n * (Is / 2) + scol / 2));
-          sds[pc] = bload_u16(rsds, routed ? oob_s / 8 : (uint32_t)(n * (Is / 16) + scol / 16));
+          const uint32_t rr = rslice + (uint32_t)n, sr = sslice + (uint32_t)n;
+          cdr[pc] = bload_u4(rdc, routed ? rr * (Ix / 2) + doff / 2 : oob_c);
+          sdr[pc] = bload_u16(rds, routed ? rr * (Ix / 16) + doff / 16 : oob_c / 8);
+          cds[pc] = bload_u4(rsdc, routed ? oob_s : sr * (Isx / 2) + scol / 2);
+          sds[pc] = bload_u16(rsds, routed ? oob_s / 8 : sr * (Isx / 16) + scol / 16);
         }
         dts = bload_f32(make_rsrc(tab_ptr<const float>(S, w0 + kWExpTs), (uint64_t)E * 3 * 4),
                         (uint32_t)(3 * de + 2) * 4);

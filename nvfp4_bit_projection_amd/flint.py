@@ -48,7 +48,7 @@ class Layer(ctypes.Structure):
 
 class StackPlan(ctypes.Structure):
     _fields_ = [("dims", Dims), ("n_layers", _I32), ("vocab", _I32), ("head", NVFP4), ("layers", _P),
-                ("table", _P), ("schedule", _I32)]
+                ("table", _P), ("schedule", _I32), ("packed", _P)]
 
 
 TRACE_POINTS = 16  # stamps per layer of flint_stack_decode_traced
@@ -67,8 +67,9 @@ def _load():
         "flint_moe_decode": ([ctypes.POINTER(Dims), ctypes.POINTER(Layer), _P, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
         "flint_lmhead_gemv": ([ctypes.POINTER(NVFP4), _I32, _I32, _P, _I32, _P, _P, _P, _SZ, _P], _I32),
         "flint_stack_table_bytes": ([_I32], _SZ),
+        "flint_stack_packed_bytes": ([ctypes.POINTER(Dims), _I32], _SZ),
         "flint_stack_prepare": ([ctypes.POINTER(Dims), ctypes.POINTER(Layer), _I32, ctypes.POINTER(NVFP4), _I32, _P,
-                                 _SZ, ctypes.POINTER(StackPlan), _P], _I32),
+                                 _SZ, _P, _SZ, ctypes.POINTER(StackPlan), _P], _I32),
         "flint_stack_decode": ([ctypes.POINTER(StackPlan), _P, _I32, ctypes.c_float, _P, _P, _P, _P, _SZ, _P], _I32),
         "flint_stack_decode_traced": ([ctypes.POINTER(StackPlan), _P, _I32, ctypes.c_float, _P, _P, _P, _P, _SZ, _P,
                                        _P], _I32),
@@ -87,7 +88,8 @@ _lib = _load()
 
 # every symbol include/flint_moe.h declares
 EXPORTED = ("flint_status_str", "flint_last_hip_error", "flint_workspace_bytes", "flint_moe_route",
-            "flint_moe_decode", "flint_lmhead_gemv", "flint_stack_table_bytes", "flint_stack_prepare",
+            "flint_moe_decode", "flint_lmhead_gemv", "flint_stack_table_bytes", "flint_stack_packed_bytes",
+            "flint_stack_prepare",
             "flint_stack_decode", "flint_stack_decode_traced", "flint_stack_error", "flint_nvfp4_quantize", "flint_nvfp4_dequantize")
 
 
@@ -243,9 +245,16 @@ class Stack:
         self._keep = (layers, head)
         tb = _lib.flint_stack_table_bytes(len(layers))
         self.table = torch.zeros(tb, dtype=torch.uint8, device=device)
+        # repacked down projections for the persistent schedule (none when the
+        # sizes only allow the kernel sequence, or that schedule is asked for)
+        pb = _lib.flint_stack_packed_bytes(ctypes.byref(dims), len(layers))
+        if schedule == SCHEDULE_KERNELS:
+            pb = 0
+        self.packed = torch.empty(pb, dtype=torch.uint8, device=device) if pb else None
         self.plan = StackPlan()
         _check(_lib.flint_stack_prepare(ctypes.byref(dims), self._layers_c, len(layers), ctypes.byref(self._head_c),
-                                        vocab, self.table.data_ptr(), tb, ctypes.byref(self.plan), _stream()),
+                                        vocab, self.table.data_ptr(), tb, _ptr(self.packed), pb,
+                                        ctypes.byref(self.plan), _stream()),
                "flint_stack_prepare")
         self.plan.schedule = schedule
         self.ws = workspace(OP_STACK, dims, 1, vocab, len(layers), device=device)

@@ -111,3 +111,12 @@ def test_quantize_and_stack_rejections(F):
     plan = F.StackPlan()
     assert L.flint_stack_decode(ctypes.byref(plan), FAKE, 1, 1e-6, None, FAKE, None, FAKE, 1 << 20, None) in (-1, -2)
     assert L.flint_stack_table_bytes(0) == 0 and L.flint_stack_table_bytes(47) > 47 * ctypes.sizeof(F.Layer)
+    # repacked down projections: the routed and shared down matrices of every
+    # layer (codes + scales), only for sizes the persistent schedule takes
+    full = F.dims_struct()
+    per_layer = 256 * 2048 * 512 // 2 + 256 * 2048 * 512 // 16 + 2048 * 1024 // 2 + 2048 * 1024 // 16
+    assert L.flint_stack_packed_bytes(ctypes.byref(full), 47) == 47 * per_layer
+    assert L.flint_stack_packed_bytes(ctypes.byref(full), 65) == 0      # more layers than the schedule takes
+    odd = F.dims_struct(n_experts=256, expert_width=96, top_k=2, shared_width=160)
+    assert L.flint_stack_packed_bytes(ctypes.byref(odd), 4) == 0
+    assert L.flint_stack_packed_bytes(None, 4) == 0
