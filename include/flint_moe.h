@@ -112,6 +112,7 @@ typedef struct {
 #define FLINT_OP_LMHEAD 3
 #define FLINT_OP_STACK 4
 #define FLINT_OP_QUANTIZE 5
+#define FLINT_OP_STACK_BATCH 6
 
 /* Bytes of workspace `op` needs for batch B (tokens), vocabulary `vocab`
  * (lmhead/stack) and L layers (stack); 0 if the arguments are invalid. */
@@ -218,6 +219,23 @@ int32_t flint_stack_decode(const flint_stack_plan* plan /*[host]*/, const float*
 int32_t flint_stack_decode_traced(const flint_stack_plan* plan /*[host]*/, const float* x, int32_t T, float eps,
                                   float* logits, int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes,
                                   int64_t* trace, void* stream);
+
+/* Small-batch decode step [P2 "How does Flint's architecture work?"; P3
+ * "The shape, read from the headers"]: B tokens (1 <= B <= 64) through the
+ * same stack and head together, each token with its own top-k routing:
+ * for every token b the result is that of flint_stack_decode on x_b alone.
+ * Per layer the B*k (token, slot) pairs are grouped by expert, so each
+ * chosen expert's matrices are read once for all the tokens that chose it;
+ * the router, the shared expert and the head are read once per step.
+ * x float [B][H]; logits float [B][vocab] or NULL; argmax int32 [B];
+ * routes_opt int32 [L][B][k] (chosen experts per layer, by logit
+ * descending).  Workspace: flint_workspace_bytes(FLINT_OP_STACK_BATCH, dims,
+ * B, vocab, L); no zero-fill needed.  Uses the plan's host layer array (the
+ * canonical layout; `packed` is not needed).  Needs expert_width and
+ * shared_width in {256, 512, 1024, 2048}. */
+int32_t flint_stack_decode_batch(const flint_stack_plan* plan /*[host]*/, const float* x, int32_t B, float eps,
+                                 float* logits, int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /* Stack workspace contract: zero-filled before the first call; afterwards it
  * carries the persistent schedule's epoch counter and must not be changed

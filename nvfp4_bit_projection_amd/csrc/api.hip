@@ -110,6 +110,9 @@ size_t flint_workspace_bytes(int32_t op, const flint_moe_dims* dims, int32_t B, 
       return StackWs(*dims, vocab).total;
     case FLINT_OP_QUANTIZE:  // B = number of matrices
       return align_up(4 * (size_t)B, 256);
+    case FLINT_OP_STACK_BATCH:
+      if (check_dims(dims) != FLINT_OK || vocab < 1 || !batch_supported(*dims, B)) return 0;
+      return BatchWs(*dims, B, vocab).total;
     default:
       return 0;
   }
@@ -310,6 +313,25 @@ int32_t flint_stack_decode_traced(const flint_stack_plan* plan, const float* x, 
   if (plan && plan->schedule == FLINT_SCHEDULE_KERNELS) return FLINT_E_UNSUPPORTED;
   if (plan && (!plan->packed || !stack_persistent_supported(plan->dims, plan->n_layers))) return FLINT_E_UNSUPPORTED;
   return stack_decode_impl(plan, x, T, eps, logits, argmax, routes_opt, ws, ws_bytes, trace, stream);
+}
+
+int32_t flint_stack_decode_batch(const flint_stack_plan* plan, const float* x, int32_t B, float eps, float* logits,
+                                 int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st;
+  if (!plan || !x || !argmax || !ws) return FLINT_E_NULL;
+  if (!plan->layers || !plan->table) return FLINT_E_NULL;
+  const flint_moe_dims& d = plan->dims;
+  if ((st = check_dims(&d))) return st;
+  if (B < 1 || B > kMaxBatch || !(eps >= 0.0f)) return FLINT_E_DIMS;
+  if (!batch_supported(d, B)) return FLINT_E_UNSUPPORTED;
+  if (!aligned16(x) || (logits && !aligned4(logits)) || !aligned4(argmax) || (routes_opt && !aligned4(routes_opt)) ||
+      !aligned16(ws))
+    return FLINT_E_ALIGN;
+  if (ws_bytes < BatchWs(d, B, plan->vocab).total) return FLINT_E_WORKSPACE;
+  if ((st = check_device())) return st;
+  hipError_t e = launch_batch_step(d, plan->layers, plan->n_layers, plan->head, plan->vocab, x, B, eps, logits, argmax,
+                                   routes_opt, ws, (hipStream_t)stream);
+  return e == hipSuccess ? FLINT_OK : hip_fail(e);
 }
 
 int32_t flint_stack_error(const void* ws, size_t ws_bytes, int32_t* error) {

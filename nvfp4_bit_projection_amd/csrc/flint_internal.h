@@ -103,6 +103,17 @@ struct StackTable {
 };
 inline size_t stack_table_bytes(int L) { return sizeof(StackTable) + sizeof(flint_moe_layer) * (size_t)(L > 1 ? L - 1 : 0); }
 
+// batched decode (batch.hip)
+constexpr int kMaxBatch = 64;
+struct BatchWs {
+  size_t h, u, logits, idx, wts, bucket, hr, hs, dr, ds, partials, total;
+  BatchWs(const flint_moe_dims& d, int B, int vocab);
+};
+bool batch_supported(const flint_moe_dims& d, int B);
+hipError_t launch_batch_step(const flint_moe_dims& d, const flint_moe_layer* layers, int L, const flint_nvfp4& head,
+                             int vocab, const float* x, int B, float eps, float* logits, int32_t* argmax,
+                             int32_t* routes, void* ws, hipStream_t s);
+
 // ---- kernel launchers (kernels.hip); all return the hipError_t of the launch
 hipError_t launch_route(const flint_moe_dims& d, const float* router, const float* x, int B, float norm_eps,
                         float* logits, int32_t* idx, float* w, uint32_t* tickets, hipStream_t s);

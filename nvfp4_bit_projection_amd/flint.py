@@ -21,7 +21,7 @@ _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 _SZ = ctypes.c_size_t
 
-OP_ROUTE, OP_DECODE, OP_LMHEAD, OP_STACK, OP_QUANTIZE = 1, 2, 3, 4, 5
+OP_ROUTE, OP_DECODE, OP_LMHEAD, OP_STACK, OP_QUANTIZE, OP_STACK_BATCH = 1, 2, 3, 4, 5, 6
 
 
 class FlintError(RuntimeError):
@@ -73,6 +73,8 @@ def _load():
         "flint_stack_decode": ([ctypes.POINTER(StackPlan), _P, _I32, ctypes.c_float, _P, _P, _P, _P, _SZ, _P], _I32),
         "flint_stack_decode_traced": ([ctypes.POINTER(StackPlan), _P, _I32, ctypes.c_float, _P, _P, _P, _P, _SZ, _P,
                                        _P], _I32),
+        "flint_stack_decode_batch": ([ctypes.POINTER(StackPlan), _P, _I32, ctypes.c_float, _P, _P, _P, _P, _SZ, _P],
+                                     _I32),
         "flint_stack_error": ([_P, _SZ, ctypes.POINTER(_I32)], _I32),
         "flint_nvfp4_quantize": ([_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _I32),
         "flint_nvfp4_dequantize": ([ctypes.POINTER(NVFP4), _I64, _I64, _P, _P], _I32),
@@ -90,7 +92,7 @@ _lib = _load()
 EXPORTED = ("flint_status_str", "flint_last_hip_error", "flint_workspace_bytes", "flint_moe_route",
             "flint_moe_decode", "flint_lmhead_gemv", "flint_stack_table_bytes", "flint_stack_packed_bytes",
             "flint_stack_prepare",
-            "flint_stack_decode", "flint_stack_decode_traced", "flint_stack_error", "flint_nvfp4_quantize", "flint_nvfp4_dequantize")
+            "flint_stack_decode", "flint_stack_decode_traced", "flint_stack_decode_batch", "flint_stack_error", "flint_nvfp4_quantize", "flint_nvfp4_dequantize")
 
 
 def lib():
@@ -275,6 +277,23 @@ class Stack:
         e = _I32(0)
         _check(_lib.flint_stack_error(self.ws.data_ptr(), self.ws.numel(), ctypes.byref(e)), "flint_stack_error")
         return e.value
+
+    def decode_batch(self, x: torch.Tensor, eps: float = 1e-6, logits: torch.Tensor | None = None,
+                     argmax: torch.Tensor | None = None, routes: torch.Tensor | None = None,
+                     want_logits: bool = True, ws: torch.Tensor | None = None):
+        """x float32 [B][H]: one step of B tokens decoded together (each with its
+        own routing); -> (logits [B][vocab] or None, argmax [B])."""
+        B = x.shape[0]
+        if want_logits and logits is None:
+            logits = torch.empty((B, self.vocab), dtype=torch.float32, device=x.device)
+        if argmax is None:
+            argmax = torch.empty(B, dtype=torch.int32, device=x.device)
+        if ws is None:
+            ws = workspace(OP_STACK_BATCH, self.dims, B, self.vocab, self.n_layers, device=x.device)
+        _check(_lib.flint_stack_decode_batch(ctypes.byref(self.plan), x.data_ptr(), B, eps, _ptr(logits),
+                                             argmax.data_ptr(), _ptr(routes), ws.data_ptr(), ws.numel(), _stream()),
+               "flint_stack_decode_batch")
+        return logits, argmax
 
     def decode(self, x: torch.Tensor, eps: float = 1e-6, logits: torch.Tensor | None = None,
                argmax: torch.Tensor | None = None, routes: torch.Tensor | None = None, want_logits: bool = True):

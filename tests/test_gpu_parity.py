@@ -308,3 +308,85 @@ def test_stack_full_size_sampled(F, full_head):
     head, persistent schedule; one screened token against the oracle."""
     _, q, V = full_head
     stack_case(F, synth.MoEDims(), L=47, vocab=V, n_tokens=1, seed0=synth.TOKEN_SEED0, schedule=2, head_q=q)
+
+
+# ------------------------------------------------------------ batched step --
+def batch_oracle_case(F, dims, L, vocab, B, seed0):
+    """B screened tokens decoded together; each against its own oracle run."""
+    flint, workload = F
+    layers = [workload.build_layer(dims, seed=l) for l in range(L)]
+    head = workload.build_head(vocab, dims.hidden)
+    W = SyntheticWeights(dims, vocab=vocab)
+    stack = flint.Stack(dims_struct(F, dims), layers, head, vocab)
+    s, chosen, refs = seed0, [], []
+    while len(chosen) < B:
+        r = stack_token(W, synth.token_f32(s, dims.hidden), L)
+        if min(r.gaps) >= MARGIN and r.argmax_gap >= MARGIN:
+            chosen.append(s)
+            refs.append(r)
+        s += 1
+    x = workload.tokens(chosen, dims.hidden)
+    routes = torch.zeros((L, B, dims.top_k), dtype=torch.int32, device="cuda")
+    logits, am = stack.decode_batch(x, routes=routes)
+    torch.cuda.synchronize()
+    for t, r in enumerate(refs):
+        for l in range(L):
+            assert sorted(routes[l, t].cpu().numpy().tolist()) == sorted(r.routes[l].tolist()), (t, l)
+        assert_close(logits[t].cpu().numpy(), r.logits, f"batch token {t}")
+        assert int(am[t]) == r.argmax, t
+
+
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_stack_batch_against_oracle(F, B):
+    """Batched decode (tokens bucketed by expert) = the oracle, token by token."""
+    batch_oracle_case(F, synth.MoEDims(n_experts=32), L=3, vocab=4099, B=B, seed0=40)
+
+
+def batch_vs_single(F, L, V, B, seed0, head=None):
+    """The batched step against the single-token persistent path, token by
+    token: routes (as sets) and argmax equal, logits within the fp32 bar."""
+    flint, workload = F
+    dims = synth.MoEDims()
+    layers = [workload.build_layer(dims, seed=l) for l in range(L)]
+    head = workload.build_head(V, dims.hidden) if head is None else head
+    stack = flint.Stack(dims_struct(F, dims), layers, head, V)
+    x = workload.tokens(range(seed0, seed0 + B), dims.hidden)
+    rb = torch.zeros((L, B, dims.top_k), dtype=torch.int32, device="cuda")
+    lb, ab = stack.decode_batch(x, routes=rb)
+    rs = torch.zeros((B, L, dims.top_k), dtype=torch.int32, device="cuda")
+    ls, as_ = stack.decode(x, routes=rs)
+    torch.cuda.synchronize()
+    assert stack.error() == 0
+    rb_s = np.sort(rb.cpu().numpy(), axis=-1)
+    rs_s = np.sort(rs.cpu().numpy(), axis=-1)
+    for t in range(B):
+        for l in range(L):
+            assert rb_s[l, t].tolist() == rs_s[t, l].tolist(), (t, l)
+        assert_close(lb[t].cpu().numpy(), ls[t].cpu().numpy(), f"batch vs single token {t}")
+    assert torch.equal(ab, as_)
+    return lb, ab
+
+
+def test_stack_batch_e256_matches_single(F):
+    batch_vs_single(F, L=4, V=16385, B=32, seed0=700)
+
+
+@pytest.mark.parametrize("B", [8, 32])
+def test_stack_batch_full_size_sampled(F, B):
+    """Config-4 shape: 47 layers of 256 experts, the 150,144-row head, B
+    tokens per step, against the single-token path for every token."""
+    batch_vs_single(F, L=47, V=150144, B=B, seed0=900 + B)
+
+
+def test_stack_batch_repeatable(F):
+    """Fixed orders everywhere: the same step twice gives identical bits."""
+    flint, workload = F
+    dims = synth.MoEDims(n_experts=32)
+    layers = [workload.build_layer(dims, seed=l) for l in range(2)]
+    head = workload.build_head(4099, dims.hidden)
+    stack = flint.Stack(dims_struct(F, dims), layers, head, 4099)
+    x = workload.tokens(range(60, 68), dims.hidden)
+    l1, a1 = stack.decode_batch(x)
+    l2, a2 = stack.decode_batch(x)
+    torch.cuda.synchronize()
+    assert torch.equal(l1, l2) and torch.equal(a1, a2)

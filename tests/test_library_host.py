@@ -120,3 +120,9 @@ def test_quantize_and_stack_rejections(F):
     odd = F.dims_struct(n_experts=256, expert_width=96, top_k=2, shared_width=160)
     assert L.flint_stack_packed_bytes(ctypes.byref(odd), 4) == 0
     assert L.flint_stack_packed_bytes(None, 4) == 0
+    # batched step: workspace only for 1 <= B <= 64; argument checks before any work
+    assert L.flint_workspace_bytes(F.OP_STACK_BATCH, ctypes.byref(full), 32, 150144, 47) > 0
+    assert L.flint_workspace_bytes(F.OP_STACK_BATCH, ctypes.byref(full), 65, 150144, 47) == 0
+    assert L.flint_workspace_bytes(F.OP_STACK_BATCH, ctypes.byref(full), 0, 150144, 47) == 0
+    assert L.flint_stack_decode_batch(None, FAKE, 8, 1e-6, None, FAKE, None, FAKE, 1 << 20, None) == -1
+    assert L.flint_stack_decode_batch(ctypes.byref(plan), FAKE, 8, 1e-6, None, FAKE, None, FAKE, 1 << 20, None) == -1
