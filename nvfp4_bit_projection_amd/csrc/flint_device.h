@@ -161,7 +161,7 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
 // bits of negative values makes signed integer order match float order.  The
 // map is its own inverse.
 __device__ __forceinline__ int ord_key(float f) {
-  const int b = __float_as_int(f);
+  const int b = __float_as_int(f + 0.0f);  // -0 -> +0: equal floats, equal keys
   return b ^ ((b >> 31) & 0x7FFFFFFF);
 }
 __device__ __forceinline__ float ord_key_value(int key) { return __int_as_float(key ^ ((key >> 31) & 0x7FFFFFFF)); }
