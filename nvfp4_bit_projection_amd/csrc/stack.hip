@@ -301,14 +301,14 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       const rsrc_t rr = make_rsrc(tab_ptr<const float>(S, w0 + kWRouter), (uint64_t)E * kHidden * 4);
       const uint32_t r0 = rrow < E ? (uint32_t)rrow : 0u;
 #pragma unroll
-      for (int i = 0; i < kHidden / 256; ++i) wr[i] = bload_f4(rr, (r0 * kHidden + 256 * i) * 4 + 16 * lane);
+      for (int i = 0; i < kHidden / 256; ++i) wr[i] = bload_f4_nt(rr, (r0 * kHidden + 256 * i) * 4 + 16 * lane);
     }
     const uint32_t row = (uint32_t)(g * Isx + (qa < Isx ? qa : 0));
     const uint64_t nc = (uint64_t)Is * kHidden / 2, ns = (uint64_t)Is * kHidden / 16;
-    cgs = bload_u4(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSgC), nc), row * (kHidden / 2) + 16 * lane);
-    sgs = bload_u16(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSgS), ns), row * (kHidden / 16) + 2 * lane);
-    cus = bload_u4(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSuC), nc), row * (kHidden / 2) + 16 * lane);
-    sus = bload_u16(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSuS), ns), row * (kHidden / 16) + 2 * lane);
+    cgs = bload_u4_nt(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSgC), nc), row * (kHidden / 2) + 16 * lane);
+    sgs = bload_u16_nt(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSgS), ns), row * (kHidden / 16) + 2 * lane);
+    cus = bload_u4_nt(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSuC), nc), row * (kHidden / 2) + 16 * lane);
+    sus = bload_u16_nt(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSuS), ns), row * (kHidden / 16) + 2 * lane);
     tgs = bload_f32(make_rsrc(tab_ptr<const float>(S, w0 + kWSgT), 4), 0);
     tus = bload_f32(make_rsrc(tab_ptr<const float>(S, w0 + kWSuT), 4), 0);
   };
@@ -343,10 +343,10 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
     const uint64_t nc = (uint64_t)E * I * kHidden / 2, ns = (uint64_t)E * I * kHidden / 16;
     const rsrc_t rts = make_rsrc(tab_ptr<const float>(S, w0 + kWExpTs), (uint64_t)E * 3 * 4);
     PairOps o;
-    o.cg = bload_u4(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWGateC), nc), row * (kHidden / 2) + 16 * lane);
-    o.cu = bload_u4(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWUpC), nc), row * (kHidden / 2) + 16 * lane);
-    o.sg = bload_u16(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWGateS), ns), row * (kHidden / 16) + 2 * lane);
-    o.su = bload_u16(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWUpS), ns), row * (kHidden / 16) + 2 * lane);
+    o.cg = bload_u4_nt(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWGateC), nc), row * (kHidden / 2) + 16 * lane);
+    o.cu = bload_u4_nt(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWUpC), nc), row * (kHidden / 2) + 16 * lane);
+    o.sg = bload_u16_nt(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWGateS), ns), row * (kHidden / 16) + 2 * lane);
+    o.su = bload_u16_nt(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWUpS), ns), row * (kHidden / 16) + 2 * lane);
     o.Sg = bload_f32(rts, (uint32_t)(3 * e + 0) * 4);
     o.Su = bload_f32(rts, (uint32_t)(3 * e + 1) * 4);
     return o;
@@ -489,10 +489,10 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
         for (int pc = 0; pc < kDownPasses; ++pc) {
           const int n = 64 * li + 8 * wv + 4 * pc + (lane >> 4);
           const uint32_t rr = rslice + (uint32_t)n, sr = sslice + (uint32_t)n;
-          cdr[pc] = bload_u4(rdc, routed ? rr * (Ix / 2) + doff / 2 : oob_c);
-          sdr[pc] = bload_u16(rds, routed ? rr * (Ix / 16) + doff / 16 : oob_c / 8);
-          cds[pc] = bload_u4(rsdc, routed ? oob_s : sr * (Isx / 2) + scol / 2);
-          sds[pc] = bload_u16(rsds, routed ? oob_s / 8 : sr * (Isx / 16) + scol / 16);
+          cdr[pc] = bload_u4_nt(rdc, routed ? rr * (Ix / 2) + doff / 2 : oob_c);
+          sdr[pc] = bload_u16_nt(rds, routed ? rr * (Ix / 16) + doff / 16 : oob_c / 8);
+          cds[pc] = bload_u4_nt(rsdc, routed ? oob_s : sr * (Isx / 2) + scol / 2);
+          sds[pc] = bload_u16_nt(rsds, routed ? oob_s / 8 : sr * (Isx / 16) + scol / 16);
         }
         dts = bload_f32(make_rsrc(tab_ptr<const float>(S, w0 + kWExpTs), (uint64_t)E * 3 * 4),
                         (uint32_t)(3 * de + 2) * 4);
@@ -616,8 +616,8 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
 #pragma unroll
         for (int q = 0; q < kHeadRowsPerWave; ++q) {
           const int row = min(r0 + q, V - 1);
-          c[q] = bload_u4(rhc, (uint32_t)row * (kHidden / 2) + 16 * lane);
-          s[q] = bload_u16(rhs, (uint32_t)row * (kHidden / 16) + 2 * lane);
+          c[q] = bload_u4_nt(rhc, (uint32_t)row * (kHidden / 2) + 16 * lane);
+          s[q] = bload_u16_nt(rhs, (uint32_t)row * (kHidden / 16) + 2 * lane);
         }
 #pragma unroll
         for (int q = 0; q < kHeadRowsPerWave; ++q) {
