@@ -102,7 +102,14 @@ __global__ __launch_bounds__(kThreads) void k_broute(const float* __restrict__ r
   __shared__ __align__(16) float sh[kStageFloats];
   const int lane = threadIdx.x & 63, e = blockIdx.x * 4 + (threadIdx.x >> 6);
   float wr[32];
-  lane_x32(router + (size_t)(e < E ? e : 0) * kHidden, lane, wr);
+  {
+    const float* rw = router + (size_t)(e < E ? e : 0) * kHidden + 32 * lane;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 a = ld_nt_f4(rw + 4 * i);
+      wr[4 * i] = a.x; wr[4 * i + 1] = a.y; wr[4 * i + 2] = a.z; wr[4 * i + 3] = a.w;
+    }
+  }
   constexpr int P = stage_tokens_per_pass<kHidden>();
   for (int b0 = 0; b0 < B; b0 += P) {
     const int nb = B - b0 < P ? B - b0 : P;
@@ -240,10 +247,10 @@ __global__ __launch_bounds__(kThreads) void k_bgateup(flint_moe_layer L, int I, 
 #pragma unroll
   for (int q = 0; q < kRowsPerWave; ++q) {
     const size_t row = (size_t)e * I + r0 + q;
-    cg[q] = *reinterpret_cast<const uint4*>(L.gate_codes + row * (kHidden / 2) + 16 * lane);
-    cu[q] = *reinterpret_cast<const uint4*>(L.up_codes + row * (kHidden / 2) + 16 * lane);
-    sg[q] = *reinterpret_cast<const uint16_t*>(L.gate_scales + row * (kHidden / 16) + 2 * lane);
-    su[q] = *reinterpret_cast<const uint16_t*>(L.up_scales + row * (kHidden / 16) + 2 * lane);
+    cg[q] = ld_nt_u4(L.gate_codes + row * (kHidden / 2) + 16 * lane);
+    cu[q] = ld_nt_u4(L.up_codes + row * (kHidden / 2) + 16 * lane);
+    sg[q] = ld_nt_u16(L.gate_scales + row * (kHidden / 16) + 2 * lane);
+    su[q] = ld_nt_u16(L.up_scales + row * (kHidden / 16) + 2 * lane);
   }
   const float Sg = L.expert_tscales[3 * e + 0], Su = L.expert_tscales[3 * e + 1];
   const int p0 = bk[kBkStart + ub], p1 = bk[kBkStart + ub + 1];
@@ -266,10 +273,10 @@ __global__ __launch_bounds__(kThreads) void k_bgateup_shared(flint_moe_layer L, 
                                                              const float* __restrict__ u, float* __restrict__ hs) {
   __shared__ __align__(16) float sh[kStageFloats];
   const int lane = threadIdx.x & 63, r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const uint4 cg = *reinterpret_cast<const uint4*>(L.shared_gate.codes + (size_t)r * (kHidden / 2) + 16 * lane);
-  const uint4 cu = *reinterpret_cast<const uint4*>(L.shared_up.codes + (size_t)r * (kHidden / 2) + 16 * lane);
-  const uint32_t sg = *reinterpret_cast<const uint16_t*>(L.shared_gate.scales + (size_t)r * (kHidden / 16) + 2 * lane);
-  const uint32_t su = *reinterpret_cast<const uint16_t*>(L.shared_up.scales + (size_t)r * (kHidden / 16) + 2 * lane);
+  const uint4 cg = ld_nt_u4(L.shared_gate.codes + (size_t)r * (kHidden / 2) + 16 * lane);
+  const uint4 cu = ld_nt_u4(L.shared_up.codes + (size_t)r * (kHidden / 2) + 16 * lane);
+  const uint32_t sg = ld_nt_u16(L.shared_gate.scales + (size_t)r * (kHidden / 16) + 2 * lane);
+  const uint32_t su = ld_nt_u16(L.shared_up.scales + (size_t)r * (kHidden / 16) + 2 * lane);
   const float Sg = *L.shared_gate.tscale, Su = *L.shared_up.tscale;
   float wg[32], wu[32];
   fp4x8_values(cg.x, wg); fp4x8_values(cg.y, wg + 8); fp4x8_values(cg.z, wg + 16); fp4x8_values(cg.w, wg + 24);
@@ -327,8 +334,8 @@ __global__ __launch_bounds__(kThreads) void k_bdown(flint_moe_layer L, int I, co
 #pragma unroll
   for (int q = 0; q < kRowsPerWave; ++q) {
     const size_t row = (size_t)e * kHidden + n0 + q * RPW;
-    c[q] = *reinterpret_cast<const uint4*>(L.down_codes + row * (I / 2) + 16 * j);
-    sc[q] = *reinterpret_cast<const uint16_t*>(L.down_scales + row * (I / 16) + 2 * j);
+    c[q] = ld_nt_u4(L.down_codes + row * (I / 2) + 16 * j);
+    sc[q] = ld_nt_u16(L.down_scales + row * (I / 16) + 2 * j);
   }
   const float S = L.expert_tscales[3 * e + 2];
   for (int p = p0; p < p1; ++p) {
@@ -353,8 +360,8 @@ __global__ __launch_bounds__(kThreads) void k_bdown_shared(flint_moe_layer L, in
   __shared__ __align__(16) float sh[kStageFloats];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int j = lane % G, n = (blockIdx.x * 4 + wv) * RPW + lane / G;
-  const uint4 c = *reinterpret_cast<const uint4*>(L.shared_down.codes + (size_t)n * (K / 2) + 16 * j);
-  const uint32_t s = *reinterpret_cast<const uint16_t*>(L.shared_down.scales + (size_t)n * (K / 16) + 2 * j);
+  const uint4 c = ld_nt_u4(L.shared_down.codes + (size_t)n * (K / 2) + 16 * j);
+  const uint32_t s = ld_nt_u16(L.shared_down.scales + (size_t)n * (K / 16) + 2 * j);
   const float S = *L.shared_down.tscale;
   float w[32];
   fp4x8_values(c.x, w); fp4x8_values(c.y, w + 8); fp4x8_values(c.z, w + 16); fp4x8_values(c.w, w + 24);
@@ -414,8 +421,8 @@ __global__ __launch_bounds__(kThreads) void k_bhead(const uint8_t* __restrict__ 
   const float S = *tscale;
   const int nwaves = gridDim.x * 4;
   for (int r = blockIdx.x * 4 + wv; r < vocab; r += nwaves) {
-    const uint4 c = *reinterpret_cast<const uint4*>(codes + (size_t)r * (kHidden / 2) + 16 * lane);
-    const uint32_t s = *reinterpret_cast<const uint16_t*>(scales + (size_t)r * (kHidden / 16) + 2 * lane);
+    const uint4 c = ld_nt_u4(codes + (size_t)r * (kHidden / 2) + 16 * lane);
+    const uint32_t s = ld_nt_u16(scales + (size_t)r * (kHidden / 16) + 2 * lane);
     float w[32];
     fp4x8_values(c.x, w); fp4x8_values(c.y, w + 8); fp4x8_values(c.z, w + 16); fp4x8_values(c.w, w + 24);
     const float d0 = e4m3_to_f32(s & 0xFF), d1 = e4m3_to_f32(s >> 8);

@@ -57,6 +57,21 @@ __device__ __forceinline__ float4 bload_f4_nt(rsrc_t r, uint32_t off) {
   return make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
 }
 
+// Streaming loads through a plain pointer (non-temporal global loads).
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt_u4(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_nt_u16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(p));
+}
+__device__ __forceinline__ float4 ld_nt_f4(const void* p) {
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 // OCP E4M3FN byte -> float (gfx950 converts OCP FP8 in hardware).
 __device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
   return __builtin_amdgcn_cvt_f32_fp8(byte, 0);

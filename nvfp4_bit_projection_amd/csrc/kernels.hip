@@ -39,8 +39,9 @@ __device__ __forceinline__ void load_x32(const float* __restrict__ x, int lane, 
   }
 }
 
-__device__ __forceinline__ uint4 ld_codes16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ uint32_t ld_scales2(const uint8_t* p) { return *reinterpret_cast<const uint16_t*>(p); }
+// weight loads stream (non-temporal): each weight byte is read once per call
+__device__ __forceinline__ uint4 ld_codes16(const uint8_t* p) { return ld_nt_u4(p); }
+__device__ __forceinline__ uint32_t ld_scales2(const uint8_t* p) { return ld_nt_u16(p); }
 
 // ----------------------------------------------------------------- router --
 // grid (ceil(E/4), B), 256 threads: one router row per wave, then the last
@@ -54,11 +55,11 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ router,
   load_x32(x + (size_t)b * kHidden, lane, norm_eps, xv);
   const int e = blockIdx.x * 4 + wv;
   if (e < E) {
-    const float4* rw = reinterpret_cast<const float4*>(router + (size_t)e * kHidden + 32 * lane);
+    const float* rw = router + (size_t)e * kHidden + 32 * lane;
     float acc = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float4 v = rw[i];
+      const float4 v = ld_nt_f4(rw + 4 * i);
       acc = __builtin_fmaf(v.x, xv[4 * i + 0], acc);
       acc = __builtin_fmaf(v.y, xv[4 * i + 1], acc);
       acc = __builtin_fmaf(v.z, xv[4 * i + 2], acc);
