@@ -207,15 +207,16 @@ int32_t flint_stack_decode(const flint_stack_plan* plan /*[host]*/, const float*
  * the phase boundaries of two workgroups (one on the first XCD, one on the
  * last) into trace, int64 [2][L+1][16], followed by the stamps of layer 1 of
  * all 256 workgroups, int64 [256][16].  Per layer l, seen by the first
- * polling wave: 0 layer start, 1 norm done, 2 router/shared rows done,
- * 3 logits arrived, 4 top-k done, 5 routed rows done, 6 hidden slice arrived,
- * 7 partial output done, 8 partials arrived, 9 new residual arrived; seen by
- * the first loading wave: 10 its router rows present, 11 router/shared
- * results stored, 12 next layer's rows requested, 13 its routed pair stored,
- * 14 its partial outputs stored; 15: the first polling wave's routed pairs
- * stored.  Row L holds the head start, the head end and the token's end.
- * Returns FLINT_E_UNSUPPORTED for the kernel-sequence schedule and for more
- * than 64 layers. */
+ * polling wave: 0 layer start, 1 norm done, 2 logits arrived, 3 top-k
+ * known, 4 its routed pairs stored, 5 hidden slice arrived, 6 partial
+ * outputs arrived, 7 new residual arrived, 15 top-k computed; seen by the
+ * first loading wave: 8 router logit stored, 9 shared pair stored, 11 routed
+ * phase started, 12 its routed pair stored, 13 partial outputs stored and
+ * the next layer's rows requested, 14 residual rows stored; 10 is unused
+ * (0).  Row L holds the head start, the head rows done, the head partials
+ * arrived, the kernel entry and the end of the kernel's set-up.  Returns
+ * FLINT_E_UNSUPPORTED for the kernel-sequence schedule and for more than 64
+ * layers. */
 int32_t flint_stack_decode_traced(const flint_stack_plan* plan /*[host]*/, const float* x, int32_t T, float eps,
                                   float* logits, int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes,
                                   int64_t* trace, void* stream);

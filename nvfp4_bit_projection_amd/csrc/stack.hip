@@ -399,7 +399,6 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
           if (lane == 0) put_pair<Scope::kXcd>(&s3[nroutedx + qa], silu(gv) * av, ep0 + 1);
         }
         FLINT_TRACE_LOAD(l, 9);
-        FLINT_TRACE_LOAD(l, 10);
       }
       wg_barrier();  // B3: logits in LDS
       if (S.bad) return false;
@@ -682,6 +681,7 @@ __global__ __launch_bounds__(kStackThreads, 1) void k_stack_decode(StackParams P
   C.Isx = C.Is / kGroups;
   C.nroutedx = C.k * C.Ix;
   C.tracing = P.trace != nullptr;
+  if (C.tracing && C.t == 0) S.tr[C.L * kTracePoints + 3] = wall_clock64();  // kernel entry
   // layer table (and head) to LDS
   {
     const uint64_t* src = reinterpret_cast<const uint64_t*>(table->layers);
@@ -697,6 +697,7 @@ __global__ __launch_bounds__(kStackThreads, 1) void k_stack_decode(StackParams P
     return;
   }
   C.base = ld_dev_u32(P.ctrl);
+  if (C.tracing && C.t == 0) S.tr[C.L * kTracePoints + 4] = wall_clock64();  // set-up done
   const bool ok = C.wv < kCommWaves ? stack_role<true>(P, S, C) : stack_role<false>(P, S, C);
   if (!ok) return;
   if (C.tracing) {
