@@ -390,3 +390,51 @@ def test_stack_batch_repeatable(F):
     l2, a2 = stack.decode_batch(x)
     torch.cuda.synchronize()
     assert torch.equal(l1, l2) and torch.equal(a1, a2)
+
+
+def test_stack_traced_matches_and_orders(F):
+    """The profiling variant decodes the same tokens, and the first polling
+    wave's stamps run forward through each layer."""
+    flint, workload = F
+    dims = synth.MoEDims(n_experts=32)
+    L, V = 3, 4099
+    layers = [workload.build_layer(dims, seed=l) for l in range(L)]
+    head = workload.build_head(V, dims.hidden)
+    stack = flint.Stack(dims_struct(F, dims), layers, head, V, schedule=2)
+    x = workload.tokens(range(70, 72), dims.hidden)
+    _, am = stack.decode(x)
+    am_t, tr = stack.decode_traced(x)
+    torch.cuda.synchronize()
+    assert stack.error() == 0
+    assert torch.equal(am, am_t)
+    P = flint.TRACE_POINTS
+    two = tr[:2 * (L + 1) * P].view(2, L + 1, P).cpu().numpy()
+    for wg in range(2):
+        for l in range(L):
+            seq = two[wg, l, [0, 1, 2, 3, 5, 6, 7]]
+            assert (np.diff(seq) >= 0).all() and seq[0] > 0, (wg, l, seq)
+        assert two[wg, L, 4] >= two[wg, L, 3] > 0   # kernel entry, set-up done
+        assert two[wg, 0, 0] >= two[wg, L, 4]        # first layer after set-up
+
+
+def test_stack_error_flag_stops_calls(F):
+    """With the workspace's error flag already raised (set from the host), a
+    persistent call does nothing and the flag is reported; zeroing the
+    workspace makes the plan usable again."""
+    flint, workload = F
+    dims = synth.MoEDims(n_experts=32)
+    layers = [workload.build_layer(dims, seed=l) for l in range(2)]
+    head = workload.build_head(4099, dims.hidden)
+    stack = flint.Stack(dims_struct(F, dims), layers, head, 4099, schedule=2)
+    x = workload.tokens(range(80, 81), dims.hidden)
+    _, good = stack.decode(x)
+    torch.cuda.synchronize()
+    stack.ws.view(torch.int32)[1] = 1            # the flag a timed-out wait would raise
+    am = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+    stack.decode(x, argmax=am, want_logits=False)
+    torch.cuda.synchronize()
+    assert stack.error() == 1 and int(am[0]) == -7
+    stack.ws.zero_()
+    stack.decode(x, argmax=am, want_logits=False)
+    torch.cuda.synchronize()
+    assert stack.error() == 0 and torch.equal(am, good)
