@@ -17,25 +17,26 @@
 // workgroups of one XCD, and li = b / 8 is the index inside the group.
 //
 // Work split of one layer (E experts, top-k, width I, shared width Is):
-//  A  every group computes all E router logits (8 rows per workgroup, the fp32
-//     router is read once per XCD) and the SwiGLU of its 1/8 slice of the
-//     shared expert's rows;
-//  B  each workgroup takes the top k of the E logits of its group, then the
-//     group computes the SwiGLU of its 1/8 slice (I/8 rows) of each chosen
-//     expert; the down-projection weights of phase C are loaded here too;
+//  A  RMSNorm of the residual; workgroup b computes router row b (the fp32
+//     router is read once per layer) and stores its logit into the logit
+//     exchange of every group; each group computes the SwiGLU of its 1/8
+//     slice of the shared expert's rows;
+//  B  the first wave of every workgroup gathers the E logits and takes the
+//     top k, then the group computes the SwiGLU of its 1/8 slice (I/8 rows)
+//     of each chosen expert; the down-projection weights of phase C are
+//     loaded here too;
 //  C  the group multiplies its slice of the hidden activations by the
 //     matching 1/8 column slice of every down matrix (routed, weighted by the
 //     routing weights, and shared): a partial output for all H rows;
 //  D  the 8 partial outputs are summed (fixed order) and added to the
 //     residual.
-// Exchanges.  A -> B logits (inside a group), B -> C hidden slice (inside a
+// Exchanges.  A -> B logits (across XCDs), B -> C hidden slice (inside a
 // group), C -> D partial outputs (across groups) and D -> A the new residual
-// (inside a group).  Values travel as 64-bit (value, epoch) pairs written
-// with device-scope stores; a consumer reads them with device-scope 128-bit
-// loads until every epoch matches, so no separate flag or barrier is needed.
-// Epochs are unique per (call, token, layer, exchange).  Every wait is
-// bounded: on time-out a workgroup raises the error flag and all workgroups
-// leave the kernel.
+// (inside a group).  Values travel as 64-bit (value, epoch) pairs; a
+// consumer reads them with 128-bit loads until every epoch matches, so no
+// separate flag or barrier is needed.  Epochs are unique per (call, token,
+// layer, exchange).  Every wait is bounded: on time-out a workgroup raises
+// the error flag and all workgroups leave the kernel.
 #include <float.h>
 #include <limits.h>
 
@@ -222,15 +223,12 @@ static_assert(sizeof(flint_nvfp4) == 3 * sizeof(uint64_t), "head entry is a poin
 struct StackLds {
   float h[kHidden];                                  // residual stream
   float u[kHidden / 32 * kRowPad];                   // normalised residual, padded rows
-  float logit[kMaxExperts];
   float hs[kSliceK / 32 * kRowPad];                  // this group's hidden slice, padded rows
   float part[kGroups * 64];                          // the 8 partial outputs of this workgroup's rows
   float hp[2 * kStackWGs];                           // head partials (max, index)
   float red[kStackWaves];
   float w[kMaxTopK];
   int32_t idx[kMaxTopK];
-  int32_t cand_k[kCommWaves * kMaxTopK];  // top-k candidates (keys) of each communication wave
-  int32_t cand_i[kCommWaves * kMaxTopK];
   float bv[kStackWaves];
   int32_t bi[kStackWaves];
   int32_t bad;
@@ -257,11 +255,12 @@ struct StackCoord {
 };
 
 // One role's pass over all tokens.  Both roles execute the same sequence of
-// workgroup barriers (marked B1..B7 per layer, H1..H4 per token) and leave
-// at the same barrier on error; returns false then.
+// workgroup barriers (marked B1, B2, B4..B7 per layer, H1..H5 per token) and
+// leave at the same barrier on error; returns false then.
 //
-// Communication role (waves 0-3): polls every exchange, takes the top k, and
-// computes 2 of the 12 routed gate/up pairs per wave and workgroup.  A wave's
+// Communication role (waves 0-3): polls every exchange (the first wave alone
+// gathers the logits and takes the top k), and computes 2 of the 12 routed
+// gate/up pairs per wave and workgroup.  A wave's
 // loads complete in issue order, so a wave that polls must not have weight
 // loads in flight.
 // Loading role (waves 4-7): router rows and the shared expert's gate/up
@@ -389,9 +388,7 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
         const float acc = router_dot();
         if (lane < kGroups) put_pair<Scope::kDevice>(&P.s2[((size_t)par * kGroups + lane) * kMaxExperts + rrow], acc, ep0);
       }
-      if constexpr (kComm) {
-        poll_pairs<Scope::kDevice>(s2, E, ep0, S.logit, wc);
-      } else {
+      if constexpr (!kComm) {
         FLINT_TRACE_LOAD(l, 8);
         if (qa < Isx) {
           const float gv = wave_sum(nvfp4_lane_dot32(cgs, sgs, xv)) * tgs;
@@ -399,59 +396,73 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
           if (lane == 0) put_pair<Scope::kXcd>(&s3[nroutedx + qa], silu(gv) * av, ep0 + 1);
         }
         FLINT_TRACE_LOAD(l, 9);
-      }
-      wg_barrier();  // B3: logits in LDS
-      if (S.bad) return false;
-      FLINT_TRACE(l, 2);
-
-      // ---------------------------------------------------------- phase B
-      // top-k in two stages on order-preserving integer keys of the logits.
-      // Stage 1: communication wave w takes the top k of logits 64 w ..
-      // 64 w + 63 (one per lane); each round takes the wave maximum and, by a
-      // ballot, its lowest lane, which holds the lowest index among equal
-      // values, and knocks that lane out.  Stage 2: wave 0 does the same over
-      // the 4 k candidates, laid out by wave and then rank, so that among
-      // equal values the lowest lane again holds the lowest index.
-      auto topk_round = [&](int& key, int r, int& my_key, int& my_l) {
-        const int m = wave_max_i32(key);
-        const uint64_t at = __builtin_amdgcn_ballot_w64(key == m);
-        const int lmax = (int)__builtin_ctzll(at);
-        if (lane == r) { my_key = m; my_l = lmax; }
-        if (lane == lmax) key = INT_MIN;
-      };
-      if constexpr (kComm) {
-        const int id = 64 * wv + lane;
-        int key = id < E ? ord_key(S.logit[id]) : INT_MIN + 1;
-        int ck = INT_MIN, cl = 0;
-        for (int r = 0; r < k; ++r) topk_round(key, r, ck, cl);
-        if (lane < k) {
-          S.cand_k[kMaxTopK * wv + lane] = ck;
-          S.cand_i[kMaxTopK * wv + lane] = 64 * wv + cl;
+      } else if (wv == 0) {
+        // ------------------------------------------------------ phase B
+        // The first communication wave alone gathers the E logits, four per
+        // lane (experts 4 lane .. 4 lane + 3), straight into registers, and
+        // takes the top k there: no LDS round trip and no barrier before it.
+        __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(s2, 0, E * 8, 0x00020000);
+        uint32_t v[8];
+        uint32_t spins = 0;
+        while (true) {
+          const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, 32 * lane, 0, poll_aux<Scope::kDevice>());
+          const auto c = __builtin_amdgcn_raw_buffer_load_b128(rs, 32 * lane + 16, 0, poll_aux<Scope::kDevice>());
+          v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+          v[4] = c[0]; v[5] = c[1]; v[6] = c[2]; v[7] = c[3];
+          bool ok = true;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) ok = ok && (4 * lane + j >= E || v[2 * j + 1] == ep0);
+          if (__builtin_amdgcn_ballot_w64(!ok) == 0 || poll_gave_up(spins, wc)) break;
         }
-      }
-      wg_barrier();  // B3b: candidates in LDS
-      if constexpr (kComm) {
-        if (wv == 0) {
-          const bool valid = lane < kCommWaves * kMaxTopK && (lane % kMaxTopK) < k;
-          int key = valid ? S.cand_k[lane] : INT_MIN;
-          const int ci = valid ? S.cand_i[lane] : INT_MAX;
-          int my_key = INT_MIN, my_l = 0;
-          for (int r = 0; r < k; ++r) topk_round(key, r, my_key, my_l);
-          const int my_i = __builtin_amdgcn_ds_bpermute(my_l << 2, ci);
-          // softmax over the k chosen logits (lane r holds the r-th; the
-          // first is the largest)
-          const float my_v = ord_key_value(my_key);
-          const float first = lane_f32(my_v, 0);
-          const float e = lane < k ? __expf(my_v - first) : 0.0f;
-          const float z = lane_f32(row16_sum(e), 0);
-          if (lane < k) {
-            S.idx[lane] = my_i;
-            S.w[lane] = e / z;
+        FLINT_TRACE(l, 2);
+        // Keys ordered by (logit descending, index ascending) as one signed
+        // 64-bit value: the order-preserving integer key of the logit above,
+        // 255 - index below.  Experts past E get the smallest key.
+        int64_t c4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * lane + j;
+          const int key = e < E ? ord_key(__uint_as_float(v[2 * j])) : INT_MIN;
+          c4[j] = (int64_t)(((uint64_t)(uint32_t)key << 32) | (uint32_t)(kMaxExperts - 1 - e));
+        }
+        // each lane sorts its four keys, largest first
+        auto cx = [&](int i, int j) {
+          const int64_t hi = c4[i] > c4[j] ? c4[i] : c4[j];
+          const int64_t lo = c4[i] > c4[j] ? c4[j] : c4[i];
+          c4[i] = hi; c4[j] = lo;
+        };
+        cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
+        // k rounds: the wave maximum of the lanes' first keys (upper halves)
+        // and, by a ballot, the lowest lane holding it; lanes cover the
+        // experts in increasing order and each lane's first key is its lowest
+        // index among equal logits, so that lane holds the lowest index.  The
+        // winning lane drops its first key.  Lane r keeps the r-th pick.
+        int my_key = INT_MIN, my_i = 0;
+        for (int r = 0; r < k; ++r) {
+          const int head = (int)(c4[0] >> 32);
+          const int m = wave_max_i32(head);
+          const int lmax = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(head == m));
+          const int low = __builtin_amdgcn_readlane((int)(uint32_t)c4[0], lmax);
+          if (lane == r) { my_key = m; my_i = kMaxExperts - 1 - low; }
+          if (lane == lmax) {
+            c4[0] = c4[1]; c4[1] = c4[2]; c4[2] = c4[3];
+            c4[3] = (int64_t)((uint64_t)(uint32_t)INT_MIN << 32);
           }
-          FLINT_TRACE(l, 15);
         }
+        // softmax over the k chosen logits (lane r holds the r-th; the first
+        // is the largest)
+        const float my_v = ord_key_value(my_key);
+        const float first = lane_f32(my_v, 0);
+        const float ex = lane < k ? __expf(my_v - first) : 0.0f;
+        const float z = lane_f32(row16_sum(ex), 0);
+        if (lane < k) {
+          S.idx[lane] = my_i;
+          S.w[lane] = ex / z;
+        }
+        FLINT_TRACE(l, 15);
       }
       wg_barrier();  // B4: top-k in LDS
+      if (S.bad) return false;
       FLINT_TRACE(l, 3);
 
       // routed gate/up pairs p = li + 32 q: q = wv + 4 pp (pp < 2) for a
