@@ -207,9 +207,10 @@ int32_t flint_stack_decode(const flint_stack_plan* plan /*[host]*/, const float*
  * the phase boundaries of two workgroups (one on the first XCD, one on the
  * last) into trace, int64 [2][L+1][16], followed by the stamps of layer 1 of
  * all 256 workgroups, int64 [256][16].  Per layer l, seen by the first
- * polling wave: 0 layer start, 1 norm done, 2 logits arrived, 3 top-k
- * known, 4 its routed pairs stored, 5 hidden slice arrived, 6 partial
- * outputs arrived, 7 new residual arrived, 15 top-k computed; seen by the
+ * polling wave: 0 layer start, 1 norm done, 2 logits arrived, 3 every pick
+ * of the top k published, 4 its routed pairs stored, 5 hidden slice arrived,
+ * 6 partial outputs arrived, 7 new residual arrived, 15 routing weights
+ * computed; seen by the
  * first loading wave: 8 router logit stored, 9 shared pair stored, 11 routed
  * phase started, 12 its routed pair stored, 13 partial outputs stored and
  * the next layer's rows requested, 14 residual rows stored; 10 is unused

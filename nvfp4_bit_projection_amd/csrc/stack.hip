@@ -232,6 +232,7 @@ struct StackLds {
   float bv[kStackWaves];
   int32_t bi[kStackWaves];
   int32_t bad;
+  int32_t nk;                                        // top-k picks published (phase B)
   uint64_t tab[kMaxStackLayers * kLayerWords + 3];   // layer table, then the head
   int64_t tr[(kTraceMaxLayers + 1) * kTracePoints];  // phase stamps of the first token
 };
@@ -255,7 +256,7 @@ struct StackCoord {
 };
 
 // One role's pass over all tokens.  Both roles execute the same sequence of
-// workgroup barriers (marked B1, B2, B4..B7 per layer, H1..H5 per token) and
+// workgroup barriers (marked B1..B5 per layer, H1..H5 per token) and
 // leave at the same barrier on error; returns false then.
 //
 // Communication role (waves 0-3): polls every exchange (the first wave alone
@@ -396,77 +397,37 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
           if (lane == 0) put_pair<Scope::kXcd>(&s3[nroutedx + qa], silu(gv) * av, ep0 + 1);
         }
         FLINT_TRACE_LOAD(l, 9);
-      } else if (wv == 0) {
-        // ------------------------------------------------------ phase B
-        // The first communication wave alone gathers the E logits, four per
-        // lane (experts 4 lane .. 4 lane + 3), straight into registers, and
-        // takes the top k there: no LDS round trip and no barrier before it.
-        __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(s2, 0, E * 8, 0x00020000);
-        uint32_t v[8];
-        uint32_t spins = 0;
-        while (true) {
-          const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, 32 * lane, 0, poll_aux<Scope::kDevice>());
-          const auto c = __builtin_amdgcn_raw_buffer_load_b128(rs, 32 * lane + 16, 0, poll_aux<Scope::kDevice>());
-          v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
-          v[4] = c[0]; v[5] = c[1]; v[6] = c[2]; v[7] = c[3];
-          bool ok = true;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) ok = ok && (4 * lane + j >= E || v[2 * j + 1] == ep0);
-          if (__builtin_amdgcn_ballot_w64(!ok) == 0 || poll_gave_up(spins, wc)) break;
-        }
-        FLINT_TRACE(l, 2);
-        // Keys ordered by (logit descending, index ascending) as one signed
-        // 64-bit value: the order-preserving integer key of the logit above,
-        // 255 - index below.  Experts past E get the smallest key.
-        int64_t c4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = 4 * lane + j;
-          const int key = e < E ? ord_key(__uint_as_float(v[2 * j])) : INT_MIN;
-          c4[j] = (int64_t)(((uint64_t)(uint32_t)key << 32) | (uint32_t)(kMaxExperts - 1 - e));
-        }
-        // each lane sorts its four keys, largest first
-        auto cx = [&](int i, int j) {
-          const int64_t hi = c4[i] > c4[j] ? c4[i] : c4[j];
-          const int64_t lo = c4[i] > c4[j] ? c4[j] : c4[i];
-          c4[i] = hi; c4[j] = lo;
-        };
-        cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
-        // k rounds: the wave maximum of the lanes' first keys (upper halves)
-        // and, by a ballot, the lowest lane holding it; lanes cover the
-        // experts in increasing order and each lane's first key is its lowest
-        // index among equal logits, so that lane holds the lowest index.  The
-        // winning lane drops its first key.  Lane r keeps the r-th pick.
-        int my_key = INT_MIN, my_i = 0;
-        for (int r = 0; r < k; ++r) {
-          const int head = (int)(c4[0] >> 32);
-          const int m = wave_max_i32(head);
-          const int lmax = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(head == m));
-          const int low = __builtin_amdgcn_readlane((int)(uint32_t)c4[0], lmax);
-          if (lane == r) { my_key = m; my_i = kMaxExperts - 1 - low; }
-          if (lane == lmax) {
-            c4[0] = c4[1]; c4[1] = c4[2]; c4[2] = c4[3];
-            c4[3] = (int64_t)((uint64_t)(uint32_t)INT_MIN << 32);
-          }
-        }
-        // softmax over the k chosen logits (lane r holds the r-th; the first
-        // is the largest)
-        const float my_v = ord_key_value(my_key);
-        const float first = lane_f32(my_v, 0);
-        const float ex = lane < k ? __expf(my_v - first) : 0.0f;
-        const float z = lane_f32(row16_sum(ex), 0);
-        if (lane < k) {
-          S.idx[lane] = my_i;
-          S.w[lane] = ex / z;
-        }
-        FLINT_TRACE(l, 15);
       }
-      wg_barrier();  // B4: top-k in LDS
-      if (S.bad) return false;
-      FLINT_TRACE(l, 3);
-
-      // routed gate/up pairs p = li + 32 q: q = wv + 4 pp (pp < 2) for a
-      // communication wave, q = 8 + lw for a loading wave.
+      // ---------------------------------------------------------- phase B
+      // The first communication wave gathers the E logits and takes the top
+      // k.  It publishes each pick in LDS as soon as its round ends (S.idx[r],
+      // then the count S.nk), and every other wave requests the gate/up rows
+      // of its pairs as soon as their expert is known, so the routed loads
+      // overlap the remaining rounds; the first wave takes the pairs of the
+      // last pick.  Routed gate/up pairs p = li + 32 q of this group's slice:
+      // q = 2 (wv - 1) + {0, 1} for communication waves 1-3, q = 6 + lw for a
+      // loading wave, q = 10 + {0, 1} for the first wave.
+      const int nk0 = (tok * L + l) * kMaxTopK;  // S.nk = nk0 + picks published in this layer
+      auto wait_picks = [&](int need) {
+        uint32_t spins = 0;
+        while (__hip_atomic_load(&S.nk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < nk0 + need) {
+          if (++spins > kSpinLimit) {
+            S.bad = 1;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      };
+      auto publish_picks = [&](int n) {
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0) __hip_atomic_store(&S.nk, nk0 + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      };
+      constexpr int kNq = kComm ? kGateUpComm : 1;
+      int pq[kNq];
+#pragma unroll
+      for (int pp = 0; pp < kNq; ++pp)
+        pq[pp] = li + kGroupWGs * (!kComm ? 2 * kCommWaves - 2 + lw : wv == 0 ? 10 + pp : 2 * (wv - 1) + pp);
       // Down-projection operands (every wave): output rows n = 64 li + 8 wv
       // + 4 pc + lane/16, 16 lanes per row, lane chunk j = 32 columns of the
       // slice; chunks j < 12 are routed columns, the rest shared ones.  These
@@ -478,66 +439,141 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       const int dslot = routed ? (32 * j) / Ix : 0;
       uint4 cdr[kDownPasses], cds[kDownPasses];
       uint32_t sdr[kDownPasses], sds[kDownPasses];
-      float dts = 0.0f, sts = 0.0f, dw = 0.0f;
-      auto load_down = [&]() {
-        const rsrc_t rdc = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWDownC), (uint64_t)E * kHidden * I / 2);
-        const rsrc_t rds = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWDownS), (uint64_t)E * kHidden * I / 16);
+      float dts = 0.0f, sts = 0.0f;
+      // column-sliced layouts (packed at prepare time): routed [E][8][H][Ix],
+      // shared [8][H][Isx], codes 2 per byte, one scale byte per 16 columns.
+      // Every lane issues both kinds of loads; the one that is not its own
+      // reads past the end of its buffer, which returns zeros and touches no
+      // memory, so the two combine with an OR and no branch is needed.
+      auto load_down_shared = [&]() {
         const rsrc_t rsdc = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSdC), (uint64_t)kHidden * Is / 2);
         const rsrc_t rsds = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSdS), (uint64_t)kHidden * Is / 16);
-        const int doff = routed ? (32 * j) % Ix : 0;  // column in the expert's slice
-        const int de = S.idx[dslot];
         const int scol = routed ? 0 : 32 * j - nroutedx;  // column in the shared slice
-        // column-sliced layouts (packed at prepare time): routed [E][8][H][Ix],
-        // shared [8][H][Isx], codes 2 per byte, one scale byte per 16 columns
-        const uint32_t rslice = (uint32_t)((de * kGroups + g) * kHidden), sslice = (uint32_t)(g * kHidden);
-        // every lane issues both loads; the one that is not its own reads
-        // past the end of its buffer, which returns zeros and touches no
-        // memory, so the pair combines with an OR and no branch is needed
-        const uint32_t oob_c = (uint32_t)((uint64_t)E * kHidden * I / 2);
+        const uint32_t sslice = (uint32_t)(g * kHidden);
         const uint32_t oob_s = (uint32_t)((uint64_t)kHidden * Is / 2);
 #pragma unroll
         for (int pc = 0; pc < kDownPasses; ++pc) {
-          const int n = 64 * li + 8 * wv + 4 * pc + (lane >> 4);
-          const uint32_t rr = rslice + (uint32_t)n, sr = sslice + (uint32_t)n;
-          cdr[pc] = bload_u4_nt(rdc, routed ? rr * (Ix / 2) + doff / 2 : oob_c);
-          sdr[pc] = bload_u16_nt(rds, routed ? rr * (Ix / 16) + doff / 16 : oob_c / 8);
+          const uint32_t sr = sslice + (uint32_t)(64 * li + 8 * wv + 4 * pc + (lane >> 4));
           cds[pc] = bload_u4_nt(rsdc, routed ? oob_s : sr * (Isx / 2) + scol / 2);
           sds[pc] = bload_u16_nt(rsds, routed ? oob_s / 8 : sr * (Isx / 16) + scol / 16);
         }
+        sts = bload_f32(make_rsrc(tab_ptr<const float>(S, w0 + kWSdT), 4), 0);
+      };
+      auto load_down_routed = [&]() {
+        const rsrc_t rdc = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWDownC), (uint64_t)E * kHidden * I / 2);
+        const rsrc_t rds = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWDownS), (uint64_t)E * kHidden * I / 16);
+        const int doff = routed ? (32 * j) % Ix : 0;  // column in the expert's slice
+        const int de = S.idx[dslot];
+        const uint32_t rslice = (uint32_t)((de * kGroups + g) * kHidden);
+        const uint32_t oob_c = (uint32_t)((uint64_t)E * kHidden * I / 2);
+#pragma unroll
+        for (int pc = 0; pc < kDownPasses; ++pc) {
+          const uint32_t rr = rslice + (uint32_t)(64 * li + 8 * wv + 4 * pc + (lane >> 4));
+          cdr[pc] = bload_u4_nt(rdc, routed ? rr * (Ix / 2) + doff / 2 : oob_c);
+          sdr[pc] = bload_u16_nt(rds, routed ? rr * (Ix / 16) + doff / 16 : oob_c / 8);
+        }
         dts = bload_f32(make_rsrc(tab_ptr<const float>(S, w0 + kWExpTs), (uint64_t)E * 3 * 4),
                         (uint32_t)(3 * de + 2) * 4);
-        sts = bload_f32(make_rsrc(tab_ptr<const float>(S, w0 + kWSdT), 4), 0);
-        dw = S.w[dslot];
       };
-      if constexpr (kComm) {
-        PairOps o[kGateUpComm];
+      PairOps o[kNq];
+      if (kComm && wv == 0) {
+        // The E logits, four per lane (experts 4 lane .. 4 lane + 3),
+        // straight into registers; the top k is taken there.
+        __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(s2, 0, E * 8, 0x00020000);
+        uint32_t v[8];
+        uint32_t spins = 0;
+        while (true) {
+          const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, 32 * lane, 0, poll_aux<Scope::kDevice>());
+          const auto c = __builtin_amdgcn_raw_buffer_load_b128(rs, 32 * lane + 16, 0, poll_aux<Scope::kDevice>());
+          v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+          v[4] = c[0]; v[5] = c[1]; v[6] = c[2]; v[7] = c[3];
+          bool ok = true;
 #pragma unroll
-        for (int pp = 0; pp < kGateUpComm; ++pp) o[pp] = load_pair(w0, li + kGroupWGs * (wv + kCommWaves * pp));
-        load_down();
-#pragma unroll
-        for (int pp = 0; pp < kGateUpComm; ++pp) {
-          const int p = li + kGroupWGs * (wv + kCommWaves * pp);
-          if (p < nroutedx) {
-            const float hval = pair_value(o[pp], xv);
-            if (lane == 0) put_pair<Scope::kXcd>(&s3[p], hval, ep0 + 1);
-          }
+          for (int jj = 0; jj < 4; ++jj) ok = ok && (4 * lane + jj >= E || v[2 * jj + 1] == ep0);
+          if (__builtin_amdgcn_ballot_w64(!ok) == 0 || poll_gave_up(spins, wc)) break;
         }
+        FLINT_TRACE(l, 2);
+        // Keys ordered by (logit descending, index ascending) as one signed
+        // 64-bit value: the order-preserving integer key of the logit above,
+        // 255 - index below.  Experts past E get the smallest key.
+        int64_t c4[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int e = 4 * lane + jj;
+          const int key = e < E ? ord_key(__uint_as_float(v[2 * jj])) : INT_MIN;
+          c4[jj] = (int64_t)(((uint64_t)(uint32_t)key << 32) | (uint32_t)(kMaxExperts - 1 - e));
+        }
+        // each lane sorts its four keys, largest first
+        auto cx = [&](int i0, int i1) {
+          const int64_t hi = c4[i0] > c4[i1] ? c4[i0] : c4[i1];
+          const int64_t lo = c4[i0] > c4[i1] ? c4[i1] : c4[i0];
+          c4[i0] = hi; c4[i1] = lo;
+        };
+        cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
+        // k rounds: the wave maximum of the lanes' first keys (upper halves)
+        // and, by a ballot, the lowest lane holding it; lanes cover the
+        // experts in increasing order and each lane's first key is its lowest
+        // index among equal logits, so that lane holds the lowest index.  The
+        // winning lane drops its first key.  Lane r keeps the r-th key.
+        int my_key = INT_MIN;
+        for (int r = 0; r < k; ++r) {
+          const int head = (int)(c4[0] >> 32);
+          const int m = wave_max_i32(head);
+          const int lmax = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(head == m));
+          const int low = __builtin_amdgcn_readlane((int)(uint32_t)c4[0], lmax);
+          if (lane == r) my_key = m;
+          if (lane == lmax) {
+            c4[0] = c4[1]; c4[1] = c4[2]; c4[2] = c4[3];
+            c4[3] = (int64_t)((uint64_t)(uint32_t)INT_MIN << 32);
+          }
+          if (lane == 0) S.idx[r] = kMaxExperts - 1 - low;
+          if (r + 1 < k) publish_picks(r + 1);
+        }
+        // this wave's own pairs (the last pick is in S.idx), then every pick
+        // is published
+#pragma unroll
+        for (int pp = 0; pp < kNq; ++pp) o[pp] = load_pair(w0, pq[pp]);
+        publish_picks(k);
+        FLINT_TRACE(l, 3);
+        load_down_shared();
+        load_down_routed();
+        // softmax over the k chosen logits (lane r holds the r-th; the first
+        // is the largest); the weights are read in phase C
+        const float my_v = ord_key_value(my_key);
+        const float first = lane_f32(my_v, 0);
+        const float ex = lane < k ? __expf(my_v - first) : 0.0f;
+        const float z = lane_f32(row16_sum(ex), 0);
+        if (lane < k) S.w[lane] = ex / z;
+        FLINT_TRACE(l, 15);
+      } else {
+        if constexpr (!kComm) FLINT_TRACE_LOAD(l, 11);
+#pragma unroll
+        for (int pp = 0; pp < kNq; ++pp) {
+          wait_picks((pq[pp] < nroutedx ? pq[pp] / Ix : 0) + 1);
+          o[pp] = load_pair(w0, pq[pp]);
+        }
+        wait_picks(k);
+        if constexpr (!kComm) {
+          if (P.routes && blockIdx.x == 0 && t - kCommThreads < k)
+            P.routes[((size_t)tok * L + l) * k + (t - kCommThreads)] = S.idx[t - kCommThreads];
+        }
+        load_down_shared();
+        load_down_routed();
+      }
+#pragma unroll
+      for (int pp = 0; pp < kNq; ++pp) {
+        if (pq[pp] < nroutedx) {
+          const float hval = pair_value(o[pp], xv);
+          if (lane == 0) put_pair<Scope::kXcd>(&s3[pq[pp]], hval, ep0 + 1);
+        }
+      }
+      if constexpr (kComm) {
         FLINT_TRACE(l, 4);
         poll_pairs<Scope::kXcd>(s3, kSliceK, ep0 + 1, S.hs, wc, true);
       } else {
-        FLINT_TRACE_LOAD(l, 11);
-        if (P.routes && blockIdx.x == 0 && t - kCommThreads < k)
-          P.routes[((size_t)tok * L + l) * k + (t - kCommThreads)] = S.idx[t - kCommThreads];
-        const int p = li + kGroupWGs * (2 * kCommWaves + lw);
-        const PairOps o = load_pair(w0, p);
-        load_down();
-        if (p < nroutedx) {
-          const float hval = pair_value(o, xv);
-          if (lane == 0) put_pair<Scope::kXcd>(&s3[p], hval, ep0 + 1);
-        }
         FLINT_TRACE_LOAD(l, 12);
       }
-      wg_barrier();  // B5: hidden slice in LDS
+      wg_barrier();  // B3: hidden slice in LDS
       if (S.bad) return false;
       FLINT_TRACE(l, 5);
 
@@ -545,7 +581,7 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       {
         float hv[32];
         lds_x32(S.hs + kRowPad * j, hv);
-        const float coef = routed ? dw * dts : sts;
+        const float coef = routed ? S.w[dslot] * dts : sts;
 #pragma unroll
         for (int pc = 0; pc < kDownPasses; ++pc) {
           const uint4 c = make_uint4(cdr[pc].x | cds[pc].x, cdr[pc].y | cds[pc].y, cdr[pc].z | cds[pc].z,
@@ -580,7 +616,7 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
         if (have_a) load_phase_a(next);
         FLINT_TRACE_LOAD(l, 13);
       }
-      wg_barrier();  // B6: partial outputs of this workgroup's rows in LDS
+      wg_barrier();  // B4: partial outputs of this workgroup's rows in LDS
       if (S.bad) return false;
       FLINT_TRACE(l, 6);
 
@@ -600,7 +636,7 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
           FLINT_TRACE_LOAD(l, 14);
         }
       }
-      wg_barrier();  // B7: new residual in LDS
+      wg_barrier();  // B5: new residual in LDS
       if (S.bad) return false;
       FLINT_TRACE(l, 7);
     }
@@ -700,7 +736,10 @@ __global__ __launch_bounds__(kStackThreads, 1) void k_stack_decode(StackParams P
     const uint64_t* hsrc = reinterpret_cast<const uint64_t*>(&table->head);
     if (C.t < 3) S.tab[kMaxStackLayers * kLayerWords + C.t] = hsrc[C.t];
   }
-  if (C.t == 0) S.bad = 0;
+  if (C.t == 0) {
+    S.bad = 0;
+    S.nk = 0;
+  }
   wg_barrier();
   if (ld_dev_u32(P.ctrl + 1)) return;  // an earlier call gave up: do nothing
   if (xcc_id() != (uint32_t)C.g) {     // the in-XCD exchanges need b -> XCD b % 8
