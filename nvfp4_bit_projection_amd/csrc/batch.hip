@@ -9,19 +9,20 @@
 // chosen expert's three matrices are streamed once for all the tokens that
 // picked it.  The shared expert, the router and the head are streamed once
 // and applied to all B tokens.  Per layer:
-//   k_bnorm     u_b = h_b / sqrt(mean(h_b^2) + eps)
-//   k_broute    logits[b][e] = router[e] . u_b   (one router row per wave)
-//   k_btopk     top-k and renormalised softmax per token (one wave per token)
-//   k_bucket    (token, slot) pairs grouped by expert, experts in index
-//               order, pairs in (token, slot) order: a histogram, a scan, a
-//               scatter in one workgroup
-//   k_bgateup   SwiGLU rows: one (gate, up) row pair per wave, applied to
-//               every pair of its expert; k_bgateup_shared the same for the
-//               shared expert and every token (tokens staged in LDS)
-//   k_bdown     down rows per 16/32-lane group, same sharing; k_bdown_shared
-//   k_bcombine  h_b += sum_s down[b][s] + shared[b]   (fixed order)
-// and at the end k_bnorm + k_bhead (rows streamed once, tokens in LDS) +
-// k_bargmax.  All arithmetic fp32; weights NVFP4 decoded in registers.
+//   k_broute     logits[b][e] = router[e] . u_b (one router row per wave, 8
+//                tokens per workgroup, fp32)
+//   k_btopk      top-k and renormalised softmax per token (one wave per token)
+//   k_bucket     (token, slot) pairs grouped by expert, experts in index
+//                order, pairs in (token, slot) order
+//   k_mm_gateup  h = silu(gate . u) * (up . u) for every chosen expert and its
+//                tokens, and for the shared expert and all tokens, on matrix
+//                cores (one launch)
+//   k_mm_down    the down projections of both, routed outputs weighted by
+//                their routing weights (one launch)
+//   k_bnorm      h_b += sum over slots (fixed order) + shared, then the next
+//                norm u_b = h_b / sqrt(mean(h_b^2) + eps)
+// and at the end k_mm_head (rows streamed once for all tokens) + k_bargmax.
+// Weights are NVFP4 decoded in registers; results as accurate as fp32.
 #include <float.h>
 #include <limits.h>
 
@@ -33,6 +34,21 @@ namespace flint {
 namespace {
 
 constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint16_t bf16_bits(__bf16 v) { return __builtin_bit_cast(uint16_t, v); }
+
+// x = hi + mid + lo, each bf16 rounded to nearest even (exact for normal x:
+// each remainder is exact in fp32 and has 8 fewer significant bits)
+__device__ __forceinline__ void split3(float x, uint16_t* o) {
+  const __bf16 hi = (__bf16)x;
+  const float r1 = x - (float)hi;
+  const __bf16 mid = (__bf16)r1;
+  const __bf16 lo = (__bf16)(r1 - (float)mid);
+  o[0] = bf16_bits(hi);
+  o[1] = bf16_bits(mid);
+  o[2] = bf16_bits(lo);
+}
+
 
 __device__ __forceinline__ void lane_x32(const float* __restrict__ v, int lane, float* xv) {
   const float4* p = reinterpret_cast<const float4*>(v + 32 * lane);
@@ -72,62 +88,38 @@ __device__ __forceinline__ void staged_x32(const float* sh, int b, int j, float*
   }
 }
 
-// ---------------------------------------------------------------- norm --
-// grid B, 256 threads: u_b = h_b * s_b, s_b = 1/sqrt(mean(h_b^2) + eps)
-__global__ __launch_bounds__(kThreads) void k_bnorm(const float* __restrict__ h, float* __restrict__ u, float eps) {
-  const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const float* hb = h + (size_t)b * kHidden;
-  float v[kHidden / kThreads];
-  float ss = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kHidden / kThreads; ++i) {
-    v[i] = hb[t + i * kThreads];
-    ss = __builtin_fmaf(v[i], v[i], ss);
-  }
-  ss = wave_sum(ss);
-  __shared__ float red[kThreads / 64];
-  if (lane == 0) red[w] = ss;
-  __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
-  const float s = 1.0f / sqrtf(tot * (1.0f / kHidden) + eps);
-#pragma unroll
-  for (int i = 0; i < kHidden / kThreads; ++i) u[(size_t)b * kHidden + t + i * kThreads] = v[i] * s;
-}
-
 // --------------------------------------------------------------- router --
-// grid ceil(E/4), 256 threads: router row e = 4 blockIdx.x + wave, read once,
-// dotted with every token (tokens staged in LDS, 12 per pass).
+// grid (ceil(E/4), ceil(B/8)), 256 threads: router row e = 4 blockIdx.x +
+// wave, dotted with tokens 8 blockIdx.y .. + 7 (staged in LDS).  The router
+// is read once per token group (2 MB per 8 tokens, from L2 after the first).
+constexpr int kRouteTok = 8;
 __global__ __launch_bounds__(kThreads) void k_broute(const float* __restrict__ router, int E,
                                                      const float* __restrict__ u, int B, float* __restrict__ logits) {
-  __shared__ __align__(16) float sh[kStageFloats];
+  __shared__ __align__(16) float sh[kRouteTok * (kHidden / 32) * kPad];
   const int lane = threadIdx.x & 63, e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b0 = blockIdx.y * kRouteTok, nb = B - b0 < kRouteTok ? B - b0 : kRouteTok;
   float wr[32];
   {
     const float* rw = router + (size_t)(e < E ? e : 0) * kHidden + 32 * lane;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float4 a = ld_nt_f4(rw + 4 * i);
+      const float4 a = *reinterpret_cast<const float4*>(rw + 4 * i);
       wr[4 * i] = a.x; wr[4 * i + 1] = a.y; wr[4 * i + 2] = a.z; wr[4 * i + 3] = a.w;
     }
   }
-  constexpr int P = stage_tokens_per_pass<kHidden>();
-  for (int b0 = 0; b0 < B; b0 += P) {
-    const int nb = B - b0 < P ? B - b0 : P;
-    __syncthreads();
-    stage_tokens<kHidden>(u, b0, nb, sh);
-    __syncthreads();
-    for (int b = 0; b < nb; ++b) {
-      float xv[32];
-      staged_x32<kHidden>(sh, b, lane, xv);
-      float a0 = 0.0f, a1 = 0.0f;
+  stage_tokens<kHidden>(u, b0, nb, sh);
+  __syncthreads();
+  for (int b = 0; b < nb; ++b) {
+    float xv[32];
+    staged_x32<kHidden>(sh, b, lane, xv);
+    float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 32; i += 2) {
-        a0 = __builtin_fmaf(wr[i], xv[i], a0);
-        a1 = __builtin_fmaf(wr[i + 1], xv[i + 1], a1);
-      }
-      const float acc = wave_sum(a0 + a1);
-      if (lane == 0 && e < E) logits[(size_t)(b0 + b) * E + e] = acc;
+    for (int i = 0; i < 32; i += 2) {
+      a0 = __builtin_fmaf(wr[i], xv[i], a0);
+      a1 = __builtin_fmaf(wr[i + 1], xv[i + 1], a1);
     }
+    const float acc = wave_sum(a0 + a1);
+    if (lane == 0 && e < E) logits[(size_t)(b0 + b) * E + e] = acc;
   }
 }
 
@@ -203,252 +195,536 @@ __device__ __forceinline__ int block_excl_scan(int v, int* sh) {  // 256 threads
   return base + x - v;
 }
 
+// One workgroup of 256 threads (E <= 256, B*k <= 512): per-expert counts by
+// LDS atomics (order-free), exclusive scans for each expert's start and each
+// chosen expert's rank, then every pair p goes to start[e] + (number of
+// earlier pairs with the same expert): pairs in (token, slot) order within
+// an expert, experts in index order, independent of timing.
 __global__ __launch_bounds__(kThreads) void k_bucket(const int32_t* __restrict__ idx_g, int nb, int E,
                                                      int32_t* __restrict__ bk) {
-  const int e = threadIdx.x;
+  const int t = threadIdx.x;
   __shared__ int sh[kThreads / 64];
   __shared__ int idx[kMaxBatch * kMaxTopK];
-  for (int p = e; p < nb; p += kThreads) idx[p] = idx_g[p];
+  __shared__ int cnt[kMaxExperts], start[kMaxExperts];
+  cnt[t] = 0;
+  for (int p = t; p < nb; p += kThreads) idx[p] = idx_g[p];
   __syncthreads();
-  int cnt = 0;
-  if (e < E)
-    for (int p = 0; p < nb; ++p) cnt += idx[p] == e;
-  const int start = block_excl_scan(cnt, sh);
-  const int rank = block_excl_scan(cnt > 0 ? 1 : 0, sh);
-  if (cnt > 0) {
-    bk[kBkExperts + rank] = e;
-    bk[kBkStart + rank] = start;
-    int o = start;
-    for (int p = 0; p < nb; ++p)
-      if (idx[p] == e) bk[kBkPairs + o++] = p;
+  for (int p = t; p < nb; p += kThreads) atomicAdd(&cnt[idx[p]], 1);
+  __syncthreads();
+  const int c = t < E ? cnt[t] : 0;
+  const int st = block_excl_scan(c, sh);
+  const int rank = block_excl_scan(c > 0 ? 1 : 0, sh);
+  start[t] = st;
+  if (c > 0) {
+    bk[kBkExperts + rank] = t;
+    bk[kBkStart + rank] = st;
   }
-  if (e == kThreads - 1) {
-    const int U = rank + (cnt > 0 ? 1 : 0);
+  if (t == kThreads - 1) {
+    const int U = rank + (c > 0 ? 1 : 0);
     bk[0] = U;
-    bk[kBkStart + U] = start + cnt;
+    bk[kBkStart + U] = st + c;
+  }
+  __syncthreads();
+  for (int p = t; p < nb; p += kThreads) {
+    const int e = idx[p];
+    int before = 0;
+    for (int q = 0; q < p; ++q) before += idx[q] == e;
+    bk[kBkPairs + start[e] + before] = p;
   }
 }
 
-// -------------------------------------------------------------- gate/up --
-// Routed: grid (I/16, Umax), 256 threads; blockIdx.y < U is the rank-u
-// expert; each wave takes 4 consecutive rows (all their loads issued at once)
-// and applies them to each of the expert's (token, slot) pairs (few per
-// expert, so a token vector comes straight from memory and serves 4 rows).
-// hr [B*k][I].
-constexpr int kRowsPerWave = 4;
-__global__ __launch_bounds__(kThreads) void k_bgateup(flint_moe_layer L, int I, int k, const float* __restrict__ u,
-                                                      const int32_t* __restrict__ bk, float* __restrict__ hr) {
-  const int lane = threadIdx.x & 63, r0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave;
-  const int ub = blockIdx.y;
-  if (ub >= bk[0] || r0 >= I) return;
-  const int e = bk[kBkExperts + ub];
-  uint4 cg[kRowsPerWave], cu[kRowsPerWave];
-  uint32_t sg[kRowsPerWave], su[kRowsPerWave];
-#pragma unroll
-  for (int q = 0; q < kRowsPerWave; ++q) {
-    const size_t row = (size_t)e * I + r0 + q;
-    cg[q] = ld_nt_u4(L.gate_codes + row * (kHidden / 2) + 16 * lane);
-    cu[q] = ld_nt_u4(L.up_codes + row * (kHidden / 2) + 16 * lane);
-    sg[q] = ld_nt_u16(L.gate_scales + row * (kHidden / 16) + 2 * lane);
-    su[q] = ld_nt_u16(L.up_scales + row * (kHidden / 16) + 2 * lane);
+// ------------------------------------------------------ matrix cores --
+// The contractions over K run on 16x16x32 matrix-core instructions with
+// results as accurate as fp32 arithmetic:
+//  - an E2M1 code times its E4M3 block scale has at most 5 significant bits,
+//    so every weight is exact in fp16 and in bf16 (decoded in registers; the
+//    fp32 tensor scale multiplies the result);
+//  - every fp32 activation is split into parts that sum to it, kept as planes
+//    [P][rows][K]: two fp16 parts (hi + lo, 22 significant bits) for inputs
+//    bounded by an RMSNorm (|u| <= sqrt(H) = 45.3: no fp16 overflow), three
+//    bf16 parts (hi + mid + lo, exact for normal values, fp32 range) for the
+//    SwiGLU outputs, which have no such bound;
+//  - products of two such parts are exact in fp32 and accumulate in fp32.
+// A workgroup of 4 waves takes one weight group (a chosen expert, the shared
+// expert, or the head) and a range of its rows; each wave takes two 16-row
+// tiles; tokens go in passes of 32 (two 16-token tiles).  The pass's
+// activation planes are copied into LDS in K segments, gathered by token;
+// a lane's weight bytes are requested three 256-wide chunks ahead.
+//
+// Operand layout (16x16x32, lane l, m = l % 16, q = l / 16): A (tokens x K)
+// token m, B (K x rows) row m, each with 8 K values of group q; C (tokens x
+// rows) row m, tokens 4q .. 4q+3.  A lane's 32 bytes of codes per chunk hold
+// K values 64q .. 64q+63 of the chunk, consumed in 8 steps of 8; the
+// activations are staged in the same K order, so the A and B operands of step
+// j are K values 64q + 8j .. 64q + 8j + 7.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+constexpr int kMmThreads = 256;
+constexpr int kMmWaves = kMmThreads / 64;
+constexpr int kMmChunk = 256;                   // K per 32-byte group of a lane's weight codes
+constexpr int kMmTok = 32;                      // tokens per pass
+constexpr int kMmStage = 8192;                  // values per plane per staged segment (rows x K)
+constexpr int kMmGateUpRows = 16 * kMmWaves;    // gate/up row pairs per workgroup
+constexpr int kMmRows = 32 * kMmWaves;          // rows per workgroup (down, head)
+
+// The two operand formats.  decode(): the 8 E2M1 codes of a 32-bit word
+// (element 2i in the low nibble of byte i) times an E4M3 block scale.
+struct FmtF16 {
+  static constexpr int P = 2;
+  typedef f16x8_t vec;
+  struct Scale {
+    float p2;     // power-of-two part of the block scale
+    _Float16 f;   // the rest: 1 + m/8, or m for a subnormal scale
+  };
+  static __device__ __forceinline__ Scale scale(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15, m = b & 7;
+    Scale s;
+    s.p2 = __uint_as_float((e ? e + 120u : 118u) << 23);  // 2^(e-7), or 2^-9
+    s.f = e ? (_Float16)(1.0f + 0.125f * (float)m) : (_Float16)(float)m;
+    return s;
   }
-  const float Sg = L.expert_tscales[3 * e + 0], Su = L.expert_tscales[3 * e + 1];
-  const int p0 = bk[kBkStart + ub], p1 = bk[kBkStart + ub + 1];
-  for (int p = p0; p < p1; ++p) {
-    const int pid = bk[kBkPairs + p];
-    float xv[32];
-    lane_x32(u + (size_t)(pid / k) * kHidden, lane, xv);
-#pragma unroll 2
-    for (int q = 0; q < kRowsPerWave; ++q) {
-      const float g = wave_sum(nvfp4_lane_dot32(cg[q], sg[q], xv)) * Sg;
-      const float a = wave_sum(nvfp4_lane_dot32(cu[q], su[q], xv)) * Su;
-      if (lane == 0) hr[(size_t)pid * I + r0 + q] = silu(g) * a;
-    }
+  static __device__ __forceinline__ vec decode(uint32_t w, Scale s) {
+    const f16x2_t ff = {s.f, s.f};
+    const f16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.p2, 0) * ff;
+    const f16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.p2, 1) * ff;
+    const f16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.p2, 2) * ff;
+    const f16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, s.p2, 3) * ff;
+    return vec{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+  }
+  static __device__ __forceinline__ f32x4_t mma(vec a, vec b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  // x = hi + lo
+  static __device__ __forceinline__ void split(float x, uint16_t* o) {
+    const _Float16 hi = (_Float16)x;
+    o[0] = __builtin_bit_cast(uint16_t, hi);
+    o[1] = __builtin_bit_cast(uint16_t, (_Float16)(x - (float)hi));
+  }
+};
+struct FmtBF16 {
+  static constexpr int P = 3;
+  typedef bf16x8_t vec;
+  typedef float Scale;
+  static __device__ __forceinline__ Scale scale(uint32_t b) { return e4m3_to_f32(b); }
+  static __device__ __forceinline__ vec decode(uint32_t w, Scale d) {
+    const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    vec r;
+    r[0] = (__bf16)(v0[0] * d); r[1] = (__bf16)(v0[1] * d);
+    r[2] = (__bf16)(v1[0] * d); r[3] = (__bf16)(v1[1] * d);
+    r[4] = (__bf16)(v2[0] * d); r[5] = (__bf16)(v2[1] * d);
+    r[6] = (__bf16)(v3[0] * d); r[7] = (__bf16)(v3[1] * d);
+    return r;
+  }
+  static __device__ __forceinline__ f32x4_t mma(vec a, vec b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void split(float x, uint16_t* o) { split3(x, o); }
+};
+template <class F>
+constexpr int mm_buf_bytes() { return F::P * kMmStage * 2; }
+
+// One wave's two 16-row weight tiles: this lane's row (m) of each, codes and
+// scales of a matrix with K columns.
+struct MmTiles {
+  const uint8_t* c[2];
+  const uint8_t* s[2];
+};
+struct MmRegs {  // a lane's weight bytes of one chunk
+  uint4 c[2][2];
+  uint32_t s[2];
+};
+__device__ __forceinline__ void mm_load_w(const MmTiles& T, int u, int q, MmRegs& R) {
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const uint8_t* cp = T.c[rt] + (kMmChunk / 2) * u + 32 * q;
+    R.c[rt][0] = ld_nt_u4(cp);
+    R.c[rt][1] = ld_nt_u4(cp + 16);
+    R.s[rt] = ld_nt_u32(T.s[rt] + (kMmChunk / 16) * u + 4 * q);
   }
 }
 
-// Shared: grid Is/4, 256 threads; wave row r, decoded once, applied to every
-// token (tokens staged in LDS).  hs [B][Is].
-__global__ __launch_bounds__(kThreads) void k_bgateup_shared(flint_moe_layer L, int Is, int B,
-                                                             const float* __restrict__ u, float* __restrict__ hs) {
-  __shared__ __align__(16) float sh[kStageFloats];
-  const int lane = threadIdx.x & 63, r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const uint4 cg = ld_nt_u4(L.shared_gate.codes + (size_t)r * (kHidden / 2) + 16 * lane);
-  const uint4 cu = ld_nt_u4(L.shared_up.codes + (size_t)r * (kHidden / 2) + 16 * lane);
-  const uint32_t sg = ld_nt_u16(L.shared_gate.scales + (size_t)r * (kHidden / 16) + 2 * lane);
-  const uint32_t su = ld_nt_u16(L.shared_up.scales + (size_t)r * (kHidden / 16) + 2 * lane);
-  const float Sg = *L.shared_gate.tscale, Su = *L.shared_up.tscale;
-  float wg[32], wu[32];
-  fp4x8_values(cg.x, wg); fp4x8_values(cg.y, wg + 8); fp4x8_values(cg.z, wg + 16); fp4x8_values(cg.w, wg + 24);
-  fp4x8_values(cu.x, wu); fp4x8_values(cu.y, wu + 8); fp4x8_values(cu.z, wu + 16); fp4x8_values(cu.w, wu + 24);
-  const float dg0 = e4m3_to_f32(sg & 0xFF), dg1 = e4m3_to_f32(sg >> 8);
-  const float du0 = e4m3_to_f32(su & 0xFF), du1 = e4m3_to_f32(su >> 8);
-  constexpr int P = stage_tokens_per_pass<kHidden>();
-  for (int b0 = 0; b0 < B; b0 += P) {
-    const int nb = B - b0 < P ? B - b0 : P;
-    __syncthreads();
-    stage_tokens<kHidden>(u, b0, nb, sh);
-    __syncthreads();
-    for (int b = 0; b < nb; ++b) {
-      float xv[32];
-      staged_x32<kHidden>(sh, b, lane, xv);
-      float g0 = 0.0f, g1 = 0.0f, a0 = 0.0f, a1 = 0.0f;
+// Staged activations: the pass's tokens padded to R rows (a power of two, 4
+// .. 32) and a K segment of kseg = min(8192 / R, K) values, P planes, in LDS
+// as [plane][row][kseg] 16-bit values; granule g (8 values) of row r sits at
+// position g ^ (r % 16), so the rows read in one step hit distinct banks.
+// The copy is made of 1 KB buffer-to-LDS loads (64 lanes x 16 B) dealt
+// round-robin to the waves; a row without a token reads past the end of the
+// planes (zeros, no memory access) and its results are dropped.
+__device__ __forceinline__ void mm_stage(rsrc_t rA, int P, int a_rows, int K, const int* srow, int R, int kseg,
+                                         int k0, unsigned char* buf, int wv, int lane) {
+  const int row_bytes = 2 * kseg, plane_bytes = R * row_bytes, ncopies = P * plane_bytes / 1024;
+  for (int cpy = wv; cpy < ncopies; cpy += kMmWaves) {
+    const int off = cpy * 1024 + 16 * lane;
+    const int p = off / plane_bytes, rem = off % plane_bytes;
+    const int r = rem / row_bytes, g = ((rem % row_bytes) >> 4) ^ (r & 15);
+    const int tr = srow[r];
+    const uint32_t src =
+        tr >= 0 ? (uint32_t)((((size_t)p * a_rows + tr) * K + k0 + 8 * g) * 2) : 0xFFFFFFF0u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (__attribute__((address_space(3))) void*)(buf + cpy * 1024), 16, src,
+                                             0, 0, 0);
+  }
+}
+
+// The matrix-core steps of one 256-wide K chunk (chunk c of the staged
+// segment): acc[rt][tt] += A(token tile tt) x B(row tile rt) over the planes.
+template <class F>
+__device__ __forceinline__ void mm_chunk(const MmRegs& R, const unsigned char* buf, int Rrows, int kseg, int c,
+                                         int ntt, int lane, f32x4_t (&acc)[2][2]) {
+  const int m = lane & 15, q = lane >> 4;
+  const int row_bytes = 2 * kseg, plane_bytes = Rrows * row_bytes;
+  typename F::Scale d[2][4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        g0 = __builtin_fmaf(wg[i], xv[i], g0);
-        g1 = __builtin_fmaf(wg[16 + i], xv[16 + i], g1);
-        a0 = __builtin_fmaf(wu[i], xv[i], a0);
-        a1 = __builtin_fmaf(wu[16 + i], xv[16 + i], a1);
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[rt][i] = F::scale((R.s[rt] >> (8 * i)) & 0xFF);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t w0 = j < 4 ? (&R.c[0][0].x)[j] : (&R.c[0][1].x)[j - 4];
+    const uint32_t w1 = j < 4 ? (&R.c[1][0].x)[j] : (&R.c[1][1].x)[j - 4];
+    const typename F::vec b0 = F::decode(w0, d[0][j / 2]);
+    const typename F::vec b1 = F::decode(w1, d[1][j / 2]);
+    const int g = (kMmChunk / 8) * c + 8 * q + j;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      if (tt < ntt) {
+        const int r = (16 * tt + m) & (Rrows - 1);
+        const unsigned char* ap = buf + r * row_bytes + ((g ^ (r & 15)) << 4);
+#pragma unroll
+        for (int p = 0; p < F::P; ++p) {
+          const typename F::vec a = *reinterpret_cast<const typename F::vec*>(ap + p * plane_bytes);
+          acc[0][tt] = F::mma(a, b0, acc[0][tt]);
+          acc[1][tt] = F::mma(a, b1, acc[1][tt]);
+        }
       }
-      const float g = wave_sum(dg0 * g0 + dg1 * g1) * Sg;
-      const float a = wave_sum(du0 * a0 + du1 * a1) * Su;
-      if (lane == 0) hs[(size_t)(b0 + b) * Is + r] = silu(g) * a;
     }
   }
 }
 
-// ---------------------------------------------------------------- down --
-// Output rows n of a K-wide down matrix (K = I routed, Is shared): a row is
-// covered by G = K/32 lanes (16 B of codes each), 64/G rows per wave.
-template <int G>
-__device__ __forceinline__ float group_reduce(float v) {
-  if constexpr (G == 16) return row16_sum(v);
-  else return group_sum<G>(v);
+// One pass: nt (<= 32) tokens whose source rows are in srow, over K = 256
+// NCH.  The caller has published srow with a barrier.  The activations are
+// staged segment by segment (a barrier pair each); a lane's weight bytes are
+// requested kAhead chunks before they are multiplied (the chunk loop is
+// unrolled, so every chunk has its own registers).
+constexpr int kAhead = 3;
+template <class F, int NCH>
+__device__ __forceinline__ void mm_pass_n(const MmTiles& T, rsrc_t rA, int a_rows, const int* srow, int nt,
+                                          unsigned char* abuf, int wv, int lane, f32x4_t (&acc)[2][2]) {
+  constexpr int K = NCH * kMmChunk;
+  const int q = lane >> 4, ntt = nt > 16 ? 2 : 1;
+  const int Rrows = nt <= 4 ? 4 : nt <= 8 ? 8 : nt <= 16 ? 16 : 32;
+  const int kseg = kMmStage / Rrows < K ? kMmStage / Rrows : K, cps = kseg / kMmChunk;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) acc[rt][tt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  MmRegs R[NCH];
+#pragma unroll
+  for (int u = 0; u < NCH && u < kAhead; ++u) mm_load_w(T, u, q, R[u]);
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    if (u % cps == 0) {  // next segment: everyone is done with the buffer, then copy
+      __syncthreads();
+      mm_stage(rA, F::P, a_rows, K, srow, Rrows, kseg, u * kMmChunk, abuf, wv, lane);
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies are in
+      __syncthreads();
+    }
+    if (u + kAhead < NCH) mm_load_w(T, u + kAhead, q, R[u + kAhead]);
+    mm_chunk<F>(R[u], abuf, Rrows, kseg, u % cps, ntt, lane, acc);
+  }
 }
 
-// Routed: grid (H / (4 * 4 * 64/G), Umax), 256 threads; each wave takes 4
-// passes of 64/G rows, all loads issued at once.
-// dr[pid][n] = w_pid * Sd_e * (Wd[e][n] . hr[pid]).
-template <int G>
-__global__ __launch_bounds__(kThreads) void k_bdown(flint_moe_layer L, int I, const int32_t* __restrict__ bk,
-                                                    const float* __restrict__ wts, const float* __restrict__ hr,
-                                                    float* __restrict__ dr) {
-  constexpr int RPW = 64 / G;  // rows per wave pass
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+// ---------------------------------------------------------------- norm --
+// grid B, 256 threads.  With dr: the layer's residual update first, h_b +=
+// (sum over slots in order of dr) + ds (fixed order).  Then u_b = h_b * s_b,
+// s_b = 1/sqrt(mean(h_b^2) + eps), as fp32 (router; skipped when u is null)
+// and as two fp16 planes up [2][B][H] (matrix cores; |u| <= sqrt(H), well
+// inside the fp16 range).
+__global__ __launch_bounds__(kThreads) void k_bnorm(float* __restrict__ h, const float* __restrict__ dr,
+                                                    const float* __restrict__ ds, int k, float* __restrict__ u,
+                                                    uint16_t* __restrict__ up, int B, float eps) {
+  const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  float* hb = h + (size_t)b * kHidden;
+  float v[kHidden / kThreads];
+  float ss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kHidden / kThreads; ++i) {
+    const int n = t + i * kThreads;
+    v[i] = hb[n];
+  }
+  if (dr) {
+    // every load issued before the sums (slots unrolled to the maximum k)
+    float y[kHidden / kThreads][kMaxTopK + 1];
+#pragma unroll
+    for (int i = 0; i < kHidden / kThreads; ++i) {
+      const int n = t + i * kThreads;
+#pragma unroll
+      for (int sl = 0; sl < kMaxTopK; ++sl) y[i][sl] = sl < k ? dr[((size_t)b * k + sl) * kHidden + n] : 0.0f;
+      y[i][kMaxTopK] = ds[(size_t)b * kHidden + n];
+    }
+#pragma unroll
+    for (int i = 0; i < kHidden / kThreads; ++i) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < kMaxTopK; ++sl)
+        if (sl < k) acc += y[i][sl];
+      v[i] += acc + y[i][kMaxTopK];
+      hb[t + i * kThreads] = v[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kHidden / kThreads; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
+  ss = wave_sum(ss);
+  __shared__ float red[kThreads / 64];
+  if (lane == 0) red[w] = ss;
+  __syncthreads();
+  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  const float s = 1.0f / sqrtf(tot * (1.0f / kHidden) + eps);
+#pragma unroll
+  for (int i = 0; i < kHidden / kThreads; ++i) {
+    const int c = t + i * kThreads;
+    const float x = v[i] * s;
+    if (u) u[(size_t)b * kHidden + c] = x;
+    uint16_t o[2];
+    FmtF16::split(x, o);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) up[((size_t)p * B + b) * kHidden + c] = o[p];
+  }
+}
+
+// ------------------------------------------------------------ gate / up --
+// grid (max(I, Is) / 128, Umax + 1), 512 threads.  Group ub < U: the rank-ub
+// chosen expert and its (token, slot) pairs; group Umax: the shared expert
+// and all B tokens.  Wave w takes gate rows and up rows r0 + 16 w .. + 15 of
+// its group (two tiles with the same rows) from the fp16 planes of the
+// normalised tokens up [2][B][H], and writes h = silu(gate) * up for each
+// token as three bf16 planes: hrp [3][B*k][I] by pair id (routed),
+// hsp [3][B][Is] by token (shared).
+__global__ __launch_bounds__(kMmThreads, 3) void k_mm_gateup(flint_moe_layer L, int I, int Is, int k, int B,
+                                                             int Umax, const uint16_t* __restrict__ up,
+                                                             const int32_t* __restrict__ bk, uint16_t* __restrict__ hrp,
+                                                             uint16_t* __restrict__ hsp, int nb) {
+  __shared__ __align__(16) unsigned char abuf[mm_buf_bytes<FmtF16>()];
+  __shared__ int srow[kMmTok], orow[kMmTok];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6, m = lane & 15, q = lane >> 4;
   const int ub = blockIdx.y;
-  if (ub >= bk[0]) return;
-  const int j = lane % G, n0 = (blockIdx.x * 4 + wv) * RPW * kRowsPerWave + lane / G;
-  const int e = bk[kBkExperts + ub], p0 = bk[kBkStart + ub], p1 = bk[kBkStart + ub + 1];
-  uint4 c[kRowsPerWave];
-  uint32_t sc[kRowsPerWave];
-#pragma unroll
-  for (int q = 0; q < kRowsPerWave; ++q) {
-    const size_t row = (size_t)e * kHidden + n0 + q * RPW;
-    c[q] = ld_nt_u4(L.down_codes + row * (I / 2) + 16 * j);
-    sc[q] = ld_nt_u16(L.down_scales + row * (I / 16) + 2 * j);
+  const bool sh = ub == Umax;
+  if (!sh && ub >= bk[0]) return;
+  const int rows = sh ? Is : I, r0 = blockIdx.x * kMmGateUpRows;
+  if (r0 >= rows) return;
+  int e = 0, p0 = 0, ntok = B;
+  if (!sh) {
+    e = bk[kBkExperts + ub];
+    p0 = bk[kBkStart + ub];
+    ntok = bk[kBkStart + ub + 1] - p0;
   }
-  const float S = L.expert_tscales[3 * e + 2];
-  for (int p = p0; p < p1; ++p) {
-    const int pid = bk[kBkPairs + p];
-    float hv[32];
-    lane_x32(hr + (size_t)pid * I, j, hv);
-    const float coef = S * wts[pid];
-#pragma unroll 2
-    for (int q = 0; q < kRowsPerWave; ++q) {
-      const float acc = group_reduce<G>(nvfp4_lane_dot32(c[q], sc[q], hv)) * coef;
-      if (j == 0) dr[(size_t)pid * kHidden + n0 + q * RPW] = acc;
-    }
+  const int row = r0 + 16 * wv + m;
+  MmTiles T;
+  float Sg, Su;
+  if (sh) {
+    T.c[0] = L.shared_gate.codes + (size_t)row * (kHidden / 2);
+    T.s[0] = L.shared_gate.scales + (size_t)row * (kHidden / 16);
+    T.c[1] = L.shared_up.codes + (size_t)row * (kHidden / 2);
+    T.s[1] = L.shared_up.scales + (size_t)row * (kHidden / 16);
+    Sg = *L.shared_gate.tscale;
+    Su = *L.shared_up.tscale;
+  } else {
+    const size_t er = (size_t)e * I + row;
+    T.c[0] = L.gate_codes + er * (kHidden / 2);
+    T.s[0] = L.gate_scales + er * (kHidden / 16);
+    T.c[1] = L.up_codes + er * (kHidden / 2);
+    T.s[1] = L.up_scales + er * (kHidden / 16);
+    Sg = L.expert_tscales[3 * e + 0];
+    Su = L.expert_tscales[3 * e + 1];
   }
-}
-
-// Shared: grid H / (4 * 64/G), 256 threads; rows decoded once, applied to
-// every token (hidden vectors staged in LDS).  ds[b][n].
-template <int G>
-__global__ __launch_bounds__(kThreads) void k_bdown_shared(flint_moe_layer L, int B, const float* __restrict__ hs,
-                                                           float* __restrict__ ds) {
-  constexpr int RPW = 64 / G, K = 32 * G;
-  __shared__ __align__(16) float sh[kStageFloats];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int j = lane % G, n = (blockIdx.x * 4 + wv) * RPW + lane / G;
-  const uint4 c = ld_nt_u4(L.shared_down.codes + (size_t)n * (K / 2) + 16 * j);
-  const uint32_t s = ld_nt_u16(L.shared_down.scales + (size_t)n * (K / 16) + 2 * j);
-  const float S = *L.shared_down.tscale;
-  float w[32];
-  fp4x8_values(c.x, w); fp4x8_values(c.y, w + 8); fp4x8_values(c.z, w + 16); fp4x8_values(c.w, w + 24);
-  const float d0 = e4m3_to_f32(s & 0xFF), d1 = e4m3_to_f32(s >> 8);
-  constexpr int P = stage_tokens_per_pass<K>();
-  for (int b0 = 0; b0 < B; b0 += P) {
-    const int nb = B - b0 < P ? B - b0 : P;
-    __syncthreads();
-    stage_tokens<K>(hs, b0, nb, sh);
-    __syncthreads();
-    for (int b = 0; b < nb; ++b) {
-      float hv[32];
-      staged_x32<K>(sh, b, j, hv);
-      float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        a0 = __builtin_fmaf(w[i], hv[i], a0);
-        a1 = __builtin_fmaf(w[16 + i], hv[16 + i], a1);
+  const rsrc_t rA = make_rsrc(up, (uint64_t)FmtF16::P * B * kHidden * 2);
+  uint16_t* outp = sh ? hsp : hrp;
+  const int ow = sh ? Is : I, orows = sh ? B : nb;
+  for (int t0 = 0; t0 < ntok; t0 += kMmTok) {
+    const int nt = ntok - t0 < kMmTok ? ntok - t0 : kMmTok;
+    __syncthreads();  // the previous pass is done with srow, orow and the buffers
+    if (t < kMmTok) {
+      int sr = -1, orr = -1;
+      if (t < nt) {
+        if (sh) {
+          sr = orr = t0 + t;
+        } else {
+          orr = bk[kBkPairs + p0 + t0 + t];
+          sr = orr / k;
+        }
       }
-      const float acc = group_reduce<G>(d0 * a0 + d1 * a1) * S;
-      if (j == 0) ds[(size_t)(b0 + b) * kHidden + n] = acc;
+      srow[t] = sr;
+      orow[t] = orr;
     }
+    __syncthreads();
+    f32x4_t acc[2][2];
+    mm_pass_n<FmtF16, kHidden / kMmChunk>(T, rA, B, srow, nt, abuf, wv, lane, acc);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * tt + 4 * q + i;
+        if (tok < nt) {
+          uint16_t o[3];
+          FmtBF16::split(silu(acc[0][tt][i] * Sg) * (acc[1][tt][i] * Su), o);
+          const int orr = orow[tok];
+#pragma unroll
+          for (int p = 0; p < 3; ++p) outp[((size_t)p * orows + orr) * ow + row] = o[p];
+        }
+      }
   }
 }
 
-// ------------------------------------------------------------- combine --
-// grid (H/256, B): h_b[n] += (sum over slots in order of dr) + ds
-__global__ __launch_bounds__(kThreads) void k_bcombine(float* __restrict__ h, const float* __restrict__ dr,
-                                                       const float* __restrict__ ds, int k) {
-  const int b = blockIdx.y, n = blockIdx.x * kThreads + threadIdx.x;
-  float y = 0.0f;
-  for (int sl = 0; sl < k; ++sl) y += dr[((size_t)b * k + sl) * kHidden + n];
-  y += ds[(size_t)b * kHidden + n];
-  h[(size_t)b * kHidden + n] += y;
+// ----------------------------------------------------------------- down --
+// grid (H / 256, Umax + 1), 512 threads; groups as for gate/up.  Wave w takes
+// output rows r0 + 32 w .. + 31.  Routed: dr[pid][n] = w_pid * S_e * (Wd[e][n]
+// . h_pid) over K = I; shared: ds[b][n] = S * (Wsd[n] . hs_b) over K = Is.
+__global__ __launch_bounds__(kMmThreads, 3) void k_mm_down(flint_moe_layer L, int I, int Is, int B, int Umax,
+                                                           const uint16_t* __restrict__ hrp,
+                                                           const uint16_t* __restrict__ hsp,
+                                                           const int32_t* __restrict__ bk,
+                                                           const float* __restrict__ wts, float* __restrict__ dr,
+                                                           float* __restrict__ ds, int nb) {
+  __shared__ __align__(16) unsigned char abuf[mm_buf_bytes<FmtBF16>()];
+  __shared__ int srow[kMmTok];
+  __shared__ float coef[kMmTok];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6, m = lane & 15, q = lane >> 4;
+  const int ub = blockIdx.y;
+  const bool sh = ub == Umax;
+  if (!sh && ub >= bk[0]) return;
+  int e = 0, p0 = 0, ntok = B;
+  if (!sh) {
+    e = bk[kBkExperts + ub];
+    p0 = bk[kBkStart + ub];
+    ntok = bk[kBkStart + ub + 1] - p0;
+  }
+  const int K = sh ? Is : I;
+  const int rbase = blockIdx.x * kMmRows + 32 * wv;
+  MmTiles T;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int row = rbase + 16 * rt + m;
+    if (sh) {
+      T.c[rt] = L.shared_down.codes + (size_t)row * (Is / 2);
+      T.s[rt] = L.shared_down.scales + (size_t)row * (Is / 16);
+    } else {
+      const size_t er = (size_t)e * kHidden + row;
+      T.c[rt] = L.down_codes + er * (I / 2);
+      T.s[rt] = L.down_scales + er * (I / 16);
+    }
+  }
+  const float S = sh ? *L.shared_down.tscale : L.expert_tscales[3 * e + 2];
+  const rsrc_t rA = sh ? make_rsrc(hsp, (uint64_t)3 * B * Is * 2) : make_rsrc(hrp, (uint64_t)3 * nb * I * 2);
+  const int a_rows = sh ? B : nb;
+  float* out = sh ? ds : dr;
+  for (int t0 = 0; t0 < ntok; t0 += kMmTok) {
+    const int nt = ntok - t0 < kMmTok ? ntok - t0 : kMmTok;
+    __syncthreads();
+    if (t < kMmTok) {
+      int sr = -1;
+      float c = 0.0f;
+      if (t < nt) {
+        sr = sh ? t0 + t : bk[kBkPairs + p0 + t0 + t];
+        c = sh ? S : S * wts[sr];
+      }
+      srow[t] = sr;
+      coef[t] = c;
+    }
+    __syncthreads();
+    f32x4_t acc[2][2];
+    if (K == 1024) mm_pass_n<FmtBF16, 4>(T, rA, a_rows, srow, nt, abuf, wv, lane, acc);
+    else if (K == 2048) mm_pass_n<FmtBF16, 8>(T, rA, a_rows, srow, nt, abuf, wv, lane, acc);
+    else mm_pass_n<FmtBF16, 2>(T, rA, a_rows, srow, nt, abuf, wv, lane, acc);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * tt + 4 * q + i;
+        if (tok < nt) {
+          const int orr = srow[tok];
+#pragma unroll
+          for (int rt = 0; rt < 2; ++rt) out[(size_t)orr * kHidden + rbase + 16 * rt + m] = acc[rt][tt][i] * coef[tok];
+        }
+      }
+  }
 }
 
 // ----------------------------------------------------------------- head --
-// grid kBHeadBlocks, 256 threads.  The B normalised hidden vectors sit in
-// LDS; each wave decodes a row once and dots it with every token; per token
-// a running (max, first index) in LDS; each block writes its per-token
-// partials, k_bargmax reduces them.
-constexpr int kBHeadBlocks = 1024;
-constexpr int kBHeadMaxTok = 16;  // tokens per pass (LDS: 16 x 9 KB, padded rows)
-
-__global__ __launch_bounds__(kThreads) void k_bhead(const uint8_t* __restrict__ codes,
-                                                    const uint8_t* __restrict__ scales,
-                                                    const float* __restrict__ tscale, int vocab,
-                                                    const float* __restrict__ z, int b0, int nb,
-                                                    float* __restrict__ logits, HeadPartial* __restrict__ partials) {
-  __shared__ __align__(16) float zs[kBHeadMaxTok * (kHidden / 32) * kPad];
-  __shared__ float bv[4][kBHeadMaxTok];
-  __shared__ int bi[4][kBHeadMaxTok];
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  stage_tokens<kHidden>(z, b0, nb, zs);
-  if (lane < kBHeadMaxTok) { bv[wv][lane] = -FLT_MAX; bi[wv][lane] = INT_MAX; }
-  __syncthreads();
-  const float S = *tscale;
-  const int nwaves = gridDim.x * 4;
-  for (int r = blockIdx.x * 4 + wv; r < vocab; r += nwaves) {
-    const uint4 c = ld_nt_u4(codes + (size_t)r * (kHidden / 2) + 16 * lane);
-    const uint32_t s = ld_nt_u16(scales + (size_t)r * (kHidden / 16) + 2 * lane);
-    float w[32];
-    fp4x8_values(c.x, w); fp4x8_values(c.y, w + 8); fp4x8_values(c.z, w + 16); fp4x8_values(c.w, w + 24);
-    const float d0 = e4m3_to_f32(s & 0xFF), d1 = e4m3_to_f32(s >> 8);
-    for (int b = 0; b < nb; ++b) {
-      float xv[32];
-      staged_x32<kHidden>(zs, b, lane, xv);
-      float a0 = 0.0f, a1 = 0.0f;
+// grid ceil(V / 256), 512 threads: rows r0 + 32 w .. + 31 of the head for
+// all B tokens (final-norm fp16 planes zp [2][B][H]); logits (optional) and, per
+// token, this workgroup's (max, first index) -> partials[b][blockIdx.x].
+// (codes and scales are not marked restrict: the rows are read again in
+// every token pass, and hoisting those loads out of the pass loop would pin
+// all of them in registers)
+__global__ __launch_bounds__(kMmThreads, 3) void k_mm_head(const uint8_t* codes, const uint8_t* scales,
+                                                           const float* __restrict__ tscale, int vocab,
+                                                           const uint16_t* __restrict__ zp, int B,
+                                                           float* __restrict__ logits,
+                                                           HeadPartial* __restrict__ partials) {
+  __shared__ __align__(16) unsigned char abuf[mm_buf_bytes<FmtF16>()];
+  __shared__ int srow[kMmTok];
+  __shared__ float bv[kMmWaves][kMmTok];
+  __shared__ int bi[kMmWaves][kMmTok];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6, m = lane & 15, q = lane >> 4;
+  const int rbase = blockIdx.x * kMmRows + 32 * wv;
+  MmTiles T;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        a0 = __builtin_fmaf(w[i], xv[i], a0);
-        a1 = __builtin_fmaf(w[16 + i], xv[16 + i], a1);
-      }
-      const float v = wave_sum(d0 * a0 + d1 * a1) * S;
-      if (lane == 0) {
-        if (logits) logits[(size_t)(b0 + b) * vocab + r] = v;
-        if (v > bv[wv][b]) { bv[wv][b] = v; bi[wv][b] = r; }  // rows rise, so ties keep the first
-      }
-    }
+  for (int rt = 0; rt < 2; ++rt) {
+    const int row = min(rbase + 16 * rt + m, vocab - 1);  // rows past the end read the last row; dropped
+    T.c[rt] = codes + (size_t)row * (kHidden / 2);
+    T.s[rt] = scales + (size_t)row * (kHidden / 16);
   }
-  __syncthreads();
-  if (t < nb) {
-    float v = bv[0][t];
-    int id = bi[0][t];
-    for (int w = 1; w < 4; ++w)
-      if (bv[w][t] > v || (bv[w][t] == v && bi[w][t] < id)) { v = bv[w][t]; id = bi[w][t]; }
-    partials[(size_t)(b0 + t) * gridDim.x + blockIdx.x] = HeadPartial{v, id};
+  const float S = *tscale;
+  const rsrc_t rA = make_rsrc(zp, (uint64_t)FmtF16::P * B * kHidden * 2);
+  for (int t0 = 0; t0 < B; t0 += kMmTok) {
+    const int nt = B - t0 < kMmTok ? B - t0 : kMmTok;
+    __syncthreads();
+    if (t < kMmTok) srow[t] = t < nt ? t0 + t : -1;
+    __syncthreads();
+    f32x4_t acc[2][2];
+    mm_pass_n<FmtF16, kHidden / kMmChunk>(T, rA, B, srow, nt, abuf, wv, lane, acc);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = 16 * tt + 4 * q + i;
+        // this lane's two rows, then the best over the 16 lanes of its DPP row
+        float v = -FLT_MAX;
+        int n = INT_MAX;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          const int row = rbase + 16 * rt + m;
+          const float x = acc[rt][tt][i] * S;
+          if (row < vocab && tok < nt) {
+            if (logits) logits[(size_t)(t0 + tok) * vocab + row] = x;
+            if (x > v) { v = x; n = row; }  // rt = 0 rows come first
+          }
+        }
+        auto step = [&](float ov, int on) {
+          if (ov > v || (ov == v && on < n)) { v = ov; n = on; }
+        };
+        step(dpp_f32<kDppXor1>(v), dpp_i32<kDppXor1>(n));
+        step(dpp_f32<kDppXor2>(v), dpp_i32<kDppXor2>(n));
+        step(dpp_f32<kDppHalfMirror>(v), dpp_i32<kDppHalfMirror>(n));
+        step(dpp_f32<kDppMirror>(v), dpp_i32<kDppMirror>(n));
+        if (m == 0) {
+          bv[wv][tok] = v;
+          bi[wv][tok] = n;
+        }
+      }
+    __syncthreads();
+    if (t < nt) {
+      float v = bv[0][t];
+      int n = bi[0][t];
+      for (int w = 1; w < kMmWaves; ++w)
+        if (bv[w][t] > v || (bv[w][t] == v && bi[w][t] < n)) { v = bv[w][t]; n = bi[w][t]; }
+      partials[(size_t)(t0 + t) * gridDim.x + blockIdx.x] = HeadPartial{v, n};
+    }
   }
 }
 
@@ -466,41 +742,32 @@ __global__ __launch_bounds__(64) void k_bargmax(const HeadPartial* __restrict__ 
   if (lane == 0) argmax[b] = id;
 }
 
-template <int G>
-hipError_t launch_bdown_routed(const flint_moe_layer& L, int I, int Umax, const int32_t* bk, const float* wts,
-                               const float* hr, float* dr, hipStream_t s) {
-  k_bdown<G><<<dim3(kHidden / (4 * (64 / G) * kRowsPerWave), Umax), kThreads, 0, s>>>(L, I, bk, wts, hr, dr);
-  return hipGetLastError();
-}
-template <int G>
-hipError_t launch_bdown_shared(const flint_moe_layer& L, int B, const float* hs, float* ds, hipStream_t s) {
-  k_bdown_shared<G><<<kHidden / (4 * (64 / G)), kThreads, 0, s>>>(L, B, hs, ds);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 bool batch_supported(const flint_moe_dims& d, int B) {
-  auto pow2_lanes = [](int K) { const int G = K / 32; return K % 32 == 0 && G >= 8 && G <= 64 && (G & (G - 1)) == 0; };
-  return d.hidden == kHidden && B >= 1 && B <= kMaxBatch && pow2_lanes(d.expert_width) && pow2_lanes(d.shared_width) &&
+  // the matrix-core kernels walk K in pairs of 256-wide chunks
+  auto width_ok = [](int K) { return K >= 512 && K <= 2048 && K % 512 == 0; };
+  return d.hidden == kHidden && B >= 1 && B <= kMaxBatch && width_ok(d.expert_width) && width_ok(d.shared_width) &&
          d.n_experts <= kMaxExperts && d.top_k <= kMaxTopK;
 }
 
+static int head_blocks(int vocab) { return (vocab + kMmRows - 1) / kMmRows; }
+
 BatchWs::BatchWs(const flint_moe_dims& d, int B, int vocab) {
-  (void)vocab;
   const int nb = B * d.top_k;
   size_t o = 0;
   h = o; o = align_up(o + 4 * (size_t)B * kHidden, 256);
   u = o; o = align_up(o + 4 * (size_t)B * kHidden, 256);
+  up = o; o = align_up(o + 2 * 2 * (size_t)B * kHidden, 256);
   logits = o; o = align_up(o + 4 * (size_t)B * d.n_experts, 256);
   idx = o; o = align_up(o + 4 * (size_t)nb, 256);
   wts = o; o = align_up(o + 4 * (size_t)nb, 256);
   bucket = o; o = align_up(o + 4 * (size_t)(kBkPairs + nb), 256);
-  hr = o; o = align_up(o + 4 * (size_t)nb * d.expert_width, 256);
-  hs = o; o = align_up(o + 4 * (size_t)B * d.shared_width, 256);
+  hr = o; o = align_up(o + 2 * 3 * (size_t)nb * d.expert_width, 256);
+  hs = o; o = align_up(o + 2 * 3 * (size_t)B * d.shared_width, 256);
   dr = o; o = align_up(o + 4 * (size_t)nb * kHidden, 256);
   ds = o; o = align_up(o + 4 * (size_t)B * kHidden, 256);
-  partials = o; o = align_up(o + sizeof(HeadPartial) * (size_t)B * kBHeadBlocks, 256);
+  partials = o; o = align_up(o + sizeof(HeadPartial) * (size_t)B * head_blocks(vocab), 256);
   total = o;
 }
 
@@ -511,53 +778,40 @@ hipError_t launch_batch_step(const flint_moe_dims& d, const flint_moe_layer* lay
   char* base = static_cast<char*>(ws);
   float* h = reinterpret_cast<float*>(base + w.h);
   float* u = reinterpret_cast<float*>(base + w.u);
+  uint16_t* up = reinterpret_cast<uint16_t*>(base + w.up);
   float* lg = reinterpret_cast<float*>(base + w.logits);
   int32_t* idx = reinterpret_cast<int32_t*>(base + w.idx);
   float* wts = reinterpret_cast<float*>(base + w.wts);
   int32_t* bk = reinterpret_cast<int32_t*>(base + w.bucket);
-  float* hr = reinterpret_cast<float*>(base + w.hr);
-  float* hs = reinterpret_cast<float*>(base + w.hs);
+  uint16_t* hrp = reinterpret_cast<uint16_t*>(base + w.hr);
+  uint16_t* hsp = reinterpret_cast<uint16_t*>(base + w.hs);
   float* dr = reinterpret_cast<float*>(base + w.dr);
   float* ds = reinterpret_cast<float*>(base + w.ds);
   HeadPartial* parts = reinterpret_cast<HeadPartial*>(base + w.partials);
   const int k = d.top_k, E = d.n_experts, I = d.expert_width, Is = d.shared_width, nb = B * k;
   const int Umax = nb < E ? nb : E;
+  const int gu_x = ((I > Is ? I : Is) + kMmGateUpRows - 1) / kMmGateUpRows;
   hipError_t e = hipMemcpyAsync(h, x, 4 * (size_t)B * kHidden, hipMemcpyDeviceToDevice, s);
+  if (e != hipSuccess) return e;
+  k_bnorm<<<B, kThreads, 0, s>>>(h, nullptr, nullptr, k, u, up, B, eps);
   for (int l = 0; l < L && e == hipSuccess; ++l) {
     const flint_moe_layer& Ly = layers[l];
-    k_bnorm<<<B, kThreads, 0, s>>>(h, u, eps);
-    k_broute<<<(E + 3) / 4, kThreads, 0, s>>>(Ly.router, E, u, B, lg);
+    k_broute<<<dim3((E + 3) / 4, (B + kRouteTok - 1) / kRouteTok), kThreads, 0, s>>>(Ly.router, E, u, B, lg);
     k_btopk<<<B, 64, 0, s>>>(lg, E, k, idx, wts);
     if (routes) e = hipMemcpyAsync(routes + (size_t)l * nb, idx, 4 * (size_t)nb, hipMemcpyDeviceToDevice, s);
     k_bucket<<<1, kThreads, 0, s>>>(idx, nb, E, bk);
-    k_bgateup<<<dim3((I + 4 * kRowsPerWave - 1) / (4 * kRowsPerWave), Umax), kThreads, 0, s>>>(Ly, I, k, u, bk, hr);
-    k_bgateup_shared<<<Is / 4, kThreads, 0, s>>>(Ly, Is, B, u, hs);
-    switch (I / 32) {
-      case 8: e = launch_bdown_routed<8>(Ly, I, Umax, bk, wts, hr, dr, s); break;
-      case 16: e = launch_bdown_routed<16>(Ly, I, Umax, bk, wts, hr, dr, s); break;
-      case 32: e = launch_bdown_routed<32>(Ly, I, Umax, bk, wts, hr, dr, s); break;
-      case 64: e = launch_bdown_routed<64>(Ly, I, Umax, bk, wts, hr, dr, s); break;
-      default: e = hipErrorInvalidValue;
-    }
-    if (e != hipSuccess) break;
-    switch (Is / 32) {
-      case 8: e = launch_bdown_shared<8>(Ly, B, hs, ds, s); break;
-      case 16: e = launch_bdown_shared<16>(Ly, B, hs, ds, s); break;
-      case 32: e = launch_bdown_shared<32>(Ly, B, hs, ds, s); break;
-      case 64: e = launch_bdown_shared<64>(Ly, B, hs, ds, s); break;
-      default: e = hipErrorInvalidValue;
-    }
-    if (e != hipSuccess) break;
-    k_bcombine<<<dim3(kHidden / kThreads, B), kThreads, 0, s>>>(h, dr, ds, k);
+    k_mm_gateup<<<dim3(gu_x, Umax + 1), kMmThreads, 0, s>>>(Ly, I, Is, k, B, Umax, up, bk, hrp, hsp, nb);
+    k_mm_down<<<dim3(kHidden / kMmRows, Umax + 1), kMmThreads, 0, s>>>(Ly, I, Is, B, Umax, hrp, hsp, bk, wts, dr, ds,
+                                                                        nb);
+    // the residual update and the next norm (after the last layer: the
+    // final norm, the head's input)
+    k_bnorm<<<B, kThreads, 0, s>>>(h, dr, ds, k, l + 1 < L ? u : nullptr, up, B, eps);
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  k_bnorm<<<B, kThreads, 0, s>>>(h, u, eps);
-  for (int b0 = 0; b0 < B; b0 += kBHeadMaxTok) {
-    const int n = B - b0 < kBHeadMaxTok ? B - b0 : kBHeadMaxTok;
-    k_bhead<<<kBHeadBlocks, kThreads, 0, s>>>(head.codes, head.scales, head.tscale, vocab, u, b0, n, logits, parts);
-  }
-  k_bargmax<<<B, 64, 0, s>>>(parts, kBHeadBlocks, argmax);
+  const int hb = head_blocks(vocab);
+  k_mm_head<<<hb, kMmThreads, 0, s>>>(head.codes, head.scales, head.tscale, vocab, up, B, logits, parts);
+  k_bargmax<<<B, 64, 0, s>>>(parts, hb, argmax);
   return hipGetLastError();
 }
 

@@ -67,6 +67,9 @@ __device__ __forceinline__ uint4 ld_nt_u4(const void* p) {
 __device__ __forceinline__ uint32_t ld_nt_u16(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(p));
 }
+__device__ __forceinline__ uint32_t ld_nt_u32(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
 __device__ __forceinline__ float4 ld_nt_f4(const void* p) {
   const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
   return make_float4(v.x, v.y, v.z, v.w);

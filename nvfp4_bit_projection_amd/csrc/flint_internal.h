@@ -106,7 +106,7 @@ inline size_t stack_table_bytes(int L) { return sizeof(StackTable) + sizeof(flin
 // batched decode (batch.hip)
 constexpr int kMaxBatch = 64;
 struct BatchWs {
-  size_t h, u, logits, idx, wts, bucket, hr, hs, dr, ds, partials, total;
+  size_t h, u, up, logits, idx, wts, bucket, hr, hs, dr, ds, partials, total;
   BatchWs(const flint_moe_dims& d, int B, int vocab);
 };
 bool batch_supported(const flint_moe_dims& d, int B);
