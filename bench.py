@@ -6,6 +6,7 @@ synthetic weights resident in HBM: one call of flint_stack_decode, i.e. one
 launch of the persistent stack kernel.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+  python bench.py --batch 32        # small-batch decode: B tokens per step
   python bench.py --copy-calib      # one 1 GiB device copy (counter calibration)
 """
 from __future__ import annotations
@@ -106,6 +107,69 @@ def copy_calib() -> int:
     return 0
 
 
+def bench_batch(args) -> int:
+    """One step = B fresh tokens through the 47 layers (per-token top-6, each
+    chosen expert's weights read once per step) and the head: one call of
+    flint_stack_decode_batch.  Bytes per step count the distinct experts of
+    every layer, taken from the routes of the same inputs."""
+    import torch
+
+    import synth
+    from nvfp4_bit_projection_amd import bytes_model as bm
+    from nvfp4_bit_projection_amd import flint, workload
+
+    torch.cuda.set_device(0)
+    dims = synth.MoEDims()
+    L, V, B = args.layers, 150144, args.batch
+    tmp = torch.empty(dims.n_experts * dims.expert_width * dims.hidden, dtype=torch.float32, device="cuda")
+    layers = [workload.build_layer(dims, seed=l, tmp=tmp) for l in range(L)]
+    head = workload.build_head(V, dims.hidden, tmp=None)
+    del tmp
+    d = flint.dims_struct(dims.hidden, dims.n_experts, dims.expert_width, dims.top_k, dims.shared_width)
+    stack = flint.Stack(d, layers, head, V, schedule=flint.SCHEDULE_KERNELS)
+    T = args.warmup + args.steps
+    x = workload.tokens([synth.TOKEN_SEED0 + t for t in range(T * B)], dims.hidden).view(T, B, dims.hidden)
+    ws = flint.workspace(flint.OP_STACK_BATCH, stack.dims, B, V, L)
+    argmax = torch.empty((T, B), dtype=torch.int32, device="cuda")
+    for t in range(args.warmup):
+        stack.decode_batch(x[t], argmax=argmax[t], want_logits=False, ws=ws)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for t in range(args.warmup, T):
+        stack.decode_batch(x[t], argmax=argmax[t], want_logits=False, ws=ws)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    # distinct experts per layer of every timed step (same inputs again, routes kept)
+    shape = bm.LayerShape()
+    routes = torch.empty((L, B, dims.top_k), dtype=torch.int32, device="cuda")
+    total = 0
+    for t in range(args.warmup, T):
+        stack.decode_batch(x[t], routes=routes, want_logits=False, ws=ws)
+        u = [len(set(routes[l].flatten().tolist())) for l in range(L)]
+        total += sum(bm.layer_bytes(shape, n) for n in u) + bm.head_bytes(V, dims.hidden)
+    step_bytes = total / args.steps
+    gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    tok_s = B * 1000.0 / ms_per_step
+    log(f"batch {B}: {args.steps} steps, {ms_per_step * 1e3:.1f} us/step, {tok_s:.1f} tok/s, "
+        f"{step_bytes / 1e9:.3f} GB/step, {gbs:.1f} GB/s")
+    result = {
+        "metric": f"decode tok/s (47-layer NVFP4 MoE+lm_head, batch {B}) and achieved HBM GB/s vs peak",
+        "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"stack47_lmhead_b{B}", "layers": L, "hidden": 2048, "experts": 256, "top_k": 6,
+                   "expert_width": 512, "shared_width": 1024, "vocab": V, "batch": B,
+                   "weights": "nvfp4 e2m1 + e4m3/16 + fp32 tensor scale; fp32 router"},
+        "roofline": {"bound": "hbm", "scope": "whole step (all kernels)", "achieved": round(gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_step": round(step_bytes)},
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +178,8 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=47)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
+    ap.add_argument("--batch", type=int, default=1,
+                    help="tokens per step; above 1 the batched step (experts deduplicated per layer) is timed")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (batch-1 decode; see DESIGN.md for how it would shard)",
@@ -121,6 +187,8 @@ def main() -> int:
         return 2
     if args.copy_calib:
         return copy_calib()
+    if args.batch > 1:
+        return bench_batch(args)
 
     import torch
 
