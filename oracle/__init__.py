@@ -56,6 +56,10 @@ def lib():
         L.oracle_f32_gemv.restype = None
         L.oracle_topk_softmax.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P, _P, _P]
         L.oracle_topk_softmax.restype = None
+        L.oracle_topk_sigmoid.argtypes = [_P, ctypes.c_int, ctypes.c_int, _P, _P, _P]
+        L.oracle_topk_sigmoid.restype = None
+        L.oracle_bf16_decode.argtypes = [_P, _I64, _P]
+        L.oracle_bf16_decode.restype = None
         L.oracle_rms_inv.argtypes = [_P, _I64, ctypes.c_double]
         L.oracle_rms_inv.restype = ctypes.c_double
         L.oracle_swiglu_expert.argtypes = [_P, _P, ctypes.c_float, _P, _P, ctypes.c_float, _P, _P, ctypes.c_float,
@@ -153,6 +157,24 @@ def topk_softmax(logits: np.ndarray, k: int):
     gap = np.zeros(1, np.float64)
     lib().oracle_topk_softmax(logits.ctypes.data, logits.size, k, idx.ctypes.data, w.ctypes.data, gap.ctypes.data)
     return idx, w, float(gap[0])
+
+
+def topk_sigmoid(logits: np.ndarray, k: int):
+    """-> (idx int32[k] ordered by (score desc, index asc), w float64[k], gap)"""
+    logits = _c(logits, np.float64)
+    idx = np.empty(k, np.int32)
+    w = np.empty(k, np.float64)
+    gap = np.zeros(1, np.float64)
+    lib().oracle_topk_sigmoid(logits.ctypes.data, logits.size, k, idx.ctypes.data, w.ctypes.data, gap.ctypes.data)
+    return idx, w, float(gap[0])
+
+
+def bf16_decode(bits: np.ndarray) -> np.ndarray:
+    """uint16 BF16 bit patterns -> float64 values (same shape)"""
+    bits = _c(bits, np.uint16)
+    out = np.empty(bits.shape, np.float64)
+    lib().oracle_bf16_decode(bits.ctypes.data, bits.size, out.ctypes.data)
+    return out
 
 
 def rms_inv(h: np.ndarray, eps: float) -> float:

@@ -262,6 +262,52 @@ void oracle_topk_softmax(const double* logits, int E, int k, int32_t* idx, doubl
   free(order);
 }
 
+/* Sigmoid routing [P3 "Flint: 125 tokens a second is what 2.5B active
+ * parameters buy at 273 GB/s", "The shape, read from the headers": the router
+ * scores experts with a sigmoid, as DeepSeek-V3 does, and has no
+ * bias-correction tensor].  Reading: score s_e = 1 / (1 + e^-l_e); the k
+ * largest scores are chosen, ties to the lower index; the weights are the
+ * chosen scores divided by their sum, with no further scaling factor.
+ * gap = k-th minus (k+1)-th largest logit, in the chosen order (INFINITY when
+ * E == k).  Not thread-safe (uses a static sort key). */
+void oracle_topk_sigmoid(const double* logits, int E, int k, int32_t* idx, double* w, double* gap) {
+  double* score = (double*)malloc(sizeof(double) * (size_t)E);
+  int* order = (int*)malloc(sizeof(int) * (size_t)E);
+  for (int e = 0; e < E; ++e) {
+    score[e] = 1.0 / (1.0 + exp(-logits[e]));
+    order[e] = e;
+  }
+  g_sort_keys = score;
+  qsort(order, (size_t)E, sizeof(int), by_logit_desc_then_index);
+  double sel = 0.0;
+  for (int i = 0; i < k; ++i) sel += score[order[i]];
+  for (int i = 0; i < k; ++i) {
+    idx[i] = order[i];
+    w[i] = score[order[i]] / sel;
+  }
+  *gap = (E > k) ? logits[order[k - 1]] - logits[order[k]] : INFINITY;
+  free(order);
+  free(score);
+}
+
+/* BF16 values [same page and section: the router is stored in BF16].  The
+ * format: bit 15 the sign, bits 14..7 a biased exponent (bias 127), bits 6..0
+ * the fraction; exponent 0 is subnormal (fraction / 128 * 2^-126).  Exponent
+ * 255 (infinities, NaN) is outside the inputs and decodes to NaN. */
+void oracle_bf16_decode(const uint16_t* b, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) {
+    int sign = b[i] >> 15, ex = (b[i] >> 7) & 0xFF, fr = b[i] & 0x7F;
+    double v;
+    if (ex == 0)
+      v = ldexp(fr / 128.0, -126);
+    else if (ex == 255)
+      v = NAN;
+    else
+      v = ldexp(1.0 + fr / 128.0, ex - 127);
+    out[i] = sign ? -v : v;
+  }
+}
+
 /* RMSNorm scale with unit gain (reading: eps inside the root):
  * 1 / sqrt(mean(h^2) + eps). */
 double oracle_rms_inv(const double* h, int64_t n, double eps) {

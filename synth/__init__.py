@@ -162,6 +162,13 @@ def router_f32(seed: int, dims: MoEDims) -> np.ndarray:
         dims.n_experts, dims.hidden)
 
 
+def router_bf16_bits(seed: int, dims: MoEDims) -> np.ndarray:
+    """The fp32 router draws stored as BF16 (uint16 bit patterns, round to
+    nearest even on the top 16 bits), as a checkpoint keeps a BF16 router."""
+    u = router_f32(seed, dims).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
 def expert_f32(seed: int, dims: MoEDims, kind: int, expert: int) -> np.ndarray:
     """One routed expert matrix: gate/up [I][H], down [H][I]."""
     H, I = dims.hidden, dims.expert_width

@@ -1,6 +1,7 @@
 """The shared input generator: known-answer vectors, distribution, reproducibility."""
 import numpy as np
 import pytest
+import torch
 from scipy import stats
 
 import synth
@@ -63,3 +64,11 @@ def test_workload_shapes():
     assert np.array_equal(full[17:22], part)
     # router rows of the E=32 workload are the first rows of the E=256 one
     assert np.array_equal(synth.router_f32(0, synth.MoEDims()).reshape(256, 2048)[:32], synth.router_f32(0, d))
+
+
+def test_router_bf16_is_nearest_even():
+    d = synth.MoEDims(n_experts=32)
+    f = synth.router_f32(3, d).ravel()
+    b = synth.router_bf16_bits(3, d).ravel()
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(b, ref)
