@@ -170,6 +170,51 @@ def bench_batch(args) -> int:
     return 0
 
 
+def bench_router(args) -> int:
+    """The router call alone (flint_moe_route_ex at E = 256) in its four
+    variants: fp32 or BF16 router, softmax or sigmoid weights.  One step = one
+    call for `--batch` tokens; bytes = the router matrix read once per token
+    (the kernel's rows are streamed once per token)."""
+    import torch
+
+    import synth
+    from nvfp4_bit_projection_amd import flint, workload
+
+    torch.cuda.set_device(0)
+    dims = synth.MoEDims()
+    B = args.batch
+    d = flint.dims_struct(dims.hidden, dims.n_experts, dims.expert_width, dims.top_k, dims.shared_width)
+    r32 = torch.empty((dims.n_experts, dims.hidden), dtype=torch.float32, device="cuda")
+    synth.normal_device(0, synth.stream_id(synth.ROUTER), r32.numel(), r32, std=synth.WEIGHT_STD)
+    r16 = r32.to(torch.bfloat16)
+    x = workload.tokens([synth.TOKEN_SEED0 + t for t in range(B)], dims.hidden)
+    ws = flint.workspace(flint.OP_ROUTE, d, B)
+    out = []
+    for name, router, scoring in (("f32_softmax", r32, flint.SCORE_SOFTMAX), ("f32_sigmoid", r32, flint.SCORE_SIGMOID),
+                                  ("bf16_softmax", r16, flint.SCORE_SOFTMAX),
+                                  ("bf16_sigmoid", r16, flint.SCORE_SIGMOID)):
+        for _ in range(args.warmup):
+            flint.route_ex(d, router, x, scoring=scoring, ws=ws)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(args.steps):
+            flint.route_ex(d, router, x, scoring=scoring, ws=ws)
+        ev1.record()
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / args.steps
+        nbytes = router.numel() * router.element_size() * B
+        gbs = nbytes / (us * 1e-6) / 1e9
+        log(f"router {name} B={B}: {us:.2f} us/call, {gbs:.1f} GB/s")
+        out.append({"variant": name, "us_per_call": round(us, 3), "bytes": nbytes, "achieved_gbs": round(gbs, 1),
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    print(json.dumps({"metric": "router call us (E=256)", "unit": "us", "batch": B, "steps": args.steps,
+                      "warmup": args.warmup, "higher_is_better": False, "data": "synthetic",
+                      "config": {"workload": f"router_e256_b{B}"}, "peak_gbs": HBM_PEAK_GBS, "variants": out}),
+          flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +225,8 @@ def main() -> int:
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--batch", type=int, default=1,
                     help="tokens per step; above 1 the batched step (experts deduplicated per layer) is timed")
+    ap.add_argument("--router", action="store_true",
+                    help="time the router call alone in its four variants (fp32/BF16 router, softmax/sigmoid)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (batch-1 decode; see DESIGN.md for how it would shard)",
@@ -187,6 +234,8 @@ def main() -> int:
         return 2
     if args.copy_calib:
         return copy_calib()
+    if args.router:
+        return bench_router(args)
     if args.batch > 1:
         return bench_batch(args)
 

@@ -131,6 +131,36 @@ int32_t flint_moe_route(const flint_moe_dims* dims /*[host]*/, const float* rout
                         int32_t* topk_idx, float* topk_w, float* logits_opt, void* ws, size_t ws_bytes,
                         void* stream);
 
+/* Router variants for flint_moe_route_ex. */
+#define FLINT_ROUTER_F32 0   /* router is float [E][H] */
+#define FLINT_ROUTER_BF16 1  /* router is BF16 bit patterns, uint16 [E][H] */
+#define FLINT_SCORE_SOFTMAX 0 /* weights as in flint_moe_route */
+#define FLINT_SCORE_SIGMOID 1 /* weights from sigmoid scores, see below */
+
+/* Router and top-k with the variants the pages describe [P3 "Flint: 125
+ * tokens a second is what 2.5B active parameters buy at 273 GB/s", "The
+ * shape, read from the headers": the router scores with a sigmoid, as
+ * DeepSeek-V3 does, without a bias-correction tensor; "Why active parameters
+ * set the speed": Recursive's build keeps the router in BF16].
+ *   router_dtype FLINT_ROUTER_F32: `router` is float [E][H], as in
+ *                flint_moe_route;
+ *                FLINT_ROUTER_BF16: `router` is uint16 [E][H] holding BF16
+ *                bit patterns, each widened exactly to fp32 (half the router
+ *                bytes); the products and sums are fp32.
+ *   scoring      FLINT_SCORE_SOFTMAX: weights exactly as flint_moe_route;
+ *                FLINT_SCORE_SIGMOID: score s_e = 1 / (1 + exp(-l_e)); the k
+ *                largest scores are chosen (the same set and order as the k
+ *                largest logits, since the sigmoid is increasing; ties to the
+ *                lower index) and topk_w[b][i] = s_i / sum_j s_j over the
+ *                chosen k, with no further scaling factor.
+ * Every other argument, the workspace (FLINT_OP_ROUTE) and the status codes
+ * are as for flint_moe_route; an unknown router_dtype or scoring returns
+ * FLINT_E_DIMS.  flint_moe_route(...) equals flint_moe_route_ex(...,
+ * FLINT_ROUTER_F32, FLINT_SCORE_SOFTMAX, ...). */
+int32_t flint_moe_route_ex(const flint_moe_dims* dims /*[host]*/, const void* router, int32_t router_dtype,
+                           int32_t scoring, const float* x, int32_t B, int32_t* topk_idx, float* topk_w,
+                           float* logits_opt, void* ws, size_t ws_bytes, void* stream);
+
 /* One MoE layer for B tokens (float [B][H]), no norm and no residual:
  *   y_b = sum_i topk_w[b][i] * E_{topk_idx[b][i]}(x_b) + Shared(x_b),
  * where each expert is SwiGLU: E(x) = Wdown (silu(Wgate x) * (Wup x)), silu

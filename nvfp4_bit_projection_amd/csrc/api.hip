@@ -136,6 +136,29 @@ int32_t flint_moe_route(const flint_moe_dims* dims, const float* router, const f
   return e == hipSuccess ? FLINT_OK : hip_fail(e);
 }
 
+int32_t flint_moe_route_ex(const flint_moe_dims* dims, const void* router, int32_t router_dtype, int32_t scoring,
+                           const float* x, int32_t B, int32_t* topk_idx, float* topk_w, float* logits_opt, void* ws,
+                           size_t ws_bytes, void* stream) {
+  int32_t st;
+  if ((st = check_dims(dims))) return st;
+  if (!router || !x || !topk_idx || !topk_w || !ws) return FLINT_E_NULL;
+  if (B < 1) return FLINT_E_DIMS;
+  if ((router_dtype != FLINT_ROUTER_F32 && router_dtype != FLINT_ROUTER_BF16) ||
+      (scoring != FLINT_SCORE_SOFTMAX && scoring != FLINT_SCORE_SIGMOID))
+    return FLINT_E_DIMS;
+  if (!aligned16(router) || !aligned16(x) || !aligned4(topk_idx) || !aligned4(topk_w) || !aligned16(ws) ||
+      (logits_opt && !aligned4(logits_opt)))
+    return FLINT_E_ALIGN;
+  RouteWs rw(dims->n_experts, B);
+  if (ws_bytes < rw.total) return FLINT_E_WORKSPACE;
+  if ((st = check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  float* logits = logits_opt ? logits_opt : carve<float>(ws, rw.logits);
+  hipError_t e = launch_route_ex(*dims, router, router_dtype == FLINT_ROUTER_BF16, scoring == FLINT_SCORE_SIGMOID, x,
+                                 B, logits, topk_idx, topk_w, carve<uint32_t>(ws, rw.tickets), s);
+  return e == hipSuccess ? FLINT_OK : hip_fail(e);
+}
+
 static int32_t decode_impl(const flint_moe_dims& d, const flint_moe_layer& L, const float* x, int B, float norm_eps,
                            float* y, bool add_to_y, int32_t* idx, float* w, void* ws, hipStream_t s) {
   DecodeWs dw(d, B);

@@ -117,6 +117,9 @@ hipError_t launch_batch_step(const flint_moe_dims& d, const flint_moe_layer* lay
 // ---- kernel launchers (kernels.hip); all return the hipError_t of the launch
 hipError_t launch_route(const flint_moe_dims& d, const float* router, const float* x, int B, float norm_eps,
                         float* logits, int32_t* idx, float* w, uint32_t* tickets, hipStream_t s);
+// router variants: BF16 router rows and/or sigmoid-score weights, no norm
+hipError_t launch_route_ex(const flint_moe_dims& d, const void* router, bool bf16, bool sigmoid, const float* x,
+                           int B, float* logits, int32_t* idx, float* w, uint32_t* tickets, hipStream_t s);
 hipError_t launch_gateup(const flint_moe_dims& d, const flint_moe_layer& L, const float* x, int B, float norm_eps,
                          const int32_t* idx, float* hact, hipStream_t s);
 hipError_t launch_down(const flint_moe_dims& d, const flint_moe_layer& L, const int32_t* idx, const float* w,

@@ -44,10 +44,46 @@ __device__ __forceinline__ uint4 ld_codes16(const uint8_t* p) { return ld_nt_u4(
 __device__ __forceinline__ uint32_t ld_scales2(const uint8_t* p) { return ld_nt_u16(p); }
 
 // ----------------------------------------------------------------- router --
+// Dot of one lane's 32 router weights (elements 32*lane .. 32*lane+31 of the
+// row) with its 32 activations.  fp32 rows: 8 x 16 B loads; BF16 rows: 4 x
+// 16 B loads, each BF16 value widened exactly (its bits are the top half of
+// the fp32 pattern).  Same fma order for both.
+__device__ __forceinline__ float router_dot32(const float* row, int lane, const float* xv) {
+  const float* rw = row + 32 * lane;
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 v = ld_nt_f4(rw + 4 * i);
+    acc = __builtin_fmaf(v.x, xv[4 * i + 0], acc);
+    acc = __builtin_fmaf(v.y, xv[4 * i + 1], acc);
+    acc = __builtin_fmaf(v.z, xv[4 * i + 2], acc);
+    acc = __builtin_fmaf(v.w, xv[4 * i + 3], acc);
+  }
+  return acc;
+}
+__device__ __forceinline__ float router_dot32(const uint16_t* row, int lane, const float* xv) {
+  const uint16_t* rw = row + 32 * lane;
+  float acc = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = ld_nt_u4(rw + 8 * i);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc = __builtin_fmaf(__uint_as_float(w[j] << 16), xv[8 * i + 2 * j + 0], acc);
+      acc = __builtin_fmaf(__uint_as_float(w[j] & 0xFFFF0000u), xv[8 * i + 2 * j + 1], acc);
+    }
+  }
+  return acc;
+}
+
 // grid (ceil(E/4), B), 256 threads: one router row per wave, then the last
 // workgroup of each token (atomic ticket) selects the top k in one wave.
-__global__ __launch_bounds__(256) void k_route(const float* __restrict__ router, int E, const float* __restrict__ x,
-                                               float norm_eps, int k, float* __restrict__ logits,
+// Weights: sigmoid == 0, softmax over the chosen logits; sigmoid != 0, the
+// chosen sigmoid scores over their sum.
+template <typename RT>
+__global__ __launch_bounds__(256) void k_route(const RT* __restrict__ router, int E, const float* __restrict__ x,
+                                               float norm_eps, int k, int sigmoid, float* __restrict__ logits,
                                                int32_t* __restrict__ idx_out, float* __restrict__ w_out,
                                                uint32_t* __restrict__ tickets) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, b = blockIdx.y;
@@ -55,16 +91,7 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ router,
   load_x32(x + (size_t)b * kHidden, lane, norm_eps, xv);
   const int e = blockIdx.x * 4 + wv;
   if (e < E) {
-    const float* rw = router + (size_t)e * kHidden + 32 * lane;
-    float acc = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 v = ld_nt_f4(rw + 4 * i);
-      acc = __builtin_fmaf(v.x, xv[4 * i + 0], acc);
-      acc = __builtin_fmaf(v.y, xv[4 * i + 1], acc);
-      acc = __builtin_fmaf(v.z, xv[4 * i + 2], acc);
-      acc = __builtin_fmaf(v.w, xv[4 * i + 3], acc);
-    }
+    float acc = router_dot32(router + (size_t)e * kHidden, lane, xv);
     acc = wave_sum(acc);
     if (lane == 0) logits[(size_t)b * E + e] = acc;
   }
@@ -102,11 +129,15 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ router,
       if (id[j] == bi) { v[j] = -FLT_MAX; id[j] = INT_MAX; }
   }
   if (lane == 0) {
+    float sc[kMaxTopK];
     float z = 0.0f;
-    for (int r = 0; r < k; ++r) z += __expf(top_v[r] - top_v[0]);
+    for (int r = 0; r < k; ++r) {
+      sc[r] = sigmoid ? 1.0f / (1.0f + __expf(-top_v[r])) : __expf(top_v[r] - top_v[0]);
+      z += sc[r];
+    }
     for (int r = 0; r < k; ++r) {
       idx_out[b * k + r] = top_i[r];
-      w_out[b * k + r] = __expf(top_v[r] - top_v[0]) / z;
+      w_out[b * k + r] = sc[r] / z;
     }
     tickets[b] = 0;  // leave the workspace zeroed for the next call
   }
@@ -412,7 +443,19 @@ __global__ void k_copy_f32(const float* __restrict__ s, float* __restrict__ d, i
 hipError_t launch_route(const flint_moe_dims& d, const float* router, const float* x, int B, float norm_eps,
                         float* logits, int32_t* idx, float* w, uint32_t* tickets, hipStream_t s) {
   dim3 grid((d.n_experts + 3) / 4, B);
-  k_route<<<grid, 256, 0, s>>>(router, d.n_experts, x, norm_eps, d.top_k, logits, idx, w, tickets);
+  k_route<float><<<grid, 256, 0, s>>>(router, d.n_experts, x, norm_eps, d.top_k, 0, logits, idx, w, tickets);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_ex(const flint_moe_dims& d, const void* router, bool bf16, bool sigmoid, const float* x,
+                           int B, float* logits, int32_t* idx, float* w, uint32_t* tickets, hipStream_t s) {
+  dim3 grid((d.n_experts + 3) / 4, B);
+  if (bf16)
+    k_route<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(router), d.n_experts, x, -1.0f, d.top_k,
+                                           sigmoid ? 1 : 0, logits, idx, w, tickets);
+  else
+    k_route<float><<<grid, 256, 0, s>>>(static_cast<const float*>(router), d.n_experts, x, -1.0f, d.top_k,
+                                        sigmoid ? 1 : 0, logits, idx, w, tickets);
   return hipGetLastError();
 }
 

@@ -64,6 +64,7 @@ def _load():
         "flint_last_hip_error": ([], _I32),
         "flint_workspace_bytes": ([_I32, ctypes.POINTER(Dims), _I32, _I32, _I32], _SZ),
         "flint_moe_route": ([ctypes.POINTER(Dims), _P, _P, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
+        "flint_moe_route_ex": ([ctypes.POINTER(Dims), _P, _I32, _I32, _P, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
         "flint_moe_decode": ([ctypes.POINTER(Dims), ctypes.POINTER(Layer), _P, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
         "flint_lmhead_gemv": ([ctypes.POINTER(NVFP4), _I32, _I32, _P, _I32, _P, _P, _P, _SZ, _P], _I32),
         "flint_stack_table_bytes": ([_I32], _SZ),
@@ -90,6 +91,7 @@ _lib = _load()
 
 # every symbol include/flint_moe.h declares
 EXPORTED = ("flint_status_str", "flint_last_hip_error", "flint_workspace_bytes", "flint_moe_route",
+            "flint_moe_route_ex",
             "flint_moe_decode", "flint_lmhead_gemv", "flint_stack_table_bytes", "flint_stack_packed_bytes",
             "flint_stack_prepare",
             "flint_stack_decode", "flint_stack_decode_traced", "flint_stack_decode_batch", "flint_stack_error", "flint_nvfp4_quantize", "flint_nvfp4_dequantize")
@@ -207,6 +209,32 @@ def route(dims: Dims, router: torch.Tensor, x: torch.Tensor, ws: torch.Tensor | 
     ws = workspace(OP_ROUTE, dims, B) if ws is None else ws
     _check(_lib.flint_moe_route(ctypes.byref(dims), router.data_ptr(), x.data_ptr(), B, idx.data_ptr(), w.data_ptr(),
                                 logits.data_ptr(), ws.data_ptr(), ws.numel(), _stream()), "flint_moe_route")
+    return idx, w, logits
+
+
+ROUTER_F32, ROUTER_BF16 = 0, 1
+SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
+
+
+def route_ex(dims: Dims, router: torch.Tensor, x: torch.Tensor, scoring: int = SCORE_SOFTMAX,
+             ws: torch.Tensor | None = None):
+    """Router variants.  router float32 [E][H], or int16/uint16 [E][H] BF16 bit
+    patterns (or a torch.bfloat16 tensor); x float32 [B][H] ->
+    (idx int32 [B][k], w float32 [B][k], logits float32 [B][E])"""
+    if router.dtype == torch.float32:
+        dtype = ROUTER_F32
+    elif router.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        dtype = ROUTER_BF16
+    else:
+        raise TypeError(f"router dtype {router.dtype} is not float32 or BF16")
+    B = x.shape[0]
+    idx = torch.empty((B, dims.top_k), dtype=torch.int32, device=x.device)
+    w = torch.empty((B, dims.top_k), dtype=torch.float32, device=x.device)
+    logits = torch.empty((B, dims.n_experts), dtype=torch.float32, device=x.device)
+    ws = workspace(OP_ROUTE, dims, B) if ws is None else ws
+    _check(_lib.flint_moe_route_ex(ctypes.byref(dims), router.data_ptr(), dtype, scoring, x.data_ptr(), B,
+                                   idx.data_ptr(), w.data_ptr(), logits.data_ptr(), ws.data_ptr(), ws.numel(),
+                                   _stream()), "flint_moe_route_ex")
     return idx, w, logits
 
 

@@ -142,6 +142,45 @@ def test_route(F, E):
         assert_close(logits[b].cpu().numpy(), rlog, "router logits")
 
 
+@pytest.mark.parametrize("E", [32, 256])
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("scoring", [0, 1])
+def test_route_variants(F, E, bf16, scoring):
+    """BF16 router and/or sigmoid-score weights against the oracle: the same
+    chosen set, weights within 1e-5, logits to the fp32 bar."""
+    flint, workload = F
+    d = synth.MoEDims(n_experts=E)
+    if bf16:
+        bits = synth.router_bf16_bits(0, d)
+        wr = oracle.bf16_decode(bits).astype(np.float32)  # exact: BF16 values are fp32 values
+        router = torch.from_numpy(bits.view(np.int16).copy()).cuda()
+    else:
+        wr = synth.router_f32(0, d)
+        router = torch.from_numpy(wr).cuda()
+    topk = oracle.topk_sigmoid if scoring else oracle.topk_softmax
+    toks, s = [], 0
+    while len(toks) < 5:
+        u = synth.token_f32(s, d.hidden).astype(np.float64)
+        logits = oracle.f32_gemv(wr, u)
+        idx, w, gap = topk(logits, d.top_k)
+        if gap >= MARGIN:
+            toks.append((s, idx, w, logits))
+        s += 1
+    x = workload.tokens([t[0] for t in toks], d.hidden)
+    idx, w, logits = flint.route_ex(dims_struct(F, d), router, x, scoring=scoring)
+    torch.cuda.synchronize()
+    for b, (_, ridx, rw, rlog) in enumerate(toks):
+        gi = idx[b].cpu().numpy()
+        assert sorted(gi.tolist()) == sorted(ridx.tolist())
+        gw = dict(zip(gi.tolist(), w[b].cpu().numpy().tolist()))
+        assert max(abs(gw[e] - we) for e, we in zip(ridx.tolist(), rw.tolist())) <= 1e-5
+        assert abs(sum(gw.values()) - 1.0) < 1e-5
+        assert_close(logits[b].cpu().numpy(), rlog, "router logits")
+    if not bf16 and scoring == 0:  # the plain call is this variant
+        i0, w0, l0 = flint.route(dims_struct(F, d), router, x)
+        assert torch.equal(i0, idx) and torch.equal(w0, w) and torch.equal(l0, logits)
+
+
 # --------------------------------------------------------------- MoE layer --
 @pytest.mark.parametrize("E,B", [(32, 1), (32, 3), (256, 1), (256, 2)])
 def test_moe_decode(F, E, B):

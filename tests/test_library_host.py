@@ -77,6 +77,21 @@ def test_route_rejections(F):
     assert r(d, FAKE, FAKE, 1, FAKE, FAKE, FAKE, need - 1) == -4
 
 
+def test_route_ex_rejections(F):
+    L = F.lib()
+    d = F.dims_struct()
+    r = lambda dt, sc, router=FAKE, wsb=None: L.flint_moe_route_ex(
+        ctypes.byref(d), router, dt, sc, FAKE, 1, FAKE, FAKE, None, FAKE,
+        F.workspace_bytes(F.OP_ROUTE, d, 1) if wsb is None else wsb, None)
+    assert r(2, 0) == -2
+    assert r(-1, 0) == -2
+    assert r(0, 2) == -2
+    assert r(1, -1) == -2
+    assert r(1, 1, router=None) == -1
+    assert r(1, 1, router=FAKE + 2) == -3
+    assert r(1, 1, wsb=F.workspace_bytes(F.OP_ROUTE, d, 1) - 1) == -4
+
+
 def test_decode_and_head_rejections(F):
     L = F.lib()
     d = F.dims_struct()
