@@ -60,6 +60,17 @@ def lib():
         L.oracle_topk_sigmoid.restype = None
         L.oracle_bf16_decode.argtypes = [_P, _I64, _P]
         L.oracle_bf16_decode.restype = None
+        L.oracle_bf16_encode.argtypes = [ctypes.c_double]
+        L.oracle_bf16_encode.restype = ctypes.c_uint16
+        L.oracle_bf16_round.argtypes = [_P, _I64, _P]
+        L.oracle_bf16_round.restype = None
+        L.oracle_head_rmsnorm.argtypes = [_P, ctypes.c_int, _P, ctypes.c_double]
+        L.oracle_head_rmsnorm.restype = None
+        L.oracle_rope.argtypes = [_P, ctypes.c_int, _I64, ctypes.c_double]
+        L.oracle_rope.restype = None
+        L.oracle_attn_decode.argtypes = ([ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_double] + [_P] * 7
+                                         + [_I64, _P, _P, _I64, _P, _P, _P, ctypes.c_int])
+        L.oracle_attn_decode.restype = ctypes.c_int
         L.oracle_rms_inv.argtypes = [_P, _I64, ctypes.c_double]
         L.oracle_rms_inv.restype = ctypes.c_double
         L.oracle_swiglu_expert.argtypes = [_P, _P, ctypes.c_float, _P, _P, ctypes.c_float, _P, _P, ctypes.c_float,
@@ -204,3 +215,69 @@ def argmax(v: np.ndarray):
     gap = np.zeros(1, np.float64)
     i = lib().oracle_argmax(v.ctypes.data, v.size, gap.ctypes.data)
     return int(i), float(gap[0])
+
+
+# --------------------------------------------------------------- attention --
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float64 values -> uint16 BF16 bit patterns (nearest, ties to even)"""
+    x = _c(x, np.float64)
+    out = np.empty(x.shape, np.uint16)
+    lib().oracle_bf16_round(x.ctypes.data, x.size, out.ctypes.data)
+    return out
+
+
+def head_rmsnorm(v: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
+    v = np.array(v, np.float64)
+    g = _c(gain, np.float32)
+    assert g.shape == v.shape
+    lib().oracle_head_rmsnorm(v.ctypes.data, v.size, g.ctypes.data, eps)
+    return v
+
+
+def rope(v: np.ndarray, pos: int, theta: float) -> np.ndarray:
+    v = np.array(v, np.float64)
+    lib().oracle_rope(v.ctypes.data, v.size, pos, theta)
+    return v
+
+
+class AttnLayer(NamedTuple):
+    """One attention layer: NVFP4 q [Hq*D][H], k and v [Hkv*D][H], o [H][Hq*D];
+    fp32 gains q_norm, k_norm [D]; fp32 sinks [Hq]."""
+    q: NVFP4
+    k: NVFP4
+    v: NVFP4
+    o: NVFP4
+    q_norm: np.ndarray
+    k_norm: np.ndarray
+    sinks: np.ndarray
+
+
+def attn_decode(L: AttnLayer, x: np.ndarray, pos: int, k_cache: np.ndarray, v_cache: np.ndarray, *, n_kv: int,
+                window: int, rope: bool, theta: float = 10000.0, eps: float = 1e-6,
+                nthreads: int | None = None):
+    """One new token at `pos`.  k_cache / v_cache uint16 [Hkv][cap][D] are
+    updated in place.  -> (y float64[H], o float64[Hq*D], qkv float64[...])"""
+    D = L.q_norm.size
+    Hq, H = L.q.rows // D, L.q.cols
+    cap = k_cache.shape[1]
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    assert k_cache.dtype == np.uint16 and v_cache.dtype == np.uint16 and k_cache.shape == (n_kv, cap, D)
+    x = _c(x, np.float64)
+    keep = []
+    cp, sp = (_P * 4)(), (_P * 4)()
+    ts = np.array([m.tscale for m in (L.q, L.k, L.v, L.o)], np.float32)
+    for i, m in enumerate((L.q, L.k, L.v, L.o)):
+        c, s = _c(m.codes, np.uint8), _c(m.scales, np.uint8)
+        keep += [c, s]
+        cp[i], sp[i] = c.ctypes.data, s.ctypes.data
+    qn, kn, sk = _c(L.q_norm, np.float32), _c(L.k_norm, np.float32), _c(L.sinks, np.float32)
+    y = np.empty(H, np.float64)
+    o = np.empty(Hq * D, np.float64)
+    qkv = np.empty(Hq * D + 2 * n_kv * D, np.float64)
+    rc = lib().oracle_attn_decode(H, Hq, n_kv, D, window, int(rope), theta, eps, cp, sp, ts.ctypes.data,
+                                  qn.ctypes.data, kn.ctypes.data, sk.ctypes.data, x.ctypes.data, pos,
+                                  k_cache.ctypes.data, v_cache.ctypes.data, cap, y.ctypes.data, o.ctypes.data,
+                                  qkv.ctypes.data, nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("attn_decode: cache too small for the window or position")
+    return y, o, qkv

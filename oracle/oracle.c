@@ -352,3 +352,156 @@ int64_t oracle_argmax(const double* v, int64_t n, double* gap) {
   if (gap) *gap = v[best] - second;
   return best;
 }
+
+/* ------------------------------------------------------------ attention -- */
+
+/* BF16 encoding of a finite double: the nearest value with 8 significant
+ * bits, ties to the even fraction; below 2^-126 the step is 2^-133
+ * (subnormals); values past the largest finite BF16 saturate to infinity.
+ * Written from the format (sign, 8-bit exponent with bias 127, 7-bit
+ * fraction), one rounding from the exact double. */
+uint16_t oracle_bf16_encode(double v) {
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e); /* a = m * 2^e with m in [0.5, 1) */
+  int ex = e - 1; /* a in [2^ex, 2^(ex+1)) */
+  if (ex < -126) ex = -126;
+  double q = ldexp(1.0, ex - 7); /* spacing of BF16 values near a */
+  double n = a / q;              /* exact: a power-of-two division */
+  double r = floor(n);
+  double f = n - r;
+  if (f > 0.5 || (f == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+  double val = r * q;
+  if (val >= ldexp(1.0, 128)) return sign | 0x7F80;
+  int e2;
+  frexp(val, &e2);
+  if (val < ldexp(1.0, -126)) return sign | (uint16_t)r; /* subnormal: fraction = r */
+  int bexp = e2 - 1 + 127;
+  uint16_t frac = (uint16_t)(ldexp(val, -(e2 - 1)) * 128.0 - 128.0);
+  return sign | (uint16_t)(bexp << 7) | frac;
+}
+
+void oracle_bf16_round(const double* x, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_encode(x[i]);
+}
+
+/* Per-head RMSNorm [P3 "The shape, read from the headers": every layer
+ * normalises each query and key head].  Reading: over the head's D values,
+ * v_i <- v_i * g_i / sqrt(mean(v^2) + eps), one gain vector g of length D
+ * shared by the heads of q (and one by the heads of k). */
+void oracle_head_rmsnorm(double* v, int D, const float* g, double eps) {
+  double s = 0.0;
+  for (int i = 0; i < D; ++i) s += v[i] * v[i];
+  double r = 1.0 / sqrt(s / D + eps);
+  for (int i = 0; i < D; ++i) v[i] = v[i] * r * (double)g[i];
+}
+
+/* Rotary position embedding [same section: the sliding-window layers use
+ * RoPE].  Reading: the pages give no base or pairing; the rotation pairs
+ * element i with element i + D/2 (i < D/2) and turns the pair by the angle
+ * pos * theta^(-2i/D):  (a, b) -> (a cos - b sin, a sin + b cos). */
+void oracle_rope(double* v, int D, int64_t pos, double theta) {
+  int h = D / 2;
+  for (int i = 0; i < h; ++i) {
+    double ang = (double)pos * pow(theta, -2.0 * i / D);
+    double c = cos(ang), s = sin(ang);
+    double a = v[i], b = v[i + h];
+    v[i] = a * c - b * s;
+    v[i + h] = a * s + b * c;
+  }
+}
+
+/* Attention over the cache for one query head [same section: grouped-query
+ * attention, 32 query heads over 4 key/value heads of dimension 128;
+ * sliding-window layers see the current token and 512 before it, the other
+ * layers the whole context; learned per-head sinks].  Reading of the sink: a
+ * logit that joins the softmax's normaliser and carries no value.
+ *   s_t = q . K_t / sqrt(D) for t in [first, pos]
+ *   M = max(max_t s_t, sink);  Z = sum_t e^(s_t - M) + e^(sink - M)
+ *   o = sum_t e^(s_t - M) / Z * V_t
+ * K_t and V_t are the BF16 cache rows at slot t mod cap. */
+static void attend_head(const double* q, int D, const uint16_t* kc, const uint16_t* vc, int64_t cap, int64_t first,
+                        int64_t pos, double sink, double* o) {
+  int64_t n = pos - first + 1;
+  double* s = (double*)malloc(sizeof(double) * (size_t)n);
+  double* row = (double*)malloc(sizeof(double) * (size_t)D);
+  double M = sink;
+  for (int64_t t = first; t <= pos; ++t) {
+    oracle_bf16_decode(kc + (t % cap) * D, D, row);
+    double acc = 0.0;
+    for (int d = 0; d < D; ++d) acc += q[d] * row[d];
+    s[t - first] = acc / sqrt((double)D);
+    if (s[t - first] > M) M = s[t - first];
+  }
+  double Z = exp(sink - M);
+  for (int64_t i = 0; i < n; ++i) Z += exp(s[i] - M);
+  for (int d = 0; d < D; ++d) o[d] = 0.0;
+  for (int64_t t = first; t <= pos; ++t) {
+    double p = exp(s[t - first] - M) / Z;
+    oracle_bf16_decode(vc + (t % cap) * D, D, row);
+    for (int d = 0; d < D; ++d) o[d] += p * row[d];
+  }
+  free(row);
+  free(s);
+}
+
+/* One attention layer for one new token at position pos (no norm before it,
+ * no residual after it):
+ *   q = Wq x, k = Wk x, v = Wv x           (NVFP4 [Hq*D][H], [Hkv*D][H] x2)
+ *   per-head RMSNorm of q and k (gains qn, kn), then RoPE at pos if rope
+ *   K[g][pos mod cap] = bf16(k_g), V[g][pos mod cap] = bf16(v_g)
+ *   o_h = attention of q_h over kv head g = h / (Hq/Hkv), positions
+ *         max(0, pos-window+1)..pos (window > 0) or 0..pos (window == 0)
+ *   y = Wo o                                (NVFP4 [H][Hq*D])
+ * mats[0..3] = q, k, v, o: codes, scales and tensor scale of each.  The
+ * caches are uint16 [Hkv][cap][D] and are updated in place.  cap must be at
+ * least `window` (window > 0) or greater than pos (window == 0); returns -1
+ * otherwise.  o_out (Hq*D) and qkv_out (Hq*D + 2*Hkv*D: q, k after norm and
+ * rotation, then v) are optional. */
+int oracle_attn_decode(int H, int Hq, int Hkv, int D, int window, int rope, double theta, double eps,
+                       const uint8_t* const* codes, const uint8_t* const* scales, const float* tscales,
+                       const float* qn, const float* kn, const float* sinks, const double* x, int64_t pos,
+                       uint16_t* kc, uint16_t* vc, int64_t cap, double* y, double* o_out, double* qkv_out,
+                       int nthreads) {
+  if (Hq % Hkv || D % 2 || pos < 0) return -1;
+  if (window > 0 ? cap < window : cap <= pos) return -1;
+  int nq = Hq * D, nk = Hkv * D;
+  double* q = (double*)malloc(sizeof(double) * (size_t)nq);
+  double* k = (double*)malloc(sizeof(double) * (size_t)nk);
+  double* v = (double*)malloc(sizeof(double) * (size_t)nk);
+  double* o = (double*)malloc(sizeof(double) * (size_t)nq);
+  oracle_nvfp4_gemv(codes[0], scales[0], tscales[0], nq, H, x, q, nthreads);
+  oracle_nvfp4_gemv(codes[1], scales[1], tscales[1], nk, H, x, k, nthreads);
+  oracle_nvfp4_gemv(codes[2], scales[2], tscales[2], nk, H, x, v, nthreads);
+  for (int h = 0; h < Hq; ++h) {
+    oracle_head_rmsnorm(q + h * D, D, qn, eps);
+    if (rope) oracle_rope(q + h * D, D, pos, theta);
+  }
+  for (int g = 0; g < Hkv; ++g) {
+    oracle_head_rmsnorm(k + g * D, D, kn, eps);
+    if (rope) oracle_rope(k + g * D, D, pos, theta);
+    oracle_bf16_round(k + g * D, D, kc + ((int64_t)g * cap + pos % cap) * D);
+    oracle_bf16_round(v + g * D, D, vc + ((int64_t)g * cap + pos % cap) * D);
+  }
+  int64_t first = (window > 0 && pos - window + 1 > 0) ? pos - window + 1 : 0;
+  int group = Hq / Hkv;
+  for (int h = 0; h < Hq; ++h) {
+    int g = h / group;
+    attend_head(q + h * D, D, kc + (int64_t)g * cap * D, vc + (int64_t)g * cap * D, cap, first, pos,
+                (double)sinks[h], o + h * D);
+  }
+  oracle_nvfp4_gemv(codes[3], scales[3], tscales[3], H, nq, o, y, nthreads);
+  if (o_out) memcpy(o_out, o, sizeof(double) * (size_t)nq);
+  if (qkv_out) {
+    memcpy(qkv_out, q, sizeof(double) * (size_t)nq);
+    memcpy(qkv_out + nq, k, sizeof(double) * (size_t)nk);
+    memcpy(qkv_out + nq + nk, v, sizeof(double) * (size_t)nk);
+  }
+  free(q);
+  free(k);
+  free(v);
+  free(o);
+  return 0;
+}

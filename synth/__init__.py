@@ -28,6 +28,9 @@ DEV_SRC_PATH = os.path.join(HERE, "synth_dev.hip")
 
 # stream kinds
 ROUTER, GATE, UP, DOWN, SHARED_GATE, SHARED_UP, SHARED_DOWN, HEAD, TOKEN = range(1, 10)
+# attention layers and the dense MLP layers (stream expert field = 0)
+ATTN_Q, ATTN_K, ATTN_V, ATTN_O, Q_NORM, K_NORM, SINK, K_CACHE, V_CACHE = range(10, 19)
+DENSE_GATE, DENSE_UP, DENSE_DOWN = range(19, 22)
 WEIGHT_STD = 0.02
 
 # seeds of the stacked workload: layer l uses weight seed l, the head 1000,
@@ -149,6 +152,60 @@ class Workload:
     token_seed: int = 0
 
 
+@dataclass(frozen=True)
+class AttnDims:
+    """Grouped-query attention of one layer: 32 query heads over 4 key/value
+    heads of dimension 128 on a 2,048-wide residual stream; window > 0 is a
+    sliding window (513 = the current token and 512 before it), 0 the whole
+    context; rope selects rotary position embedding (theta = its base)."""
+    hidden: int = 2048
+    n_q: int = 32
+    n_kv: int = 4
+    head_dim: int = 128
+    window: int = 513
+    rope: bool = True
+    theta: float = 10000.0
+
+
+SLIDING = AttnDims()
+FULL = AttnDims(window=0, rope=False)
+DENSE_WIDTH = 6144
+
+
+def bf16_bits(f: np.ndarray) -> np.ndarray:
+    """float32 draws stored as BF16 (uint16 bit patterns, nearest even)."""
+    u = np.ascontiguousarray(f, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def attn_f32(seed: int, d: AttnDims, kind: int) -> np.ndarray:
+    """q [Hq*D][H], k and v [Hkv*D][H], o [H][Hq*D], N(0, 0.02)."""
+    nq, nk = d.n_q * d.head_dim, d.n_kv * d.head_dim
+    shape = {ATTN_Q: (nq, d.hidden), ATTN_K: (nk, d.hidden), ATTN_V: (nk, d.hidden), ATTN_O: (d.hidden, nq)}[kind]
+    return normal(seed, stream_id(kind), shape[0] * shape[1], std=WEIGHT_STD).reshape(shape)
+
+
+def attn_gain(seed: int, d: AttnDims, kind: int) -> np.ndarray:
+    """q or k head-norm gain [D], N(1, 0.1)."""
+    return normal(seed, stream_id(kind), d.head_dim, mean=1.0, std=0.1)
+
+
+def attn_sinks(seed: int, d: AttnDims) -> np.ndarray:
+    """per-query-head sink logits [Hq], N(0, 1)."""
+    return normal(seed, stream_id(SINK), d.n_q)
+
+
+def kv_cache_bits(seed: int, d: AttnDims, cap: int, kind: int) -> np.ndarray:
+    """A filled cache [Hkv][cap][D] of BF16 N(0, 1) rows (K_CACHE or V_CACHE)."""
+    return bf16_bits(normal(seed, stream_id(kind), d.n_kv * cap * d.head_dim)).reshape(d.n_kv, cap, d.head_dim)
+
+
+def dense_f32(seed: int, hidden: int, width: int, kind: int) -> np.ndarray:
+    """Dense MLP matrix: gate/up [width][hidden], down [hidden][width]."""
+    shape = (hidden, width) if kind == DENSE_DOWN else (width, hidden)
+    return normal(seed, stream_id(kind), hidden * width, std=WEIGHT_STD).reshape(shape)
+
+
 # the workloads this repository measures and tests
 MOE_LAYER_E32 = Workload("moe_layer_e32", MoEDims(n_experts=32))
 MOE_LAYER_E256 = Workload("moe_layer_e256", MoEDims())
@@ -165,8 +222,7 @@ def router_f32(seed: int, dims: MoEDims) -> np.ndarray:
 def router_bf16_bits(seed: int, dims: MoEDims) -> np.ndarray:
     """The fp32 router draws stored as BF16 (uint16 bit patterns, round to
     nearest even on the top 16 bits), as a checkpoint keeps a BF16 router."""
-    u = router_f32(seed, dims).view(np.uint32).astype(np.uint64)
-    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    return bf16_bits(router_f32(seed, dims))
 
 
 def expert_f32(seed: int, dims: MoEDims, kind: int, expert: int) -> np.ndarray:
