@@ -4,6 +4,7 @@
 #include <atomic>
 #include <string.h>
 
+#include "flint_common.h"
 #include "flint_internal.h"
 
 using namespace flint;
@@ -72,6 +73,9 @@ template <typename T>
 T* carve(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
 }  // namespace
+
+int32_t flint::api_hip_fail(hipError_t e) { return hip_fail(e); }
+int32_t flint::api_check_device() { return check_device(); }
 
 extern "C" {
 

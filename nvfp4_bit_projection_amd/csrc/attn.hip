@@ -1,0 +1,520 @@
+// attn.hip -- the rest of a decode step for gfx950: one grouped-query
+// attention layer over a BF16 key/value cache, the dense SwiGLU MLP, and the
+// generic NVFP4 GEMV both are built from.
+//
+// Method [P3 "Flint: 125 tokens a second is what 2.5B active parameters buy
+// at 273 GB/s", "The shape, read from the headers": 32 query heads over 4
+// key/value heads of dimension 128, per-head QK RMSNorm, learned per-head
+// sinks, sliding-window (513) layers with RoPE and full-context layers
+// without positional encoding; "Why active parameters set the speed": a BF16
+// key and value per token and layer; "Built from scratch?": dense MLP layers
+// 6,144 wide].
+//
+// One attention layer at batch 1 is three launches:
+//   k_gemv (q, k, v rows of three NVFP4 matrices, K = 2048)
+//   k_attn (grid: context chunks x key/value heads) -- head norms and RoPE of
+//          the group's queries, the current key/value written to the cache,
+//          flash-decoding over 64-position sub-chunks staged in LDS, then the
+//          last workgroup of each key/value head merges the chunks with the
+//          sinks
+//   k_gemv (o rows, K = n_q * 128)
+// Every stage is bound by HBM bandwidth: weights and cache rows are read
+// once per token with 128-bit loads.
+#include <float.h>
+#include <math.h>
+
+#include "../../include/flint_attn.h"
+#include "flint_common.h"
+#include "flint_device.h"
+
+namespace flint {
+namespace {
+
+constexpr int kHid = 2048;        // the hidden size with kernels
+constexpr int kD = 128;           // head dimension
+constexpr int kSub = 64;          // positions per sub-chunk: one per lane
+constexpr int kMaxChunks = 64;    // context chunks per key/value head
+constexpr int kMaxGroup = 8;      // query heads per key/value head
+constexpr int kPart = kD + 2;     // chunk record: running max, sum, o[128]
+constexpr int kMaxDenseB = 64;
+
+inline size_t al256(size_t v) { return (v + 255) / 256 * 256; }
+
+// --------------------------------------------------------- NVFP4 GEMV ------
+struct GemvMat {
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* tscale;
+  int rows;
+};
+struct GemvSet {
+  GemvMat m[3];
+};
+
+// y[b][r] = S * (W[r] . x_b) over the rows of up to three matrices stacked
+// (all rows of m[0], then m[1], then m[2]); with PAIR the rows of m[0] and
+// m[1] are taken together: y[b][r] = silu(S0 W0[r].x_b) * (S1 W1[r].x_b).
+// K = KI * 2048: lane l holds x[i*2048 + 32l .. +31] for i < KI in registers
+// and reads 16 code bytes and 2 scale bytes per row and i.  A wave takes R
+// rows per step (their loads issued together), waves stride over the rows;
+// grid.y is the token.
+template <int KI, int R, bool PAIR>
+__global__ __launch_bounds__(256) void k_gemv(GemvSet M, int total_rows, const float* __restrict__ x, int ldx,
+                                              float* __restrict__ y, int ldy) {
+  constexpr int K = KI * kHid;
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.y;
+  float xv[KI * 32];
+  const float* xb = x + (size_t)b * ldx;
+#pragma unroll
+  for (int i = 0; i < KI; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(xb + i * kHid + 32 * lane + 4 * q);
+      xv[32 * i + 4 * q + 0] = v.x;
+      xv[32 * i + 4 * q + 1] = v.y;
+      xv[32 * i + 4 * q + 2] = v.z;
+      xv[32 * i + 4 * q + 3] = v.w;
+    }
+  const int nwaves = gridDim.x * 4;
+  for (int r0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R; r0 < total_rows; r0 += nwaves * R) {
+    uint4 c[R][KI], c2[PAIR ? R : 1][KI];
+    uint32_t s[R][KI], s2[PAIR ? R : 1][KI];
+    float S[R], S2[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      int lr = min(r0 + j, total_rows - 1);
+      const uint8_t* cp = M.m[0].codes;
+      const uint8_t* sp = M.m[0].scales;
+      const float* tp = M.m[0].tscale;
+      if (!PAIR && lr >= M.m[0].rows) {
+        lr -= M.m[0].rows;
+        if (lr >= M.m[1].rows) {
+          lr -= M.m[1].rows;
+          cp = M.m[2].codes; sp = M.m[2].scales; tp = M.m[2].tscale;
+        } else {
+          cp = M.m[1].codes; sp = M.m[1].scales; tp = M.m[1].tscale;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < KI; ++i) {
+        c[j][i] = ld_nt_u4(cp + (size_t)lr * (K / 2) + i * (kHid / 2) + 16 * lane);
+        s[j][i] = ld_nt_u16(sp + (size_t)lr * (K / 16) + i * (kHid / 16) + 2 * lane);
+      }
+      S[j] = *tp;
+      if constexpr (PAIR) {
+#pragma unroll
+        for (int i = 0; i < KI; ++i) {
+          c2[j][i] = ld_nt_u4(M.m[1].codes + (size_t)lr * (K / 2) + i * (kHid / 2) + 16 * lane);
+          s2[j][i] = ld_nt_u16(M.m[1].scales + (size_t)lr * (K / 16) + i * (kHid / 16) + 2 * lane);
+        }
+        S2[j] = *M.m[1].tscale;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      float a = 0.0f;
+#pragma unroll
+      for (int i = 0; i < KI; ++i) a += nvfp4_lane_dot32(c[j][i], s[j][i], xv + 32 * i);
+      float v = wave_sum(a) * S[j];
+      if constexpr (PAIR) {
+        float a2 = 0.0f;
+#pragma unroll
+        for (int i = 0; i < KI; ++i) a2 += nvfp4_lane_dot32(c2[j][i], s2[j][i], xv + 32 * i);
+        v = silu(v) * (wave_sum(a2) * S2[j]);
+      }
+      if (lane == 0 && r0 + j < total_rows) y[(size_t)b * ldy + r0 + j] = v;
+    }
+  }
+}
+
+template <int KI, int R, bool PAIR>
+hipError_t gemv_launch(const GemvSet& M, int rows, const float* x, int ldx, float* y, int ldy, int B,
+                       hipStream_t st) {
+  const int waves = (rows + R - 1) / R;
+  int blocks = (waves + 3) / 4;
+  if (blocks > 2048) blocks = 2048;
+  k_gemv<KI, R, PAIR><<<dim3(blocks, B), 256, 0, st>>>(M, rows, x, ldx, y, ldy);
+  return hipGetLastError();
+}
+
+// K in {2048, 4096, 6144, 8192}; PAIR only at K = 2048
+hipError_t launch_gemv(const GemvSet& M, int rows, int K, bool pair, const float* x, int ldx, float* y, int ldy,
+                       int B, hipStream_t st) {
+  if (pair) return gemv_launch<1, 2, true>(M, rows, x, ldx, y, ldy, B, st);
+  switch (K / kHid) {
+    case 1: return gemv_launch<1, 4, false>(M, rows, x, ldx, y, ldy, B, st);
+    case 2: return gemv_launch<2, 2, false>(M, rows, x, ldx, y, ldy, B, st);
+    case 3: return gemv_launch<3, 2, false>(M, rows, x, ldx, y, ldy, B, st);
+    default: return gemv_launch<4, 2, false>(M, rows, x, ldx, y, ldy, B, st);
+  }
+}
+
+// ------------------------------------------------------------ attention --
+__device__ __forceinline__ uint32_t bf16_rne(float f) {  // finite f
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+struct AttnArgs {
+  const float* qkv;  // raw q [n_q*D], k [n_kv*D], v [n_kv*D] of this token
+  const float* q_norm;
+  const float* k_norm;
+  const float* sinks;
+  uint16_t* kc;  // [n_kv][cap][D]
+  uint16_t* vc;
+  long long cap, pos, first;
+  int n_q, n_kv, group;
+  int per;      // sub-chunks per chunk
+  int n_sub;    // sub-chunks in first .. pos
+  int nchunks;  // chunks per key/value head (= grid.x)
+  int rope;
+  float eps;
+  double log2_theta;
+  float* part;  // [n_kv][kMaxGroup][kMaxChunks][kPart]
+  float* o;     // [n_q*D]
+  uint32_t* tickets;  // [n_kv], zero between calls
+};
+
+// grid (nchunks, n_kv), 256 threads.  Chunk c covers sub-chunks
+// [c*per, min((c+1)*per, n_sub)) of 64 positions from `first`; the last chunk
+// holds `pos`.  Wave w owns query heads 2w and 2w+1 of the group.
+__global__ __launch_bounds__(256) void k_attn(AttnArgs A) {
+  __shared__ uint32_t sKt[64 * kSub];    // key BF16 pairs, [dim pair][position]
+  __shared__ uint32_t sV[kSub * 64];     // value BF16 pairs, [position][dim pair]
+  __shared__ float sq[kMaxGroup][kD];    // queries: normalised, rotated, / sqrt(D)
+  __shared__ float sp[kMaxGroup][kSub];  // probabilities of the current sub-chunk
+  __shared__ __align__(16) uint16_t scur[2][kD];  // this token's key and value (BF16)
+  __shared__ uint32_t last;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = blockIdx.y, c = blockIdx.x;
+  const int nq = A.n_q * kD, nk = A.n_kv * kD;
+  const int s_begin = c * A.per;
+  const int s_end = min(s_begin + A.per, A.n_sub);
+  const bool has_cur = (s_end == A.n_sub);
+  const long long cur_slot = A.pos % A.cap;
+
+  // cache rows of one sub-chunk: thread tid loads 16 bytes (segment tid & 15)
+  // of rows (tid >> 4) + 16 j; rows at or past pos are zero here
+  uint4 kk[4], vv[4];
+  auto load_sub = [&](int s) {
+    const long long p0 = A.first + (long long)s * kSub;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long long t = p0 + (tid >> 4) + 16 * j;
+      if (t < A.pos) {
+        const long long off = ((long long)g * A.cap + t % A.cap) * kD + (tid & 15) * 8;
+        kk[j] = *reinterpret_cast<const uint4*>(A.kc + off);
+        vv[j] = *reinterpret_cast<const uint4*>(A.vc + off);
+      } else {
+        kk[j] = make_uint4(0, 0, 0, 0);
+        vv[j] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  load_sub(s_begin);
+
+  // RoPE angle of the pair (lane, lane + 64): pos * theta^(-2 lane / D), in
+  // double so that large positions keep their phase
+  float cs = 1.0f, sn = 0.0f;
+  if (A.rope) {
+    const double ang = (double)A.pos * exp2(-2.0 * lane / kD * A.log2_theta);
+    cs = (float)cos(ang);
+    sn = (float)sin(ang);
+  }
+  const float qscale = 0.08838834764831845f;  // 1 / sqrt(128)
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int hh = 2 * wv + k;
+    if (hh < A.group) {
+      const int h = g * A.group + hh;
+      float a = A.qkv[h * kD + lane], b = A.qkv[h * kD + 64 + lane];
+      const float r = 1.0f / sqrtf(wave_sum(a * a + b * b) * (1.0f / kD) + A.eps);
+      a = a * r * A.q_norm[lane];
+      b = b * r * A.q_norm[lane + 64];
+      if (A.rope) {
+        const float a2 = a * cs - b * sn;
+        b = a * sn + b * cs;
+        a = a2;
+      }
+      sq[hh][lane] = a * qscale;
+      sq[hh][lane + 64] = b * qscale;
+    }
+  }
+  // this token's key (wave 0) and value (wave 1), rounded to BF16, into the
+  // cache slot of pos and into LDS for the last sub-chunk
+  if (has_cur && wv < 2) {
+    const float* src = A.qkv + nq + (wv == 0 ? 0 : nk) + g * kD;
+    float a = src[lane], b = src[lane + 64];
+    if (wv == 0) {
+      const float r = 1.0f / sqrtf(wave_sum(a * a + b * b) * (1.0f / kD) + A.eps);
+      a = a * r * A.k_norm[lane];
+      b = b * r * A.k_norm[lane + 64];
+      if (A.rope) {
+        const float a2 = a * cs - b * sn;
+        b = a * sn + b * cs;
+        a = a2;
+      }
+    }
+    const uint16_t ba = (uint16_t)bf16_rne(a), bb = (uint16_t)bf16_rne(b);
+    uint16_t* dst = (wv == 0 ? A.kc : A.vc) + ((long long)g * A.cap + cur_slot) * kD;
+    dst[lane] = ba;
+    dst[lane + 64] = bb;
+    scur[wv][lane] = ba;
+    scur[wv][lane + 64] = bb;
+  }
+
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
+  float o_run[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+  for (int s = s_begin; s < s_end; ++s) {
+    const long long p0 = A.first + (long long)s * kSub;
+    const int nvalid = (int)min((long long)kSub, A.pos + 1 - p0);
+    __syncthreads();  // LDS of the previous sub-chunk consumed; sq, scur written
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = (tid >> 4) + 16 * j, seg = tid & 15;
+      uint4 kw = kk[j], vw = vv[j];
+      if (p0 + r == A.pos) {
+        kw = *reinterpret_cast<const uint4*>(&scur[0][seg * 8]);
+        vw = *reinterpret_cast<const uint4*>(&scur[1][seg * 8]);
+      }
+      *reinterpret_cast<uint4*>(&sV[r * 64 + seg * 4]) = vw;
+      sKt[(seg * 4 + 0) * kSub + r] = kw.x;
+      sKt[(seg * 4 + 1) * kSub + r] = kw.y;
+      sKt[(seg * 4 + 2) * kSub + r] = kw.z;
+      sKt[(seg * 4 + 3) * kSub + r] = kw.w;
+    }
+    if (s + 1 < s_end) load_sub(s + 1);
+    __syncthreads();
+    // scores s_t = q . K_t (lane = position t), then the running softmax
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int hh = 2 * wv + k;
+      if (hh < A.group) {
+        float acc = 0.0f;
+#pragma unroll 8
+        for (int dp = 0; dp < 64; ++dp) {
+          const uint32_t w = sKt[dp * kSub + lane];
+          acc = __builtin_fmaf(sq[hh][2 * dp], bf16_lo(w), acc);
+          acc = __builtin_fmaf(sq[hh][2 * dp + 1], bf16_hi(w), acc);
+        }
+        const float sc = lane < nvalid ? acc : -INFINITY;
+        const float m_new = fmaxf(m_run[k], wave_max(sc));
+        const float p = lane < nvalid ? __expf(sc - m_new) : 0.0f;
+        const float alpha = (m_run[k] == -INFINITY) ? 0.0f : __expf(m_run[k] - m_new);
+        l_run[k] = l_run[k] * alpha + wave_sum(p);
+        o_run[k][0] *= alpha;
+        o_run[k][1] *= alpha;
+        m_run[k] = m_new;
+        sp[hh][lane] = p;
+      }
+    }
+    __syncthreads();
+    // o += p_t V_t: lane owns dims 2 lane, 2 lane + 1
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int hh = 2 * wv + k;
+      if (hh < A.group) {
+        float o0 = o_run[k][0], o1 = o_run[k][1];
+        for (int t = 0; t < nvalid; ++t) {
+          const uint32_t w = sV[t * 64 + lane];
+          const float p = sp[hh][t];
+          o0 = __builtin_fmaf(p, bf16_lo(w), o0);
+          o1 = __builtin_fmaf(p, bf16_hi(w), o1);
+        }
+        o_run[k][0] = o0;
+        o_run[k][1] = o1;
+      }
+    }
+  }
+  // chunk records
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int hh = 2 * wv + k;
+    if (hh < A.group) {
+      float* P = A.part + (((size_t)g * kMaxGroup + hh) * kMaxChunks + c) * kPart;
+      if (lane == 0) {
+        P[0] = m_run[k];
+        P[1] = l_run[k];
+      }
+      *reinterpret_cast<float2*>(P + 2 + 2 * lane) = make_float2(o_run[k][0], o_run[k][1]);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    __threadfence();
+    last = (atomicAdd(&A.tickets[g], 1u) == (uint32_t)A.nchunks - 1);
+  }
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  // the last chunk of this key/value head merges all chunks with the sink
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int hh = 2 * wv + k;
+    if (hh < A.group) {
+      const int h = g * A.group + hh;
+      const float sink = A.sinks[h];
+      const float* P0 = A.part + ((size_t)g * kMaxGroup + hh) * kMaxChunks * kPart;
+      float M = sink;
+      for (int cc = 0; cc < A.nchunks; ++cc) M = fmaxf(M, ld_dev_f32(P0 + cc * kPart));
+      float Z = __expf(sink - M), o0 = 0.0f, o1 = 0.0f;
+      for (int cc = 0; cc < A.nchunks; ++cc) {
+        const float* P = P0 + cc * kPart;
+        const float f = __expf(ld_dev_f32(P) - M);
+        Z = __builtin_fmaf(f, ld_dev_f32(P + 1), Z);
+        o0 = __builtin_fmaf(f, ld_dev_f32(P + 2 + 2 * lane), o0);
+        o1 = __builtin_fmaf(f, ld_dev_f32(P + 3 + 2 * lane), o1);
+      }
+      A.o[h * kD + 2 * lane] = o0 / Z;
+      A.o[h * kD + 2 * lane + 1] = o1 / Z;
+    }
+  }
+  if (tid == 0) A.tickets[g] = 0;  // leave the workspace zeroed for the next call
+}
+
+// --------------------------------------------------------- host helpers --
+struct AttnWs {
+  size_t qkv, o, part, tickets, total;
+  explicit AttnWs(const flint_attn_dims& d) {
+    const size_t nq = (size_t)d.n_q_heads * kD, nk = (size_t)d.n_kv_heads * kD;
+    size_t off = 0;
+    qkv = off; off = al256(off + 4 * (nq + 2 * nk));
+    o = off; off = al256(off + 4 * nq);
+    part = off; off = al256(off + 4 * (size_t)d.n_kv_heads * kMaxGroup * kMaxChunks * kPart);
+    tickets = off; off = al256(off + 4 * (size_t)d.n_kv_heads);
+    total = off;
+  }
+};
+
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int32_t check_attn_dims(const flint_attn_dims* d) {
+  if (!d) return FLINT_E_NULL;
+  if (d->hidden < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 2 || d->head_dim % 2 ||
+      d->n_q_heads % d->n_kv_heads || d->window < 0 || (d->rope != 0 && d->rope != 1) || !(d->eps >= 0.0f) ||
+      (d->rope && !(d->rope_theta > 0.0f)))
+    return FLINT_E_DIMS;
+  if (d->hidden != kHid || d->head_dim != kD || d->n_q_heads % 16 || d->n_q_heads > 64 ||
+      d->n_q_heads / d->n_kv_heads > kMaxGroup)
+    return FLINT_E_UNSUPPORTED;
+  return FLINT_OK;
+}
+
+int32_t check_mat(const flint_nvfp4* q) {
+  if (!q || !q->codes || !q->scales || !q->tscale) return FLINT_E_NULL;
+  if (!al16(q->codes) || !al4(q->scales) || !al4(q->tscale)) return FLINT_E_ALIGN;
+  return FLINT_OK;
+}
+
+GemvMat gm(const flint_nvfp4& q, int rows) { return GemvMat{q.codes, q.scales, q.tscale, rows}; }
+
+}  // namespace
+}  // namespace flint
+
+using namespace flint;
+
+extern "C" {
+
+size_t flint_attn_workspace_bytes(const flint_attn_dims* dims) {
+  if (check_attn_dims(dims) != FLINT_OK) return 0;
+  return AttnWs(*dims).total;
+}
+
+int32_t flint_attn_decode(const flint_attn_dims* dims, const flint_attn_layer* layer, const float* x, int32_t pos,
+                          uint16_t* k_cache, uint16_t* v_cache, int32_t cap, float* y, void* ws, size_t ws_bytes,
+                          void* stream) {
+  int32_t st;
+  if ((st = check_attn_dims(dims))) return st;
+  if (!layer || !x || !k_cache || !v_cache || !y || !ws) return FLINT_E_NULL;
+  if (!layer->q_norm || !layer->k_norm || !layer->sinks) return FLINT_E_NULL;
+  if ((st = check_mat(&layer->q)) || (st = check_mat(&layer->k)) || (st = check_mat(&layer->v)) ||
+      (st = check_mat(&layer->o)))
+    return st;
+  const flint_attn_dims& d = *dims;
+  if (pos < 0 || cap < 1) return FLINT_E_DIMS;
+  if (d.window > 0 ? cap < d.window : cap <= pos) return FLINT_E_DIMS;
+  if (!al16(x) || !al16(y) || !al16(k_cache) || !al16(v_cache) || !al16(ws) || !al4(layer->q_norm) ||
+      !al4(layer->k_norm) || !al4(layer->sinks))
+    return FLINT_E_ALIGN;
+  const AttnWs w(d);
+  if (ws_bytes < w.total) return FLINT_E_WORKSPACE;
+  if ((st = api_check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = static_cast<char*>(ws);
+  float* qkv = reinterpret_cast<float*>(base + w.qkv);
+  float* o = reinterpret_cast<float*>(base + w.o);
+  const int nq = d.n_q_heads * kD, nk = d.n_kv_heads * kD;
+
+  GemvSet in{};
+  in.m[0] = gm(layer->q, nq);
+  in.m[1] = gm(layer->k, nk);
+  in.m[2] = gm(layer->v, nk);
+  hipError_t e = launch_gemv(in, nq + 2 * nk, kHid, false, x, 0, qkv, 0, 1, s);
+  if (e != hipSuccess) return api_hip_fail(e);
+
+  AttnArgs A{};
+  A.qkv = qkv;
+  A.q_norm = layer->q_norm;
+  A.k_norm = layer->k_norm;
+  A.sinks = layer->sinks;
+  A.kc = k_cache;
+  A.vc = v_cache;
+  A.cap = cap;
+  A.pos = pos;
+  A.first = (d.window > 0 && pos - d.window + 1 > 0) ? pos - d.window + 1 : 0;
+  A.n_q = d.n_q_heads;
+  A.n_kv = d.n_kv_heads;
+  A.group = d.n_q_heads / d.n_kv_heads;
+  const long long n = (long long)pos - A.first + 1;
+  A.n_sub = (int)((n + kSub - 1) / kSub);
+  A.per = (A.n_sub + kMaxChunks - 1) / kMaxChunks;
+  A.nchunks = (A.n_sub + A.per - 1) / A.per;
+  A.rope = d.rope;
+  A.eps = d.eps;
+  A.log2_theta = d.rope ? log2((double)d.rope_theta) : 0.0;
+  A.part = reinterpret_cast<float*>(base + w.part);
+  A.o = o;
+  A.tickets = reinterpret_cast<uint32_t*>(base + w.tickets);
+  k_attn<<<dim3(A.nchunks, d.n_kv_heads), 256, 0, s>>>(A);
+  e = hipGetLastError();
+  if (e != hipSuccess) return api_hip_fail(e);
+
+  GemvSet out{};
+  out.m[0] = gm(layer->o, kHid);
+  e = launch_gemv(out, kHid, nq, false, o, 0, y, 0, 1, s);
+  return e == hipSuccess ? FLINT_OK : api_hip_fail(e);
+}
+
+size_t flint_dense_workspace_bytes(int32_t hidden, int32_t width, int32_t B) {
+  if (hidden != kHid || width < kHid || width % kHid || width > 4 * kHid || B < 1 || B > kMaxDenseB) return 0;
+  return al256(4 * (size_t)B * width);
+}
+
+int32_t flint_dense_mlp(const flint_nvfp4* gate, const flint_nvfp4* up, const flint_nvfp4* down, int32_t hidden,
+                        int32_t width, const float* x, int32_t B, float* y, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st;
+  if ((st = check_mat(gate)) || (st = check_mat(up)) || (st = check_mat(down))) return st;
+  if (!x || !y || !ws) return FLINT_E_NULL;
+  if (hidden < 1 || width < 1 || B < 1) return FLINT_E_DIMS;
+  if (hidden != kHid || width % kHid || width > 4 * kHid || B > kMaxDenseB) return FLINT_E_UNSUPPORTED;
+  if (!al16(x) || !al16(y) || !al16(ws)) return FLINT_E_ALIGN;
+  if (ws_bytes < flint_dense_workspace_bytes(hidden, width, B)) return FLINT_E_WORKSPACE;
+  if ((st = api_check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  float* h = static_cast<float*>(ws);
+  GemvSet gu{};
+  gu.m[0] = gm(*gate, width);
+  gu.m[1] = gm(*up, width);
+  hipError_t e = launch_gemv(gu, width, kHid, true, x, kHid, h, width, B, s);
+  if (e != hipSuccess) return api_hip_fail(e);
+  GemvSet dn{};
+  dn.m[0] = gm(*down, kHid);
+  e = launch_gemv(dn, kHid, width, false, h, width, y, kHid, B, s);
+  return e == hipSuccess ? FLINT_OK : api_hip_fail(e);
+}
+
+}  // extern "C"

@@ -51,6 +51,16 @@ class StackPlan(ctypes.Structure):
                 ("table", _P), ("schedule", _I32), ("packed", _P)]
 
 
+class AttnDims(ctypes.Structure):
+    _fields_ = [("hidden", _I32), ("n_q_heads", _I32), ("n_kv_heads", _I32), ("head_dim", _I32), ("window", _I32),
+                ("rope", _I32), ("rope_theta", ctypes.c_float), ("eps", ctypes.c_float)]
+
+
+class AttnLayer(ctypes.Structure):
+    _fields_ = [("q", NVFP4), ("k", NVFP4), ("v", NVFP4), ("o", NVFP4), ("q_norm", _P), ("k_norm", _P),
+                ("sinks", _P)]
+
+
 TRACE_POINTS = 16  # stamps per layer of flint_stack_decode_traced
 SCHEDULE_AUTO, SCHEDULE_KERNELS, SCHEDULE_PERSISTENT = 0, 1, 2
 
@@ -79,6 +89,12 @@ def _load():
         "flint_stack_error": ([_P, _SZ, ctypes.POINTER(_I32)], _I32),
         "flint_nvfp4_quantize": ([_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _I32),
         "flint_nvfp4_dequantize": ([ctypes.POINTER(NVFP4), _I64, _I64, _P, _P], _I32),
+        "flint_attn_workspace_bytes": ([ctypes.POINTER(AttnDims)], _SZ),
+        "flint_attn_decode": ([ctypes.POINTER(AttnDims), ctypes.POINTER(AttnLayer), _P, _I32, _P, _P, _I32, _P, _P,
+                               _SZ, _P], _I32),
+        "flint_dense_workspace_bytes": ([_I32, _I32, _I32], _SZ),
+        "flint_dense_mlp": ([ctypes.POINTER(NVFP4), ctypes.POINTER(NVFP4), ctypes.POINTER(NVFP4), _I32, _I32, _P,
+                             _I32, _P, _P, _SZ, _P], _I32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -94,7 +110,10 @@ EXPORTED = ("flint_status_str", "flint_last_hip_error", "flint_workspace_bytes",
             "flint_moe_route_ex",
             "flint_moe_decode", "flint_lmhead_gemv", "flint_stack_table_bytes", "flint_stack_packed_bytes",
             "flint_stack_prepare",
-            "flint_stack_decode", "flint_stack_decode_traced", "flint_stack_decode_batch", "flint_stack_error", "flint_nvfp4_quantize", "flint_nvfp4_dequantize")
+            "flint_stack_decode", "flint_stack_decode_traced", "flint_stack_decode_batch", "flint_stack_error",
+            "flint_nvfp4_quantize", "flint_nvfp4_dequantize",
+            # include/flint_attn.h
+            "flint_attn_workspace_bytes", "flint_attn_decode", "flint_dense_workspace_bytes", "flint_dense_mlp")
 
 
 def lib():
@@ -335,3 +354,65 @@ class Stack:
                                        _ptr(routes), self.ws.data_ptr(), self.ws.numel(), _stream()),
                "flint_stack_decode")
         return logits, argmax
+
+
+# ------------------------------------------------- attention and dense MLP --
+@dataclass
+class AttnWeights:
+    """One attention layer: NVFP4 q [Hq*D][H], k and v [Hkv*D][H], o [H][Hq*D];
+    float32 q_norm, k_norm [D] and sinks [Hq]."""
+    q: NVFP4Tensor
+    k: NVFP4Tensor
+    v: NVFP4Tensor
+    o: NVFP4Tensor
+    q_norm: torch.Tensor
+    k_norm: torch.Tensor
+    sinks: torch.Tensor
+
+    def c(self) -> AttnLayer:
+        return AttnLayer(self.q.c(), self.k.c(), self.v.c(), self.o.c(), self.q_norm.data_ptr(),
+                         self.k_norm.data_ptr(), self.sinks.data_ptr())
+
+
+def attn_dims_struct(hidden=2048, n_q=32, n_kv=4, head_dim=128, window=513, rope=True, theta=10000.0,
+                     eps=1e-6) -> AttnDims:
+    return AttnDims(hidden, n_q, n_kv, head_dim, window, int(rope), theta, eps)
+
+
+def attn_workspace(dims: AttnDims, device="cuda") -> torch.Tensor:
+    n = _lib.flint_attn_workspace_bytes(ctypes.byref(dims))
+    if n == 0:
+        raise ValueError("unsupported attention dims")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def attn_decode(dims: AttnDims, layer: AttnWeights, x: torch.Tensor, pos: int, k_cache: torch.Tensor,
+                v_cache: torch.Tensor, ws: torch.Tensor | None = None, y: torch.Tensor | None = None) -> torch.Tensor:
+    """x float32 [H]; k_cache, v_cache int16/uint16 [Hkv][cap][D] (BF16 bits),
+    updated in place at slot pos % cap -> y float32 [H]"""
+    assert k_cache.shape == v_cache.shape and k_cache.element_size() == 2
+    cap = k_cache.shape[1]
+    ws = attn_workspace(dims, x.device) if ws is None else ws
+    y = torch.empty(dims.hidden, dtype=torch.float32, device=x.device) if y is None else y
+    lc = layer.c()
+    _check(_lib.flint_attn_decode(ctypes.byref(dims), ctypes.byref(lc), x.data_ptr(), pos, k_cache.data_ptr(),
+                                  v_cache.data_ptr(), cap, y.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
+           "flint_attn_decode")
+    return y
+
+
+def dense_mlp(gate: NVFP4Tensor, up: NVFP4Tensor, down: NVFP4Tensor, x: torch.Tensor,
+              ws: torch.Tensor | None = None, y: torch.Tensor | None = None) -> torch.Tensor:
+    """x float32 [B][H] -> y float32 [B][H] = down(silu(gate x) * up x)"""
+    B, H = x.shape
+    width = gate.codes.shape[-2]
+    if ws is None:
+        n = _lib.flint_dense_workspace_bytes(H, width, B)
+        if n == 0:
+            raise ValueError("unsupported dense MLP sizes")
+        ws = torch.empty(n, dtype=torch.uint8, device=x.device)
+    y = torch.empty((B, H), dtype=torch.float32, device=x.device) if y is None else y
+    g, u, d = gate.c(), up.c(), down.c()
+    _check(_lib.flint_dense_mlp(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), H, width, x.data_ptr(), B,
+                                y.data_ptr(), ws.data_ptr(), ws.numel(), _stream()), "flint_dense_mlp")
+    return y

@@ -10,7 +10,7 @@ import torch
 import synth
 
 from . import flint
-from .flint import LayerWeights, NVFP4Tensor
+from .flint import AttnWeights, LayerWeights, NVFP4Tensor
 
 
 def _fill(seed: int, kind: int, expert0: int, n_streams: int, n: int, out: torch.Tensor, std: float) -> torch.Tensor:
@@ -63,6 +63,41 @@ def build_head(vocab: int, hidden: int, seed: int = synth.HEAD_SEED, device="cud
     ws = flint.workspace(flint.OP_QUANTIZE, None, B=1, device=device)
     c, s, ts = _pack(t, 1, vocab, hidden, ws)
     return NVFP4Tensor(c[0], s[0], ts)
+
+
+def _matrix(seed: int, kind: int, rows: int, cols: int, device, ws: torch.Tensor) -> NVFP4Tensor:
+    t = torch.empty(rows * cols, dtype=torch.float32, device=device)
+    _fill(seed, kind, 0, 1, rows * cols, t, synth.WEIGHT_STD)
+    c, s, ts = _pack(t, 1, rows, cols, ws)
+    return NVFP4Tensor(c[0], s[0], ts)
+
+
+def build_attn(d: synth.AttnDims, seed: int, device="cuda") -> AttnWeights:
+    """One attention layer drawn with weight seed `seed` (streams as in ``synth``)."""
+    nq, nk, H = d.n_q * d.head_dim, d.n_kv * d.head_dim, d.hidden
+    ws = flint.workspace(flint.OP_QUANTIZE, None, B=1, device=device)
+    q = _matrix(seed, synth.ATTN_Q, nq, H, device, ws)
+    k = _matrix(seed, synth.ATTN_K, nk, H, device, ws)
+    v = _matrix(seed, synth.ATTN_V, nk, H, device, ws)
+    o = _matrix(seed, synth.ATTN_O, H, nq, device, ws)
+    vec = lambda kind, n, mean, std: synth.normal_device(seed, synth.stream_id(kind), n, torch.empty(
+        n, dtype=torch.float32, device=device), mean=mean, std=std)
+    return AttnWeights(q, k, v, o, vec(synth.Q_NORM, d.head_dim, 1.0, 0.1), vec(synth.K_NORM, d.head_dim, 1.0, 0.1),
+                       vec(synth.SINK, d.n_q, 0.0, 1.0))
+
+
+def kv_cache(d: synth.AttnDims, seed: int, cap: int, kind: int, device="cuda") -> torch.Tensor:
+    """A filled BF16 cache [Hkv][cap][D] (int16 bit patterns), as ``synth.kv_cache_bits``."""
+    n = d.n_kv * cap * d.head_dim
+    t = synth.normal_device(seed, synth.stream_id(kind), n, torch.empty(n, dtype=torch.float32, device=device))
+    return t.to(torch.bfloat16).view(torch.int16).view(d.n_kv, cap, d.head_dim)
+
+
+def build_dense(seed: int, hidden: int, width: int, device="cuda") -> tuple[NVFP4Tensor, NVFP4Tensor, NVFP4Tensor]:
+    ws = flint.workspace(flint.OP_QUANTIZE, None, B=1, device=device)
+    return (_matrix(seed, synth.DENSE_GATE, width, hidden, device, ws),
+            _matrix(seed, synth.DENSE_UP, width, hidden, device, ws),
+            _matrix(seed, synth.DENSE_DOWN, hidden, width, device, ws))
 
 
 def tokens(seeds, hidden: int, device="cuda") -> torch.Tensor:

@@ -7,7 +7,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "flint_moe.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("flint_moe.h", "flint_attn.h")]
 
 
 @pytest.fixture(scope="module")
@@ -20,7 +20,7 @@ def F():
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(flint_[a-z0-9_]+)\s*\(", text)))
 
@@ -141,3 +141,38 @@ def test_quantize_and_stack_rejections(F):
     assert L.flint_workspace_bytes(F.OP_STACK_BATCH, ctypes.byref(full), 0, 150144, 47) == 0
     assert L.flint_stack_decode_batch(None, FAKE, 8, 1e-6, None, FAKE, None, FAKE, 1 << 20, None) == -1
     assert L.flint_stack_decode_batch(ctypes.byref(plan), FAKE, 8, 1e-6, None, FAKE, None, FAKE, 1 << 20, None) == -1
+
+
+def test_attn_and_dense_rejections(F):
+    L = F.lib()
+    d = F.attn_dims_struct()
+    assert L.flint_attn_workspace_bytes(ctypes.byref(d)) > 0
+    assert L.flint_attn_workspace_bytes(ctypes.byref(F.attn_dims_struct(head_dim=64))) == 0
+    assert L.flint_attn_workspace_bytes(ctypes.byref(F.attn_dims_struct(n_q=32, n_kv=2))) == 0  # group 16
+    assert L.flint_attn_workspace_bytes(ctypes.byref(F.attn_dims_struct(n_q=24, n_kv=4))) == 0
+    m = F.NVFP4(FAKE, FAKE, FAKE)
+    lay = F.AttnLayer(m, m, m, m, FAKE, FAKE, FAKE)
+    need = L.flint_attn_workspace_bytes(ctypes.byref(d))
+    call = lambda dims, layer, pos, cap, wsb=need, x=FAKE: L.flint_attn_decode(
+        ctypes.byref(dims), ctypes.byref(layer), x, pos, FAKE, FAKE, cap, FAKE, FAKE, wsb, None)
+    assert call(d, lay, 0, 513, x=None) == -1
+    assert call(d, lay, -1, 513) == -2
+    assert call(d, lay, 0, 512) == -2                      # ring smaller than the window
+    full = F.attn_dims_struct(window=0, rope=False)
+    assert call(full, lay, 100, 100) == -2                 # full context needs cap > pos
+    assert call(d, lay, 0, 513, wsb=need - 1) == -4
+    assert call(d, lay, 0, 513, x=FAKE + 4) == -3
+    assert call(F.attn_dims_struct(rope=True, theta=0.0), lay, 0, 513) == -2
+    assert call(F.attn_dims_struct(head_dim=64), lay, 0, 513) == -8
+    bad = F.AttnLayer(m, m, m, F.NVFP4(FAKE, None, FAKE), FAKE, FAKE, FAKE)
+    assert call(d, bad, 0, 513) == -1
+    # dense MLP
+    assert L.flint_dense_workspace_bytes(2048, 6144, 1) > 0
+    assert L.flint_dense_workspace_bytes(2048, 5000, 1) == 0
+    assert L.flint_dense_workspace_bytes(2048, 6144, 65) == 0
+    dn = lambda width, B, wsb: L.flint_dense_mlp(ctypes.byref(m), ctypes.byref(m), ctypes.byref(m), 2048, width,
+                                                 FAKE, B, FAKE, FAKE, wsb, None)
+    ok = L.flint_dense_workspace_bytes(2048, 6144, 2)
+    assert dn(6144, 0, ok) == -2
+    assert dn(5000, 1, ok) == -8
+    assert dn(6144, 2, ok - 1) == -4
