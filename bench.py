@@ -215,6 +215,101 @@ def bench_router(args) -> int:
     return 0
 
 
+def bench_attn(args) -> int:
+    """One attention layer at decode (flint_attn_decode) for a sliding-window
+    layer and for full-context layers at several context lengths, and the
+    dense MLP (flint_dense_mlp, width 6144).  Each configuration: eager calls
+    timed with HIP events, and the same calls replayed from a HIP graph (no
+    host work between launches; every replay's output is checked against the
+    eager one).  Bytes per call: the NVFP4 weights read once, plus the BF16
+    keys and values of the attended positions."""
+    import torch
+
+    import synth
+    from nvfp4_bit_projection_amd import flint, workload
+
+    torch.cuda.set_device(0)
+    H = 2048
+    steps, warm = args.steps, args.warmup
+    out = []
+
+    def timed(fn, check):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        ref = check().clone()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(steps):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        eager_us = ev0.elapsed_time(ev1) * 1e3 / steps
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for _ in range(16):
+                fn()
+        for _ in range(3):  # replays agree with the eager result
+            g.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(check(), ref):
+                raise RuntimeError("graph replay differs from the eager call")
+        reps = max(1, steps // 16)
+        ev0.record()
+        for _ in range(reps):
+            g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        return eager_us, ev0.elapsed_time(ev1) * 1e3 / (reps * 16)
+
+    nq, nk = 32 * 128, 4 * 128
+    w_bytes = (nq + 2 * nk) * H * 9 // 16 + H * nq * 9 // 16
+    for name, d, ctx in (("sliding513", synth.SLIDING, 4096), ("full_1k", synth.FULL, 1024),
+                         ("full_8k", synth.FULL, 8192), ("full_32k", synth.FULL, 32768),
+                         ("full_128k", synth.FULL, 131072)):
+        W = workload.build_attn(d, 0)
+        cap = 513 if d.window else ctx
+        kc = workload.kv_cache(d, 1, cap, synth.K_CACHE)
+        vc = workload.kv_cache(d, 1, cap, synth.V_CACHE)
+        x = workload.tokens([synth.TOKEN_SEED0], H)[0]
+        dc = flint.attn_dims_struct(H, d.n_q, d.n_kv, d.head_dim, d.window, d.rope, d.theta)
+        ws = flint.attn_workspace(dc)
+        y = torch.empty(H, dtype=torch.float32, device="cuda")
+        pos = ctx - 1
+        n = min(pos + 1, d.window) if d.window else pos + 1
+        nbytes = w_bytes + n * d.n_kv * d.head_dim * 2 * 2
+        eager_us, graph_us = timed(lambda: flint.attn_decode(dc, W, x, pos, kc, vc, ws=ws, y=y), lambda: y)
+        gbs = nbytes / (graph_us * 1e-6) / 1e9
+        log(f"attention {name}: {n} positions, {eager_us:.2f} us eager, {graph_us:.2f} us graph, {gbs:.0f} GB/s")
+        out.append({"layer": name, "positions": n, "bytes": nbytes, "us_eager": round(eager_us, 2),
+                    "us_graph": round(graph_us, 2), "achieved_gbs": round(gbs, 1),
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)})
+        del W, kc, vc, ws
+    g, u, dn = workload.build_dense(0, H, synth.DENSE_WIDTH)
+    x = workload.tokens([synth.TOKEN_SEED0], H)
+    yd = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    wsd = torch.empty(4 * synth.DENSE_WIDTH, dtype=torch.uint8, device="cuda")
+    nbytes = 3 * synth.DENSE_WIDTH * H * 9 // 16
+    eager_us, graph_us = timed(lambda: flint.dense_mlp(g, u, dn, x, ws=wsd, y=yd), lambda: yd)
+    gbs = nbytes / (graph_us * 1e-6) / 1e9
+    log(f"dense MLP 6144: {eager_us:.2f} us eager, {graph_us:.2f} us graph, {gbs:.0f} GB/s")
+    out.append({"layer": "dense_6144", "bytes": nbytes, "us_eager": round(eager_us, 2),
+                "us_graph": round(graph_us, 2), "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    print(json.dumps({"metric": "attention and dense layer us per token (batch 1)", "unit": "us",
+                      "higher_is_better": False, "steps": steps, "warmup": warm, "data": "synthetic",
+                      "config": {"workload": "flint_attn_dense_b1", "q_heads": 32, "kv_heads": 4, "head_dim": 128,
+                                 "hidden": H, "window": 513, "dense_width": synth.DENSE_WIDTH,
+                                 "weights": "nvfp4; bf16 kv cache"},
+                      "peak_gbs": HBM_PEAK_GBS, "layers": out}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,6 +322,8 @@ def main() -> int:
                     help="tokens per step; above 1 the batched step (experts deduplicated per layer) is timed")
     ap.add_argument("--router", action="store_true",
                     help="time the router call alone in its four variants (fp32/BF16 router, softmax/sigmoid)")
+    ap.add_argument("--attn", action="store_true",
+                    help="time one attention layer (sliding and full context) and the dense MLP")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (batch-1 decode; see DESIGN.md for how it would shard)",
@@ -236,6 +333,8 @@ def main() -> int:
         return copy_calib()
     if args.router:
         return bench_router(args)
+    if args.attn:
+        return bench_attn(args)
     if args.batch > 1:
         return bench_batch(args)
 

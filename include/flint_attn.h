@@ -89,8 +89,8 @@ size_t flint_attn_workspace_bytes(const flint_attn_dims* dims /*[host]*/);
  * values (written by earlier calls or by the caller).  Only the slot of `pos`
  * is written.  cap must be >= window (window > 0; a ring of slots) or > pos
  * (window == 0), else FLINT_E_DIMS; pos >= 0.
- * Workspace: flint_attn_workspace_bytes(dims), zero-filled before first use;
- * calls that may overlap need distinct workspaces and caches. */
+ * Workspace: flint_attn_workspace_bytes(dims) (no zero-fill needed); calls
+ * that may overlap need distinct workspaces and caches. */
 int32_t flint_attn_decode(const flint_attn_dims* dims /*[host]*/, const flint_attn_layer* layer /*[host]*/,
                           const float* x, int32_t pos, uint16_t* k_cache, uint16_t* v_cache, int32_t cap, float* y,
                           void* ws, size_t ws_bytes, void* stream);

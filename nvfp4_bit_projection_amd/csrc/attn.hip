@@ -10,14 +10,14 @@
 // key and value per token and layer; "Built from scratch?": dense MLP layers
 // 6,144 wide].
 //
-// One attention layer at batch 1 is three launches:
-//   k_gemv (q, k, v rows of three NVFP4 matrices, K = 2048)
-//   k_attn (grid: context chunks x key/value heads) -- head norms and RoPE of
-//          the group's queries, the current key/value written to the cache,
-//          flash-decoding over 64-position sub-chunks staged in LDS, then the
-//          last workgroup of each key/value head merges the chunks with the
-//          sinks
-//   k_gemv (o rows, K = n_q * 128)
+// One attention layer at batch 1 is four launches:
+//   k_gemv       q, k, v rows of three NVFP4 matrices, K = 2048
+//   k_attn       grid: context chunks x key/value heads -- head norms and
+//                RoPE of the group's queries, the current key/value written
+//                to the cache, flash-decoding over 64-position sub-chunks
+//                staged in LDS; one record (max, sum, o) per chunk and head
+//   k_attn_merge one workgroup per query head: the chunk records and the sink
+//   k_gemv       o rows, K = n_q * 128
 // Every stage is bound by HBM bandwidth: weights and cache rows are read
 // once per token with 128-bit loads.
 #include <float.h>
@@ -33,7 +33,9 @@ namespace {
 constexpr int kHid = 2048;        // the hidden size with kernels
 constexpr int kD = 128;           // head dimension
 constexpr int kSub = 64;          // positions per sub-chunk: one per lane
-constexpr int kMaxChunks = 64;    // context chunks per key/value head
+constexpr int kMaxChunks = 256;   // context chunks per key/value head
+constexpr int kKRow = 65;         // LDS key row stride in dwords: lane t reads bank (t + dp) mod 64
+static_assert(kMaxChunks % 64 == 0, "the merge holds kMaxChunks / 64 chunks per lane");
 constexpr int kMaxGroup = 8;      // query heads per key/value head
 constexpr int kPart = kD + 2;     // chunk record: running max, sum, o[128]
 constexpr int kMaxDenseB = 64;
@@ -172,22 +174,20 @@ struct AttnArgs {
   int nchunks;  // chunks per key/value head (= grid.x)
   int rope;
   float eps;
-  double log2_theta;
+  float rope_cos[kD / 2], rope_sin[kD / 2];  // angle of pair i at pos (host, double)
   float* part;  // [n_kv][kMaxGroup][kMaxChunks][kPart]
-  float* o;     // [n_q*D]
-  uint32_t* tickets;  // [n_kv], zero between calls
 };
 
 // grid (nchunks, n_kv), 256 threads.  Chunk c covers sub-chunks
 // [c*per, min((c+1)*per, n_sub)) of 64 positions from `first`; the last chunk
-// holds `pos`.  Wave w owns query heads 2w and 2w+1 of the group.
+// holds `pos`.  Wave w owns query heads 2w and 2w+1 of the group (a second
+// head past the group is computed on a copy of the first and dropped).
 __global__ __launch_bounds__(256) void k_attn(AttnArgs A) {
-  __shared__ uint32_t sKt[64 * kSub];    // key BF16 pairs, [dim pair][position]
+  __shared__ uint32_t sK[kSub * kKRow];  // key BF16 pairs, [position][dim pair], padded rows
   __shared__ uint32_t sV[kSub * 64];     // value BF16 pairs, [position][dim pair]
-  __shared__ float sq[kMaxGroup][kD];    // queries: normalised, rotated, / sqrt(D)
-  __shared__ float sp[kMaxGroup][kSub];  // probabilities of the current sub-chunk
-  __shared__ __align__(16) uint16_t scur[2][kD];  // this token's key and value (BF16)
-  __shared__ uint32_t last;
+  __shared__ __align__(16) float sq[kMaxGroup][kD];    // queries: normalised, rotated, / sqrt(D)
+  __shared__ __align__(16) float sp[kMaxGroup][kSub];  // probabilities of the current sub-chunk
+  __shared__ __align__(16) uint16_t scur[2][kD];       // this token's key and value (BF16)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = blockIdx.y, c = blockIdx.x;
   const int nq = A.n_q * kD, nk = A.n_kv * kD;
@@ -216,14 +216,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs A) {
   };
   load_sub(s_begin);
 
-  // RoPE angle of the pair (lane, lane + 64): pos * theta^(-2 lane / D), in
-  // double so that large positions keep their phase
-  float cs = 1.0f, sn = 0.0f;
-  if (A.rope) {
-    const double ang = (double)A.pos * exp2(-2.0 * lane / kD * A.log2_theta);
-    cs = (float)cos(ang);
-    sn = (float)sin(ang);
-  }
+  const float cs = A.rope ? A.rope_cos[lane] : 1.0f, sn = A.rope ? A.rope_sin[lane] : 0.0f;
   const float qscale = 0.08838834764831845f;  // 1 / sqrt(128)
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
@@ -266,6 +259,8 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs A) {
     scur[wv][lane + 64] = bb;
   }
 
+  const int h0 = min(2 * wv, A.group - 1), h1 = min(2 * wv + 1, A.group - 1);
+  const bool act = 2 * wv < A.group;  // wave-uniform
   float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
   float o_run[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
   for (int s = s_begin; s < s_end; ++s) {
@@ -281,52 +276,66 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs A) {
         vw = *reinterpret_cast<const uint4*>(&scur[1][seg * 8]);
       }
       *reinterpret_cast<uint4*>(&sV[r * 64 + seg * 4]) = vw;
-      sKt[(seg * 4 + 0) * kSub + r] = kw.x;
-      sKt[(seg * 4 + 1) * kSub + r] = kw.y;
-      sKt[(seg * 4 + 2) * kSub + r] = kw.z;
-      sKt[(seg * 4 + 3) * kSub + r] = kw.w;
+      sK[r * kKRow + seg * 4 + 0] = kw.x;
+      sK[r * kKRow + seg * 4 + 1] = kw.y;
+      sK[r * kKRow + seg * 4 + 2] = kw.z;
+      sK[r * kKRow + seg * 4 + 3] = kw.w;
     }
     if (s + 1 < s_end) load_sub(s + 1);
     __syncthreads();
-    // scores s_t = q . K_t (lane = position t), then the running softmax
+    if (act) {
+      // scores of both heads at position t = lane: four independent chains
+      float a0 = 0.0f, a1 = 0.0f, b0 = 0.0f, b1 = 0.0f;
+      const float2* q0 = reinterpret_cast<const float2*>(sq[h0]);
+      const float2* q1 = reinterpret_cast<const float2*>(sq[h1]);
+#pragma unroll 16
+      for (int dp = 0; dp < 64; ++dp) {
+        const uint32_t w = sK[lane * kKRow + dp];
+        const float k0 = bf16_lo(w), k1 = bf16_hi(w);
+        const float2 qa = q0[dp], qb = q1[dp];
+        a0 = __builtin_fmaf(qa.x, k0, a0);
+        a1 = __builtin_fmaf(qa.y, k1, a1);
+        b0 = __builtin_fmaf(qb.x, k0, b0);
+        b1 = __builtin_fmaf(qb.y, k1, b1);
+      }
+      const float sc[2] = {lane < nvalid ? a0 + a1 : -INFINITY, lane < nvalid ? b0 + b1 : -INFINITY};
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int hh = 2 * wv + k;
-      if (hh < A.group) {
-        float acc = 0.0f;
-#pragma unroll 8
-        for (int dp = 0; dp < 64; ++dp) {
-          const uint32_t w = sKt[dp * kSub + lane];
-          acc = __builtin_fmaf(sq[hh][2 * dp], bf16_lo(w), acc);
-          acc = __builtin_fmaf(sq[hh][2 * dp + 1], bf16_hi(w), acc);
-        }
-        const float sc = lane < nvalid ? acc : -INFINITY;
-        const float m_new = fmaxf(m_run[k], wave_max(sc));
-        const float p = lane < nvalid ? __expf(sc - m_new) : 0.0f;
+      for (int k = 0; k < 2; ++k) {
+        const float m_new = fmaxf(m_run[k], wave_max(sc[k]));
+        const float p = lane < nvalid ? __expf(sc[k] - m_new) : 0.0f;
         const float alpha = (m_run[k] == -INFINITY) ? 0.0f : __expf(m_run[k] - m_new);
         l_run[k] = l_run[k] * alpha + wave_sum(p);
         o_run[k][0] *= alpha;
         o_run[k][1] *= alpha;
         m_run[k] = m_new;
-        sp[hh][lane] = p;
+        sp[2 * wv + k][lane] = p;  // rows of this wave only
       }
     }
     __syncthreads();
-    // o += p_t V_t: lane owns dims 2 lane, 2 lane + 1
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int hh = 2 * wv + k;
-      if (hh < A.group) {
-        float o0 = o_run[k][0], o1 = o_run[k][1];
-        for (int t = 0; t < nvalid; ++t) {
-          const uint32_t w = sV[t * 64 + lane];
-          const float p = sp[hh][t];
-          o0 = __builtin_fmaf(p, bf16_lo(w), o0);
-          o1 = __builtin_fmaf(p, bf16_hi(w), o1);
-        }
-        o_run[k][0] = o0;
-        o_run[k][1] = o1;
+    if (act) {
+      // o += p_t V_t over all 64 rows (p = 0 and V = 0 past the valid ones);
+      // lane owns dims 2 lane, 2 lane + 1
+      float x0 = 0.0f, x1 = 0.0f, y0 = 0.0f, y1 = 0.0f, z0 = 0.0f, z1 = 0.0f, w0 = 0.0f, w1 = 0.0f;
+      const float4* p0v = reinterpret_cast<const float4*>(sp[2 * wv]);
+      const float4* p1v = reinterpret_cast<const float4*>(sp[2 * wv + 1]);
+#pragma unroll 4
+      for (int t4 = 0; t4 < kSub / 4; ++t4) {
+        const float4 pa = p0v[t4], pb = p1v[t4];
+        const uint32_t v0 = sV[(4 * t4 + 0) * 64 + lane], v1 = sV[(4 * t4 + 1) * 64 + lane];
+        const uint32_t v2 = sV[(4 * t4 + 2) * 64 + lane], v3 = sV[(4 * t4 + 3) * 64 + lane];
+        x0 = __builtin_fmaf(pa.x, bf16_lo(v0), x0); x1 = __builtin_fmaf(pa.x, bf16_hi(v0), x1);
+        y0 = __builtin_fmaf(pa.y, bf16_lo(v1), y0); y1 = __builtin_fmaf(pa.y, bf16_hi(v1), y1);
+        x0 = __builtin_fmaf(pa.z, bf16_lo(v2), x0); x1 = __builtin_fmaf(pa.z, bf16_hi(v2), x1);
+        y0 = __builtin_fmaf(pa.w, bf16_lo(v3), y0); y1 = __builtin_fmaf(pa.w, bf16_hi(v3), y1);
+        z0 = __builtin_fmaf(pb.x, bf16_lo(v0), z0); z1 = __builtin_fmaf(pb.x, bf16_hi(v0), z1);
+        w0 = __builtin_fmaf(pb.y, bf16_lo(v1), w0); w1 = __builtin_fmaf(pb.y, bf16_hi(v1), w1);
+        z0 = __builtin_fmaf(pb.z, bf16_lo(v2), z0); z1 = __builtin_fmaf(pb.z, bf16_hi(v2), z1);
+        w0 = __builtin_fmaf(pb.w, bf16_lo(v3), w0); w1 = __builtin_fmaf(pb.w, bf16_hi(v3), w1);
       }
+      o_run[0][0] += x0 + y0;
+      o_run[0][1] += x1 + y1;
+      o_run[1][0] += z0 + w0;
+      o_run[1][1] += z1 + w1;
     }
   }
   // chunk records
@@ -342,49 +351,79 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs A) {
       *reinterpret_cast<float2*>(P + 2 + 2 * lane) = make_float2(o_run[k][0], o_run[k][1]);
     }
   }
-  __syncthreads();
-  if (tid == 0) {
-    __threadfence();
-    last = (atomicAdd(&A.tickets[g], 1u) == (uint32_t)A.nchunks - 1);
-  }
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  // the last chunk of this key/value head merges all chunks with the sink
+}
+
+// grid (n_q), 256 threads: query head h merges its chunk records with the
+// sink.  All loads are issued at once: wave w takes chunks w, w+4, ... for
+// the dim pair of its lane; lanes over chunks (kMaxChunks / 64 each) give the
+// maximum M, the weights f_c = e^(m_c - M) and Z; the four waves' sums meet
+// in LDS.
+template <int NC>  // NC >= nchunks: 64 or kMaxChunks
+__global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ part, const float* __restrict__ sinks,
+                                                    int group, int nchunks, float* __restrict__ o) {
+  constexpr int kPerLane = NC / 64;
+  __shared__ float2 sred[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int h = blockIdx.x, g = h / group, hh = h % group;
+  const float* P0 = part + ((size_t)g * kMaxGroup + hh) * kMaxChunks * kPart;
+  float2 ov[NC / 4];
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int hh = 2 * wv + k;
-    if (hh < A.group) {
-      const int h = g * A.group + hh;
-      const float sink = A.sinks[h];
-      const float* P0 = A.part + ((size_t)g * kMaxGroup + hh) * kMaxChunks * kPart;
-      float M = sink;
-      for (int cc = 0; cc < A.nchunks; ++cc) M = fmaxf(M, ld_dev_f32(P0 + cc * kPart));
-      float Z = __expf(sink - M), o0 = 0.0f, o1 = 0.0f;
-      for (int cc = 0; cc < A.nchunks; ++cc) {
-        const float* P = P0 + cc * kPart;
-        const float f = __expf(ld_dev_f32(P) - M);
-        Z = __builtin_fmaf(f, ld_dev_f32(P + 1), Z);
-        o0 = __builtin_fmaf(f, ld_dev_f32(P + 2 + 2 * lane), o0);
-        o1 = __builtin_fmaf(f, ld_dev_f32(P + 3 + 2 * lane), o1);
-      }
-      A.o[h * kD + 2 * lane] = o0 / Z;
-      A.o[h * kD + 2 * lane + 1] = o1 / Z;
-    }
+  for (int i = 0; i < NC / 4; ++i) {
+    const int cc = wv + 4 * i;
+    ov[i] = cc < nchunks ? *reinterpret_cast<const float2*>(P0 + cc * kPart + 2 + 2 * lane) : make_float2(0.f, 0.f);
   }
-  if (tid == 0) A.tickets[g] = 0;  // leave the workspace zeroed for the next call
+  float m[kPerLane], l[kPerLane];
+  const float sink = sinks[h];
+  float M = sink;
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const int cc = lane + 64 * i;
+    m[i] = cc < nchunks ? P0[cc * kPart] : -INFINITY;
+    l[i] = cc < nchunks ? P0[cc * kPart + 1] : 0.0f;
+    M = fmaxf(M, m[i]);
+  }
+  M = wave_max(M);
+  float f[kPerLane], zl = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    f[i] = (lane + 64 * i) < nchunks ? __expf(m[i] - M) : 0.0f;
+    zl = __builtin_fmaf(f[i], l[i], zl);
+  }
+  const float Z = wave_sum(zl) + __expf(sink - M);
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NC / 4; ++i) {
+    const int cc = wv + 4 * i;  // wave-uniform
+    float fi = f[0];
+#pragma unroll
+    for (int q = 1; q < kPerLane; ++q)
+      if ((cc >> 6) == q) fi = f[q];
+    const float fc = lane_f32(fi, cc & 63);
+    a0 = __builtin_fmaf(fc, ov[i].x, a0);
+    a1 = __builtin_fmaf(fc, ov[i].y, a1);
+  }
+  sred[wv][lane] = make_float2(a0, a1);
+  __syncthreads();
+  if (wv == 0) {
+    float2 t = sred[0][lane];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      t.x += sred[w][lane].x;
+      t.y += sred[w][lane].y;
+    }
+    *reinterpret_cast<float2*>(o + h * kD + 2 * lane) = make_float2(t.x / Z, t.y / Z);
+  }
 }
 
 // --------------------------------------------------------- host helpers --
 struct AttnWs {
-  size_t qkv, o, part, tickets, total;
+  size_t qkv, o, part, total;
   explicit AttnWs(const flint_attn_dims& d) {
     const size_t nq = (size_t)d.n_q_heads * kD, nk = (size_t)d.n_kv_heads * kD;
     size_t off = 0;
     qkv = off; off = al256(off + 4 * (nq + 2 * nk));
     o = off; off = al256(off + 4 * nq);
     part = off; off = al256(off + 4 * (size_t)d.n_kv_heads * kMaxGroup * kMaxChunks * kPart);
-    tickets = off; off = al256(off + 4 * (size_t)d.n_kv_heads);
     total = off;
   }
 };
@@ -475,11 +514,19 @@ int32_t flint_attn_decode(const flint_attn_dims* dims, const flint_attn_layer* l
   A.nchunks = (A.n_sub + A.per - 1) / A.per;
   A.rope = d.rope;
   A.eps = d.eps;
-  A.log2_theta = d.rope ? log2((double)d.rope_theta) : 0.0;
+  for (int i = 0; i < kD / 2; ++i) {
+    const double ang = d.rope ? (double)pos * pow((double)d.rope_theta, -2.0 * i / kD) : 0.0;
+    A.rope_cos[i] = (float)cos(ang);
+    A.rope_sin[i] = (float)sin(ang);
+  }
   A.part = reinterpret_cast<float*>(base + w.part);
-  A.o = o;
-  A.tickets = reinterpret_cast<uint32_t*>(base + w.tickets);
   k_attn<<<dim3(A.nchunks, d.n_kv_heads), 256, 0, s>>>(A);
+  e = hipGetLastError();
+  if (e != hipSuccess) return api_hip_fail(e);
+  if (A.nchunks <= 64)
+    k_attn_merge<64><<<d.n_q_heads, 256, 0, s>>>(A.part, layer->sinks, A.group, A.nchunks, o);
+  else
+    k_attn_merge<kMaxChunks><<<d.n_q_heads, 256, 0, s>>>(A.part, layer->sinks, A.group, A.nchunks, o);
   e = hipGetLastError();
   if (e != hipSuccess) return api_hip_fail(e);
 
