@@ -71,6 +71,12 @@ def lib():
         L.oracle_attn_decode.argtypes = ([ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_double] + [_P] * 7
                                          + [_I64, _P, _P, _I64, _P, _P, _P, ctypes.c_int])
         L.oracle_attn_decode.restype = ctypes.c_int
+        L.oracle_int4_quantize.argtypes = [_P, _I64, _I64, _P, _P, _P]
+        L.oracle_int4_quantize.restype = None
+        L.oracle_int4_dequantize.argtypes = [_P, _P, _P, _I64, _I64, _P]
+        L.oracle_int4_dequantize.restype = None
+        L.oracle_int4_gemv.argtypes = [_P, _P, _P, _I64, _I64, _P, _P, ctypes.c_int]
+        L.oracle_int4_gemv.restype = None
         L.oracle_rms_inv.argtypes = [_P, _I64, ctypes.c_double]
         L.oracle_rms_inv.restype = ctypes.c_double
         L.oracle_swiglu_expert.argtypes = [_P, _P, ctypes.c_float, _P, _P, ctypes.c_float, _P, _P, ctypes.c_float,
@@ -281,3 +287,42 @@ def attn_decode(L: AttnLayer, x: np.ndarray, pos: int, k_cache: np.ndarray, v_ca
     if rc != 0:
         raise ValueError("attn_decode: cache too small for the window or position")
     return y, o, qkv
+
+
+# ------------------------------------------------------ INT4 affine codec --
+class INT4(NamedTuple):
+    """Group-64 affine INT4: codes uint8 [rows][cols/2] (element 2j in the low
+    nibble of byte j), BF16 scales and offsets uint16 [rows][cols/64]."""
+    codes: np.ndarray
+    scales: np.ndarray
+    biases: np.ndarray
+    rows: int
+    cols: int
+
+
+def int4_quantize(w: np.ndarray) -> INT4:
+    w = _c(w, np.float32)
+    rows, cols = w.shape
+    assert cols % 64 == 0
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.empty((rows, cols // 64), np.uint16)
+    biases = np.empty((rows, cols // 64), np.uint16)
+    lib().oracle_int4_quantize(w.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data, biases.ctypes.data)
+    return INT4(codes, scales, biases, rows, cols)
+
+
+def int4_dequantize(q: INT4) -> np.ndarray:
+    out = np.empty((q.rows, q.cols), np.float32)
+    c, s, b = _c(q.codes, np.uint8), _c(q.scales, np.uint16), _c(q.biases, np.uint16)
+    lib().oracle_int4_dequantize(c.ctypes.data, s.ctypes.data, b.ctypes.data, q.rows, q.cols, out.ctypes.data)
+    return out
+
+
+def int4_gemv(q: INT4, x: np.ndarray) -> np.ndarray:
+    x = _c(x, np.float64)
+    assert x.shape == (q.cols,)
+    y = np.empty(q.rows, np.float64)
+    c, s, b = _c(q.codes, np.uint8), _c(q.scales, np.uint16), _c(q.biases, np.uint16)
+    lib().oracle_int4_gemv(c.ctypes.data, s.ctypes.data, b.ctypes.data, q.rows, q.cols, x.ctypes.data,
+                           y.ctypes.data, 1)
+    return y

@@ -505,3 +505,83 @@ int oracle_attn_decode(int H, int Hq, int Hkv, int D, int window, int rope, doub
   free(o);
   return 0;
 }
+
+/* ------------------------------------------------------ INT4 affine codec -- */
+
+/* Group-64 affine INT4 [P3 "Why active parameters set the speed": Recursive's
+ * Apple build stores each group of 64 weights as 4-bit codes plus a BF16
+ * scale and a BF16 offset, 4.5 bits per weight].  Reading (min-max affine
+ * quantisation, the pages give no rule): for each group of 64 consecutive
+ * values along a row, in fp32 arithmetic,
+ *   scale  s = bf16(fl32((max - min) / 15)),  offset b = bf16(min),
+ *   code   q = clamp(rint(fl32(fl32(w - b) / s)), 0, 15), or 0 when s == 0,
+ * with BF16 rounding to nearest even and rint ties to even.  Codes are packed
+ * two per byte, element 2j in the low nibble of byte j.  The decisions are
+ * taken in fp32, the precision the device quantiser uses. */
+void oracle_int4_quantize(const float* w, int64_t rows, int64_t cols, uint8_t* codes, uint16_t* scales,
+                          uint16_t* biases) {
+  int64_t groups = cols / 64;
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t g = 0; g < groups; ++g) {
+      const float* v = w + r * cols + g * 64;
+      float lo = v[0], hi = v[0];
+      for (int i = 1; i < 64; ++i) {
+        if (v[i] < lo) lo = v[i];
+        if (v[i] > hi) hi = v[i];
+      }
+      float range = hi - lo;
+      float sf = range / 15.0f;
+      uint16_t sb = oracle_bf16_encode((double)sf), bb = oracle_bf16_encode((double)lo);
+      double sv, bv;
+      oracle_bf16_decode(&sb, 1, &sv);
+      oracle_bf16_decode(&bb, 1, &bv);
+      scales[r * groups + g] = sb;
+      biases[r * groups + g] = bb;
+      for (int i = 0; i < 64; ++i) {
+        int q = 0;
+        if (sv != 0.0) {
+          float t = (v[i] - (float)bv) / (float)sv;
+          float rq = rintf(t);
+          q = rq < 0.0f ? 0 : rq > 15.0f ? 15 : (int)rq;
+        }
+        int64_t k = g * 64 + i;
+        uint8_t* byte = codes + r * (cols / 2) + k / 2;
+        if (k % 2 == 0)
+          *byte = (uint8_t)((*byte & 0xF0) | q);
+        else
+          *byte = (uint8_t)((*byte & 0x0F) | (q << 4));
+      }
+    }
+  }
+}
+
+/* Dequantised value fl32(s * q + b): s * q is exact, the sum rounds once. */
+void oracle_int4_dequantize(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t rows,
+                            int64_t cols, float* out) {
+  int64_t groups = cols / 64;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t g = 0; g < groups; ++g) {
+      double s, b;
+      oracle_bf16_decode(&scales[r * groups + g], 1, &s);
+      oracle_bf16_decode(&biases[r * groups + g], 1, &b);
+      for (int64_t k = g * 64; k < g * 64 + 64; ++k) {
+        uint8_t byte = codes[r * (cols / 2) + k / 2];
+        int q = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+        out[r * cols + k] = (float)(s * q + b);
+      }
+    }
+}
+
+/* y = W x over the dequantised INT4 matrix, double accumulation. */
+void oracle_int4_gemv(const uint8_t* codes, const uint16_t* scales, const uint16_t* biases, int64_t rows,
+                      int64_t cols, const double* x, double* y, int nthreads) {
+  float* row = (float*)malloc(sizeof(float) * (size_t)cols);
+  (void)nthreads;
+  for (int64_t r = 0; r < rows; ++r) {
+    oracle_int4_dequantize(codes + r * (cols / 2), scales + r * (cols / 64), biases + r * (cols / 64), 1, cols, row);
+    double acc = 0.0;
+    for (int64_t k = 0; k < cols; ++k) acc += (double)row[k] * x[k];
+    y[r] = acc;
+  }
+  free(row);
+}
