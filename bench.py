@@ -310,6 +310,73 @@ def bench_attn(args) -> int:
     return 0
 
 
+def bench_int4(args) -> int:
+    """The 150,144 x 2,048 output head as group-64 affine INT4 (BF16 scale and
+    offset) against the same head as NVFP4: one GEMV + argmax per token
+    (flint_int4_gemv, flint_lmhead_gemv), timed from HIP-graph replays.  Both
+    formats read 1,152 bytes per row."""
+    import torch
+
+    import synth
+    from nvfp4_bit_projection_amd import flint, workload
+
+    torch.cuda.set_device(0)
+    V, H = 150144, 2048
+    w = torch.empty(V * H, dtype=torch.float32, device="cuda")
+    synth.normal_device(synth.HEAD_SEED, synth.stream_id(synth.HEAD), V * H, w, std=synth.WEIGHT_STD)
+    q4 = flint.int4_quantize(w.view(V, H))
+    del w
+    head = workload.build_head(V, H)
+    x = workload.tokens([synth.TOKEN_SEED0], H)
+    nbytes = V * (H // 2 + H // 16)
+    ws4 = torch.zeros(flint.lib().flint_int4_gemv_workspace_bytes(1), dtype=torch.uint8, device="cuda")
+    y4 = torch.empty((1, V), dtype=torch.float32, device="cuda")
+    a4 = torch.empty(1, dtype=torch.int32, device="cuda")
+    wsn = flint.workspace(flint.OP_LMHEAD, None, 1, V)
+    yn = torch.empty((1, V), dtype=torch.float32, device="cuda")
+    an = torch.empty(1, dtype=torch.int32, device="cuda")
+    out = []
+    for name, fn, check in (
+            ("int4_g64_head", lambda: flint.int4_gemv(q4, x, ws=ws4, y=y4, argmax=a4), lambda: y4),
+            ("int4_g64_gemv_no_argmax", lambda: flint.int4_gemv(q4, x, want_argmax=False, ws=ws4, y=y4), lambda: y4),
+            ("nvfp4_head", lambda: flint.lmhead(head, V, x, ws=wsn, logits=yn, argmax=an), lambda: yn)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        ref = check().clone() if check else None
+        with torch.cuda.graph(g):
+            for _ in range(16):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        if check is not None and not torch.equal(check(), ref):
+            raise RuntimeError("graph replay differs from the eager call")
+        reps = max(1, args.steps // 16)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(reps):
+            g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / (reps * 16)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        log(f"{name}: {us:.2f} us per token, {gbs:.0f} GB/s")
+        out.append({"kernel": name, "us": round(us, 2), "bytes": nbytes, "achieved_gbs": round(gbs, 1),
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    print(json.dumps({"metric": "output head GEMV + argmax us per token (batch 1)", "unit": "us",
+                      "higher_is_better": False, "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
+                      "config": {"workload": "lmhead_v150144_int4_vs_nvfp4", "vocab": V, "hidden": H},
+                      "peak_gbs": HBM_PEAK_GBS, "heads": out}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -324,6 +391,8 @@ def main() -> int:
                     help="time the router call alone in its four variants (fp32/BF16 router, softmax/sigmoid)")
     ap.add_argument("--attn", action="store_true",
                     help="time one attention layer (sliding and full context) and the dense MLP")
+    ap.add_argument("--int4", action="store_true",
+                    help="time the output head as group-64 affine INT4 against the NVFP4 head")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (batch-1 decode; see DESIGN.md for how it would shard)",
@@ -335,6 +404,8 @@ def main() -> int:
         return bench_router(args)
     if args.attn:
         return bench_attn(args)
+    if args.int4:
+        return bench_int4(args)
     if args.batch > 1:
         return bench_batch(args)
 

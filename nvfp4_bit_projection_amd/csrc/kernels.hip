@@ -77,15 +77,13 @@ __device__ __forceinline__ float router_dot32(const uint16_t* row, int lane, con
   return acc;
 }
 
-// grid (ceil(E/4), B), 256 threads: one router row per wave, then the last
-// workgroup of each token (atomic ticket) selects the top k in one wave.
-// Weights: sigmoid == 0, softmax over the chosen logits; sigmoid != 0, the
-// chosen sigmoid scores over their sum.
+// grid (ceil(E/4), B), 256 threads: one router row per wave.  The top k is
+// chosen by k_topk (next launch): a last-workgroup ticket would need a
+// device-scope release fence in every workgroup, each writing back the XCD's
+// L2.
 template <typename RT>
 __global__ __launch_bounds__(256) void k_route(const RT* __restrict__ router, int E, const float* __restrict__ x,
-                                               float norm_eps, int k, int sigmoid, float* __restrict__ logits,
-                                               int32_t* __restrict__ idx_out, float* __restrict__ w_out,
-                                               uint32_t* __restrict__ tickets) {
+                                               float norm_eps, float* __restrict__ logits) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, b = blockIdx.y;
   float xv[32];
   load_x32(x + (size_t)b * kHidden, lane, norm_eps, xv);
@@ -95,22 +93,21 @@ __global__ __launch_bounds__(256) void k_route(const RT* __restrict__ router, in
     acc = wave_sum(acc);
     if (lane == 0) logits[(size_t)b * E + e] = acc;
   }
-  __shared__ uint32_t last;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    last = (atomicAdd(&tickets[b], 1u) == gridDim.x - 1);
-  }
-  __syncthreads();
-  if (!last || wv != 0) return;
-  __threadfence();
-  // top-k over E <= 256 logits: 4 per lane, k rounds of a (value, index) max
+}
+
+// grid (B), 64 threads: the k largest of E <= 256 logits (4 per lane, k
+// rounds of a (value, index) max; ties to the lower index), ordered by logit,
+// and their weights: sigmoid == 0, softmax over the chosen logits; sigmoid !=
+// 0, the chosen sigmoid scores over their sum.
+__global__ __launch_bounds__(64) void k_topk(const float* __restrict__ logits, int E, int k, int sigmoid,
+                                             int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+  const int lane = threadIdx.x, b = blockIdx.x;
   float v[4];
   int id[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     id[j] = lane + 64 * j;
-    v[j] = (id[j] < E) ? ld_dev_f32(&logits[(size_t)b * E + id[j]]) : -FLT_MAX;
+    v[j] = (id[j] < E) ? logits[(size_t)b * E + id[j]] : -FLT_MAX;
     if (id[j] >= E) id[j] = INT_MAX;
   }
   float top_v[kMaxTopK];
@@ -139,7 +136,6 @@ __global__ __launch_bounds__(256) void k_route(const RT* __restrict__ router, in
       idx_out[b * k + r] = top_i[r];
       w_out[b * k + r] = sc[r] / z;
     }
-    tickets[b] = 0;  // leave the workspace zeroed for the next call
   }
 }
 
@@ -257,13 +253,16 @@ __global__ __launch_bounds__(256) void k_down(flint_moe_layer L, int I, int k, i
 // -------------------------------------------------------------- lm head --
 // grid (kHeadBlocks, B), 256 threads.  Each wave streams rows r0.. r0+R-1,
 // then jumps by the total wave count; logits and a running (max, first index)
-// per wave; the last workgroup of each token reduces the per-block maxima.
+// per wave; each workgroup writes its best, and k_head_argmax (next launch)
+// reduces them.  (A last-workgroup ticket would need a device-scope release
+// fence in every workgroup, which writes back the XCD's L2 each time: it cost
+// more than the GEMV.)
 constexpr int kHeadRows = 4;
 __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
                                                 const float* __restrict__ tscale, int vocab,
                                                 const float* __restrict__ x, float norm_eps,
                                                 float* __restrict__ logits, int32_t* __restrict__ argmax,
-                                                HeadPartial* __restrict__ partials, uint32_t* __restrict__ tickets) {
+                                                HeadPartial* __restrict__ partials) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, b = blockIdx.y;
   float xv[32];
   load_x32(x + (size_t)b * kHidden, lane, norm_eps, xv);
@@ -293,7 +292,6 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ code
   }
   __shared__ float sv[4];
   __shared__ int si[4];
-  __shared__ uint32_t last;
   if (lane == 0) { sv[wv] = best; si[wv] = besti; }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -302,25 +300,21 @@ __global__ __launch_bounds__(256) void k_lmhead(const uint8_t* __restrict__ code
     for (int w = 1; w < 4; ++w)
       if (sv[w] > bv || (sv[w] == bv && si[w] < bi)) { bv = sv[w]; bi = si[w]; }
     partials[(size_t)b * gridDim.x + blockIdx.x] = HeadPartial{bv, bi};
-    __threadfence();
-    last = (atomicAdd(&tickets[b], 1u) == gridDim.x - 1);
   }
-  __syncthreads();
-  if (!last || wv != 0) return;
-  __threadfence();
+}
+
+// grid (B), 64 threads: the first index of the largest of n block maxima
+__global__ __launch_bounds__(64) void k_head_argmax(const HeadPartial* __restrict__ partials, int n,
+                                                    int32_t* __restrict__ argmax) {
+  const int lane = threadIdx.x, b = blockIdx.x;
   float bv = -FLT_MAX;
   int bi = INT_MAX;
-  for (int i = lane; i < (int)gridDim.x; i += 64) {
-    const HeadPartial* hp = &partials[(size_t)b * gridDim.x + i];
-    const float v = ld_dev_f32(&hp->value);
-    const int id = (int)ld_dev_u32(reinterpret_cast<const uint32_t*>(&hp->index));
-    if (v > bv || (v == bv && id < bi)) { bv = v; bi = id; }
+  for (int i = lane; i < n; i += 64) {
+    const HeadPartial hp = partials[(size_t)b * n + i];
+    if (hp.value > bv || (hp.value == bv && hp.index < bi)) { bv = hp.value; bi = hp.index; }
   }
   wave_argmax(bv, bi);
-  if (lane == 0) {
-    argmax[b] = bi;
-    tickets[b] = 0;
-  }
+  if (lane == 0) argmax[b] = bi;
 }
 
 // ------------------------------------------------------------- quantiser --
@@ -442,20 +436,26 @@ __global__ void k_copy_f32(const float* __restrict__ s, float* __restrict__ d, i
 // --------------------------------------------------------------- launchers --
 hipError_t launch_route(const flint_moe_dims& d, const float* router, const float* x, int B, float norm_eps,
                         float* logits, int32_t* idx, float* w, uint32_t* tickets, hipStream_t s) {
+  (void)tickets;
   dim3 grid((d.n_experts + 3) / 4, B);
-  k_route<float><<<grid, 256, 0, s>>>(router, d.n_experts, x, norm_eps, d.top_k, 0, logits, idx, w, tickets);
+  k_route<float><<<grid, 256, 0, s>>>(router, d.n_experts, x, norm_eps, logits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_topk<<<B, 64, 0, s>>>(logits, d.n_experts, d.top_k, 0, idx, w);
   return hipGetLastError();
 }
 
 hipError_t launch_route_ex(const flint_moe_dims& d, const void* router, bool bf16, bool sigmoid, const float* x,
                            int B, float* logits, int32_t* idx, float* w, uint32_t* tickets, hipStream_t s) {
+  (void)tickets;
   dim3 grid((d.n_experts + 3) / 4, B);
   if (bf16)
-    k_route<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(router), d.n_experts, x, -1.0f, d.top_k,
-                                           sigmoid ? 1 : 0, logits, idx, w, tickets);
+    k_route<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(router), d.n_experts, x, -1.0f, logits);
   else
-    k_route<float><<<grid, 256, 0, s>>>(static_cast<const float*>(router), d.n_experts, x, -1.0f, d.top_k,
-                                        sigmoid ? 1 : 0, logits, idx, w, tickets);
+    k_route<float><<<grid, 256, 0, s>>>(static_cast<const float*>(router), d.n_experts, x, -1.0f, logits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_topk<<<B, 64, 0, s>>>(logits, d.n_experts, d.top_k, sigmoid ? 1 : 0, idx, w);
   return hipGetLastError();
 }
 
@@ -477,8 +477,11 @@ hipError_t launch_down(const flint_moe_dims& d, const flint_moe_layer& L, const 
 hipError_t launch_lmhead(const flint_nvfp4& head, int vocab, const float* x, int B, float norm_eps, float* logits,
                          int32_t* argmax, HeadPartial* partials, uint32_t* tickets, hipStream_t s) {
   dim3 grid(kHeadBlocks, B);
-  k_lmhead<<<grid, 256, 0, s>>>(head.codes, head.scales, head.tscale, vocab, x, norm_eps, logits, argmax, partials,
-                                tickets);
+  (void)tickets;
+  k_lmhead<<<grid, 256, 0, s>>>(head.codes, head.scales, head.tscale, vocab, x, norm_eps, logits, argmax, partials);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_head_argmax<<<B, 64, 0, s>>>(partials, kHeadBlocks, argmax);
   return hipGetLastError();
 }
 

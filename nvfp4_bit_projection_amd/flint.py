@@ -61,6 +61,10 @@ class AttnLayer(ctypes.Structure):
                 ("sinks", _P)]
 
 
+class INT4(ctypes.Structure):
+    _fields_ = [("codes", _P), ("scales", _P), ("biases", _P)]
+
+
 TRACE_POINTS = 16  # stamps per layer of flint_stack_decode_traced
 SCHEDULE_AUTO, SCHEDULE_KERNELS, SCHEDULE_PERSISTENT = 0, 1, 2
 
@@ -93,6 +97,10 @@ def _load():
         "flint_attn_decode": ([ctypes.POINTER(AttnDims), ctypes.POINTER(AttnLayer), _P, _I32, _P, _P, _I32, _P, _P,
                                _SZ, _P], _I32),
         "flint_dense_workspace_bytes": ([_I32, _I32, _I32], _SZ),
+        "flint_int4_quantize": ([_P, _I64, _I64, _P, _P, _P, _P], _I32),
+        "flint_int4_dequantize": ([ctypes.POINTER(INT4), _I64, _I64, _P, _P], _I32),
+        "flint_int4_gemv_workspace_bytes": ([_I32], _SZ),
+        "flint_int4_gemv": ([ctypes.POINTER(INT4), _I32, _I32, _P, _I32, _P, _P, _P, _SZ, _P], _I32),
         "flint_dense_mlp": ([ctypes.POINTER(NVFP4), ctypes.POINTER(NVFP4), ctypes.POINTER(NVFP4), _I32, _I32, _P,
                              _I32, _P, _P, _SZ, _P], _I32),
     }
@@ -113,7 +121,9 @@ EXPORTED = ("flint_status_str", "flint_last_hip_error", "flint_workspace_bytes",
             "flint_stack_decode", "flint_stack_decode_traced", "flint_stack_decode_batch", "flint_stack_error",
             "flint_nvfp4_quantize", "flint_nvfp4_dequantize",
             # include/flint_attn.h
-            "flint_attn_workspace_bytes", "flint_attn_decode", "flint_dense_workspace_bytes", "flint_dense_mlp")
+            "flint_attn_workspace_bytes", "flint_attn_decode", "flint_dense_workspace_bytes", "flint_dense_mlp",
+            # include/flint_int4.h
+            "flint_int4_quantize", "flint_int4_dequantize", "flint_int4_gemv_workspace_bytes", "flint_int4_gemv")
 
 
 def lib():
@@ -416,3 +426,53 @@ def dense_mlp(gate: NVFP4Tensor, up: NVFP4Tensor, down: NVFP4Tensor, x: torch.Te
     _check(_lib.flint_dense_mlp(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d), H, width, x.data_ptr(), B,
                                 y.data_ptr(), ws.data_ptr(), ws.numel(), _stream()), "flint_dense_mlp")
     return y
+
+
+# ------------------------------------------------------- INT4 affine codec --
+@dataclass
+class INT4Tensor:
+    """codes uint8 [rows][cols/2], BF16 scales and offsets int16 [rows][cols/64]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    biases: torch.Tensor
+
+    def c(self) -> INT4:
+        return INT4(self.codes.data_ptr(), self.scales.data_ptr(), self.biases.data_ptr())
+
+
+def int4_quantize(w: torch.Tensor) -> INT4Tensor:
+    """w float32 cuda [rows][cols] (cols a multiple of 64) -> INT4Tensor"""
+    rows, cols = w.shape
+    w = w.contiguous()
+    codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((rows, cols // 64), dtype=torch.int16, device=w.device)
+    biases = torch.empty((rows, cols // 64), dtype=torch.int16, device=w.device)
+    _check(_lib.flint_int4_quantize(w.data_ptr(), rows, cols, codes.data_ptr(), scales.data_ptr(), biases.data_ptr(),
+                                    _stream()), "flint_int4_quantize")
+    return INT4Tensor(codes, scales, biases)
+
+
+def int4_dequantize(q: INT4Tensor) -> torch.Tensor:
+    rows, half = q.codes.shape
+    out = torch.empty((rows, 2 * half), dtype=torch.float32, device=q.codes.device)
+    c = q.c()
+    _check(_lib.flint_int4_dequantize(ctypes.byref(c), rows, 2 * half, out.data_ptr(), _stream()),
+           "flint_int4_dequantize")
+    return out
+
+
+def int4_gemv(q: INT4Tensor, x: torch.Tensor, want_argmax: bool = True, ws: torch.Tensor | None = None,
+              y: torch.Tensor | None = None, argmax: torch.Tensor | None = None):
+    """x float32 [B][cols] -> (y float32 [B][rows], argmax int32 [B] or None)"""
+    B, cols = x.shape
+    rows = q.codes.shape[0]
+    if ws is None:
+        ws = torch.zeros(_lib.flint_int4_gemv_workspace_bytes(B), dtype=torch.uint8, device=x.device)
+    y = torch.empty((B, rows), dtype=torch.float32, device=x.device) if y is None else y
+    if want_argmax and argmax is None:
+        argmax = torch.empty(B, dtype=torch.int32, device=x.device)
+    c = q.c()
+    _check(_lib.flint_int4_gemv(ctypes.byref(c), rows, cols, x.data_ptr(), B, y.data_ptr(),
+                                _ptr(argmax) if want_argmax else None, ws.data_ptr(), ws.numel(), _stream()),
+           "flint_int4_gemv")
+    return y, (argmax if want_argmax else None)

@@ -7,7 +7,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("flint_moe.h", "flint_attn.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("flint_moe.h", "flint_attn.h", "flint_int4.h")]
 
 
 @pytest.fixture(scope="module")
@@ -176,3 +176,21 @@ def test_attn_and_dense_rejections(F):
     assert dn(6144, 0, ok) == -2
     assert dn(5000, 1, ok) == -8
     assert dn(6144, 2, ok - 1) == -4
+
+
+def test_int4_rejections(F):
+    L = F.lib()
+    assert L.flint_int4_gemv_workspace_bytes(1) > 0 and L.flint_int4_gemv_workspace_bytes(65) == 0
+    q = F.INT4(FAKE, FAKE, FAKE)
+    need = L.flint_int4_gemv_workspace_bytes(2)
+    gv = lambda rows, cols, B, wsb=need, x=FAKE: L.flint_int4_gemv(ctypes.byref(q), rows, cols, x, B, FAKE, None,
+                                                                   FAKE, wsb, None)
+    assert gv(100, 2048, 2, x=None) == -1
+    assert gv(0, 2048, 2) == -2
+    assert gv(100, 1024, 2) == -8
+    assert gv(100, 2048, 65) == -8
+    assert gv(100, 2048, 2, wsb=need - 1) == -4
+    assert gv(100, 2048, 2, x=FAKE + 8) == -3
+    assert L.flint_int4_quantize(FAKE, 4, 100, FAKE, FAKE, FAKE, None) == -2
+    assert L.flint_int4_quantize(FAKE, 4, 128, FAKE, FAKE + 1, FAKE, None) == -3
+    assert L.flint_int4_quantize(None, 4, 128, FAKE, FAKE, FAKE, None) == -1
