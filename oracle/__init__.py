@@ -77,6 +77,10 @@ def lib():
         L.oracle_int4_dequantize.restype = None
         L.oracle_int4_gemv.argtypes = [_P, _P, _P, _I64, _I64, _P, _P, ctypes.c_int]
         L.oracle_int4_gemv.restype = None
+        L.oracle_nvfp4_gemm.argtypes = [_P, _P, ctypes.c_float, _I64, _I64, _P, _I64, _P, ctypes.c_int]
+        L.oracle_nvfp4_gemm.restype = None
+        L.oracle_nvfp4_gemm_a4.argtypes = [_P, _P, ctypes.c_float, _I64, _I64, _P, _I64, _P, ctypes.c_int]
+        L.oracle_nvfp4_gemm_a4.restype = None
         L.oracle_rms_inv.argtypes = [_P, _I64, ctypes.c_double]
         L.oracle_rms_inv.restype = ctypes.c_double
         L.oracle_swiglu_expert.argtypes = [_P, _P, ctypes.c_float, _P, _P, ctypes.c_float, _P, _P, ctypes.c_float,
@@ -326,3 +330,22 @@ def int4_gemv(q: INT4, x: np.ndarray) -> np.ndarray:
     lib().oracle_int4_gemv(c.ctypes.data, s.ctypes.data, b.ctypes.data, q.rows, q.cols, x.ctypes.data,
                            y.ctypes.data, 1)
     return y
+
+
+# ------------------------------------------------------------ prefill GEMM --
+def nvfp4_gemm(q: NVFP4, X: np.ndarray, a4: bool = False, nthreads: int | None = None) -> np.ndarray:
+    """X [T][K] -> Y float64 [T][N] = X deq(W)^T; with a4 the activations are
+    first quantised to NVFP4 (one tensor scale over X)."""
+    T, K = X.shape
+    assert K == q.cols
+    Y = np.empty((T, q.rows), np.float64)
+    codes, scales = _c(q.codes, np.uint8), _c(q.scales, np.uint8)
+    if a4:
+        Xf = _c(X, np.float32)
+        lib().oracle_nvfp4_gemm_a4(codes.ctypes.data, scales.ctypes.data, q.tscale, q.rows, q.cols, Xf.ctypes.data,
+                                   T, Y.ctypes.data, nthreads or default_threads())
+    else:
+        Xd = _c(X, np.float64)
+        lib().oracle_nvfp4_gemm(codes.ctypes.data, scales.ctypes.data, q.tscale, q.rows, q.cols, Xd.ctypes.data, T,
+                                Y.ctypes.data, nthreads or default_threads())
+    return Y

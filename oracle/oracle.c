@@ -585,3 +585,38 @@ void oracle_int4_gemv(const uint8_t* codes, const uint16_t* scales, const uint16
   }
   free(row);
 }
+
+/* ------------------------------------------------------- prefill GEMM ---- */
+
+/* Prompt processing [P1 "Flint-40B-A2B: AI-Built MoE Coding Model Hits 125
+ * tok/s on MacBook Pro", "Custom Inference Kernels": kernels for prompt
+ * processing; P2 "How did the Eureka Machine build Flint?": kernels for
+ * low-bit projections and prompt processing].  T tokens at once through one
+ * NVFP4 matrix W [N][K]:
+ *   Y[t][n] = sum_k deq(W)[n][k] * X[t][k]        (X at full precision),
+ * which is the decode GEMV once per token. */
+void oracle_nvfp4_gemm(const uint8_t* codes, const uint8_t* scales, float tscale, int64_t N, int64_t K,
+                       const double* X, int64_t T, double* Y, int nthreads) {
+  for (int64_t t = 0; t < T; ++t) oracle_nvfp4_gemv(codes, scales, tscale, N, K, X + t * K, Y + t * N, nthreads);
+}
+
+/* The A4 variant: the activations are quantised with the same NVFP4 codec
+ * first (reading: X [T][K] is one tensor, so one fp32 scale over all of it;
+ * E4M3 block scales per 16 values along K), then multiplied exactly:
+ *   Y[t][n] = sum_k deq(W)[n][k] * deq(Xq)[t][k]. */
+void oracle_nvfp4_gemm_a4(const uint8_t* codes, const uint8_t* scales, float tscale, int64_t N, int64_t K,
+                          const float* X, int64_t T, double* Y, int nthreads) {
+  uint8_t* xc = (uint8_t*)malloc((size_t)(T * K / 2));
+  uint8_t* xs = (uint8_t*)malloc((size_t)(T * K / 16));
+  float* xd = (float*)malloc(sizeof(float) * (size_t)(T * K));
+  double* xv = (double*)malloc(sizeof(double) * (size_t)(T * K));
+  float xS;
+  oracle_nvfp4_quantize(X, T, K, xc, xs, &xS, nthreads);
+  oracle_nvfp4_dequantize(xc, xs, xS, T, K, xd);
+  for (int64_t i = 0; i < T * K; ++i) xv[i] = (double)xd[i];
+  oracle_nvfp4_gemm(codes, scales, tscale, N, K, xv, T, Y, nthreads);
+  free(xc);
+  free(xs);
+  free(xd);
+  free(xv);
+}
