@@ -97,6 +97,8 @@ def _load():
         "flint_attn_decode": ([ctypes.POINTER(AttnDims), ctypes.POINTER(AttnLayer), _P, _I32, _P, _P, _I32, _P, _P,
                                _SZ, _P], _I32),
         "flint_dense_workspace_bytes": ([_I32, _I32, _I32], _SZ),
+        "flint_nvfp4_gemm_workspace_bytes": ([_I32, _I32, _I32], _SZ),
+        "flint_nvfp4_gemm": ([ctypes.POINTER(NVFP4), _I32, _I32, _P, _I32, _I32, _P, _P, _SZ, _P], _I32),
         "flint_int4_quantize": ([_P, _I64, _I64, _P, _P, _P, _P], _I32),
         "flint_int4_dequantize": ([ctypes.POINTER(INT4), _I64, _I64, _P, _P], _I32),
         "flint_int4_gemv_workspace_bytes": ([_I32], _SZ),
@@ -123,7 +125,9 @@ EXPORTED = ("flint_status_str", "flint_last_hip_error", "flint_workspace_bytes",
             # include/flint_attn.h
             "flint_attn_workspace_bytes", "flint_attn_decode", "flint_dense_workspace_bytes", "flint_dense_mlp",
             # include/flint_int4.h
-            "flint_int4_quantize", "flint_int4_dequantize", "flint_int4_gemv_workspace_bytes", "flint_int4_gemv")
+            "flint_int4_quantize", "flint_int4_dequantize", "flint_int4_gemv_workspace_bytes", "flint_int4_gemv",
+            # include/flint_gemm.h
+            "flint_nvfp4_gemm_workspace_bytes", "flint_nvfp4_gemm")
 
 
 def lib():
@@ -476,3 +480,27 @@ def int4_gemv(q: INT4Tensor, x: torch.Tensor, want_argmax: bool = True, ws: torc
                                 _ptr(argmax) if want_argmax else None, ws.data_ptr(), ws.numel(), _stream()),
            "flint_int4_gemv")
     return y, (argmax if want_argmax else None)
+
+
+# ------------------------------------------------------------ prefill GEMM --
+GEMM_A32, GEMM_A4 = 0, 1
+
+
+def gemm_workspace(T: int, K: int, mode: int, device="cuda") -> torch.Tensor:
+    n = _lib.flint_nvfp4_gemm_workspace_bytes(T, K, mode)
+    if n == 0:
+        raise ValueError("unsupported GEMM sizes")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def nvfp4_gemm(q: NVFP4Tensor, X: torch.Tensor, mode: int = GEMM_A32, ws: torch.Tensor | None = None,
+               Y: torch.Tensor | None = None) -> torch.Tensor:
+    """X float32 [T][K] -> Y float32 [T][N] = X deq(W)^T (A4: X quantised to NVFP4 first)"""
+    T, K = X.shape
+    N = q.codes.shape[-2]
+    ws = gemm_workspace(T, K, mode, X.device) if ws is None else ws
+    Y = torch.empty((T, N), dtype=torch.float32, device=X.device) if Y is None else Y
+    w = q.c()
+    _check(_lib.flint_nvfp4_gemm(ctypes.byref(w), N, K, X.data_ptr(), T, mode, Y.data_ptr(), ws.data_ptr(),
+                                 ws.numel(), _stream()), "flint_nvfp4_gemm")
+    return Y

@@ -7,7 +7,7 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("flint_moe.h", "flint_attn.h", "flint_int4.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("flint_moe.h", "flint_attn.h", "flint_int4.h", "flint_gemm.h")]
 
 
 @pytest.fixture(scope="module")
@@ -194,3 +194,21 @@ def test_int4_rejections(F):
     assert L.flint_int4_quantize(FAKE, 4, 100, FAKE, FAKE, FAKE, None) == -2
     assert L.flint_int4_quantize(FAKE, 4, 128, FAKE, FAKE + 1, FAKE, None) == -3
     assert L.flint_int4_quantize(None, 4, 128, FAKE, FAKE, FAKE, None) == -1
+
+
+def test_gemm_rejections(F):
+    L = F.lib()
+    assert L.flint_nvfp4_gemm_workspace_bytes(8, 2048, 0) > 0
+    assert L.flint_nvfp4_gemm_workspace_bytes(8, 2048, 1) > L.flint_nvfp4_gemm_workspace_bytes(8, 2048, 0)
+    assert L.flint_nvfp4_gemm_workspace_bytes(8, 100, 0) == 0
+    assert L.flint_nvfp4_gemm_workspace_bytes(8, 2048, 2) == 0
+    m = F.NVFP4(FAKE, FAKE, FAKE)
+    need = L.flint_nvfp4_gemm_workspace_bytes(8, 2048, 1)
+    g = lambda N, K, T, mode, wsb=need, x=FAKE: L.flint_nvfp4_gemm(ctypes.byref(m), N, K, x, T, mode, FAKE, FAKE,
+                                                                   wsb, None)
+    assert g(10, 2048, 8, 1, x=None) == -1
+    assert g(0, 2048, 8, 1) == -2
+    assert g(10, 2048, 8, 3) == -2
+    assert g(10, 2000, 8, 0) == -8
+    assert g(10, 2048, 8, 1, wsb=need - 1) == -4
+    assert g(10, 2048, 8, 1, x=FAKE + 4) == -3
