@@ -377,6 +377,72 @@ def bench_int4(args) -> int:
     return 0
 
 
+def bench_gemm(args) -> int:
+    """Prompt processing: T tokens through one NVFP4 matrix (flint_nvfp4_gemm)
+    for a few of the model's shapes, A32 and A4, timed from HIP-graph replays.
+    Flops = 2 T N K (the algorithmic count; A32 runs two fp16 products per
+    multiply-add, so its ceiling is half the fp16 peak)."""
+    import torch
+
+    import synth
+    from nvfp4_bit_projection_amd import flint
+
+    torch.cuda.set_device(0)
+    peak = 2500.0  # dense fp16 MFMA TFLOP/s
+    out = []
+    for name, N, K in (("shared_gate_1024x2048", 1024, 2048), ("dense_gate_6144x2048", 6144, 2048),
+                       ("dense_down_2048x6144", 2048, 6144), ("head_150144x2048", 150144, 2048)):
+        w = torch.empty(N * K, dtype=torch.float32, device="cuda")
+        synth.normal_device(7, synth.stream_id(synth.HEAD), N * K, w, std=synth.WEIGHT_STD)
+        q = flint.quantize(w.view(N, K))
+        del w
+        for T in (512, 2048):
+            X = torch.empty(T * K, dtype=torch.float32, device="cuda")
+            synth.normal_device(8, synth.stream_id(synth.TOKEN), T * K, X)
+            X = X.view(T, K)
+            for mode, mname in ((flint.GEMM_A32, "a32"), (flint.GEMM_A4, "a4")):
+                ws = flint.gemm_workspace(T, K, mode)
+                Y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+                fn = lambda: flint.nvfp4_gemm(q, X, mode, ws=ws, Y=Y)
+                for _ in range(2):
+                    fn()
+                torch.cuda.synchronize()
+                ref = Y.clone()
+                g = torch.cuda.CUDAGraph()
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    fn()
+                torch.cuda.current_stream().wait_stream(side)
+                torch.cuda.synchronize()
+                with torch.cuda.graph(g):
+                    for _ in range(4):
+                        fn()
+                g.replay()
+                torch.cuda.synchronize()
+                if not torch.equal(Y, ref):
+                    raise RuntimeError("graph replay differs from the eager call")
+                reps = max(1, min(args.steps, 64) // 4)
+                ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ev0.record()
+                for _ in range(reps):
+                    g.replay()
+                ev1.record()
+                torch.cuda.synchronize()
+                us = ev0.elapsed_time(ev1) * 1e3 / (reps * 4)
+                tf = 2.0 * T * N * K / (us * 1e-6) / 1e12
+                log(f"gemm {name} T={T} {mname}: {us:.1f} us, {tf:.1f} TFLOP/s ({100 * tf / peak:.1f}% of fp16 peak)")
+                out.append({"shape": name, "T": T, "mode": mname, "us": round(us, 2), "tflops": round(tf, 1),
+                            "frac_fp16_peak": round(tf / peak, 4)})
+                del ws, Y
+            del X
+        del q
+    print(json.dumps({"metric": "prefill GEMM TFLOP/s (NVFP4 weights)", "unit": "TFLOP/s", "higher_is_better": True,
+                      "data": "synthetic", "config": {"workload": "nvfp4_prefill_gemm"}, "peak_tflops": peak,
+                      "results": out}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -393,6 +459,7 @@ def main() -> int:
                     help="time one attention layer (sliding and full context) and the dense MLP")
     ap.add_argument("--int4", action="store_true",
                     help="time the output head as group-64 affine INT4 against the NVFP4 head")
+    ap.add_argument("--gemm", action="store_true", help="time the prefill GEMM (A32 and A4) on model shapes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (batch-1 decode; see DESIGN.md for how it would shard)",
@@ -406,6 +473,8 @@ def main() -> int:
         return bench_attn(args)
     if args.int4:
         return bench_int4(args)
+    if args.gemm:
+        return bench_gemm(args)
     if args.batch > 1:
         return bench_batch(args)
 

@@ -21,8 +21,9 @@
 // gfx950's scaled-FP4 MFMA takes one power-of-two scale per 32 values, so it
 // cannot carry NVFP4's E4M3 scale per 16 exactly; it is not used.
 //
-// Tiling: a workgroup (4 waves) owns 128 weight rows x 32 tokens; each wave
-// 32 rows (two 16-row tiles) x the 32 tokens (two 16-token tiles).  K runs in
+// Tiling: a workgroup (4 waves) owns 256 weight rows x 32 tokens; each wave
+// 64 rows (four 16-row tiles) x the 32 tokens (two 16-token tiles), so every
+// activation fragment read from LDS feeds four products.  K runs in
 // chunks of 256: the chunk's activations are staged in LDS as fp16 parts
 // (double-buffered; the next chunk's global loads are issued before the
 // current chunk's products), each lane's weight bytes for the next chunk are
@@ -41,7 +42,8 @@ typedef __attribute__((ext_vector_type(8))) _Float16 h8_t;
 typedef __attribute__((ext_vector_type(2))) _Float16 h2_t;
 typedef __attribute__((ext_vector_type(4))) float f4_t;
 
-constexpr int kGRows = 128;   // weight rows per workgroup
+constexpr int kRT = 4;        // 16-row weight tiles per wave
+constexpr int kGRows = 64 * kRT;  // weight rows per workgroup
 constexpr int kGTok = 32;     // tokens per workgroup
 constexpr int kGChunk = 256;  // K per stage
 constexpr int kGRowBytes = kGChunk * 2;            // one token's fp16 part of a chunk
@@ -143,15 +145,15 @@ __device__ __forceinline__ void stage_store(const Stage<P>& st, unsigned char* b
   }
 }
 
-// a lane's weight bytes of one chunk for its two row tiles: 64 values
+// a lane's weight bytes of one chunk for its row tiles: 64 values
 // (K = kc + 64 q .. +64) of row m of each tile
 struct WFrag {
-  uint4 c[2][2];
-  uint32_t s[2];
+  uint4 c[kRT][2];
+  uint32_t s[kRT];
 };
 __device__ __forceinline__ void wfrag_load(const GemmArgs& A, const int* rows, int kc, int q, WFrag& f) {
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < kRT; ++rt) {
     const uint8_t* cp = A.wc + (size_t)rows[rt] * (A.K / 2) + kc / 2 + 32 * q;
     f.c[rt][0] = ld_nt_u4(cp);
     f.c[rt][1] = ld_nt_u4(cp + 16);
@@ -163,12 +165,14 @@ template <int P>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
   __shared__ __align__(16) unsigned char sbuf[2][P * kGPartBytes];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, m = lane & 15, q = lane >> 4;
-  const int n0 = blockIdx.x * kGRows + 32 * wv, t0 = blockIdx.y * kGTok;
-  const int rows[2] = {min(n0 + m, A.N - 1), min(n0 + 16 + m, A.N - 1)};
-  const int nch = A.K / kGChunk;
-  f4_t acc[2][2];
+  const int n0 = blockIdx.x * kGRows + 16 * kRT * wv, t0 = blockIdx.y * kGTok;
+  int rows[kRT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
+  for (int rt = 0; rt < kRT; ++rt) rows[rt] = min(n0 + 16 * rt + m, A.N - 1);
+  const int nch = A.K / kGChunk;
+  f4_t acc[kRT][2];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt)
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) acc[rt][tt] = f4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -186,17 +190,12 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
       wfrag_load(A, rows, (c + 1) * kGChunk, q, nxt);
     }
     const unsigned char* buf = sbuf[c & 1];
-    H16Scale d[2][4];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d[rt][i] = h16_scale((cur.s[rt] >> (8 * i)) & 0xFF);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t w0 = (&cur.c[0][j >> 2].x)[j & 3];
-      const uint32_t w1 = (&cur.c[1][j >> 2].x)[j & 3];
-      const h8_t b0 = h16_decode(w0, d[0][j >> 1]);
-      const h8_t b1 = h16_decode(w1, d[1][j >> 1]);
+      h8_t b[kRT];
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt)
+        b[rt] = h16_decode((&cur.c[rt][j >> 2].x)[j & 3], h16_scale((cur.s[rt] >> (8 * (j >> 1))) & 0xFF));
       const int g = 8 * q + j;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -205,8 +204,9 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
 #pragma unroll
         for (int p = 0; p < P; ++p) {
           const h8_t a = *reinterpret_cast<const h8_t*>(ap + p * kGPartBytes);
-          acc[0][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b0, acc[0][tt], 0, 0, 0);
-          acc[1][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b1, acc[1][tt], 0, 0, 0);
+#pragma unroll
+          for (int rt = 0; rt < kRT; ++rt)
+            acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[rt], acc[rt][tt], 0, 0, 0);
         }
       }
     }
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
   // lane (m, q) holds tokens 4q .. 4q+3 of each token tile for weight row m
   const float S = *A.wS * (P == 1 ? *A.xS : 1.0f);
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < kRT; ++rt) {
     const int n = n0 + 16 * rt + m;
     if (n >= A.N) continue;
 #pragma unroll
