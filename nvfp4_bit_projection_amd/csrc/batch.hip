@@ -771,6 +771,13 @@ BatchWs::BatchWs(const flint_moe_dims& d, int B, int vocab) {
   total = o;
 }
 
+// 4-byte word copy (the step uses kernels only, so it can be captured in a
+// HIP graph)
+__global__ __launch_bounds__(kThreads) void k_copy_words(const uint32_t* __restrict__ src,
+                                                         uint32_t* __restrict__ dst, int n) {
+  for (int i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads) dst[i] = src[i];
+}
+
 hipError_t launch_batch_step(const flint_moe_dims& d, const flint_moe_layer* layers, int L, const flint_nvfp4& head,
                              int vocab, const float* x, int B, float eps, float* logits, int32_t* argmax,
                              int32_t* routes, void* ws, hipStream_t s) {
@@ -791,14 +798,18 @@ hipError_t launch_batch_step(const flint_moe_dims& d, const flint_moe_layer* lay
   const int k = d.top_k, E = d.n_experts, I = d.expert_width, Is = d.shared_width, nb = B * k;
   const int Umax = nb < E ? nb : E;
   const int gu_x = ((I > Is ? I : Is) + kMmGateUpRows - 1) / kMmGateUpRows;
-  hipError_t e = hipMemcpyAsync(h, x, 4 * (size_t)B * kHidden, hipMemcpyDeviceToDevice, s);
+  k_copy_words<<<(B * kHidden + kThreads - 1) / kThreads, kThreads, 0, s>>>(
+      reinterpret_cast<const uint32_t*>(x), reinterpret_cast<uint32_t*>(h), B * kHidden);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   k_bnorm<<<B, kThreads, 0, s>>>(h, nullptr, nullptr, k, u, up, B, eps);
   for (int l = 0; l < L && e == hipSuccess; ++l) {
     const flint_moe_layer& Ly = layers[l];
     k_broute<<<dim3((E + 3) / 4, (B + kRouteTok - 1) / kRouteTok), kThreads, 0, s>>>(Ly.router, E, u, B, lg);
     k_btopk<<<B, 64, 0, s>>>(lg, E, k, idx, wts);
-    if (routes) e = hipMemcpyAsync(routes + (size_t)l * nb, idx, 4 * (size_t)nb, hipMemcpyDeviceToDevice, s);
+    if (routes)
+      k_copy_words<<<1, kThreads, 0, s>>>(reinterpret_cast<const uint32_t*>(idx),
+                                          reinterpret_cast<uint32_t*>(routes + (size_t)l * nb), nb);
     k_bucket<<<1, kThreads, 0, s>>>(idx, nb, E, bk);
     k_mm_gateup<<<dim3(gu_x, Umax + 1), kMmThreads, 0, s>>>(Ly, I, Is, k, B, Umax, up, bk, hrp, hsp, nb);
     k_mm_down<<<dim3(kHidden / kMmRows, Umax + 1), kMmThreads, 0, s>>>(Ly, I, Is, B, Umax, hrp, hsp, bk, wts, dr, ds,
