@@ -134,3 +134,50 @@ def stack_token(W: SyntheticWeights, x: np.ndarray, layers: int, layer_seeds=Non
         res.logits = nvfp4_gemv(W.head(), z, nthreads)
         res.argmax, res.argmax_gap = argmax(res.logits)
     return res
+
+
+# ------------------------------------------------------------- whole model --
+# Sources: [P2] "How does Flint's architecture work?" (49 layers: 2 dense,
+# then 47 MoE; 35 sliding-window and 14 full-attention layers; 32 query and
+# 4 key/value heads); [P3] "The shape, read from the headers" (the attention
+# and the norms of every layer).  Readings: every layer is pre-norm twice,
+# h += Attn(rmsnorm(h)) then h += F(rmsnorm(h)), each RMSNorm with unit gain
+# and eps inside the root, and a last one before the head.
+
+@dataclass
+class ModelResult:
+    logits: np.ndarray
+    argmax: int
+    argmax_gap: float
+    h: np.ndarray                                      # final residual
+    gaps: list = field(default_factory=list)           # routing gap of each MoE layer
+
+
+def model_token(W: SyntheticWeights, attn: list, attn_dims: list, dense: list, moe_seeds: list, head: NVFP4,
+                x: np.ndarray, pos: int, k_caches: list, v_caches: list, eps: float = 1e-6,
+                nthreads: int | None = None) -> ModelResult:
+    """One token through the layers (attention, then dense MLP for the first
+    len(dense) layers and MoE for the rest) and the head.  k_caches and
+    v_caches (uint16 [n_kv][cap][D] each) are updated in place."""
+    from . import attn_decode
+    nd = len(dense)
+    h = np.asarray(x, np.float64).copy()
+    res = ModelResult(np.zeros(0), -1, 0.0, h)
+    for l in range(len(attn)):
+        d = attn_dims[l]
+        u = h * rms_inv(h, eps)
+        y, _, _ = attn_decode(attn[l], u, pos, k_caches[l], v_caches[l], n_kv=d.n_kv, window=d.window, rope=d.rope,
+                              theta=d.theta, nthreads=nthreads)
+        h = h + y
+        u = h * rms_inv(h, eps)
+        if l < nd:
+            h = h + swiglu_expert(*dense[l], u, nthreads)
+        else:
+            lr = moe_layer(W, moe_seeds[l - nd], u, nthreads=nthreads)
+            res.gaps.append(lr.gap)
+            h = h + lr.y
+    z = h * rms_inv(h, eps)
+    res.logits = nvfp4_gemv(head, z, nthreads)
+    res.argmax, res.argmax_gap = argmax(res.logits)
+    res.h = h
+    return res
