@@ -177,6 +177,30 @@ static int32_t decode_impl(const flint_moe_dims& d, const flint_moe_layer& L, co
   return e == hipSuccess ? FLINT_OK : hip_fail(e);
 }
 
+}  // extern "C"
+
+int32_t flint::api_moe_check(const flint_moe_dims* d, const flint_moe_layer* L) {
+  int32_t st;
+  if ((st = check_dims(d))) return st;
+  return check_layer(L);
+}
+size_t flint::api_moe_ws_bytes(const flint_moe_dims& d) { return DecodeWs(d, 1).total; }
+hipError_t flint::api_moe_run(const flint_moe_dims& d, const flint_moe_layer& L, const float* x, float norm_eps,
+                              float* y, bool add, void* ws, hipStream_t s) {
+  const DecodeWs dw(d, 1);
+  const RouteWs rw(d.n_experts, 1);
+  char* base = static_cast<char*>(ws);
+  int32_t* idx = carve<int32_t>(ws, dw.idx);
+  float* w = carve<float>(ws, dw.wts);
+  hipError_t e = launch_route(d, L.router, x, 1, norm_eps, carve<float>(base + dw.route, rw.logits), idx, w,
+                              carve<uint32_t>(base + dw.route, rw.tickets), s);
+  if (e == hipSuccess) e = launch_gateup(d, L, x, 1, norm_eps, idx, carve<float>(ws, dw.hact), s);
+  if (e == hipSuccess) e = launch_down(d, L, idx, w, carve<float>(ws, dw.hact), 1, y, add, s);
+  return e;
+}
+
+extern "C" {
+
 int32_t flint_moe_decode(const flint_moe_dims* dims, const flint_moe_layer* layer, const float* x, int32_t B, float* y,
                          int32_t* topk_idx_opt, float* topk_w_opt, void* ws, size_t ws_bytes, void* stream) {
   int32_t st;

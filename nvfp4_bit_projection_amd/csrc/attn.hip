@@ -60,9 +60,11 @@ struct GemvSet {
 // and reads 16 code bytes and 2 scale bytes per row and i.  A wave takes R
 // rows per step (their loads issued together), waves stride over the rows;
 // grid.y is the token.
+// norm_eps >= 0: x is first scaled by 1 / sqrt(mean(x^2) + norm_eps) (RMSNorm
+// with unit gain, every wave over the whole vector); accumulate: y += result.
 template <int KI, int R, bool PAIR>
 __global__ __launch_bounds__(256) void k_gemv(GemvSet M, int total_rows, const float* __restrict__ x, int ldx,
-                                              float* __restrict__ y, int ldy) {
+                                              float* __restrict__ y, int ldy, float norm_eps, int accumulate) {
   constexpr int K = KI * kHid;
   const int lane = threadIdx.x & 63;
   const int b = blockIdx.y;
@@ -78,6 +80,14 @@ __global__ __launch_bounds__(256) void k_gemv(GemvSet M, int total_rows, const f
       xv[32 * i + 4 * q + 2] = v.z;
       xv[32 * i + 4 * q + 3] = v.w;
     }
+  if (norm_eps >= 0.0f) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < KI * 32; ++i) ss = __builtin_fmaf(xv[i], xv[i], ss);
+    const float r = 1.0f / sqrtf(wave_sum(ss) * (1.0f / K) + norm_eps);
+#pragma unroll
+    for (int i = 0; i < KI * 32; ++i) xv[i] *= r;
+  }
   const int nwaves = gridDim.x * 4;
   for (int r0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R; r0 < total_rows; r0 += nwaves * R) {
     uint4 c[R][KI], c2[PAIR ? R : 1][KI];
@@ -125,30 +135,33 @@ __global__ __launch_bounds__(256) void k_gemv(GemvSet M, int total_rows, const f
         for (int i = 0; i < KI; ++i) a2 += nvfp4_lane_dot32(c2[j][i], s2[j][i], xv + 32 * i);
         v = silu(v) * (wave_sum(a2) * S2[j]);
       }
-      if (lane == 0 && r0 + j < total_rows) y[(size_t)b * ldy + r0 + j] = v;
+      if (lane == 0 && r0 + j < total_rows) {
+        float* yp = y + (size_t)b * ldy + r0 + j;
+        *yp = accumulate ? *yp + v : v;
+      }
     }
   }
 }
 
 template <int KI, int R, bool PAIR>
-hipError_t gemv_launch(const GemvSet& M, int rows, const float* x, int ldx, float* y, int ldy, int B,
-                       hipStream_t st) {
+hipError_t gemv_launch(const GemvSet& M, int rows, const float* x, int ldx, float* y, int ldy, int B, float norm_eps,
+                       bool acc, hipStream_t st) {
   const int waves = (rows + R - 1) / R;
   int blocks = (waves + 3) / 4;
   if (blocks > 2048) blocks = 2048;
-  k_gemv<KI, R, PAIR><<<dim3(blocks, B), 256, 0, st>>>(M, rows, x, ldx, y, ldy);
+  k_gemv<KI, R, PAIR><<<dim3(blocks, B), 256, 0, st>>>(M, rows, x, ldx, y, ldy, norm_eps, acc ? 1 : 0);
   return hipGetLastError();
 }
 
 // K in {2048, 4096, 6144, 8192}; PAIR only at K = 2048
 hipError_t launch_gemv(const GemvSet& M, int rows, int K, bool pair, const float* x, int ldx, float* y, int ldy,
-                       int B, hipStream_t st) {
-  if (pair) return gemv_launch<1, 2, true>(M, rows, x, ldx, y, ldy, B, st);
+                       int B, hipStream_t st, float norm_eps = -1.0f, bool acc = false) {
+  if (pair) return gemv_launch<1, 2, true>(M, rows, x, ldx, y, ldy, B, norm_eps, acc, st);
   switch (K / kHid) {
-    case 1: return gemv_launch<1, 4, false>(M, rows, x, ldx, y, ldy, B, st);
-    case 2: return gemv_launch<2, 2, false>(M, rows, x, ldx, y, ldy, B, st);
-    case 3: return gemv_launch<3, 2, false>(M, rows, x, ldx, y, ldy, B, st);
-    default: return gemv_launch<4, 2, false>(M, rows, x, ldx, y, ldy, B, st);
+    case 1: return gemv_launch<1, 4, false>(M, rows, x, ldx, y, ldy, B, norm_eps, acc, st);
+    case 2: return gemv_launch<2, 2, false>(M, rows, x, ldx, y, ldy, B, norm_eps, acc, st);
+    case 3: return gemv_launch<3, 2, false>(M, rows, x, ldx, y, ldy, B, norm_eps, acc, st);
+    default: return gemv_launch<4, 2, false>(M, rows, x, ldx, y, ldy, B, norm_eps, acc, st);
   }
 }
 
@@ -454,52 +467,45 @@ GemvMat gm(const flint_nvfp4& q, int rows) { return GemvMat{q.codes, q.scales, q
 }  // namespace
 }  // namespace flint
 
-using namespace flint;
-
-extern "C" {
-
-size_t flint_attn_workspace_bytes(const flint_attn_dims* dims) {
-  if (check_attn_dims(dims) != FLINT_OK) return 0;
-  return AttnWs(*dims).total;
-}
-
-int32_t flint_attn_decode(const flint_attn_dims* dims, const flint_attn_layer* layer, const float* x, int32_t pos,
-                          uint16_t* k_cache, uint16_t* v_cache, int32_t cap, float* y, void* ws, size_t ws_bytes,
-                          void* stream) {
+int32_t flint::attn_check(const flint_attn_dims* dims, const flint_attn_layer* layer, int pos, const void* kc,
+                          const void* vc, int cap) {
   int32_t st;
   if ((st = check_attn_dims(dims))) return st;
-  if (!layer || !x || !k_cache || !v_cache || !y || !ws) return FLINT_E_NULL;
+  if (!layer || !kc || !vc) return FLINT_E_NULL;
   if (!layer->q_norm || !layer->k_norm || !layer->sinks) return FLINT_E_NULL;
   if ((st = check_mat(&layer->q)) || (st = check_mat(&layer->k)) || (st = check_mat(&layer->v)) ||
       (st = check_mat(&layer->o)))
     return st;
-  const flint_attn_dims& d = *dims;
   if (pos < 0 || cap < 1) return FLINT_E_DIMS;
-  if (d.window > 0 ? cap < d.window : cap <= pos) return FLINT_E_DIMS;
-  if (!al16(x) || !al16(y) || !al16(k_cache) || !al16(v_cache) || !al16(ws) || !al4(layer->q_norm) ||
-      !al4(layer->k_norm) || !al4(layer->sinks))
+  if (dims->window > 0 ? cap < dims->window : cap <= pos) return FLINT_E_DIMS;
+  if (!al16(kc) || !al16(vc) || !al4(layer->q_norm) || !al4(layer->k_norm) || !al4(layer->sinks))
     return FLINT_E_ALIGN;
+  return FLINT_OK;
+}
+
+size_t flint::attn_ws_bytes(const flint_attn_dims& d) { return AttnWs(d).total; }
+
+hipError_t flint::attn_run(const flint_attn_dims& d, const flint_attn_layer& layer, const float* x, float norm_eps,
+                           int pos, uint16_t* k_cache, uint16_t* v_cache, int cap, float* y, bool accumulate, void* ws,
+                           hipStream_t s) {
   const AttnWs w(d);
-  if (ws_bytes < w.total) return FLINT_E_WORKSPACE;
-  if ((st = api_check_device())) return st;
-  hipStream_t s = (hipStream_t)stream;
   char* base = static_cast<char*>(ws);
   float* qkv = reinterpret_cast<float*>(base + w.qkv);
   float* o = reinterpret_cast<float*>(base + w.o);
   const int nq = d.n_q_heads * kD, nk = d.n_kv_heads * kD;
 
   GemvSet in{};
-  in.m[0] = gm(layer->q, nq);
-  in.m[1] = gm(layer->k, nk);
-  in.m[2] = gm(layer->v, nk);
-  hipError_t e = launch_gemv(in, nq + 2 * nk, kHid, false, x, 0, qkv, 0, 1, s);
-  if (e != hipSuccess) return api_hip_fail(e);
+  in.m[0] = gm(layer.q, nq);
+  in.m[1] = gm(layer.k, nk);
+  in.m[2] = gm(layer.v, nk);
+  hipError_t e = launch_gemv(in, nq + 2 * nk, kHid, false, x, 0, qkv, 0, 1, s, norm_eps);
+  if (e != hipSuccess) return e;
 
   AttnArgs A{};
   A.qkv = qkv;
-  A.q_norm = layer->q_norm;
-  A.k_norm = layer->k_norm;
-  A.sinks = layer->sinks;
+  A.q_norm = layer.q_norm;
+  A.k_norm = layer.k_norm;
+  A.sinks = layer.sinks;
   A.kc = k_cache;
   A.vc = v_cache;
   A.cap = cap;
@@ -522,17 +528,61 @@ int32_t flint_attn_decode(const flint_attn_dims* dims, const flint_attn_layer* l
   A.part = reinterpret_cast<float*>(base + w.part);
   k_attn<<<dim3(A.nchunks, d.n_kv_heads), 256, 0, s>>>(A);
   e = hipGetLastError();
-  if (e != hipSuccess) return api_hip_fail(e);
+  if (e != hipSuccess) return e;
   if (A.nchunks <= 64)
-    k_attn_merge<64><<<d.n_q_heads, 256, 0, s>>>(A.part, layer->sinks, A.group, A.nchunks, o);
+    k_attn_merge<64><<<d.n_q_heads, 256, 0, s>>>(A.part, layer.sinks, A.group, A.nchunks, o);
   else
-    k_attn_merge<kMaxChunks><<<d.n_q_heads, 256, 0, s>>>(A.part, layer->sinks, A.group, A.nchunks, o);
+    k_attn_merge<kMaxChunks><<<d.n_q_heads, 256, 0, s>>>(A.part, layer.sinks, A.group, A.nchunks, o);
   e = hipGetLastError();
-  if (e != hipSuccess) return api_hip_fail(e);
+  if (e != hipSuccess) return e;
 
   GemvSet out{};
-  out.m[0] = gm(layer->o, kHid);
-  e = launch_gemv(out, kHid, nq, false, o, 0, y, 0, 1, s);
+  out.m[0] = gm(layer.o, kHid);
+  return launch_gemv(out, kHid, nq, false, o, 0, y, 0, 1, s, -1.0f, accumulate);
+}
+
+int32_t flint::dense_check(const flint_nvfp4* gate, const flint_nvfp4* up, const flint_nvfp4* down, int hidden,
+                           int width) {
+  int32_t st;
+  if ((st = check_mat(gate)) || (st = check_mat(up)) || (st = check_mat(down))) return st;
+  if (hidden < 1 || width < 1) return FLINT_E_DIMS;
+  if (hidden != kHid || width % kHid || width > 4 * kHid) return FLINT_E_UNSUPPORTED;
+  return FLINT_OK;
+}
+
+hipError_t flint::dense_run(const flint_nvfp4& gate, const flint_nvfp4& up, const flint_nvfp4& down, int width,
+                            const float* x, float norm_eps, float* y, bool accumulate, void* ws, hipStream_t s) {
+  float* h = static_cast<float*>(ws);
+  GemvSet gu{};
+  gu.m[0] = gm(gate, width);
+  gu.m[1] = gm(up, width);
+  hipError_t e = launch_gemv(gu, width, kHid, true, x, kHid, h, width, 1, s, norm_eps);
+  if (e != hipSuccess) return e;
+  GemvSet dn{};
+  dn.m[0] = gm(down, kHid);
+  return launch_gemv(dn, kHid, width, false, h, width, y, kHid, 1, s, -1.0f, accumulate);
+}
+
+using namespace flint;
+
+extern "C" {
+
+size_t flint_attn_workspace_bytes(const flint_attn_dims* dims) {
+  if (check_attn_dims(dims) != FLINT_OK) return 0;
+  return AttnWs(*dims).total;
+}
+
+int32_t flint_attn_decode(const flint_attn_dims* dims, const flint_attn_layer* layer, const float* x, int32_t pos,
+                          uint16_t* k_cache, uint16_t* v_cache, int32_t cap, float* y, void* ws, size_t ws_bytes,
+                          void* stream) {
+  int32_t st;
+  if ((st = check_attn_dims(dims))) return st;
+  if (!x || !y || !ws) return FLINT_E_NULL;
+  if ((st = attn_check(dims, layer, pos, k_cache, v_cache, cap))) return st;
+  if (!al16(x) || !al16(y) || !al16(ws)) return FLINT_E_ALIGN;
+  if (ws_bytes < AttnWs(*dims).total) return FLINT_E_WORKSPACE;
+  if ((st = api_check_device())) return st;
+  hipError_t e = attn_run(*dims, *layer, x, -1.0f, pos, k_cache, v_cache, cap, y, false, ws, (hipStream_t)stream);
   return e == hipSuccess ? FLINT_OK : api_hip_fail(e);
 }
 

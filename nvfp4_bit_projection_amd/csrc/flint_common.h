@@ -3,7 +3,10 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
+
+#include "../../include/flint_attn.h"
 
 namespace flint {
 
@@ -11,5 +14,27 @@ namespace flint {
 int32_t api_hip_fail(hipError_t e);
 // FLINT_OK when the current device is gfx950 (cached per device)
 int32_t api_check_device();
+
+// One MoE layer for one token (kernel sequence), validated by the caller:
+// y = MoE(rmsnorm(x)) (norm_eps < 0: no norm), added to y when add is set.
+// Workspace api_moe_ws_bytes(d).
+int32_t api_moe_check(const flint_moe_dims* d, const flint_moe_layer* L);
+size_t api_moe_ws_bytes(const flint_moe_dims& d);
+hipError_t api_moe_run(const flint_moe_dims& d, const flint_moe_layer& L, const float* x, float norm_eps, float* y,
+                       bool add, void* ws, hipStream_t s);
+
+// One attention layer for one token (attn.hip), validated by attn_check:
+// y (+)= Attn(rmsnorm(x)) with the cache update of flint_attn_decode.
+int32_t attn_check(const flint_attn_dims* d, const flint_attn_layer* L, int pos, const void* kc, const void* vc,
+                   int cap);
+size_t attn_ws_bytes(const flint_attn_dims& d);
+hipError_t attn_run(const flint_attn_dims& d, const flint_attn_layer& L, const float* x, float norm_eps, int pos,
+                    uint16_t* kc, uint16_t* vc, int cap, float* y, bool accumulate, void* ws, hipStream_t s);
+
+// Dense SwiGLU MLP for one token (attn.hip): y (+)= down(silu(gate u) * up u),
+// u = rmsnorm(x); workspace 4 * width bytes.
+int32_t dense_check(const flint_nvfp4* g, const flint_nvfp4* u, const flint_nvfp4* d, int hidden, int width);
+hipError_t dense_run(const flint_nvfp4& g, const flint_nvfp4& u, const flint_nvfp4& d, int width, const float* x,
+                     float norm_eps, float* y, bool accumulate, void* ws, hipStream_t s);
 
 }  // namespace flint

@@ -1,0 +1,122 @@
+// model.hip -- one whole decode step: per layer the attention (attn.hip), then
+// the dense MLP (attn.hip) or the MoE layer (kernels.hip), each reading the
+// residual stream through a unit-gain RMSNorm folded into its first kernel
+// and adding its output back into the residual in its last one; then the
+// NVFP4 head with argmax.
+//
+// Layer plan [P2 "Recursive Releases Flint, a 40B MoE Coding Model That Runs
+// Locally at 125 Tokens per Second", "How does Flint's architecture work?":
+// 49 layers, 2 dense then 47 MoE; 35 sliding-window and 14 full-attention
+// layers].
+#include "../../include/flint_model.h"
+#include "flint_common.h"
+#include "flint_internal.h"
+
+namespace flint {
+namespace {
+
+__global__ __launch_bounds__(256) void k_copy_vec(const float* __restrict__ s, float* __restrict__ d, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) d[i] = s[i];
+}
+
+struct ModelWs {
+  size_t h, scratch, total;
+  explicit ModelWs(size_t scratch_bytes) {
+    size_t o = 0;
+    h = o; o = align_up(o + 4 * (size_t)kHidden, 256);
+    scratch = o; o = align_up(o + scratch_bytes, 256);
+    total = o;
+  }
+};
+
+// the scratch the layers and the head need in turn (they run one after the
+// other on one stream, so they share it); 0 if the model is invalid
+size_t model_scratch(const flint_model* m) {
+  if (!m || m->n_layers < 1 || m->n_dense < 0 || m->n_dense > m->n_layers || !m->is_full || !m->attn ||
+      !m->k_cache || !m->v_cache || !m->cap || (m->n_dense > 0 && !m->dense) ||
+      (m->n_dense < m->n_layers && !m->moe_layers) || m->vocab < 1)
+    return 0;
+  size_t s = HeadWs(1).total;
+  const size_t a0 = flint_attn_workspace_bytes(&m->sliding), a1 = flint_attn_workspace_bytes(&m->full);
+  if (a0 == 0 || a1 == 0) return 0;
+  s = s > a0 ? s : a0;
+  s = s > a1 ? s : a1;
+  if (m->n_dense > 0) s = s > 4 * (size_t)m->dense_width ? s : 4 * (size_t)m->dense_width;
+  if (m->n_dense < m->n_layers) {
+    if (api_moe_check(&m->moe, &m->moe_layers[0]) != FLINT_OK) return 0;
+    const size_t mw = api_moe_ws_bytes(m->moe);
+    s = s > mw ? s : mw;
+  }
+  return s;
+}
+
+}  // namespace
+}  // namespace flint
+
+using namespace flint;
+
+extern "C" {
+
+size_t flint_model_workspace_bytes(const flint_model* m) {
+  const size_t s = model_scratch(m);
+  return s ? ModelWs(s).total : 0;
+}
+
+int32_t flint_model_decode(const flint_model* m, const float* x, int32_t pos, float* logits_opt, int32_t* argmax,
+                           float* h_out_opt, void* ws, size_t ws_bytes, void* stream) {
+  if (!m || !x || !argmax || !ws) return FLINT_E_NULL;
+  const size_t scratch = model_scratch(m);
+  if (scratch == 0) return FLINT_E_DIMS;
+  if (m->moe.hidden != kHidden || m->sliding.hidden != kHidden || m->full.hidden != kHidden)
+    return FLINT_E_UNSUPPORTED;
+  if (!(m->eps >= 0.0f) || pos < 0) return FLINT_E_DIMS;
+  int32_t st;
+  for (int l = 0; l < m->n_layers; ++l) {
+    if (m->is_full[l] != 0 && m->is_full[l] != 1) return FLINT_E_DIMS;
+    const flint_attn_dims* ad = m->is_full[l] ? &m->full : &m->sliding;
+    if ((st = attn_check(ad, &m->attn[l], pos, m->k_cache[l], m->v_cache[l], m->cap[l]))) return st;
+    if (l < m->n_dense) {
+      const flint_nvfp4* dn = m->dense + 3 * l;
+      if ((st = dense_check(dn, dn + 1, dn + 2, kHidden, m->dense_width))) return st;
+    } else if ((st = api_moe_check(&m->moe, &m->moe_layers[l - m->n_dense]))) {
+      return st;
+    }
+  }
+  if (!m->head.codes || !m->head.scales || !m->head.tscale) return FLINT_E_NULL;
+  if (((uintptr_t)x & 15) || ((uintptr_t)ws & 15) || ((uintptr_t)m->head.codes & 15) ||
+      ((uintptr_t)argmax & 3) || ((uintptr_t)logits_opt & 3) || ((uintptr_t)h_out_opt & 3))
+    return FLINT_E_ALIGN;
+  const ModelWs w(scratch);
+  if (ws_bytes < w.total) return FLINT_E_WORKSPACE;
+  if ((st = api_check_device())) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* base = static_cast<char*>(ws);
+  float* h = reinterpret_cast<float*>(base + w.h);
+  void* sc = base + w.scratch;
+  k_copy_vec<<<8, 256, 0, s>>>(x, h, kHidden);
+  hipError_t e = hipGetLastError();
+  for (int l = 0; l < m->n_layers && e == hipSuccess; ++l) {
+    const flint_attn_dims& ad = m->is_full[l] ? m->full : m->sliding;
+    e = attn_run(ad, m->attn[l], h, m->eps, pos, m->k_cache[l], m->v_cache[l], m->cap[l], h, true, sc, s);
+    if (e != hipSuccess) break;
+    if (l < m->n_dense) {
+      const flint_nvfp4* dn = m->dense + 3 * l;
+      e = dense_run(dn[0], dn[1], dn[2], m->dense_width, h, m->eps, h, true, sc, s);
+    } else {
+      e = api_moe_run(m->moe, m->moe_layers[l - m->n_dense], h, m->eps, h, true, sc, s);
+    }
+  }
+  if (e == hipSuccess) {
+    const HeadWs hw(1);
+    e = launch_lmhead(m->head, m->vocab, h, 1, m->eps, logits_opt, argmax,
+                      reinterpret_cast<HeadPartial*>(static_cast<char*>(sc) + hw.partials),
+                      reinterpret_cast<uint32_t*>(static_cast<char*>(sc) + hw.tickets), s);
+  }
+  if (e == hipSuccess && h_out_opt) {
+    k_copy_vec<<<8, 256, 0, s>>>(h, h_out_opt, kHidden);
+    e = hipGetLastError();
+  }
+  return e == hipSuccess ? FLINT_OK : api_hip_fail(e);
+}
+
+}  // extern "C"

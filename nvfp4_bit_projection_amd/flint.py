@@ -61,6 +61,12 @@ class AttnLayer(ctypes.Structure):
                 ("sinks", _P)]
 
 
+class ModelC(ctypes.Structure):
+    _fields_ = [("n_layers", _I32), ("n_dense", _I32), ("dense_width", _I32), ("moe", Dims), ("sliding", AttnDims),
+                ("full", AttnDims), ("is_full", _P), ("attn", _P), ("k_cache", _P), ("v_cache", _P), ("cap", _P),
+                ("dense", _P), ("moe_layers", _P), ("head", NVFP4), ("vocab", _I32), ("eps", ctypes.c_float)]
+
+
 class INT4(ctypes.Structure):
     _fields_ = [("codes", _P), ("scales", _P), ("biases", _P)]
 
@@ -97,6 +103,8 @@ def _load():
         "flint_attn_decode": ([ctypes.POINTER(AttnDims), ctypes.POINTER(AttnLayer), _P, _I32, _P, _P, _I32, _P, _P,
                                _SZ, _P], _I32),
         "flint_dense_workspace_bytes": ([_I32, _I32, _I32], _SZ),
+        "flint_model_workspace_bytes": ([ctypes.POINTER(ModelC)], _SZ),
+        "flint_model_decode": ([ctypes.POINTER(ModelC), _P, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
         "flint_nvfp4_gemm_workspace_bytes": ([_I32, _I32, _I32], _SZ),
         "flint_nvfp4_gemm": ([ctypes.POINTER(NVFP4), _I32, _I32, _P, _I32, _I32, _P, _P, _SZ, _P], _I32),
         "flint_int4_quantize": ([_P, _I64, _I64, _P, _P, _P, _P], _I32),
@@ -127,7 +135,9 @@ EXPORTED = ("flint_status_str", "flint_last_hip_error", "flint_workspace_bytes",
             # include/flint_int4.h
             "flint_int4_quantize", "flint_int4_dequantize", "flint_int4_gemv_workspace_bytes", "flint_int4_gemv",
             # include/flint_gemm.h
-            "flint_nvfp4_gemm_workspace_bytes", "flint_nvfp4_gemm")
+            "flint_nvfp4_gemm_workspace_bytes", "flint_nvfp4_gemm",
+            # include/flint_model.h
+            "flint_model_workspace_bytes", "flint_model_decode")
 
 
 def lib():
@@ -504,3 +514,46 @@ def nvfp4_gemm(q: NVFP4Tensor, X: torch.Tensor, mode: int = GEMM_A32, ws: torch.
     _check(_lib.flint_nvfp4_gemm(ctypes.byref(w), N, K, X.data_ptr(), T, mode, Y.data_ptr(), ws.data_ptr(),
                                  ws.numel(), _stream()), "flint_nvfp4_gemm")
     return Y
+
+
+# ------------------------------------------------------------- whole model --
+class Model:
+    """A whole decode model: per layer an attention layer (sliding or full),
+    then a dense MLP (the first n_dense layers) or a MoE layer, then the head.
+    Keeps the C structs, the host arrays and the tensors alive."""
+
+    def __init__(self, moe_dims: Dims, sliding: AttnDims, full: AttnDims, attn: list, is_full: list,
+                 k_caches: list, v_caches: list, dense: list, moe_layers: list, head: NVFP4Tensor, vocab: int,
+                 dense_width: int = 6144, eps: float = 1e-6):
+        n = len(attn)
+        assert len(is_full) == n == len(k_caches) == len(v_caches) == len(dense) + len(moe_layers)
+        self.keep = (attn, k_caches, v_caches, dense, moe_layers, head)
+        self._attn = (AttnLayer * n)(*[a.c() for a in attn])
+        self._is_full = (_I32 * n)(*[int(f) for f in is_full])
+        self._kc = (_P * n)(*[t.data_ptr() for t in k_caches])
+        self._vc = (_P * n)(*[t.data_ptr() for t in v_caches])
+        self._cap = (_I32 * n)(*[int(t.shape[1]) for t in k_caches])
+        nd = len(dense)
+        self._dense = (NVFP4 * max(1, 3 * nd))(*[m.c() for trio in dense for m in trio])
+        self._moe = (Layer * max(1, len(moe_layers)))(*[L.c() for L in moe_layers])
+        self.vocab = vocab
+        self.c = ModelC(n, nd, dense_width, moe_dims, sliding, full, ctypes.cast(self._is_full, _P),
+                        ctypes.cast(self._attn, _P), ctypes.cast(self._kc, _P), ctypes.cast(self._vc, _P),
+                        ctypes.cast(self._cap, _P), ctypes.cast(self._dense, _P) if nd else None,
+                        ctypes.cast(self._moe, _P) if moe_layers else None, head.c(), vocab, eps)
+        nbytes = _lib.flint_model_workspace_bytes(ctypes.byref(self.c))
+        if nbytes == 0:
+            raise ValueError("invalid model")
+        self.ws = torch.zeros(nbytes, dtype=torch.uint8, device=head.codes.device)
+
+    def decode(self, x: torch.Tensor, pos: int, logits: torch.Tensor | None = None, argmax: torch.Tensor | None = None,
+               want_logits: bool = True, h_out: torch.Tensor | None = None):
+        """x float32 [H] at position pos -> (logits [vocab] or None, argmax int32 [1])"""
+        if want_logits and logits is None:
+            logits = torch.empty(self.vocab, dtype=torch.float32, device=x.device)
+        if argmax is None:
+            argmax = torch.empty(1, dtype=torch.int32, device=x.device)
+        _check(_lib.flint_model_decode(ctypes.byref(self.c), x.data_ptr(), pos, _ptr(logits) if want_logits else None,
+                                       argmax.data_ptr(), _ptr(h_out), self.ws.data_ptr(), self.ws.numel(),
+                                       _stream()), "flint_model_decode")
+        return (logits if want_logits else None), argmax

@@ -7,7 +7,8 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("flint_moe.h", "flint_attn.h", "flint_int4.h", "flint_gemm.h")]
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("flint_moe.h", "flint_attn.h", "flint_int4.h", "flint_gemm.h",
+                                                       "flint_model.h")]
 
 
 @pytest.fixture(scope="module")
@@ -212,3 +213,33 @@ def test_gemm_rejections(F):
     assert g(10, 2000, 8, 0) == -8
     assert g(10, 2048, 8, 1, wsb=need - 1) == -4
     assert g(10, 2048, 8, 1, x=FAKE + 4) == -3
+
+
+def test_model_rejections(F):
+    L = F.lib()
+    m = F.NVFP4(FAKE, FAKE, FAKE)
+    n = 3
+    attn = (F.AttnLayer * n)(*[F.AttnLayer(m, m, m, m, FAKE, FAKE, FAKE) for _ in range(n)])
+    is_full = (ctypes.c_int32 * n)(0, 1, 0)
+    kc = (ctypes.c_void_p * n)(FAKE, FAKE, FAKE)
+    cap = (ctypes.c_int32 * n)(513, 1024, 513)
+    dense = (F.NVFP4 * 3)(m, m, m)
+    moe = (F.Layer * 2)(*[F.Layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, m, m, m) for _ in range(2)])
+    mc = F.ModelC(n, 1, 6144, F.dims_struct(), F.attn_dims_struct(), F.attn_dims_struct(window=0, rope=False),
+                  ctypes.cast(is_full, ctypes.c_void_p), ctypes.cast(attn, ctypes.c_void_p),
+                  ctypes.cast(kc, ctypes.c_void_p), ctypes.cast(kc, ctypes.c_void_p), ctypes.cast(cap, ctypes.c_void_p),
+                  ctypes.cast(dense, ctypes.c_void_p), ctypes.cast(moe, ctypes.c_void_p), m, 150144, 1e-6)
+    need = L.flint_model_workspace_bytes(ctypes.byref(mc))
+    assert need > 0
+    dec = lambda pos, wsb=need, x=FAKE: L.flint_model_decode(ctypes.byref(mc), x, pos, None, FAKE, None, FAKE, wsb,
+                                                             None)
+    assert dec(10, x=None) == -1
+    assert dec(-1) == -2
+    assert dec(2000) == -2                 # the full layer's cache holds 1024 positions
+    assert dec(10, wsb=need - 1) == -4
+    assert dec(10, x=FAKE + 4) == -3
+    is_full[1] = 2
+    assert dec(10) == -2
+    is_full[1] = 1
+    mc.n_dense = 4
+    assert L.flint_model_workspace_bytes(ctypes.byref(mc)) == 0
