@@ -443,6 +443,77 @@ def bench_gemm(args) -> int:
     return 0
 
 
+def full_attention_layer(l: int) -> bool:
+    """14 of 49 layers attend to the whole context; the pages do not give
+    which, so two of every seven (layers 3, 6, 10, 13, ...)."""
+    return l % 7 in (3, 6)
+
+
+def bench_model(args) -> int:
+    """One token through the whole model (flint_model_decode): 49 layers, each
+    attention (35 sliding-window with RoPE, 14 full-context) then a dense MLP
+    (layers 0-1, width 6,144) or a MoE layer (47 layers, the same weights as
+    the MoE stack), then the 150,144-row head with argmax, at a context of
+    `--context` positions.  Bytes per token: every weight the token touches
+    plus the keys and values it attends to."""
+    import torch
+
+    import synth
+    from nvfp4_bit_projection_amd import bytes_model as bm
+    from nvfp4_bit_projection_amd import flint, workload
+
+    torch.cuda.set_device(0)
+    H, V, NL, ND, DW = 2048, 150144, 49, 2, synth.DENSE_WIDTH
+    md = synth.MoEDims()
+    ctx, T = args.context, args.warmup + args.steps
+    is_full = [full_attention_layer(l) for l in range(NL)]
+    dims = [synth.FULL if f else synth.SLIDING for f in is_full]
+    caps = [ctx + T if f else 513 for f in is_full]
+    tmp = torch.empty(md.n_experts * md.expert_width * md.hidden, dtype=torch.float32, device="cuda")
+    moe = [workload.build_layer(md, seed=l, tmp=tmp) for l in range(NL - ND)]
+    del tmp
+    attn = [workload.build_attn(dims[l], 100 + l) for l in range(NL)]
+    dense = [workload.build_dense(200 + l, H, DW) for l in range(ND)]
+    kc = [workload.kv_cache(dims[l], 300 + l, caps[l], synth.K_CACHE) for l in range(NL)]
+    vc = [workload.kv_cache(dims[l], 300 + l, caps[l], synth.V_CACHE) for l in range(NL)]
+    head = workload.build_head(V, H)
+    ad = lambda d: flint.attn_dims_struct(H, d.n_q, d.n_kv, d.head_dim, d.window, d.rope, d.theta)
+    M = flint.Model(flint.dims_struct(md.hidden, md.n_experts, md.expert_width, md.top_k, md.shared_width),
+                    ad(synth.SLIDING), ad(synth.FULL), attn, is_full, kc, vc, dense, moe, head, V, dense_width=DW)
+    x = workload.tokens([synth.TOKEN_SEED0 + t for t in range(T)], H)
+    am = torch.empty((T, 1), dtype=torch.int32, device="cuda")
+    p0 = ctx - 1
+    for t in range(args.warmup):
+        M.decode(x[t], p0 + t, argmax=am[t], want_logits=False)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for t in range(args.warmup, T):
+        M.decode(x[t], p0 + t, argmax=am[t], want_logits=False)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    shape = bm.LayerShape()
+    w_attn = NL * ((32 + 2 * 4) * 128 * H * 9 // 16 + H * 32 * 128 * 9 // 16)
+    w_dense = ND * 3 * DW * H * 9 // 16
+    w_moe = (NL - ND) * bm.layer_bytes(shape)
+    pos_mid = p0 + args.warmup + args.steps // 2
+    kv = sum((min(pos_mid + 1, 513) if not f else pos_mid + 1) * 2048 for f in is_full)
+    nbytes = w_attn + w_dense + w_moe + bm.head_bytes(V, H) + kv
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"model 49 layers, context {ctx}: {ms * 1e3:.1f} us/token, {1000.0 / ms:.1f} tok/s, "
+        f"{nbytes / 1e9:.3f} GB/token (KV {kv / 1e6:.1f} MB), {gbs:.0f} GB/s")
+    print(json.dumps({"metric": f"whole-model decode tok/s (49 layers + head, context {ctx}, batch 1)",
+                      "value": round(1000.0 / ms, 2), "unit": "tok/s", "steps": args.steps, "warmup": args.warmup,
+                      "ms_per_step": round(ms, 4), "higher_is_better": True, "data": "synthetic", "dtype": "f32",
+                      "config": {"workload": f"flint49_ctx{ctx}_b1", "layers": NL, "dense_layers": ND,
+                                 "full_attention_layers": sum(is_full), "context": ctx},
+                      "roofline": {"bound": "hbm", "scope": "whole step (all kernels)", "achieved": round(gbs, 1),
+                                   "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                   "bytes_per_token": nbytes}}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -460,6 +531,8 @@ def main() -> int:
     ap.add_argument("--int4", action="store_true",
                     help="time the output head as group-64 affine INT4 against the NVFP4 head")
     ap.add_argument("--gemm", action="store_true", help="time the prefill GEMM (A32 and A4) on model shapes")
+    ap.add_argument("--model", action="store_true", help="time the whole 49-layer model (attention + dense/MoE)")
+    ap.add_argument("--context", type=int, default=1024, help="context length for --model")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (batch-1 decode; see DESIGN.md for how it would shard)",
@@ -475,6 +548,8 @@ def main() -> int:
         return bench_int4(args)
     if args.gemm:
         return bench_gemm(args)
+    if args.model:
+        return bench_model(args)
     if args.batch > 1:
         return bench_batch(args)
 
