@@ -136,7 +136,7 @@ int32_t flint_moe_route(const flint_moe_dims* dims, const float* router, const f
   if ((st = check_device())) return st;
   hipStream_t s = (hipStream_t)stream;
   float* logits = logits_opt ? logits_opt : carve<float>(ws, rw.logits);
-  hipError_t e = launch_route(*dims, router, x, B, -1.0f, logits, topk_idx, topk_w, carve<uint32_t>(ws, rw.tickets), s);
+  hipError_t e = launch_route(*dims, router, x, B, -1.0f, logits, topk_idx, topk_w, s);
   return e == hipSuccess ? FLINT_OK : hip_fail(e);
 }
 
@@ -159,7 +159,7 @@ int32_t flint_moe_route_ex(const flint_moe_dims* dims, const void* router, int32
   hipStream_t s = (hipStream_t)stream;
   float* logits = logits_opt ? logits_opt : carve<float>(ws, rw.logits);
   hipError_t e = launch_route_ex(*dims, router, router_dtype == FLINT_ROUTER_BF16, scoring == FLINT_SCORE_SIGMOID, x,
-                                 B, logits, topk_idx, topk_w, carve<uint32_t>(ws, rw.tickets), s);
+                                 B, logits, topk_idx, topk_w, s);
   return e == hipSuccess ? FLINT_OK : hip_fail(e);
 }
 
@@ -169,9 +169,8 @@ static int32_t decode_impl(const flint_moe_dims& d, const flint_moe_layer& L, co
   RouteWs rw(d.n_experts, B);
   char* base = static_cast<char*>(ws);
   float* logits = carve<float>(base + dw.route, rw.logits);
-  uint32_t* tickets = carve<uint32_t>(base + dw.route, rw.tickets);
   float* hact = carve<float>(ws, dw.hact);
-  hipError_t e = launch_route(d, L.router, x, B, norm_eps, logits, idx, w, tickets, s);
+  hipError_t e = launch_route(d, L.router, x, B, norm_eps, logits, idx, w, s);
   if (e == hipSuccess) e = launch_gateup(d, L, x, B, norm_eps, idx, hact, s);
   if (e == hipSuccess) e = launch_down(d, L, idx, w, hact, B, y, add_to_y, s);
   return e == hipSuccess ? FLINT_OK : hip_fail(e);
@@ -192,8 +191,7 @@ hipError_t flint::api_moe_run(const flint_moe_dims& d, const flint_moe_layer& L,
   char* base = static_cast<char*>(ws);
   int32_t* idx = carve<int32_t>(ws, dw.idx);
   float* w = carve<float>(ws, dw.wts);
-  hipError_t e = launch_route(d, L.router, x, 1, norm_eps, carve<float>(base + dw.route, rw.logits), idx, w,
-                              carve<uint32_t>(base + dw.route, rw.tickets), s);
+  hipError_t e = launch_route(d, L.router, x, 1, norm_eps, carve<float>(base + dw.route, rw.logits), idx, w, s);
   if (e == hipSuccess) e = launch_gateup(d, L, x, 1, norm_eps, idx, carve<float>(ws, dw.hact), s);
   if (e == hipSuccess) e = launch_down(d, L, idx, w, carve<float>(ws, dw.hact), 1, y, add, s);
   return e;
@@ -231,7 +229,7 @@ int32_t flint_lmhead_gemv(const flint_nvfp4* head, int32_t vocab, int32_t hidden
   if (ws_bytes < hw.total) return FLINT_E_WORKSPACE;
   if ((st = check_device())) return st;
   hipError_t e = launch_lmhead(*head, vocab, x, B, -1.0f, logits, argmax, carve<HeadPartial>(ws, hw.partials),
-                               carve<uint32_t>(ws, hw.tickets), (hipStream_t)stream);
+                               (hipStream_t)stream);
   return e == hipSuccess ? FLINT_OK : hip_fail(e);
 }
 
@@ -344,8 +342,7 @@ static int32_t stack_decode_impl(const flint_stack_plan* plan, const float* x, i
       if (st) return st;
     }
     e = launch_lmhead(plan->head, plan->vocab, h, 1, eps, logits ? logits + (size_t)t * plan->vocab : nullptr,
-                      argmax + t, carve<HeadPartial>(base + sw.head, hw.partials),
-                      carve<uint32_t>(base + sw.head, hw.tickets), s);
+                      argmax + t, carve<HeadPartial>(base + sw.head, hw.partials), s);
     if (e != hipSuccess) return hip_fail(e);
   }
   return FLINT_OK;

@@ -26,10 +26,9 @@ struct HeadPartial {
 
 // Workspace layouts.  Every section starts on a 256-byte boundary.
 struct RouteWs {
-  size_t tickets, logits, total;
+  size_t logits, total;
   RouteWs(int E, int B) {
     size_t o = 0;
-    tickets = o; o = align_up(o + 4 * (size_t)B, 256);
     logits = o; o = align_up(o + 4 * (size_t)B * E, 256);
     total = o;
   }
@@ -49,10 +48,9 @@ struct DecodeWs {
 };
 
 struct HeadWs {
-  size_t tickets, partials, total;
+  size_t partials, total;
   explicit HeadWs(int B) {
     size_t o = 0;
-    tickets = o; o = align_up(o + 4 * (size_t)B, 256);
     partials = o; o = align_up(o + sizeof(HeadPartial) * (size_t)B * kHeadBlocks, 256);
     total = o;
   }
@@ -116,16 +114,16 @@ hipError_t launch_batch_step(const flint_moe_dims& d, const flint_moe_layer* lay
 
 // ---- kernel launchers (kernels.hip); all return the hipError_t of the launch
 hipError_t launch_route(const flint_moe_dims& d, const float* router, const float* x, int B, float norm_eps,
-                        float* logits, int32_t* idx, float* w, uint32_t* tickets, hipStream_t s);
+                        float* logits, int32_t* idx, float* w, hipStream_t s);
 // router variants: BF16 router rows and/or sigmoid-score weights, no norm
 hipError_t launch_route_ex(const flint_moe_dims& d, const void* router, bool bf16, bool sigmoid, const float* x,
-                           int B, float* logits, int32_t* idx, float* w, uint32_t* tickets, hipStream_t s);
+                           int B, float* logits, int32_t* idx, float* w, hipStream_t s);
 hipError_t launch_gateup(const flint_moe_dims& d, const flint_moe_layer& L, const float* x, int B, float norm_eps,
                          const int32_t* idx, float* hact, hipStream_t s);
 hipError_t launch_down(const flint_moe_dims& d, const flint_moe_layer& L, const int32_t* idx, const float* w,
                        const float* hact, int B, float* y, bool add_to_y, hipStream_t s);
 hipError_t launch_lmhead(const flint_nvfp4& head, int vocab, const float* x, int B, float norm_eps, float* logits,
-                         int32_t* argmax, HeadPartial* partials, uint32_t* tickets, hipStream_t s);
+                         int32_t* argmax, HeadPartial* partials, hipStream_t s);
 hipError_t launch_quantize(const float* w, int64_t n_mats, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, float* tscales, uint32_t* amax_bits, hipStream_t s);
 hipError_t launch_dequantize(const flint_nvfp4& q, int64_t rows, int64_t cols, float* out, hipStream_t s);

@@ -435,8 +435,7 @@ __global__ void k_copy_f32(const float* __restrict__ s, float* __restrict__ d, i
 
 // --------------------------------------------------------------- launchers --
 hipError_t launch_route(const flint_moe_dims& d, const float* router, const float* x, int B, float norm_eps,
-                        float* logits, int32_t* idx, float* w, uint32_t* tickets, hipStream_t s) {
-  (void)tickets;
+                        float* logits, int32_t* idx, float* w, hipStream_t s) {
   dim3 grid((d.n_experts + 3) / 4, B);
   k_route<float><<<grid, 256, 0, s>>>(router, d.n_experts, x, norm_eps, logits);
   hipError_t e = hipGetLastError();
@@ -446,8 +445,7 @@ hipError_t launch_route(const flint_moe_dims& d, const float* router, const floa
 }
 
 hipError_t launch_route_ex(const flint_moe_dims& d, const void* router, bool bf16, bool sigmoid, const float* x,
-                           int B, float* logits, int32_t* idx, float* w, uint32_t* tickets, hipStream_t s) {
-  (void)tickets;
+                           int B, float* logits, int32_t* idx, float* w, hipStream_t s) {
   dim3 grid((d.n_experts + 3) / 4, B);
   if (bf16)
     k_route<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(router), d.n_experts, x, -1.0f, logits);
@@ -475,9 +473,8 @@ hipError_t launch_down(const flint_moe_dims& d, const flint_moe_layer& L, const 
 }
 
 hipError_t launch_lmhead(const flint_nvfp4& head, int vocab, const float* x, int B, float norm_eps, float* logits,
-                         int32_t* argmax, HeadPartial* partials, uint32_t* tickets, hipStream_t s) {
+                         int32_t* argmax, HeadPartial* partials, hipStream_t s) {
   dim3 grid(kHeadBlocks, B);
-  (void)tickets;
   k_lmhead<<<grid, 256, 0, s>>>(head.codes, head.scales, head.tscale, vocab, x, norm_eps, logits, argmax, partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

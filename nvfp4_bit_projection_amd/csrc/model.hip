@@ -109,8 +109,7 @@ int32_t flint_model_decode(const flint_model* m, const float* x, int32_t pos, fl
   if (e == hipSuccess) {
     const HeadWs hw(1);
     e = launch_lmhead(m->head, m->vocab, h, 1, m->eps, logits_opt, argmax,
-                      reinterpret_cast<HeadPartial*>(static_cast<char*>(sc) + hw.partials),
-                      reinterpret_cast<uint32_t*>(static_cast<char*>(sc) + hw.tickets), s);
+                      reinterpret_cast<HeadPartial*>(static_cast<char*>(sc) + hw.partials), s);
   }
   if (e == hipSuccess && h_out_opt) {
     k_copy_vec<<<8, 256, 0, s>>>(h, h_out_opt, kHidden);
