@@ -390,8 +390,25 @@ def bench_gemm(args) -> int:
     torch.cuda.set_device(0)
     peak = 2500.0  # dense fp16 MFMA TFLOP/s
     out = []
-    for name, N, K in (("shared_gate_1024x2048", 1024, 2048), ("dense_gate_6144x2048", 6144, 2048),
-                       ("dense_down_2048x6144", 2048, 6144), ("head_150144x2048", 150144, 2048)):
+    shapes = (("shared_gate_1024x2048", 1024, 2048), ("dense_gate_6144x2048", 6144, 2048),
+              ("dense_down_2048x6144", 2048, 6144), ("head_150144x2048", 150144, 2048))
+    if args.gemm_case:  # one shape, token count and mode, a few plain calls (for counter runs)
+        name, T, mode = args.gemm_case.split(":")
+        N, K = next((n, k) for nm, n, k in shapes if nm == name)
+        w = torch.empty(N * K, dtype=torch.float32, device="cuda")
+        synth.normal_device(7, synth.stream_id(synth.HEAD), N * K, w, std=synth.WEIGHT_STD)
+        q = flint.quantize(w.view(N, K))
+        del w
+        X = torch.empty(int(T) * K, dtype=torch.float32, device="cuda")
+        synth.normal_device(8, synth.stream_id(synth.TOKEN), int(T) * K, X)
+        ws = flint.gemm_workspace(int(T), K, int(mode))
+        Y = torch.empty((int(T), N), dtype=torch.float32, device="cuda")
+        for _ in range(args.steps):
+            flint.nvfp4_gemm(q, X.view(int(T), K), int(mode), ws=ws, Y=Y)
+        torch.cuda.synchronize()
+        log(f"gemm case {args.gemm_case}: {args.steps} calls done")
+        return 0
+    for name, N, K in shapes:
         w = torch.empty(N * K, dtype=torch.float32, device="cuda")
         synth.normal_device(7, synth.stream_id(synth.HEAD), N * K, w, std=synth.WEIGHT_STD)
         q = flint.quantize(w.view(N, K))
@@ -531,6 +548,7 @@ def main() -> int:
     ap.add_argument("--int4", action="store_true",
                     help="time the output head as group-64 affine INT4 against the NVFP4 head")
     ap.add_argument("--gemm", action="store_true", help="time the prefill GEMM (A32 and A4) on model shapes")
+    ap.add_argument("--gemm-case", default="", help="with --gemm: only SHAPE:T:MODE, e.g. head_150144x2048:512:0")
     ap.add_argument("--model", action="store_true", help="time the whole 49-layer model (attention + dense/MoE)")
     ap.add_argument("--context", type=int, default=1024, help="context length for --model")
     args = ap.parse_args()
