@@ -131,13 +131,16 @@ def bench_batch(args) -> int:
     x = workload.tokens([synth.TOKEN_SEED0 + t for t in range(T * B)], dims.hidden).view(T, B, dims.hidden)
     ws = flint.workspace(flint.OP_STACK_BATCH, stack.dims, B, V, L)
     argmax = torch.empty((T, B), dtype=torch.int32, device="cuda")
+    tiled = bool(args.tiled)
+    if tiled:
+        stack.make_batch_tiles()
     for t in range(args.warmup):
-        stack.decode_batch(x[t], argmax=argmax[t], want_logits=False, ws=ws)
+        stack.decode_batch(x[t], argmax=argmax[t], want_logits=False, ws=ws, tiled=tiled)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     for t in range(args.warmup, T):
-        stack.decode_batch(x[t], argmax=argmax[t], want_logits=False, ws=ws)
+        stack.decode_batch(x[t], argmax=argmax[t], want_logits=False, ws=ws, tiled=tiled)
     ev1.record()
     torch.cuda.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / args.steps
@@ -152,7 +155,7 @@ def bench_batch(args) -> int:
     step_bytes = total / args.steps
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
     tok_s = B * 1000.0 / ms_per_step
-    log(f"batch {B}: {args.steps} steps, {ms_per_step * 1e3:.1f} us/step, {tok_s:.1f} tok/s, "
+    log(f"batch {B}{' tiled' if tiled else ''}: {args.steps} steps, {ms_per_step * 1e3:.1f} us/step, {tok_s:.1f} tok/s, "
         f"{step_bytes / 1e9:.3f} GB/step, {gbs:.1f} GB/s")
     result = {
         "metric": f"decode tok/s (47-layer NVFP4 MoE+lm_head, batch {B}) and achieved HBM GB/s vs peak",
@@ -161,7 +164,8 @@ def bench_batch(args) -> int:
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"stack47_lmhead_b{B}", "layers": L, "hidden": 2048, "experts": 256, "top_k": 6,
                    "expert_width": 512, "shared_width": 1024, "vocab": V, "batch": B,
-                   "weights": "nvfp4 e2m1 + e4m3/16 + fp32 tensor scale; fp32 router"},
+                   "weights": "nvfp4 e2m1 + e4m3/16 + fp32 tensor scale; fp32 router",
+                   "gate_up_layout": "tiled copy" if tiled else "row-major"},
         "roofline": {"bound": "hbm", "scope": "whole step (all kernels)", "achieved": round(gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_step": round(step_bytes)},
@@ -541,6 +545,8 @@ def main() -> int:
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--batch", type=int, default=1,
                     help="tokens per step; above 1 the batched step (experts deduplicated per layer) is timed")
+    ap.add_argument("--tiled", action="store_true",
+                    help="with --batch: read the gate/up weights from the tiled copy (flint_stack_batch_tiles)")
     ap.add_argument("--router", action="store_true",
                     help="time the router call alone in its four variants (fp32/BF16 router, softmax/sigmoid)")
     ap.add_argument("--attn", action="store_true",

@@ -269,6 +269,25 @@ int32_t flint_stack_decode_batch(const flint_stack_plan* plan /*[host]*/, const 
                                  float* logits, int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* Optional tiled copy of every layer's gate and up matrices (routed experts
+ * and the shared expert) for the batched step: the same codes and scales,
+ * reordered so that each 16-row x 256-column block is one contiguous 2 KB
+ * run of codes and one 256-byte run of scales, in the order the matrix-core
+ * kernel reads them (2 (E I + Is) (H/2 + H/16) bytes per layer, 1.24 GB for
+ * the 47 Flint layers).
+ * flint_stack_batch_tiles_bytes: size of that copy for L layers (0 if the
+ * sizes are not supported by the batched step).  flint_stack_batch_tiles
+ * fills `tiles` (device, caller-owned) from the plan's layers; call it again
+ * after the weights change.  flint_stack_decode_batch_tiled is
+ * flint_stack_decode_batch with the gate/up rows read from `tiles`
+ * (bit-identical results). */
+size_t flint_stack_batch_tiles_bytes(const flint_moe_dims* dims /*[host]*/, int32_t L);
+int32_t flint_stack_batch_tiles(const flint_stack_plan* plan /*[host]*/, void* tiles, size_t tiles_bytes,
+                                void* stream);
+int32_t flint_stack_decode_batch_tiled(const flint_stack_plan* plan /*[host]*/, const void* tiles, const float* x,
+                                       int32_t B, float eps, float* logits, int32_t* argmax, int32_t* routes_opt,
+                                       void* ws, size_t ws_bytes, void* stream);
+
 /* Stack workspace contract: zero-filled before the first call; afterwards it
  * carries the persistent schedule's epoch counter and must not be changed
  * between calls.  Every wait inside the persistent kernel is bounded; if one

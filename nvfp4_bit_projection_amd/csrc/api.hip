@@ -382,6 +382,48 @@ int32_t flint_stack_decode_batch(const flint_stack_plan* plan, const float* x, i
   return e == hipSuccess ? FLINT_OK : hip_fail(e);
 }
 
+size_t flint_stack_batch_tiles_bytes(const flint_moe_dims* dims, int32_t L) {
+  if (check_dims(dims) != FLINT_OK || L < 1 || !batch_supported(*dims, 1)) return 0;
+  return (size_t)L * batch_tiles_layer_bytes(*dims);
+}
+
+int32_t flint_stack_batch_tiles(const flint_stack_plan* plan, void* tiles, size_t tiles_bytes, void* stream) {
+  if (!plan || !tiles || !plan->layers) return FLINT_E_NULL;
+  int32_t st;
+  if ((st = check_dims(&plan->dims))) return st;
+  const size_t need = flint_stack_batch_tiles_bytes(&plan->dims, plan->n_layers);
+  if (need == 0) return FLINT_E_UNSUPPORTED;
+  if (!aligned16(tiles)) return FLINT_E_ALIGN;
+  if (tiles_bytes < need) return FLINT_E_WORKSPACE;
+  for (int l = 0; l < plan->n_layers; ++l)
+    if ((st = check_layer(&plan->layers[l]))) return st;
+  if ((st = check_device())) return st;
+  hipError_t e = launch_batch_tiles(plan->dims, plan->layers, plan->n_layers, static_cast<uint8_t*>(tiles),
+                                    (hipStream_t)stream);
+  return e == hipSuccess ? FLINT_OK : hip_fail(e);
+}
+
+int32_t flint_stack_decode_batch_tiled(const flint_stack_plan* plan, const void* tiles, const float* x, int32_t B,
+                                       float eps, float* logits, int32_t* argmax, int32_t* routes_opt, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  int32_t st;
+  if (!plan || !tiles || !x || !argmax || !ws) return FLINT_E_NULL;
+  if (!plan->layers || !plan->table) return FLINT_E_NULL;
+  const flint_moe_dims& d = plan->dims;
+  if ((st = check_dims(&d))) return st;
+  if (B < 1 || B > kMaxBatch || !(eps >= 0.0f)) return FLINT_E_DIMS;
+  if (!batch_supported(d, B)) return FLINT_E_UNSUPPORTED;
+  if (!aligned16(tiles) || !aligned16(x) || (logits && !aligned4(logits)) || !aligned4(argmax) ||
+      (routes_opt && !aligned4(routes_opt)) || !aligned16(ws))
+    return FLINT_E_ALIGN;
+  if (ws_bytes < BatchWs(d, B, plan->vocab).total) return FLINT_E_WORKSPACE;
+  if ((st = check_device())) return st;
+  hipError_t e = launch_batch_step_tiled(d, plan->layers, plan->n_layers, plan->head, plan->vocab, x, B, eps, logits,
+                                         argmax, routes_opt, ws, (hipStream_t)stream,
+                                         static_cast<const uint8_t*>(tiles));
+  return e == hipSuccess ? FLINT_OK : hip_fail(e);
+}
+
 int32_t flint_stack_error(const void* ws, size_t ws_bytes, int32_t* error) {
   if (!ws || !error) return FLINT_E_NULL;
   if (ws_bytes < 256) return FLINT_E_WORKSPACE;

@@ -26,7 +26,10 @@
 #include <float.h>
 #include <limits.h>
 
+#include <type_traits>
+
 #include "flint_device.h"
+#include "flint_common.h"
 #include "flint_internal.h"
 
 namespace flint {
@@ -329,25 +332,48 @@ struct FmtBF16 {
 template <class F>
 constexpr int mm_buf_bytes() { return F::P * kMmStage * 2; }
 
-// One wave's two 16-row weight tiles: this lane's row (m) of each, codes and
-// scales of a matrix with K columns.
+// One wave's two 16-row weight tiles, in one of two layouts (a type with a
+// static load).
+// Row-major matrices: c, s point at this lane's first code and scale bytes
+// of chunk 0 of each tile; the lane's 32 code bytes of a chunk are contiguous
+// (second half 16 bytes on) and chunks are 128 code / 16 scale bytes apart,
+// so one address per tile serves every chunk (offsets fit the instruction).
+// Tiled copies (flint_stack_batch_tiles): each (16-row tile, chunk) is one
+// 2 KB block of codes, lane L = 16 q + m holding bytes 16 L and 1024 + 16 L,
+// and one 256-byte block of scales (4 L); the wave's tiles are buffer
+// resources rc, rs (16 KB of codes, 2 KB of scales) read at the lane offset
+// plus a constant.
 struct MmTiles {
   const uint8_t* c[2];
   const uint8_t* s[2];
+  rsrc_t rc[2], rs[2];
+  uint32_t lane;
 };
 struct MmRegs {  // a lane's weight bytes of one chunk
   uint4 c[2][2];
   uint32_t s[2];
 };
-__device__ __forceinline__ void mm_load_w(const MmTiles& T, int u, int q, MmRegs& R) {
+struct MmRowMajor {
+  static __device__ __forceinline__ void load(const MmTiles& T, int u, MmRegs& R) {
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const uint8_t* cp = T.c[rt] + (kMmChunk / 2) * u + 32 * q;
-    R.c[rt][0] = ld_nt_u4(cp);
-    R.c[rt][1] = ld_nt_u4(cp + 16);
-    R.s[rt] = ld_nt_u32(T.s[rt] + (kMmChunk / 16) * u + 4 * q);
+    for (int rt = 0; rt < 2; ++rt) {
+      const uint8_t* cp = T.c[rt] + (kMmChunk / 2) * u;
+      R.c[rt][0] = ld_nt_u4(cp);
+      R.c[rt][1] = ld_nt_u4(cp + 16);
+      R.s[rt] = ld_nt_u32(T.s[rt] + (kMmChunk / 16) * u);
+    }
   }
-}
+};
+struct MmTiled {
+  static __device__ __forceinline__ void load(const MmTiles& T, int u, MmRegs& R) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      R.c[rt][0] = bload_u4_nt(T.rc[rt], 16 * T.lane + 2048 * u);
+      R.c[rt][1] = bload_u4_nt(T.rc[rt], 16 * T.lane + 2048 * u + 1024);
+      R.s[rt] = __builtin_amdgcn_raw_buffer_load_b32(T.rs[rt], 4 * T.lane + 256 * u, 0, kAuxNT);
+    }
+  }
+};
 
 // Staged activations: the pass's tokens padded to R rows (a power of two, 4
 // .. 32) and a K segment of kseg = min(8192 / R, K) values, P planes, in LDS
@@ -412,11 +438,11 @@ __device__ __forceinline__ void mm_chunk(const MmRegs& R, const unsigned char* b
 // requested kAhead chunks before they are multiplied (the chunk loop is
 // unrolled, so every chunk has its own registers).
 constexpr int kAhead = 3;
-template <class F, int NCH>
+template <class F, int NCH, class Lay = MmRowMajor>
 __device__ __forceinline__ void mm_pass_n(const MmTiles& T, rsrc_t rA, int a_rows, const int* srow, int nt,
                                           unsigned char* abuf, int wv, int lane, f32x4_t (&acc)[2][2]) {
   constexpr int K = NCH * kMmChunk;
-  const int q = lane >> 4, ntt = nt > 16 ? 2 : 1;
+  const int ntt = nt > 16 ? 2 : 1;
   const int Rrows = nt <= 4 ? 4 : nt <= 8 ? 8 : nt <= 16 ? 16 : 32;
   const int kseg = kMmStage / Rrows < K ? kMmStage / Rrows : K, cps = kseg / kMmChunk;
 #pragma unroll
@@ -425,7 +451,7 @@ __device__ __forceinline__ void mm_pass_n(const MmTiles& T, rsrc_t rA, int a_row
     for (int tt = 0; tt < 2; ++tt) acc[rt][tt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   MmRegs R[NCH];
 #pragma unroll
-  for (int u = 0; u < NCH && u < kAhead; ++u) mm_load_w(T, u, q, R[u]);
+  for (int u = 0; u < NCH && u < kAhead; ++u) Lay::load(T, u, R[u]);
 #pragma unroll
   for (int u = 0; u < NCH; ++u) {
     if (u % cps == 0) {  // next segment: everyone is done with the buffer, then copy
@@ -434,7 +460,7 @@ __device__ __forceinline__ void mm_pass_n(const MmTiles& T, rsrc_t rA, int a_row
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies are in
       __syncthreads();
     }
-    if (u + kAhead < NCH) mm_load_w(T, u + kAhead, q, R[u + kAhead]);
+    if (u + kAhead < NCH) Lay::load(T, u + kAhead, R[u + kAhead]);
     mm_chunk<F>(R[u], abuf, Rrows, kseg, u % cps, ntt, lane, acc);
   }
 }
@@ -505,10 +531,12 @@ __global__ __launch_bounds__(kThreads) void k_bnorm(float* __restrict__ h, const
 // normalised tokens up [2][B][H], and writes h = silu(gate) * up for each
 // token as three bf16 planes: hrp [3][B*k][I] by pair id (routed),
 // hsp [3][B][Is] by token (shared).
+template <bool TILED>
 __global__ __launch_bounds__(kMmThreads, 3) void k_mm_gateup(flint_moe_layer L, int I, int Is, int k, int B,
                                                              int Umax, const uint16_t* __restrict__ up,
                                                              const int32_t* __restrict__ bk, uint16_t* __restrict__ hrp,
-                                                             uint16_t* __restrict__ hsp, int nb) {
+                                                             uint16_t* __restrict__ hsp, int nb,
+                                                             const uint8_t* tiles, int E) {
   __shared__ __align__(16) unsigned char abuf[mm_buf_bytes<FmtF16>()];
   __shared__ int srow[kMmTok], orow[kMmTok];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, m = lane & 15, q = lane >> 4;
@@ -526,19 +554,37 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_mm_gateup(flint_moe_layer L, 
   const int row = r0 + 16 * wv + m;
   MmTiles T;
   float Sg, Su;
+  if (TILED) {
+    // this layer's tiled gate and up matrices (routed experts' tiles, then
+    // the shared expert's): codes [2][nt][H/256][2 KB], then scales
+    // [2][nt][H/256][256 B], nt = E I / 16 + Is / 16
+    const size_t ntile = (size_t)E * (I / 16) + Is / 16;
+    const size_t mat_c = ntile * 16 * (kHidden / 2), mat_s = ntile * 16 * (kHidden / 16);
+    const int wtile = __builtin_amdgcn_readfirstlane((r0 + 16 * wv) / 16);  // the same in every lane
+    const size_t tile = (sh ? (size_t)E * (I / 16) : (size_t)e * (I / 16)) + wtile;
+    const uint8_t* tc = tiles + tile * (kHidden / kMmChunk) * 2048;
+    const uint8_t* ts = tiles + 2 * mat_c + tile * (kHidden / kMmChunk) * 256;
+    T.rc[0] = make_rsrc(tc, (kHidden / kMmChunk) * 2048);
+    T.rc[1] = make_rsrc(tc + mat_c, (kHidden / kMmChunk) * 2048);
+    T.rs[0] = make_rsrc(ts, (kHidden / kMmChunk) * 256);
+    T.rs[1] = make_rsrc(ts + mat_s, (kHidden / kMmChunk) * 256);
+    T.lane = lane;
+  } else if (sh) {
+    T.c[0] = L.shared_gate.codes + (size_t)row * (kHidden / 2) + 32 * q;
+    T.s[0] = L.shared_gate.scales + (size_t)row * (kHidden / 16) + 4 * q;
+    T.c[1] = L.shared_up.codes + (size_t)row * (kHidden / 2) + 32 * q;
+    T.s[1] = L.shared_up.scales + (size_t)row * (kHidden / 16) + 4 * q;
+  } else {
+    const size_t er = (size_t)e * I + row;
+    T.c[0] = L.gate_codes + er * (kHidden / 2) + 32 * q;
+    T.s[0] = L.gate_scales + er * (kHidden / 16) + 4 * q;
+    T.c[1] = L.up_codes + er * (kHidden / 2) + 32 * q;
+    T.s[1] = L.up_scales + er * (kHidden / 16) + 4 * q;
+  }
   if (sh) {
-    T.c[0] = L.shared_gate.codes + (size_t)row * (kHidden / 2);
-    T.s[0] = L.shared_gate.scales + (size_t)row * (kHidden / 16);
-    T.c[1] = L.shared_up.codes + (size_t)row * (kHidden / 2);
-    T.s[1] = L.shared_up.scales + (size_t)row * (kHidden / 16);
     Sg = *L.shared_gate.tscale;
     Su = *L.shared_up.tscale;
   } else {
-    const size_t er = (size_t)e * I + row;
-    T.c[0] = L.gate_codes + er * (kHidden / 2);
-    T.s[0] = L.gate_scales + er * (kHidden / 16);
-    T.c[1] = L.up_codes + er * (kHidden / 2);
-    T.s[1] = L.up_scales + er * (kHidden / 16);
     Sg = L.expert_tscales[3 * e + 0];
     Su = L.expert_tscales[3 * e + 1];
   }
@@ -563,7 +609,8 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_mm_gateup(flint_moe_layer L, 
     }
     __syncthreads();
     f32x4_t acc[2][2];
-    mm_pass_n<FmtF16, kHidden / kMmChunk>(T, rA, B, srow, nt, abuf, wv, lane, acc);
+    mm_pass_n<FmtF16, kHidden / kMmChunk, typename std::conditional<TILED, MmTiled, MmRowMajor>::type>(
+        T, rA, B, srow, nt, abuf, wv, lane, acc);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -610,12 +657,12 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_mm_down(flint_moe_layer L, in
   for (int rt = 0; rt < 2; ++rt) {
     const int row = rbase + 16 * rt + m;
     if (sh) {
-      T.c[rt] = L.shared_down.codes + (size_t)row * (Is / 2);
-      T.s[rt] = L.shared_down.scales + (size_t)row * (Is / 16);
+      T.c[rt] = L.shared_down.codes + (size_t)row * (Is / 2) + 32 * q;
+      T.s[rt] = L.shared_down.scales + (size_t)row * (Is / 16) + 4 * q;
     } else {
       const size_t er = (size_t)e * kHidden + row;
-      T.c[rt] = L.down_codes + er * (I / 2);
-      T.s[rt] = L.down_scales + er * (I / 16);
+      T.c[rt] = L.down_codes + er * (I / 2) + 32 * q;
+      T.s[rt] = L.down_scales + er * (I / 16) + 4 * q;
     }
   }
   const float S = sh ? *L.shared_down.tscale : L.expert_tscales[3 * e + 2];
@@ -676,8 +723,8 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_mm_head(const uint8_t* codes,
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const int row = min(rbase + 16 * rt + m, vocab - 1);  // rows past the end read the last row; dropped
-    T.c[rt] = codes + (size_t)row * (kHidden / 2);
-    T.s[rt] = scales + (size_t)row * (kHidden / 16);
+    T.c[rt] = codes + (size_t)row * (kHidden / 2) + 32 * q;
+    T.s[rt] = scales + (size_t)row * (kHidden / 16) + 4 * q;
   }
   const float S = *tscale;
   const rsrc_t rA = make_rsrc(zp, (uint64_t)FmtF16::P * B * kHidden * 2);
@@ -771,6 +818,63 @@ BatchWs::BatchWs(const flint_moe_dims& d, int B, int vocab) {
   total = o;
 }
 
+// Tiled copy of one layer's gate and up matrices for k_mm_gateup: the routed
+// experts' 16-row tiles (expert e, rows 16 j .. 16 j + 15 at tile e I/16 + j),
+// then the shared expert's (tile E I/16 + j); codes [2][nt][H/256][2 KB], then
+// scales [2][nt][H/256][256 B] (the MmTiled layout).  One thread per (matrix,
+// tile, chunk, lane L = 16 q + m): row 16 j + m, K values 64 q .. +63 of the
+// chunk.
+__global__ __launch_bounds__(kThreads) void k_tile_gateup(flint_moe_layer L, int E, int I, int Is,
+                                                          uint8_t* __restrict__ dst) {
+  constexpr int nch = kHidden / kMmChunk;
+  const size_t nrt = (size_t)E * (I / 16), ntile = nrt + Is / 16;
+  const size_t mat_c = ntile * 16 * (kHidden / 2), mat_s = ntile * 16 * (kHidden / 16);
+  const size_t per_mat = ntile * nch * 64, total = 2 * per_mat;
+  for (size_t i = blockIdx.x * (size_t)kThreads + threadIdx.x; i < total; i += (size_t)gridDim.x * kThreads) {
+    const int kind = (int)(i / per_mat);
+    size_t r = i % per_mat;
+    const int lane = (int)(r % 64);
+    r /= 64;
+    const int u = (int)(r % nch);
+    r /= nch;  // the tile
+    const int m = lane & 15, q = lane >> 4;
+    const uint8_t *sc, *ss;
+    if (r < nrt) {
+      const size_t row = r * 16 + m;  // e I + 16 j + m
+      sc = (kind ? L.up_codes : L.gate_codes) + row * (kHidden / 2);
+      ss = (kind ? L.up_scales : L.gate_scales) + row * (kHidden / 16);
+    } else {
+      const size_t row = (r - nrt) * 16 + m;
+      const flint_nvfp4& W = kind ? L.shared_up : L.shared_gate;
+      sc = W.codes + row * (kHidden / 2);
+      ss = W.scales + row * (kHidden / 16);
+    }
+    sc += (kMmChunk / 2) * u + 32 * q;
+    ss += (kMmChunk / 16) * u + 4 * q;
+    uint8_t* dc = dst + kind * mat_c + (r * nch + u) * 2048 + 16 * lane;
+    uint8_t* ds = dst + 2 * mat_c + kind * mat_s + (r * nch + u) * 256 + 4 * lane;
+    *reinterpret_cast<uint4*>(dc) = *reinterpret_cast<const uint4*>(sc);
+    *reinterpret_cast<uint4*>(dc + 1024) = *reinterpret_cast<const uint4*>(sc + 16);
+    *reinterpret_cast<uint32_t*>(ds) = *reinterpret_cast<const uint32_t*>(ss);
+  }
+}
+
+size_t batch_tiles_layer_bytes(const flint_moe_dims& d) {
+  return 2 * ((size_t)d.n_experts * d.expert_width + d.shared_width) * (kHidden / 2 + kHidden / 16);
+}
+
+hipError_t launch_batch_tiles(const flint_moe_dims& d, const flint_moe_layer* layers, int L, uint8_t* tiles,
+                              hipStream_t s) {
+  const size_t per = batch_tiles_layer_bytes(d);
+  for (int l = 0; l < L; ++l) {
+    k_tile_gateup<<<2048, kThreads, 0, s>>>(layers[l], d.n_experts, d.expert_width, d.shared_width,
+                                            tiles + (size_t)l * per);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 // 4-byte word copy (the step uses kernels only, so it can be captured in a
 // HIP graph)
 __global__ __launch_bounds__(kThreads) void k_copy_words(const uint32_t* __restrict__ src,
@@ -778,9 +882,9 @@ __global__ __launch_bounds__(kThreads) void k_copy_words(const uint32_t* __restr
   for (int i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads) dst[i] = src[i];
 }
 
-hipError_t launch_batch_step(const flint_moe_dims& d, const flint_moe_layer* layers, int L, const flint_nvfp4& head,
-                             int vocab, const float* x, int B, float eps, float* logits, int32_t* argmax,
-                             int32_t* routes, void* ws, hipStream_t s) {
+hipError_t launch_batch_step_tiled(const flint_moe_dims& d, const flint_moe_layer* layers, int L,
+                                   const flint_nvfp4& head, int vocab, const float* x, int B, float eps, float* logits,
+                                   int32_t* argmax, int32_t* routes, void* ws, hipStream_t s, const uint8_t* tiles) {
   const BatchWs w(d, B, vocab);
   char* base = static_cast<char*>(ws);
   float* h = reinterpret_cast<float*>(base + w.h);
@@ -811,7 +915,12 @@ hipError_t launch_batch_step(const flint_moe_dims& d, const flint_moe_layer* lay
       k_copy_words<<<1, kThreads, 0, s>>>(reinterpret_cast<const uint32_t*>(idx),
                                           reinterpret_cast<uint32_t*>(routes + (size_t)l * nb), nb);
     k_bucket<<<1, kThreads, 0, s>>>(idx, nb, E, bk);
-    k_mm_gateup<<<dim3(gu_x, Umax + 1), kMmThreads, 0, s>>>(Ly, I, Is, k, B, Umax, up, bk, hrp, hsp, nb);
+    if (tiles)
+      k_mm_gateup<true><<<dim3(gu_x, Umax + 1), kMmThreads, 0, s>>>(
+          Ly, I, Is, k, B, Umax, up, bk, hrp, hsp, nb, tiles + (size_t)l * batch_tiles_layer_bytes(d), E);
+    else
+      k_mm_gateup<false><<<dim3(gu_x, Umax + 1), kMmThreads, 0, s>>>(Ly, I, Is, k, B, Umax, up, bk, hrp, hsp, nb,
+                                                                      nullptr, E);
     k_mm_down<<<dim3(kHidden / kMmRows, Umax + 1), kMmThreads, 0, s>>>(Ly, I, Is, B, Umax, hrp, hsp, bk, wts, dr, ds,
                                                                         nb);
     // the residual update and the next norm (after the last layer: the
@@ -824,6 +933,12 @@ hipError_t launch_batch_step(const flint_moe_dims& d, const flint_moe_layer* lay
   k_mm_head<<<hb, kMmThreads, 0, s>>>(head.codes, head.scales, head.tscale, vocab, up, B, logits, parts);
   k_bargmax<<<B, 64, 0, s>>>(parts, hb, argmax);
   return hipGetLastError();
+}
+
+hipError_t launch_batch_step(const flint_moe_dims& d, const flint_moe_layer* layers, int L, const flint_nvfp4& head,
+                             int vocab, const float* x, int B, float eps, float* logits, int32_t* argmax,
+                             int32_t* routes, void* ws, hipStream_t s) {
+  return launch_batch_step_tiled(d, layers, L, head, vocab, x, B, eps, logits, argmax, routes, ws, s, nullptr);
 }
 
 }  // namespace flint

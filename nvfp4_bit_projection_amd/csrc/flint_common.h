@@ -37,4 +37,13 @@ int32_t dense_check(const flint_nvfp4* g, const flint_nvfp4* u, const flint_nvfp
 hipError_t dense_run(const flint_nvfp4& g, const flint_nvfp4& u, const flint_nvfp4& d, int width, const float* x,
                      float norm_eps, float* y, bool accumulate, void* ws, hipStream_t s);
 
+// Batched step with the routed gate/up matrices read from a tiled copy
+// (batch.hip); tiles == nullptr reads the row-major weights.
+size_t batch_tiles_layer_bytes(const flint_moe_dims& d);
+hipError_t launch_batch_tiles(const flint_moe_dims& d, const flint_moe_layer* layers, int L, uint8_t* tiles,
+                              hipStream_t s);
+hipError_t launch_batch_step_tiled(const flint_moe_dims& d, const flint_moe_layer* layers, int L,
+                                   const flint_nvfp4& head, int vocab, const float* x, int B, float eps, float* logits,
+                                   int32_t* argmax, int32_t* routes, void* ws, hipStream_t s, const uint8_t* tiles);
+
 }  // namespace flint

@@ -97,6 +97,10 @@ def _load():
         "flint_stack_decode_batch": ([ctypes.POINTER(StackPlan), _P, _I32, ctypes.c_float, _P, _P, _P, _P, _SZ, _P],
                                      _I32),
         "flint_stack_error": ([_P, _SZ, ctypes.POINTER(_I32)], _I32),
+        "flint_stack_batch_tiles_bytes": ([ctypes.POINTER(Dims), _I32], _SZ),
+        "flint_stack_batch_tiles": ([ctypes.POINTER(StackPlan), _P, _SZ, _P], _I32),
+        "flint_stack_decode_batch_tiled": ([ctypes.POINTER(StackPlan), _P, _P, _I32, ctypes.c_float, _P, _P, _P, _P,
+                                            _SZ, _P], _I32),
         "flint_nvfp4_quantize": ([_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _I32),
         "flint_nvfp4_dequantize": ([ctypes.POINTER(NVFP4), _I64, _I64, _P, _P], _I32),
         "flint_attn_workspace_bytes": ([ctypes.POINTER(AttnDims)], _SZ),
@@ -129,6 +133,7 @@ EXPORTED = ("flint_status_str", "flint_last_hip_error", "flint_workspace_bytes",
             "flint_moe_decode", "flint_lmhead_gemv", "flint_stack_table_bytes", "flint_stack_packed_bytes",
             "flint_stack_prepare",
             "flint_stack_decode", "flint_stack_decode_traced", "flint_stack_decode_batch", "flint_stack_error",
+            "flint_stack_batch_tiles_bytes", "flint_stack_batch_tiles", "flint_stack_decode_batch_tiled",
             "flint_nvfp4_quantize", "flint_nvfp4_dequantize",
             # include/flint_attn.h
             "flint_attn_workspace_bytes", "flint_attn_decode", "flint_dense_workspace_bytes", "flint_dense_mlp",
@@ -349,11 +354,22 @@ class Stack:
         _check(_lib.flint_stack_error(self.ws.data_ptr(), self.ws.numel(), ctypes.byref(e)), "flint_stack_error")
         return e.value
 
+    def make_batch_tiles(self):
+        """Allocate and fill the tiled gate/up copy used by decode_batch(tiled=True)."""
+        n = _lib.flint_stack_batch_tiles_bytes(ctypes.byref(self.dims), self.n_layers)
+        if n == 0:
+            raise ValueError("the batched step does not take these sizes")
+        self.tiles = torch.empty(n, dtype=torch.uint8, device=self.ws.device)
+        _check(_lib.flint_stack_batch_tiles(ctypes.byref(self.plan), self.tiles.data_ptr(), n, _stream()),
+               "flint_stack_batch_tiles")
+        return self.tiles
+
     def decode_batch(self, x: torch.Tensor, eps: float = 1e-6, logits: torch.Tensor | None = None,
                      argmax: torch.Tensor | None = None, routes: torch.Tensor | None = None,
-                     want_logits: bool = True, ws: torch.Tensor | None = None):
+                     want_logits: bool = True, ws: torch.Tensor | None = None, tiled: bool = False):
         """x float32 [B][H]: one step of B tokens decoded together (each with its
-        own routing); -> (logits [B][vocab] or None, argmax [B])."""
+        own routing); -> (logits [B][vocab] or None, argmax [B]).  tiled: read
+        the gate/up rows from make_batch_tiles()'s copy."""
         B = x.shape[0]
         if want_logits and logits is None:
             logits = torch.empty((B, self.vocab), dtype=torch.float32, device=x.device)
@@ -361,9 +377,15 @@ class Stack:
             argmax = torch.empty(B, dtype=torch.int32, device=x.device)
         if ws is None:
             ws = workspace(OP_STACK_BATCH, self.dims, B, self.vocab, self.n_layers, device=x.device)
-        _check(_lib.flint_stack_decode_batch(ctypes.byref(self.plan), x.data_ptr(), B, eps, _ptr(logits),
-                                             argmax.data_ptr(), _ptr(routes), ws.data_ptr(), ws.numel(), _stream()),
-               "flint_stack_decode_batch")
+        if tiled:
+            _check(_lib.flint_stack_decode_batch_tiled(ctypes.byref(self.plan), self.tiles.data_ptr(), x.data_ptr(), B,
+                                                       eps, _ptr(logits), argmax.data_ptr(), _ptr(routes),
+                                                       ws.data_ptr(), ws.numel(), _stream()),
+                   "flint_stack_decode_batch_tiled")
+        else:
+            _check(_lib.flint_stack_decode_batch(ctypes.byref(self.plan), x.data_ptr(), B, eps, _ptr(logits),
+                                                 argmax.data_ptr(), _ptr(routes), ws.data_ptr(), ws.numel(),
+                                                 _stream()), "flint_stack_decode_batch")
         return logits, argmax
 
     def decode(self, x: torch.Tensor, eps: float = 1e-6, logits: torch.Tensor | None = None,

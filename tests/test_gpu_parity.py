@@ -417,6 +417,26 @@ def test_stack_batch_full_size_sampled(F, B):
     batch_vs_single(F, L=47, V=150144, B=B, seed0=900 + B)
 
 
+@pytest.mark.parametrize("E,B", [(32, 8), (256, 32), (8, 48)])
+def test_stack_batch_tiled_identical(F, E, B):
+    """The batched step reading the gate/up rows from the tiled copy gives
+    the same bits as reading the row-major weights (E=8, B=48: experts with
+    more than 32 tokens, two passes)."""
+    flint, workload = F
+    dims = synth.MoEDims(n_experts=E)
+    layers = [workload.build_layer(dims, seed=l) for l in range(3)]
+    head = workload.build_head(4099, dims.hidden)
+    stack = flint.Stack(dims_struct(F, dims), layers, head, 4099)
+    stack.make_batch_tiles()
+    x = workload.tokens(range(80, 80 + B), dims.hidden)
+    rt = torch.zeros((3, B, dims.top_k), dtype=torch.int32, device="cuda")
+    rr = torch.zeros_like(rt)
+    l1, a1 = stack.decode_batch(x, routes=rr)
+    l2, a2 = stack.decode_batch(x, routes=rt, tiled=True)
+    torch.cuda.synchronize()
+    assert torch.equal(l1, l2) and torch.equal(a1, a2) and torch.equal(rr, rt)
+
+
 def test_stack_batch_repeatable(F):
     """Fixed orders everywhere: the same step twice gives identical bits."""
     flint, workload = F
