@@ -500,7 +500,8 @@ def bench_model(args) -> int:
     head = workload.build_head(V, H)
     ad = lambda d: flint.attn_dims_struct(H, d.n_q, d.n_kv, d.head_dim, d.window, d.rope, d.theta)
     M = flint.Model(flint.dims_struct(md.hidden, md.n_experts, md.expert_width, md.top_k, md.shared_width),
-                    ad(synth.SLIDING), ad(synth.FULL), attn, is_full, kc, vc, dense, moe, head, V, dense_width=DW)
+                    ad(synth.SLIDING), ad(synth.FULL), attn, is_full, kc, vc, dense, moe, head, V, dense_width=DW,
+                    persistent_moe=not args.moe_kernels)
     x = workload.tokens([synth.TOKEN_SEED0 + t for t in range(T)], H)
     am = torch.empty((T, 1), dtype=torch.int32, device="cuda")
     p0 = ctx - 1
@@ -513,6 +514,9 @@ def bench_model(args) -> int:
         M.decode(x[t], p0 + t, argmax=am[t], want_logits=False)
     ev1.record()
     torch.cuda.synchronize()
+    if M.error():
+        log("the persistent MoE kernel reported a timed-out wait")
+        return 1
     ms = ev0.elapsed_time(ev1) / args.steps
     shape = bm.LayerShape()
     w_attn = NL * ((32 + 2 * 4) * 128 * H * 9 // 16 + H * 32 * 128 * 9 // 16)
@@ -522,13 +526,14 @@ def bench_model(args) -> int:
     kv = sum((min(pos_mid + 1, 513) if not f else pos_mid + 1) * 2048 for f in is_full)
     nbytes = w_attn + w_dense + w_moe + bm.head_bytes(V, H) + kv
     gbs = nbytes / (ms * 1e-3) / 1e9
-    log(f"model 49 layers, context {ctx}: {ms * 1e3:.1f} us/token, {1000.0 / ms:.1f} tok/s, "
+    sched = "kernel sequence" if args.moe_kernels else "persistent, one layer per launch"
+    log(f"model 49 layers, context {ctx}, MoE {sched}: {ms * 1e3:.1f} us/token, {1000.0 / ms:.1f} tok/s, "
         f"{nbytes / 1e9:.3f} GB/token (KV {kv / 1e6:.1f} MB), {gbs:.0f} GB/s")
     print(json.dumps({"metric": f"whole-model decode tok/s (49 layers + head, context {ctx}, batch 1)",
                       "value": round(1000.0 / ms, 2), "unit": "tok/s", "steps": args.steps, "warmup": args.warmup,
                       "ms_per_step": round(ms, 4), "higher_is_better": True, "data": "synthetic", "dtype": "f32",
                       "config": {"workload": f"flint49_ctx{ctx}_b1", "layers": NL, "dense_layers": ND,
-                                 "full_attention_layers": sum(is_full), "context": ctx},
+                                 "full_attention_layers": sum(is_full), "context": ctx, "moe_schedule": sched},
                       "roofline": {"bound": "hbm", "scope": "whole step (all kernels)", "achieved": round(gbs, 1),
                                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                                    "bytes_per_token": nbytes}}), flush=True)
@@ -557,6 +562,8 @@ def main() -> int:
     ap.add_argument("--gemm-case", default="", help="with --gemm: only SHAPE:T:MODE, e.g. head_150144x2048:512:0")
     ap.add_argument("--model", action="store_true", help="time the whole 49-layer model (attention + dense/MoE)")
     ap.add_argument("--context", type=int, default=1024, help="context length for --model")
+    ap.add_argument("--moe-kernels", action="store_true",
+                    help="with --model: run the MoE layers as the kernel sequence instead of the persistent kernel")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (batch-1 decode; see DESIGN.md for how it would shard)",

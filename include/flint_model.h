@@ -45,6 +45,14 @@ typedef struct {
   flint_nvfp4 head;                  /* [vocab][hidden] */
   int32_t vocab;
   float eps;                         /* block and final norms (1e-6) */
+  /* Optional (may be NULL): a plan of the same MoE layers, prepared by
+   * flint_stack_prepare with repacked down projections (its head and vocab
+   * are not used).  With it every MoE layer runs as one launch of the
+   * persistent stack kernel (one layer, no head); without it, as the kernel
+   * sequence of flint_moe_decode.  The plan's dims must equal `moe`, its
+   * n_layers must be n_layers - n_dense, and the sizes must allow the
+   * persistent schedule (FLINT_E_UNSUPPORTED otherwise). */
+  const flint_stack_plan* moe_plan;  /* [host] */
 } flint_model;
 
 /* Workspace bytes for flint_model_decode (0 if the model is invalid). */
@@ -54,9 +62,17 @@ size_t flint_model_workspace_bytes(const flint_model* m /*[host]*/);
  * logits_opt (float [vocab], may be NULL) and argmax (int32 [1]); every
  * layer's cache slot pos mod cap[l] is written as in flint_attn_decode.
  * h_out_opt (float [hidden]) receives the final residual when non-NULL.
- * Workspace: flint_model_workspace_bytes(m), zero-filled before first use. */
+ * Workspace: flint_model_workspace_bytes(m), zero-filled before first use;
+ * with moe_plan it carries the persistent kernel's epoch counter from call to
+ * call (as the stack workspace does) and must not be changed between calls. */
 int32_t flint_model_decode(const flint_model* m /*[host]*/, const float* x, int32_t pos, float* logits_opt,
                            int32_t* argmax, float* h_out_opt, void* ws, size_t ws_bytes, void* stream);
+
+/* The watchdog flag of the persistent MoE layers (as flint_stack_error):
+ * synchronously copies it to *error [host] (0: none; always 0 without
+ * moe_plan).  A set flag makes later calls skip their MoE layers until the
+ * workspace is zeroed again. */
+int32_t flint_model_error(const flint_model* m /*[host]*/, const void* ws, size_t ws_bytes, int32_t* error);
 
 #ifdef __cplusplus
 }

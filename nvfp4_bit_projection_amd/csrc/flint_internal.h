@@ -130,9 +130,11 @@ hipError_t launch_dequantize(const flint_nvfp4& q, int64_t rows, int64_t cols, f
 hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s);
 hipError_t launch_slice_cols(const uint8_t* src, uint8_t* dst, int64_t outer, int rows, int rb, int G,
                              hipStream_t s);
+// vocab == 0: no head, T == 1; layers l0 .. l0 + L - 1 of the table, the
+// final residual to h_out (which may be x).
 hipError_t launch_stack_persistent(const flint_moe_dims& d, int L, int vocab, const void* table, const float* x,
                                    int T, float eps, float* logits, int32_t* argmax, int32_t* routes, void* ws,
-                                   int64_t* trace, hipStream_t s);
+                                   int64_t* trace, hipStream_t s, int l0 = 0, float* h_out = nullptr);
 hipError_t read_stack_error(const void* ws, int32_t* out);
 
 }  // namespace flint

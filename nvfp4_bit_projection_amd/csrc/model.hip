@@ -19,10 +19,13 @@ __global__ __launch_bounds__(256) void k_copy_vec(const float* __restrict__ s, f
   for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) d[i] = s[i];
 }
 
+// persist: the persistent MoE kernel's exchange area (control words first),
+// kept from call to call; scratch: shared by the layers in turn
 struct ModelWs {
-  size_t h, scratch, total;
-  explicit ModelWs(size_t scratch_bytes) {
+  size_t persist, h, scratch, total;
+  ModelWs(size_t scratch_bytes, bool persistent) {
     size_t o = 0;
+    persist = o; o = align_up(o + (persistent ? stack_persistent_ws_bytes() : 0), 256);
     h = o; o = align_up(o + 4 * (size_t)kHidden, 256);
     scratch = o; o = align_up(o + scratch_bytes, 256);
     total = o;
@@ -50,6 +53,19 @@ size_t model_scratch(const flint_model* m) {
   return s;
 }
 
+// the optional plan of the MoE layers matches the model and allows the
+// persistent schedule
+int32_t check_moe_plan(const flint_model* m) {
+  const flint_stack_plan* p = m->moe_plan;
+  if (!p) return FLINT_OK;
+  if (!p->table || !p->packed) return FLINT_E_NULL;
+  const flint_moe_dims &a = p->dims, &b = m->moe;
+  if (a.hidden != b.hidden || a.n_experts != b.n_experts || a.expert_width != b.expert_width ||
+      a.top_k != b.top_k || a.shared_width != b.shared_width || p->n_layers != m->n_layers - m->n_dense)
+    return FLINT_E_DIMS;
+  return stack_persistent_supported(a, 1) ? FLINT_OK : FLINT_E_UNSUPPORTED;
+}
+
 }  // namespace
 }  // namespace flint
 
@@ -59,7 +75,7 @@ extern "C" {
 
 size_t flint_model_workspace_bytes(const flint_model* m) {
   const size_t s = model_scratch(m);
-  return s ? ModelWs(s).total : 0;
+  return s ? ModelWs(s, m->moe_plan != nullptr).total : 0;
 }
 
 int32_t flint_model_decode(const flint_model* m, const float* x, int32_t pos, float* logits_opt, int32_t* argmax,
@@ -82,11 +98,12 @@ int32_t flint_model_decode(const flint_model* m, const float* x, int32_t pos, fl
       return st;
     }
   }
+  if ((st = check_moe_plan(m))) return st;
   if (!m->head.codes || !m->head.scales || !m->head.tscale) return FLINT_E_NULL;
   if (((uintptr_t)x & 15) || ((uintptr_t)ws & 15) || ((uintptr_t)m->head.codes & 15) ||
       ((uintptr_t)argmax & 3) || ((uintptr_t)logits_opt & 3) || ((uintptr_t)h_out_opt & 3))
     return FLINT_E_ALIGN;
-  const ModelWs w(scratch);
+  const ModelWs w(scratch, m->moe_plan != nullptr);
   if (ws_bytes < w.total) return FLINT_E_WORKSPACE;
   if ((st = api_check_device())) return st;
   hipStream_t s = (hipStream_t)stream;
@@ -102,6 +119,12 @@ int32_t flint_model_decode(const flint_model* m, const float* x, int32_t pos, fl
     if (l < m->n_dense) {
       const flint_nvfp4* dn = m->dense + 3 * l;
       e = dense_run(dn[0], dn[1], dn[2], m->dense_width, h, m->eps, h, true, sc, s);
+    } else if (m->moe_plan) {
+      // one launch of the persistent kernel: layer l - n_dense of the plan's
+      // table, no head, the residual updated in place (every workgroup has
+      // read h before any can store: each needs all 256 router logits first)
+      e = launch_stack_persistent(m->moe, 1, 0, m->moe_plan->table, h, 1, m->eps, nullptr, nullptr, nullptr,
+                                  base + w.persist, nullptr, s, l - m->n_dense, h);
     } else {
       e = api_moe_run(m->moe, m->moe_layers[l - m->n_dense], h, m->eps, h, true, sc, s);
     }
@@ -115,6 +138,20 @@ int32_t flint_model_decode(const flint_model* m, const float* x, int32_t pos, fl
     k_copy_vec<<<8, 256, 0, s>>>(h, h_out_opt, kHidden);
     e = hipGetLastError();
   }
+  return e == hipSuccess ? FLINT_OK : api_hip_fail(e);
+}
+
+int32_t flint_model_error(const flint_model* m, const void* ws, size_t ws_bytes, int32_t* error) {
+  if (!m || !ws || !error) return FLINT_E_NULL;
+  const size_t scratch = model_scratch(m);
+  if (scratch == 0) return FLINT_E_DIMS;
+  const ModelWs w(scratch, m->moe_plan != nullptr);
+  if (ws_bytes < w.total) return FLINT_E_WORKSPACE;
+  *error = 0;
+  if (!m->moe_plan) return FLINT_OK;
+  int32_t st = api_check_device();
+  if (st) return st;
+  const hipError_t e = read_stack_error(static_cast<const char*>(ws) + w.persist, error);
   return e == hipSuccess ? FLINT_OK : api_hip_fail(e);
 }
 

@@ -75,6 +75,7 @@ __device__ __forceinline__ int padded(int e) { return (e >> 5) * kRowPad + (e & 
 
 struct StackParams {
   const StackTable* table;
+  int l0;  // first layer of the table to run
   int L, E, I, k, Is, V, T;
   float eps;
   const float* x;
@@ -88,6 +89,7 @@ struct StackParams {
   uint64_t* s4b;   // [2][8][2048] residual
   uint64_t* hp;    // [2][256][2]  head (max, index)
   int64_t* trace;  // optional [2][L+1][kTracePoints] phase timestamps of workgroups 0 and 255
+  float* h_out;    // k_stack_decode<false> (one token, no head): the final residual [H]
 };
 
 constexpr int kTracePoints = 16;
@@ -268,7 +270,7 @@ struct StackCoord {
 // (phase A), one routed gate/up pair and the down-projection operands
 // (phase B), the partial outputs (phase C), the residual rows (phase D), and
 // the next layer's router and shared rows, requested ahead of time.
-template <bool kComm>
+template <bool kComm, bool kHead>
 __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& C) {
   const int t = C.t, lane = C.lane, wv = C.wv, g = C.g, li = C.li;
   const int L = C.L, E = C.E, I = C.I, k = C.k, Is = C.Is, V = C.V;
@@ -641,6 +643,15 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       FLINT_TRACE(l, 7);
     }
 
+    if constexpr (!kHead) {
+      // no head (a single token, one or more layers of a longer model): the
+      // first XCD's workgroups store their rows of the new residual
+      if constexpr (kComm) {
+        if (wv == 0 && g == 0) P.h_out[64 * li + lane] = S.h[64 * li + lane];
+      }
+      continue;
+    }
+
     // -------------------------------------------------------------- head
     FLINT_TRACE(L, 0);
     rms_to_u(S.h, S.u, S.red, P.eps);  // H1, H2
@@ -712,6 +723,8 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
 #undef FLINT_TRACE_AT
 }
 
+// kHead false: one token, no head, the final residual to P.h_out
+template <bool kHead>
 __global__ __launch_bounds__(kStackThreads, 1) void k_stack_decode(StackParams P,
                                                                   const StackTable* __restrict__ table) {
   __shared__ StackLds S;
@@ -731,7 +744,7 @@ __global__ __launch_bounds__(kStackThreads, 1) void k_stack_decode(StackParams P
   if (C.tracing && C.t == 0) S.tr[C.L * kTracePoints + 3] = wall_clock64();  // kernel entry
   // layer table (and head) to LDS
   {
-    const uint64_t* src = reinterpret_cast<const uint64_t*>(table->layers);
+    const uint64_t* src = reinterpret_cast<const uint64_t*>(table->layers + P.l0);
     for (int i = C.t; i < C.L * kLayerWords; i += kStackThreads) S.tab[i] = src[i];
     const uint64_t* hsrc = reinterpret_cast<const uint64_t*>(&table->head);
     if (C.t < 3) S.tab[kMaxStackLayers * kLayerWords + C.t] = hsrc[C.t];
@@ -748,7 +761,7 @@ __global__ __launch_bounds__(kStackThreads, 1) void k_stack_decode(StackParams P
   }
   C.base = ld_dev_u32(P.ctrl);
   if (C.tracing && C.t == 0) S.tr[C.L * kTracePoints + 4] = wall_clock64();  // set-up done
-  const bool ok = C.wv < kCommWaves ? stack_role<true>(P, S, C) : stack_role<false>(P, S, C);
+  const bool ok = C.wv < kCommWaves ? stack_role<true, kHead>(P, S, C) : stack_role<false, kHead>(P, S, C);
   if (!ok) return;
   if (C.tracing) {
     const int L = C.L, t = C.t;
@@ -782,10 +795,12 @@ size_t stack_persistent_ws_bytes() {
 
 hipError_t launch_stack_persistent(const flint_moe_dims& d, int L, int vocab, const void* table, const float* x,
                                    int T, float eps, float* logits, int32_t* argmax, int32_t* routes, void* ws,
-                                   int64_t* trace, hipStream_t s) {
+                                   int64_t* trace, hipStream_t s, int l0, float* h_out) {
   StackParams P;
   P.trace = trace;
   P.table = static_cast<const StackTable*>(table);
+  P.l0 = l0;
+  P.h_out = h_out;
   P.L = L; P.E = d.n_experts; P.I = d.expert_width; P.k = d.top_k; P.Is = d.shared_width; P.V = vocab; P.T = T;
   P.eps = eps; P.x = x; P.logits = logits; P.argmax = argmax; P.routes = routes;
   char* w = static_cast<char*>(ws);
@@ -811,14 +826,21 @@ hipError_t launch_stack_persistent(const flint_moe_dims& d, int L, int vocab, co
   int r = resident[dev].load();
   if (r == 0) {
     int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stack_decode, kStackThreads, 0);
+    int per_cu2 = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stack_decode<true>, kStackThreads, 0);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu2, k_stack_decode<false>, kStackThreads, 0);
+    per_cu = per_cu < per_cu2 ? per_cu : per_cu2;
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     r = per_cu * cus >= kStackWGs ? 1 : -1;
     resident[dev].store(r);
   }
   if (r != 1) return hipErrorCooperativeLaunchTooLarge;
-  k_stack_decode<<<dim3(kStackWGs), dim3(kStackThreads), 0, s>>>(P, tab);
+  if (vocab > 0)
+    k_stack_decode<true><<<dim3(kStackWGs), dim3(kStackThreads), 0, s>>>(P, tab);
+  else
+    k_stack_decode<false><<<dim3(kStackWGs), dim3(kStackThreads), 0, s>>>(P, tab);
   return hipGetLastError();
 }
 

@@ -64,7 +64,8 @@ class AttnLayer(ctypes.Structure):
 class ModelC(ctypes.Structure):
     _fields_ = [("n_layers", _I32), ("n_dense", _I32), ("dense_width", _I32), ("moe", Dims), ("sliding", AttnDims),
                 ("full", AttnDims), ("is_full", _P), ("attn", _P), ("k_cache", _P), ("v_cache", _P), ("cap", _P),
-                ("dense", _P), ("moe_layers", _P), ("head", NVFP4), ("vocab", _I32), ("eps", ctypes.c_float)]
+                ("dense", _P), ("moe_layers", _P), ("head", NVFP4), ("vocab", _I32), ("eps", ctypes.c_float),
+                ("moe_plan", _P)]
 
 
 class INT4(ctypes.Structure):
@@ -109,6 +110,7 @@ def _load():
         "flint_dense_workspace_bytes": ([_I32, _I32, _I32], _SZ),
         "flint_model_workspace_bytes": ([ctypes.POINTER(ModelC)], _SZ),
         "flint_model_decode": ([ctypes.POINTER(ModelC), _P, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
+        "flint_model_error": ([ctypes.POINTER(ModelC), _P, _SZ, ctypes.POINTER(_I32)], _I32),
         "flint_nvfp4_gemm_workspace_bytes": ([_I32, _I32, _I32], _SZ),
         "flint_nvfp4_gemm": ([ctypes.POINTER(NVFP4), _I32, _I32, _P, _I32, _I32, _P, _P, _SZ, _P], _I32),
         "flint_int4_quantize": ([_P, _I64, _I64, _P, _P, _P, _P], _I32),
@@ -142,7 +144,7 @@ EXPORTED = ("flint_status_str", "flint_last_hip_error", "flint_workspace_bytes",
             # include/flint_gemm.h
             "flint_nvfp4_gemm_workspace_bytes", "flint_nvfp4_gemm",
             # include/flint_model.h
-            "flint_model_workspace_bytes", "flint_model_decode")
+            "flint_model_workspace_bytes", "flint_model_decode", "flint_model_error")
 
 
 def lib():
@@ -546,7 +548,10 @@ class Model:
 
     def __init__(self, moe_dims: Dims, sliding: AttnDims, full: AttnDims, attn: list, is_full: list,
                  k_caches: list, v_caches: list, dense: list, moe_layers: list, head: NVFP4Tensor, vocab: int,
-                 dense_width: int = 6144, eps: float = 1e-6):
+                 dense_width: int = 6144, eps: float = 1e-6, persistent_moe: bool = False):
+        """persistent_moe: run every MoE layer as one launch of the persistent
+        stack kernel (a plan with repacked down projections is prepared here);
+        otherwise as the kernel sequence."""
         n = len(attn)
         assert len(is_full) == n == len(k_caches) == len(v_caches) == len(dense) + len(moe_layers)
         self.keep = (attn, k_caches, v_caches, dense, moe_layers, head)
@@ -562,7 +567,13 @@ class Model:
         self.c = ModelC(n, nd, dense_width, moe_dims, sliding, full, ctypes.cast(self._is_full, _P),
                         ctypes.cast(self._attn, _P), ctypes.cast(self._kc, _P), ctypes.cast(self._vc, _P),
                         ctypes.cast(self._cap, _P), ctypes.cast(self._dense, _P) if nd else None,
-                        ctypes.cast(self._moe, _P) if moe_layers else None, head.c(), vocab, eps)
+                        ctypes.cast(self._moe, _P) if moe_layers else None, head.c(), vocab, eps, None)
+        self.moe_stack = None
+        if persistent_moe:
+            self.moe_stack = Stack(moe_dims, moe_layers, head, vocab, device=head.codes.device)
+            if self.moe_stack.packed is None:
+                raise ValueError("these MoE sizes do not allow the persistent schedule")
+            self.c.moe_plan = ctypes.cast(ctypes.pointer(self.moe_stack.plan), _P)
         nbytes = _lib.flint_model_workspace_bytes(ctypes.byref(self.c))
         if nbytes == 0:
             raise ValueError("invalid model")
@@ -579,3 +590,10 @@ class Model:
                                        argmax.data_ptr(), _ptr(h_out), self.ws.data_ptr(), self.ws.numel(),
                                        _stream()), "flint_model_decode")
         return (logits if want_logits else None), argmax
+
+    def error(self) -> int:
+        """The persistent MoE layers' watchdog flag (0: none); synchronises."""
+        e = _I32(0)
+        _check(_lib.flint_model_error(ctypes.byref(self.c), self.ws.data_ptr(), self.ws.numel(), ctypes.byref(e)),
+               "flint_model_error")
+        return e.value

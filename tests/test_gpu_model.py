@@ -1,10 +1,11 @@
 """GPU parity of the whole decode step (flint_model_decode through the C ABI)
 against the oracle's composition: a small model (a dense layer, then MoE
 layers of 32 experts; sliding and full attention layers alternating) over a
-few consecutive tokens sharing the caches.  Logits within relative L2 <= 1e-4
-and max-abs <= 2e-3 * max|ref|, argmax exact, the written cache rows within
-that bar plus one BF16 rounding step; token seeds whose oracle routing or head
-margin is below 1e-5 are skipped."""
+few consecutive tokens sharing the caches, with the MoE layers as the kernel
+sequence and as the persistent kernel (one layer per launch).  Logits within
+relative L2 <= 1e-4 and max-abs <= 2e-3 * max|ref|, argmax exact, the written
+cache rows within that bar plus one BF16 rounding step; token seeds whose
+oracle routing or head margin is below 1e-5 are skipped."""
 import numpy as np
 import pytest
 import torch
@@ -32,7 +33,10 @@ def attn_oracle(seed, d):
                             synth.attn_sinks(seed, d))
 
 
-def test_small_model_consecutive_tokens(F):
+@pytest.mark.parametrize("persistent_moe", [False, True])
+def test_small_model_consecutive_tokens(F, persistent_moe):
+    """persistent_moe: the MoE layers as one launch each of the persistent
+    stack kernel (no head); otherwise as the kernel sequence."""
     flint, workload = F
     H, V, DW = 2048, 4096, 2048
     md = synth.MoEDims(n_experts=32)
@@ -59,7 +63,8 @@ def test_small_model_consecutive_tokens(F):
     vg = [torch.from_numpy(c.view(np.int16).copy()).cuda() for c in vc]
     ad = lambda d: flint.attn_dims_struct(H, d.n_q, d.n_kv, d.head_dim, d.window, d.rope, d.theta)
     M = flint.Model(flint.dims_struct(md.hidden, md.n_experts, md.expert_width, md.top_k, md.shared_width),
-                    ad(sliding), ad(full), attn_g, is_full, kg, vg, dense_g, moe_g, head, V, dense_width=DW)
+                    ad(sliding), ad(full), attn_g, is_full, kg, vg, dense_g, moe_g, head, V, dense_width=DW,
+                    persistent_moe=persistent_moe)
     pos, seed, done = 30, 40, 0
     while done < 3:
         x = synth.token_f32(seed, H)
@@ -68,7 +73,7 @@ def test_small_model_consecutive_tokens(F):
         seed += 1
         if min(r.gaps) < MARGIN or r.argmax_gap < MARGIN:
             continue  # a near tie: another token
-        print(f"model token pos={pos} seed={seed - 1}", flush=True)
+        print(f"model token pos={pos} seed={seed - 1} persistent_moe={persistent_moe}", flush=True)
         lg, am = M.decode(torch.from_numpy(x).cuda(), pos)
         torch.cuda.synchronize()
         got = lg.cpu().numpy().astype(np.float64)
@@ -91,3 +96,4 @@ def test_small_model_consecutive_tokens(F):
                 assert not bad.any(), (l, pos, np.argwhere(bad)[:4].tolist(), gv[bad][:4], ov[bad][:4])
         pos += 1
         done += 1
+    assert M.error() == 0

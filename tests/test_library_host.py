@@ -243,3 +243,43 @@ def test_model_rejections(F):
     is_full[1] = 1
     mc.n_dense = 4
     assert L.flint_model_workspace_bytes(ctypes.byref(mc)) == 0
+
+
+def test_model_moe_plan_rejections(F):
+    """The optional persistent plan of the MoE layers must match the model."""
+    L = F.lib()
+    m = F.NVFP4(FAKE, FAKE, FAKE)
+    n = 3
+    attn = (F.AttnLayer * n)(*[F.AttnLayer(m, m, m, m, FAKE, FAKE, FAKE) for _ in range(n)])
+    is_full = (ctypes.c_int32 * n)(0, 1, 0)
+    kc = (ctypes.c_void_p * n)(FAKE, FAKE, FAKE)
+    cap = (ctypes.c_int32 * n)(513, 1024, 513)
+    dense = (F.NVFP4 * 3)(m, m, m)
+    moe = (F.Layer * 2)(*[F.Layer(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, m, m, m) for _ in range(2)])
+    mc = F.ModelC(n, 1, 6144, F.dims_struct(), F.attn_dims_struct(), F.attn_dims_struct(window=0, rope=False),
+                  ctypes.cast(is_full, ctypes.c_void_p), ctypes.cast(attn, ctypes.c_void_p),
+                  ctypes.cast(kc, ctypes.c_void_p), ctypes.cast(kc, ctypes.c_void_p), ctypes.cast(cap, ctypes.c_void_p),
+                  ctypes.cast(dense, ctypes.c_void_p), ctypes.cast(moe, ctypes.c_void_p), m, 150144, 1e-6)
+    plain = L.flint_model_workspace_bytes(ctypes.byref(mc))
+    err = ctypes.c_int32(7)
+    assert L.flint_model_error(ctypes.byref(mc), FAKE, plain, ctypes.byref(err)) == 0 and err.value == 0
+    plan = F.StackPlan()
+    plan.dims = F.dims_struct()
+    plan.n_layers = 2
+    plan.vocab = 150144
+    plan.table = FAKE
+    plan.packed = FAKE
+    mc.moe_plan = ctypes.cast(ctypes.pointer(plan), ctypes.c_void_p)
+    need = L.flint_model_workspace_bytes(ctypes.byref(mc))
+    assert need > plain                    # the persistent kernel's exchange area
+    dec = lambda wsb=need: L.flint_model_decode(ctypes.byref(mc), FAKE, 10, None, FAKE, None, FAKE, wsb, None)
+    assert dec(wsb=need - 1) == -4
+    assert L.flint_model_error(ctypes.byref(mc), FAKE, need - 1, ctypes.byref(err)) == -4
+    plan.n_layers = 3                      # the model has 2 MoE layers
+    assert dec() == -2
+    plan.n_layers = 2
+    plan.dims = F.dims_struct(n_experts=128)
+    assert dec() == -2
+    plan.dims = F.dims_struct()
+    plan.packed = None                     # no repacked down projections
+    assert dec() == -1
