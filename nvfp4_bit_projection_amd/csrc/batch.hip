@@ -438,12 +438,7 @@ __device__ __forceinline__ void mm_chunk(const MmRegs& R, const unsigned char* b
 // requested kAhead chunks before they are multiplied (the chunk loop is
 // unrolled, so every chunk has its own registers).
 constexpr int kAhead = 3;
-#ifndef GU_AHEAD
-#define GU_AHEAD 8
-#define GU_OCC 2
-#endif
-constexpr int kGateUpAhead = GU_AHEAD, kGateUpOcc = GU_OCC;
-template <class F, int NCH, class Lay = MmRowMajor, int AHEAD = kAhead>
+template <class F, int NCH, class Lay = MmRowMajor>
 __device__ __forceinline__ void mm_pass_n(const MmTiles& T, rsrc_t rA, int a_rows, const int* srow, int nt,
                                           unsigned char* abuf, int wv, int lane, f32x4_t (&acc)[2][2]) {
   constexpr int K = NCH * kMmChunk;
@@ -456,7 +451,7 @@ __device__ __forceinline__ void mm_pass_n(const MmTiles& T, rsrc_t rA, int a_row
     for (int tt = 0; tt < 2; ++tt) acc[rt][tt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   MmRegs R[NCH];
 #pragma unroll
-  for (int u = 0; u < NCH && u < AHEAD; ++u) Lay::load(T, u, R[u]);
+  for (int u = 0; u < NCH && u < kAhead; ++u) Lay::load(T, u, R[u]);
 #pragma unroll
   for (int u = 0; u < NCH; ++u) {
     if (u % cps == 0) {  // next segment: everyone is done with the buffer, then copy
@@ -465,7 +460,7 @@ __device__ __forceinline__ void mm_pass_n(const MmTiles& T, rsrc_t rA, int a_row
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies are in
       __syncthreads();
     }
-    if (u + AHEAD < NCH) Lay::load(T, u + AHEAD, R[u + AHEAD]);
+    if (u + kAhead < NCH) Lay::load(T, u + kAhead, R[u + kAhead]);
     mm_chunk<F>(R[u], abuf, Rrows, kseg, u % cps, ntt, lane, acc);
   }
 }
@@ -537,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void k_bnorm(float* __restrict__ h, const
 // token as three bf16 planes: hrp [3][B*k][I] by pair id (routed),
 // hsp [3][B][Is] by token (shared).
 template <bool TILED>
-__global__ __launch_bounds__(kMmThreads, kGateUpOcc) void k_mm_gateup(flint_moe_layer L, int I, int Is, int k, int B,
+__global__ __launch_bounds__(kMmThreads, 3) void k_mm_gateup(flint_moe_layer L, int I, int Is, int k, int B,
                                                              int Umax, const uint16_t* __restrict__ up,
                                                              const int32_t* __restrict__ bk, uint16_t* __restrict__ hrp,
                                                              uint16_t* __restrict__ hsp, int nb,
@@ -614,8 +609,8 @@ __global__ __launch_bounds__(kMmThreads, kGateUpOcc) void k_mm_gateup(flint_moe_
     }
     __syncthreads();
     f32x4_t acc[2][2];
-    mm_pass_n<FmtF16, kHidden / kMmChunk, typename std::conditional<TILED, MmTiled, MmRowMajor>::type,
-              kGateUpAhead>(T, rA, B, srow, nt, abuf, wv, lane, acc);
+    mm_pass_n<FmtF16, kHidden / kMmChunk, typename std::conditional<TILED, MmTiled, MmRowMajor>::type>(
+        T, rA, B, srow, nt, abuf, wv, lane, acc);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
