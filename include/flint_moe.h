@@ -273,8 +273,8 @@ int32_t flint_stack_decode_batch(const flint_stack_plan* plan /*[host]*/, const 
  * and the shared expert) for the batched step: the same codes and scales,
  * reordered so that each 16-row x 256-column block is one contiguous 2 KB
  * run of codes and one 256-byte run of scales, in the order the matrix-core
- * kernel reads them (2 (E I + Is) (H/2 + H/16) bytes per layer, 1.24 GB for
- * the 47 Flint layers).
+ * kernel reads them (2 (E I + Is) (H/2 + H/16) bytes per layer: 304 MB per
+ * Flint layer, 14.3 GB for the 47).
  * flint_stack_batch_tiles_bytes: size of that copy for L layers (0 if the
  * sizes are not supported by the batched step).  flint_stack_batch_tiles
  * fills `tiles` (device, caller-owned) from the plan's layers; call it again
