@@ -149,7 +149,7 @@ def bench_batch(args) -> int:
     routes = torch.empty((L, B, dims.top_k), dtype=torch.int32, device="cuda")
     total = 0
     for t in range(args.warmup, T):
-        stack.decode_batch(x[t], routes=routes, want_logits=False, ws=ws)
+        stack.decode_batch(x[t], routes=routes, want_logits=False, ws=ws, tiled=tiled)
         u = [len(set(routes[l].flatten().tolist())) for l in range(L)]
         total += sum(bm.layer_bytes(shape, n) for n in u) + bm.head_bytes(V, dims.hidden)
     step_bytes = total / args.steps
