@@ -484,22 +484,26 @@ int32_t flint::attn_check(const flint_attn_dims* dims, const flint_attn_layer* l
 }
 
 size_t flint::attn_ws_bytes(const flint_attn_dims& d) { return AttnWs(d).total; }
+size_t flint::attn_qkv_offset(const flint_attn_dims& d) { return AttnWs(d).qkv; }
 
 hipError_t flint::attn_run(const flint_attn_dims& d, const flint_attn_layer& layer, const float* x, float norm_eps,
                            int pos, uint16_t* k_cache, uint16_t* v_cache, int cap, float* y, bool accumulate, void* ws,
-                           hipStream_t s) {
+                           hipStream_t s, bool qkv_ready) {
   const AttnWs w(d);
   char* base = static_cast<char*>(ws);
   float* qkv = reinterpret_cast<float*>(base + w.qkv);
   float* o = reinterpret_cast<float*>(base + w.o);
   const int nq = d.n_q_heads * kD, nk = d.n_kv_heads * kD;
 
-  GemvSet in{};
-  in.m[0] = gm(layer.q, nq);
-  in.m[1] = gm(layer.k, nk);
-  in.m[2] = gm(layer.v, nk);
-  hipError_t e = launch_gemv(in, nq + 2 * nk, kHid, false, x, 0, qkv, 0, 1, s, norm_eps);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (!qkv_ready) {
+    GemvSet in{};
+    in.m[0] = gm(layer.q, nq);
+    in.m[1] = gm(layer.k, nk);
+    in.m[2] = gm(layer.v, nk);
+    e = launch_gemv(in, nq + 2 * nk, kHid, false, x, 0, qkv, 0, 1, s, norm_eps);
+    if (e != hipSuccess) return e;
+  }
 
   AttnArgs A{};
   A.qkv = qkv;

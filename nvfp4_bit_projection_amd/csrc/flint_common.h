@@ -28,8 +28,13 @@ hipError_t api_moe_run(const flint_moe_dims& d, const flint_moe_layer& L, const 
 int32_t attn_check(const flint_attn_dims* d, const flint_attn_layer* L, int pos, const void* kc, const void* vc,
                    int cap);
 size_t attn_ws_bytes(const flint_attn_dims& d);
+// Byte offset in the workspace of q, k, v (float [n_q D + 2 n_kv D]).
+size_t attn_qkv_offset(const flint_attn_dims& d);
+// qkv_ready: q, k, v of rmsnorm(x) are already in the workspace (written by
+// the kernel before), so the projection is skipped.
 hipError_t attn_run(const flint_attn_dims& d, const flint_attn_layer& L, const float* x, float norm_eps, int pos,
-                    uint16_t* kc, uint16_t* vc, int cap, float* y, bool accumulate, void* ws, hipStream_t s);
+                    uint16_t* kc, uint16_t* vc, int cap, float* y, bool accumulate, void* ws, hipStream_t s,
+                    bool qkv_ready = false);
 
 // Dense SwiGLU MLP for one token (attn.hip): y (+)= down(silu(gate u) * up u),
 // u = rmsnorm(x); workspace 4 * width bytes.

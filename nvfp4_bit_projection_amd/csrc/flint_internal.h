@@ -130,11 +130,22 @@ hipError_t launch_dequantize(const flint_nvfp4& q, int64_t rows, int64_t cols, f
 hipError_t launch_copy_f32(const float* src, float* dst, int n, hipStream_t s);
 hipError_t launch_slice_cols(const uint8_t* src, uint8_t* dst, int64_t outer, int rows, int rb, int G,
                              hipStream_t s);
+// Rows of up to three NVFP4 matrices with K = hidden (a following attention
+// layer's q, k and v) applied to the RMSNorm of the final residual at the end
+// of a no-head launch: out[r] for r over rows[0] + rows[1] + rows[2].
+struct StackQkv {
+  const uint8_t* codes[3];
+  const uint8_t* scales[3];
+  const float* tscale[3];
+  int rows[3];
+  float* out;
+};
 // vocab == 0: no head, T == 1; layers l0 .. l0 + L - 1 of the table, the
-// final residual to h_out (which may be x).
+// final residual to h_out (which may be x), and with qkv its rows.
 hipError_t launch_stack_persistent(const flint_moe_dims& d, int L, int vocab, const void* table, const float* x,
                                    int T, float eps, float* logits, int32_t* argmax, int32_t* routes, void* ws,
-                                   int64_t* trace, hipStream_t s, int l0 = 0, float* h_out = nullptr);
+                                   int64_t* trace, hipStream_t s, int l0 = 0, float* h_out = nullptr,
+                                   const StackQkv* qkv = nullptr);
 hipError_t read_stack_error(const void* ws, int32_t* out);
 
 }  // namespace flint

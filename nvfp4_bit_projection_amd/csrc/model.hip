@@ -112,9 +112,12 @@ int32_t flint_model_decode(const flint_model* m, const float* x, int32_t pos, fl
   void* sc = base + w.scratch;
   k_copy_vec<<<8, 256, 0, s>>>(x, h, kHidden);
   hipError_t e = hipGetLastError();
+  bool qkv_ready = false;  // this layer's q, k, v were computed by the kernel before
   for (int l = 0; l < m->n_layers && e == hipSuccess; ++l) {
     const flint_attn_dims& ad = m->is_full[l] ? m->full : m->sliding;
-    e = attn_run(ad, m->attn[l], h, m->eps, pos, m->k_cache[l], m->v_cache[l], m->cap[l], h, true, sc, s);
+    e = attn_run(ad, m->attn[l], h, m->eps, pos, m->k_cache[l], m->v_cache[l], m->cap[l], h, true, sc, s,
+                 qkv_ready);
+    qkv_ready = false;
     if (e != hipSuccess) break;
     if (l < m->n_dense) {
       const flint_nvfp4* dn = m->dense + 3 * l;
@@ -122,9 +125,27 @@ int32_t flint_model_decode(const flint_model* m, const float* x, int32_t pos, fl
     } else if (m->moe_plan) {
       // one launch of the persistent kernel: layer l - n_dense of the plan's
       // table, no head, the residual updated in place (every workgroup has
-      // read h before any can store: each needs all 256 router logits first)
+      // read h before any can store: each needs all 256 router logits first);
+      // it also applies the next layer's q, k, v projections to the norm of
+      // the new residual, which it holds in every workgroup
+      StackQkv nx{};
+      const bool next = l + 1 < m->n_layers;
+      if (next) {
+        const flint_attn_dims& an = m->is_full[l + 1] ? m->full : m->sliding;
+        const flint_attn_layer& A = m->attn[l + 1];
+        const flint_nvfp4* mats[3] = {&A.q, &A.k, &A.v};
+        for (int i = 0; i < 3; ++i) {
+          nx.codes[i] = mats[i]->codes;
+          nx.scales[i] = mats[i]->scales;
+          nx.tscale[i] = mats[i]->tscale;
+        }
+        nx.rows[0] = an.n_q_heads * an.head_dim;
+        nx.rows[1] = nx.rows[2] = an.n_kv_heads * an.head_dim;
+        nx.out = reinterpret_cast<float*>(static_cast<char*>(sc) + attn_qkv_offset(an));
+      }
       e = launch_stack_persistent(m->moe, 1, 0, m->moe_plan->table, h, 1, m->eps, nullptr, nullptr, nullptr,
-                                  base + w.persist, nullptr, s, l - m->n_dense, h);
+                                  base + w.persist, nullptr, s, l - m->n_dense, h, next ? &nx : nullptr);
+      qkv_ready = next;
     } else {
       e = api_moe_run(m->moe, m->moe_layers[l - m->n_dense], h, m->eps, h, true, sc, s);
     }

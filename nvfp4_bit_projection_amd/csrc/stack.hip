@@ -90,6 +90,7 @@ struct StackParams {
   uint64_t* hp;    // [2][256][2]  head (max, index)
   int64_t* trace;  // optional [2][L+1][kTracePoints] phase timestamps of workgroups 0 and 255
   float* h_out;    // k_stack_decode<false> (one token, no head): the final residual [H]
+  StackQkv qkv;    // k_stack_decode<false>: rows applied to the final residual's norm (out == nullptr: none)
 };
 
 constexpr int kTracePoints = 16;
@@ -649,6 +650,42 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       if constexpr (kComm) {
         if (wv == 0 && g == 0) P.h_out[64 * li + lane] = S.h[64 * li + lane];
       }
+      if (P.qkv.out) {
+        // the following layer's q, k, v rows of the new residual's norm (the
+        // norm every workgroup has in LDS): one row per wave and step, all
+        // of a wave's rows requested before any is reduced
+        rms_to_u(S.h, S.u, S.red, P.eps);  // Q1, Q2
+        float xv[32];
+        lds_x32(S.u + kRowPad * lane, xv);
+        const int n0 = P.qkv.rows[0], n01 = n0 + P.qkv.rows[1], R = n01 + P.qkv.rows[2];
+        const int gw = blockIdx.x * kStackWaves + wv, nw = kStackWGs * kStackWaves;
+        constexpr int kQ = 3;
+        for (int r0 = gw; r0 < R; r0 += kQ * nw) {
+          uint4 c[kQ];
+          uint32_t sc[kQ];
+#pragma unroll
+          for (int q = 0; q < kQ; ++q) {
+            const int r = r0 + q * nw;  // wave-uniform
+            c[q] = make_uint4(0, 0, 0, 0);
+            sc[q] = 0;
+            if (r < R) {
+              const int m = r < n0 ? 0 : r < n01 ? 1 : 2;
+              const size_t lr = (size_t)(r - (m == 0 ? 0 : m == 1 ? n0 : n01));
+              c[q] = ld_nt_u4(P.qkv.codes[m] + lr * (kHidden / 2) + 16 * lane);
+              sc[q] = ld_nt_u16(P.qkv.scales[m] + lr * (kHidden / 16) + 2 * lane);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < kQ; ++q) {
+            const int r = r0 + q * nw;
+            if (r < R) {
+              const int m = r < n0 ? 0 : r < n01 ? 1 : 2;
+              const float v = wave_sum(nvfp4_lane_dot32(c[q], sc[q], xv)) * *P.qkv.tscale[m];
+              if (lane == 0) P.qkv.out[r] = v;
+            }
+          }
+        }
+      }
       continue;
     }
 
@@ -795,9 +832,10 @@ size_t stack_persistent_ws_bytes() {
 
 hipError_t launch_stack_persistent(const flint_moe_dims& d, int L, int vocab, const void* table, const float* x,
                                    int T, float eps, float* logits, int32_t* argmax, int32_t* routes, void* ws,
-                                   int64_t* trace, hipStream_t s, int l0, float* h_out) {
+                                   int64_t* trace, hipStream_t s, int l0, float* h_out, const StackQkv* qkv) {
   StackParams P;
   P.trace = trace;
+  P.qkv = qkv ? *qkv : StackQkv{};
   P.table = static_cast<const StackTable*>(table);
   P.l0 = l0;
   P.h_out = h_out;
