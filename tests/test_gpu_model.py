@@ -33,18 +33,21 @@ def attn_oracle(seed, d):
                             synth.attn_sinks(seed, d))
 
 
-@pytest.mark.parametrize("persistent_moe", [False, True])
-def test_small_model_consecutive_tokens(F, persistent_moe):
+@pytest.mark.parametrize("persistent_moe,pos0,window,cap_full",
+                         [(False, 30, 8, 64), (True, 30, 8, 64), (True, 700, 513, 1024)])
+def test_small_model_consecutive_tokens(F, persistent_moe, pos0, window, cap_full):
     """persistent_moe: the MoE layers as one launch each of the persistent
-    stack kernel (no head); otherwise as the kernel sequence."""
+    stack kernel (no head); otherwise as the kernel sequence.  pos0 = 700:
+    contexts of several 64-position chunks (513 and 701..703 positions: 9
+    and 11 chunks per key/value head, merged with the sinks)."""
     flint, workload = F
     H, V, DW = 2048, 4096, 2048
     md = synth.MoEDims(n_experts=32)
-    sliding = synth.AttnDims(window=8, rope=True)
+    sliding = synth.AttnDims(window=window, rope=True)
     full = synth.AttnDims(window=0, rope=False)
     is_full = [0, 1, 0, 1]
     dims = [full if f else sliding for f in is_full]
-    caps = [64 if f else 8 for f in is_full]
+    caps = [cap_full if f else window for f in is_full]
     nl, nd = 4, 1
     moe_seeds = [0, 1, 2]
     # oracle side
@@ -65,7 +68,7 @@ def test_small_model_consecutive_tokens(F, persistent_moe):
     M = flint.Model(flint.dims_struct(md.hidden, md.n_experts, md.expert_width, md.top_k, md.shared_width),
                     ad(sliding), ad(full), attn_g, is_full, kg, vg, dense_g, moe_g, head, V, dense_width=DW,
                     persistent_moe=persistent_moe)
-    pos, seed, done = 30, 40, 0
+    pos, seed, done = pos0, 40, 0
     while done < 3:
         x = synth.token_f32(seed, H)
         trial_k, trial_v = [c.copy() for c in kc], [c.copy() for c in vc]
@@ -86,7 +89,7 @@ def test_small_model_consecutive_tokens(F, persistent_moe):
             for g_, o_ in ((kg[l], kc[l]), (vg[l], vc[l])):
                 gb = g_.cpu().numpy().view(np.uint16)
                 written = np.zeros(o_.shape[1], bool)
-                written[[p_ % o_.shape[1] for p_ in range(30, pos + 1)]] = True
+                written[[p_ % o_.shape[1] for p_ in range(pos0, pos + 1)]] = True
                 assert np.array_equal(gb[:, ~written], o_[:, ~written])
                 # the written values: the fp32 bar (max-abs <= 2e-3 * max|ref|
                 # per written row) plus one BF16 rounding step
