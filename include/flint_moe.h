@@ -264,7 +264,7 @@ int32_t flint_stack_decode_traced(const flint_stack_plan* plan /*[host]*/, const
  * descending).  Workspace: flint_workspace_bytes(FLINT_OP_STACK_BATCH, dims,
  * B, vocab, L); no zero-fill needed.  Uses the plan's host layer array (the
  * canonical layout; `packed` is not needed).  Needs expert_width and
- * shared_width in {256, 512, 1024, 2048}. */
+ * shared_width in {512, 1024, 2048} (FLINT_E_UNSUPPORTED otherwise). */
 int32_t flint_stack_decode_batch(const flint_stack_plan* plan /*[host]*/, const float* x, int32_t B, float eps,
                                  float* logits, int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes,
                                  void* stream);

@@ -792,8 +792,8 @@ __global__ __launch_bounds__(64) void k_bargmax(const HeadPartial* __restrict__ 
 }  // namespace
 
 bool batch_supported(const flint_moe_dims& d, int B) {
-  // the matrix-core kernels walk K in pairs of 256-wide chunks
-  auto width_ok = [](int K) { return K >= 512 && K <= 2048 && K % 512 == 0; };
+  // the down projection's K loop is instantiated for 2, 4 and 8 chunks of 256
+  auto width_ok = [](int K) { return K == 512 || K == 1024 || K == 2048; };
   return d.hidden == kHidden && B >= 1 && B <= kMaxBatch && width_ok(d.expert_width) && width_ok(d.shared_width) &&
          d.n_experts <= kMaxExperts && d.top_k <= kMaxTopK;
 }
