@@ -141,8 +141,9 @@ def test_quantize_and_stack_rejections(F):
     assert L.flint_workspace_bytes(F.OP_STACK_BATCH, ctypes.byref(full), 65, 150144, 47) == 0
     assert L.flint_workspace_bytes(F.OP_STACK_BATCH, ctypes.byref(full), 0, 150144, 47) == 0
     # expert and shared widths: 512, 1024 or 2048 only
-    for I, Is, ok in ((1024, 2048, True), (1536, 1024, False), (512, 1536, False), (256, 1024, False)):
-        dm = F.dims_struct(expert_width=I, shared_width=Is)
+    for I, Is, ok in ((1024, 2048, True), (512, 512, True), (1536, 512, False), (512, 1536, False),
+                      (256, 1024, False)):
+        dm = F.dims_struct(expert_width=I, shared_width=Is, top_k=2)
         assert (L.flint_workspace_bytes(F.OP_STACK_BATCH, ctypes.byref(dm), 8, 150144, 47) > 0) == ok, (I, Is)
     assert L.flint_stack_decode_batch(None, FAKE, 8, 1e-6, None, FAKE, None, FAKE, 1 << 20, None) == -1
     assert L.flint_stack_decode_batch(ctypes.byref(plan), FAKE, 8, 1e-6, None, FAKE, None, FAKE, 1 << 20, None) == -1
