@@ -165,7 +165,7 @@ def bench_batch(args) -> int:
         "config": {"workload": f"stack47_lmhead_b{B}", "layers": L, "hidden": 2048, "experts": 256, "top_k": 6,
                    "expert_width": 512, "shared_width": 1024, "vocab": V, "batch": B,
                    "weights": "nvfp4 e2m1 + e4m3/16 + fp32 tensor scale; fp32 router",
-                   "gate_up_layout": "tiled copy" if tiled else "row-major"},
+                   "expert_weight_layout": "tiled copy" if tiled else "row-major"},
         "roofline": {"bound": "hbm", "scope": "whole step (all kernels)", "achieved": round(gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_step": round(step_bytes)},
@@ -551,7 +551,7 @@ def main() -> int:
     ap.add_argument("--batch", type=int, default=1,
                     help="tokens per step; above 1 the batched step (experts deduplicated per layer) is timed")
     ap.add_argument("--tiled", action="store_true",
-                    help="with --batch: read the gate/up weights from the tiled copy (flint_stack_batch_tiles)")
+                    help="with --batch: read the expert weights from the tiled copy (flint_stack_batch_tiles)")
     ap.add_argument("--router", action="store_true",
                     help="time the router call alone in its four variants (fp32/BF16 router, softmax/sigmoid)")
     ap.add_argument("--attn", action="store_true",

@@ -269,17 +269,17 @@ int32_t flint_stack_decode_batch(const flint_stack_plan* plan /*[host]*/, const 
                                  float* logits, int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes,
                                  void* stream);
 
-/* Optional tiled copy of every layer's gate and up matrices (routed experts
- * and the shared expert) for the batched step: the same codes and scales,
- * reordered so that each 16-row x 256-column block is one contiguous 2 KB
- * run of codes and one 256-byte run of scales, in the order the matrix-core
- * kernel reads them (2 (E I + Is) (H/2 + H/16) bytes per layer: 304 MB per
- * Flint layer, 14.3 GB for the 47).
+/* Optional tiled copy of every layer's gate, up and down matrices (routed
+ * experts and the shared expert) for the batched step: the same codes and
+ * scales, reordered so that each 16-row x 256-column block is one contiguous
+ * 2 KB run of codes and one 256-byte run of scales, in the order the
+ * matrix-core kernels read them (3 (E I + Is) H (1/2 + 1/16) bytes per
+ * layer: 456.5 MB per Flint layer, 21.5 GB for the 47).
  * flint_stack_batch_tiles_bytes: size of that copy for L layers (0 if the
  * sizes are not supported by the batched step).  flint_stack_batch_tiles
  * fills `tiles` (device, caller-owned) from the plan's layers; call it again
  * after the weights change.  flint_stack_decode_batch_tiled is
- * flint_stack_decode_batch with the gate/up rows read from `tiles`
+ * flint_stack_decode_batch with the expert weights read from `tiles`
  * (bit-identical results). */
 size_t flint_stack_batch_tiles_bytes(const flint_moe_dims* dims /*[host]*/, int32_t L);
 int32_t flint_stack_batch_tiles(const flint_stack_plan* plan /*[host]*/, void* tiles, size_t tiles_bytes,

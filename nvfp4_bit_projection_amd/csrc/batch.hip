@@ -375,6 +375,23 @@ struct MmTiled {
   }
 };
 
+// Byte offsets of the down matrices in one layer's tiled copy, after the
+// gate/up part: routed codes [E][H/16][I/256][2 KB], shared codes
+// [H/16][Is/256][2 KB], routed scales [E][H/16][I/256][256 B], shared scales
+// [H/16][Is/256][256 B]; total = the layer's bytes.
+struct DownTiles {
+  size_t routed_c, shared_c, routed_s, shared_s, total;
+  __host__ __device__ DownTiles(int E, int I, int Is) {
+    const size_t ntile = (size_t)E * (I / 16) + Is / 16;  // gate/up tiles
+    size_t o = 2 * ntile * 16 * (kHidden / 2 + kHidden / 16);
+    routed_c = o; o += (size_t)E * kHidden * (I / 2);
+    shared_c = o; o += (size_t)kHidden * (Is / 2);
+    routed_s = o; o += (size_t)E * kHidden * (I / 16);
+    shared_s = o; o += (size_t)kHidden * (Is / 16);
+    total = o;
+  }
+};
+
 // Staged activations: the pass's tokens padded to R rows (a power of two, 4
 // .. 32) and a K segment of kseg = min(8192 / R, K) values, P planes, in LDS
 // as [plane][row][kseg] 16-bit values; granule g (8 values) of row r sits at
@@ -631,12 +648,14 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_mm_gateup(flint_moe_layer L, 
 // grid (H / 256, Umax + 1), 512 threads; groups as for gate/up.  Wave w takes
 // output rows r0 + 32 w .. + 31.  Routed: dr[pid][n] = w_pid * S_e * (Wd[e][n]
 // . h_pid) over K = I; shared: ds[b][n] = S * (Wsd[n] . hs_b) over K = Is.
+template <bool TILED>
 __global__ __launch_bounds__(kMmThreads, 3) void k_mm_down(flint_moe_layer L, int I, int Is, int B, int Umax,
                                                            const uint16_t* __restrict__ hrp,
                                                            const uint16_t* __restrict__ hsp,
                                                            const int32_t* __restrict__ bk,
                                                            const float* __restrict__ wts, float* __restrict__ dr,
-                                                           float* __restrict__ ds, int nb) {
+                                                           float* __restrict__ ds, int nb, const uint8_t* dtiles,
+                                                           int E) {
   __shared__ __align__(16) unsigned char abuf[mm_buf_bytes<FmtBF16>()];
   __shared__ int srow[kMmTok];
   __shared__ float coef[kMmTok];
@@ -653,18 +672,37 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_mm_down(flint_moe_layer L, in
   const int K = sh ? Is : I;
   const int rbase = blockIdx.x * kMmRows + 32 * wv;
   MmTiles T;
+  if constexpr (TILED) {
+    // this layer's tiled down matrices (DownTiles): the routed experts'
+    // 16-row tiles, then the shared expert's, each tile's K chunks in a row
+    const DownTiles D(E, I, Is);
+    const int nch = K / kMmChunk;
+    const int t0 = __builtin_amdgcn_readfirstlane(rbase / 16);  // the same in every lane
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int row = rbase + 16 * rt + m;
-    if (sh) {
-      T.c[rt] = L.shared_down.codes + (size_t)row * (Is / 2) + 32 * q;
-      T.s[rt] = L.shared_down.scales + (size_t)row * (Is / 16) + 4 * q;
-    } else {
-      const size_t er = (size_t)e * kHidden + row;
-      T.c[rt] = L.down_codes + er * (I / 2) + 32 * q;
-      T.s[rt] = L.down_scales + er * (I / 16) + 4 * q;
+    for (int rt = 0; rt < 2; ++rt) {
+      // tile of rows rbase + 16 rt .. + 15: the shared expert's, or expert e's
+      const size_t tile = sh ? (size_t)t0 + rt : (size_t)e * (kHidden / 16) + t0 + rt;
+      const size_t cb = (sh ? D.shared_c : D.routed_c) + tile * nch * 2048;
+      const size_t sb = (sh ? D.shared_s : D.routed_s) + tile * nch * 256;
+      T.rc[rt] = make_rsrc(dtiles + cb, (uint64_t)nch * 2048);
+      T.rs[rt] = make_rsrc(dtiles + sb, (uint64_t)nch * 256);
+    }
+    T.lane = lane;
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const int row = rbase + 16 * rt + m;
+      if (sh) {
+        T.c[rt] = L.shared_down.codes + (size_t)row * (Is / 2) + 32 * q;
+        T.s[rt] = L.shared_down.scales + (size_t)row * (Is / 16) + 4 * q;
+      } else {
+        const size_t er = (size_t)e * kHidden + row;
+        T.c[rt] = L.down_codes + er * (I / 2) + 32 * q;
+        T.s[rt] = L.down_scales + er * (I / 16) + 4 * q;
+      }
     }
   }
+  using Lay = typename std::conditional<TILED, MmTiled, MmRowMajor>::type;
   const float S = sh ? *L.shared_down.tscale : L.expert_tscales[3 * e + 2];
   const rsrc_t rA = sh ? make_rsrc(hsp, (uint64_t)3 * B * Is * 2) : make_rsrc(hrp, (uint64_t)3 * nb * I * 2);
   const int a_rows = sh ? B : nb;
@@ -684,9 +722,9 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_mm_down(flint_moe_layer L, in
     }
     __syncthreads();
     f32x4_t acc[2][2];
-    if (K == 1024) mm_pass_n<FmtBF16, 4>(T, rA, a_rows, srow, nt, abuf, wv, lane, acc);
-    else if (K == 2048) mm_pass_n<FmtBF16, 8>(T, rA, a_rows, srow, nt, abuf, wv, lane, acc);
-    else mm_pass_n<FmtBF16, 2>(T, rA, a_rows, srow, nt, abuf, wv, lane, acc);
+    if (K == 1024) mm_pass_n<FmtBF16, 4, Lay>(T, rA, a_rows, srow, nt, abuf, wv, lane, acc);
+    else if (K == 2048) mm_pass_n<FmtBF16, 8, Lay>(T, rA, a_rows, srow, nt, abuf, wv, lane, acc);
+    else mm_pass_n<FmtBF16, 2, Lay>(T, rA, a_rows, srow, nt, abuf, wv, lane, acc);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -859,16 +897,45 @@ __global__ __launch_bounds__(kThreads) void k_tile_gateup(flint_moe_layer L, int
   }
 }
 
+// Tiled copy of rows x K NVFP4 (row-major codes and scales) for the MmTiled
+// layout: [rows/16][K/256][2 KB] codes, [rows/16][K/256][256 B] scales.  One
+// thread per (tile, chunk, lane L = 16 q + m).
+__global__ __launch_bounds__(kThreads) void k_tile_rows(const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ scales, size_t rows, int K,
+                                                        uint8_t* __restrict__ dc, uint8_t* __restrict__ ds) {
+  const int nch = K / kMmChunk;
+  const size_t total = rows / 16 * nch * 64;
+  for (size_t i = blockIdx.x * (size_t)kThreads + threadIdx.x; i < total; i += (size_t)gridDim.x * kThreads) {
+    const int lane = (int)(i % 64);
+    const size_t r = i / 64;  // tile * nch + chunk
+    const int u = (int)(r % nch);
+    const size_t tile = r / nch;
+    const int m = lane & 15, q = lane >> 4;
+    const size_t row = tile * 16 + m;
+    const uint8_t* sc = codes + row * (K / 2) + (kMmChunk / 2) * u + 32 * q;
+    const uint8_t* ss = scales + row * (K / 16) + (kMmChunk / 16) * u + 4 * q;
+    *reinterpret_cast<uint4*>(dc + r * 2048 + 16 * lane) = *reinterpret_cast<const uint4*>(sc);
+    *reinterpret_cast<uint4*>(dc + r * 2048 + 1024 + 16 * lane) = *reinterpret_cast<const uint4*>(sc + 16);
+    *reinterpret_cast<uint32_t*>(ds + r * 256 + 4 * lane) = *reinterpret_cast<const uint32_t*>(ss);
+  }
+}
+
 size_t batch_tiles_layer_bytes(const flint_moe_dims& d) {
-  return 2 * ((size_t)d.n_experts * d.expert_width + d.shared_width) * (kHidden / 2 + kHidden / 16);
+  return DownTiles(d.n_experts, d.expert_width, d.shared_width).total;
 }
 
 hipError_t launch_batch_tiles(const flint_moe_dims& d, const flint_moe_layer* layers, int L, uint8_t* tiles,
                               hipStream_t s) {
   const size_t per = batch_tiles_layer_bytes(d);
   for (int l = 0; l < L; ++l) {
-    k_tile_gateup<<<2048, kThreads, 0, s>>>(layers[l], d.n_experts, d.expert_width, d.shared_width,
-                                            tiles + (size_t)l * per);
+    uint8_t* base = tiles + (size_t)l * per;
+    const DownTiles D(d.n_experts, d.expert_width, d.shared_width);
+    const flint_moe_layer& Ly = layers[l];
+    k_tile_gateup<<<2048, kThreads, 0, s>>>(Ly, d.n_experts, d.expert_width, d.shared_width, base);
+    k_tile_rows<<<2048, kThreads, 0, s>>>(Ly.down_codes, Ly.down_scales, (size_t)d.n_experts * kHidden,
+                                          d.expert_width, base + D.routed_c, base + D.routed_s);
+    k_tile_rows<<<2048, kThreads, 0, s>>>(Ly.shared_down.codes, Ly.shared_down.scales, kHidden, d.shared_width,
+                                          base + D.shared_c, base + D.shared_s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -921,8 +988,12 @@ hipError_t launch_batch_step_tiled(const flint_moe_dims& d, const flint_moe_laye
     else
       k_mm_gateup<false><<<dim3(gu_x, Umax + 1), kMmThreads, 0, s>>>(Ly, I, Is, k, B, Umax, up, bk, hrp, hsp, nb,
                                                                       nullptr, E);
-    k_mm_down<<<dim3(kHidden / kMmRows, Umax + 1), kMmThreads, 0, s>>>(Ly, I, Is, B, Umax, hrp, hsp, bk, wts, dr, ds,
-                                                                        nb);
+    if (tiles)
+      k_mm_down<true><<<dim3(kHidden / kMmRows, Umax + 1), kMmThreads, 0, s>>>(
+          Ly, I, Is, B, Umax, hrp, hsp, bk, wts, dr, ds, nb, tiles + (size_t)l * batch_tiles_layer_bytes(d), E);
+    else
+      k_mm_down<false><<<dim3(kHidden / kMmRows, Umax + 1), kMmThreads, 0, s>>>(Ly, I, Is, B, Umax, hrp, hsp, bk,
+                                                                               wts, dr, ds, nb, nullptr, E);
     // the residual update and the next norm (after the last layer: the
     // final norm, the head's input)
     k_bnorm<<<B, kThreads, 0, s>>>(h, dr, ds, k, l + 1 < L ? u : nullptr, up, B, eps);

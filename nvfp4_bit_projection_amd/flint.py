@@ -357,7 +357,7 @@ class Stack:
         return e.value
 
     def make_batch_tiles(self):
-        """Allocate and fill the tiled gate/up copy used by decode_batch(tiled=True)."""
+        """Allocate and fill the tiled copy of the expert weights used by decode_batch(tiled=True)."""
         n = _lib.flint_stack_batch_tiles_bytes(ctypes.byref(self.dims), self.n_layers)
         if n == 0:
             raise ValueError("the batched step does not take these sizes")
@@ -371,7 +371,7 @@ class Stack:
                      want_logits: bool = True, ws: torch.Tensor | None = None, tiled: bool = False):
         """x float32 [B][H]: one step of B tokens decoded together (each with its
         own routing); -> (logits [B][vocab] or None, argmax [B]).  tiled: read
-        the gate/up rows from make_batch_tiles()'s copy."""
+        the expert weights from make_batch_tiles()'s copy."""
         B = x.shape[0]
         if want_logits and logits is None:
             logits = torch.empty((B, self.vocab), dtype=torch.float32, device=x.device)

@@ -419,7 +419,7 @@ def test_stack_batch_full_size_sampled(F, B):
 
 @pytest.mark.parametrize("E,B", [(32, 8), (256, 32), (8, 48)])
 def test_stack_batch_tiled_identical(F, E, B):
-    """The batched step reading the gate/up rows from the tiled copy gives
+    """The batched step reading the expert weights from the tiled copy gives
     the same bits as reading the row-major weights (E=8, B=48: experts with
     more than 32 tokens, two passes)."""
     flint, workload = F
