@@ -483,54 +483,58 @@ __device__ __forceinline__ void mm_pass_n(const MmTiles& T, rsrc_t rA, int a_row
 }
 
 // ---------------------------------------------------------------- norm --
-// grid B, 256 threads.  With dr: the layer's residual update first, h_b +=
+// grid B, 1,024 threads.  With dr: the layer's residual update first, h_b +=
 // (sum over slots in order of dr) + ds (fixed order).  Then u_b = h_b * s_b,
 // s_b = 1/sqrt(mean(h_b^2) + eps), as fp32 (router; skipped when u is null)
 // and as two fp16 planes up [2][B][H] (matrix cores; |u| <= sqrt(H), well
 // inside the fp16 range).
-__global__ __launch_bounds__(kThreads) void k_bnorm(float* __restrict__ h, const float* __restrict__ dr,
+constexpr int kNormThreads = 1024;  // 2 values per thread: more loads in flight per token
+__global__ __launch_bounds__(kNormThreads) void k_bnorm(float* __restrict__ h, const float* __restrict__ dr,
                                                     const float* __restrict__ ds, int k, float* __restrict__ u,
                                                     uint16_t* __restrict__ up, int B, float eps) {
   const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
   float* hb = h + (size_t)b * kHidden;
-  float v[kHidden / kThreads];
+  float v[kHidden / kNormThreads];
   float ss = 0.0f;
 #pragma unroll
-  for (int i = 0; i < kHidden / kThreads; ++i) {
-    const int n = t + i * kThreads;
+  for (int i = 0; i < kHidden / kNormThreads; ++i) {
+    const int n = t + i * kNormThreads;
     v[i] = hb[n];
   }
   if (dr) {
     // every load issued before the sums (slots unrolled to the maximum k)
-    float y[kHidden / kThreads][kMaxTopK + 1];
+    float y[kHidden / kNormThreads][kMaxTopK + 1];
 #pragma unroll
-    for (int i = 0; i < kHidden / kThreads; ++i) {
-      const int n = t + i * kThreads;
+    for (int i = 0; i < kHidden / kNormThreads; ++i) {
+      const int n = t + i * kNormThreads;
 #pragma unroll
       for (int sl = 0; sl < kMaxTopK; ++sl) y[i][sl] = sl < k ? dr[((size_t)b * k + sl) * kHidden + n] : 0.0f;
       y[i][kMaxTopK] = ds[(size_t)b * kHidden + n];
     }
 #pragma unroll
-    for (int i = 0; i < kHidden / kThreads; ++i) {
+    for (int i = 0; i < kHidden / kNormThreads; ++i) {
       float acc = 0.0f;
 #pragma unroll
       for (int sl = 0; sl < kMaxTopK; ++sl)
         if (sl < k) acc += y[i][sl];
       v[i] += acc + y[i][kMaxTopK];
-      hb[t + i * kThreads] = v[i];
+      hb[t + i * kNormThreads] = v[i];
     }
   }
 #pragma unroll
-  for (int i = 0; i < kHidden / kThreads; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
+  for (int i = 0; i < kHidden / kNormThreads; ++i) ss = __builtin_fmaf(v[i], v[i], ss);
   ss = wave_sum(ss);
-  __shared__ float red[kThreads / 64];
+  __shared__ float red[kNormThreads / 64];
   if (lane == 0) red[w] = ss;
   __syncthreads();
-  const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+  float r4[4];  // fixed order: four sums of four, then their pairs
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r4[j] = (red[4 * j] + red[4 * j + 1]) + (red[4 * j + 2] + red[4 * j + 3]);
+  const float tot = (r4[0] + r4[1]) + (r4[2] + r4[3]);
   const float s = 1.0f / sqrtf(tot * (1.0f / kHidden) + eps);
 #pragma unroll
-  for (int i = 0; i < kHidden / kThreads; ++i) {
-    const int c = t + i * kThreads;
+  for (int i = 0; i < kHidden / kNormThreads; ++i) {
+    const int c = t + i * kNormThreads;
     const float x = v[i] * s;
     if (u) u[(size_t)b * kHidden + c] = x;
     uint16_t o[2];
@@ -973,7 +977,7 @@ hipError_t launch_batch_step_tiled(const flint_moe_dims& d, const flint_moe_laye
       reinterpret_cast<const uint32_t*>(x), reinterpret_cast<uint32_t*>(h), B * kHidden);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_bnorm<<<B, kThreads, 0, s>>>(h, nullptr, nullptr, k, u, up, B, eps);
+  k_bnorm<<<B, kNormThreads, 0, s>>>(h, nullptr, nullptr, k, u, up, B, eps);
   for (int l = 0; l < L && e == hipSuccess; ++l) {
     const flint_moe_layer& Ly = layers[l];
     k_broute<<<dim3((E + 3) / 4, (B + kRouteTok - 1) / kRouteTok), kThreads, 0, s>>>(Ly.router, E, u, B, lg);
@@ -996,7 +1000,7 @@ hipError_t launch_batch_step_tiled(const flint_moe_dims& d, const flint_moe_laye
                                                                                wts, dr, ds, nb, nullptr, E);
     // the residual update and the next norm (after the last layer: the
     // final norm, the head's input)
-    k_bnorm<<<B, kThreads, 0, s>>>(h, dr, ds, k, l + 1 < L ? u : nullptr, up, B, eps);
+    k_bnorm<<<B, kNormThreads, 0, s>>>(h, dr, ds, k, l + 1 < L ? u : nullptr, up, B, eps);
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
