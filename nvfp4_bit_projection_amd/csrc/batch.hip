@@ -454,10 +454,12 @@ __device__ __forceinline__ void mm_chunk(const MmRegs& R, const unsigned char* b
 // One pass: nt (<= 32) tokens whose source rows are in srow, over K = 256
 // NCH.  The caller has published srow with a barrier.  The activations are
 // staged segment by segment (a barrier pair each); a lane's weight bytes are
-// requested kAhead chunks before they are multiplied (the chunk loop is
-// unrolled, so every chunk has its own registers).
-constexpr int kAhead = 3;
-template <class F, int NCH, class Lay = MmRowMajor>
+// requested AHEAD chunks before they are multiplied (the chunk loop is
+// unrolled, so every chunk has its own registers).  From the tiled copy, two
+// chunks ahead suit small grids and one suits many (token, slot) pairs, and
+// so many workgroups (three was slower at B = 8 and 32); from row-major
+// weights three are best at B = 8 and as good at B = 32.
+template <class F, int NCH, class Lay = MmRowMajor, int AHEAD = 2>
 __device__ __forceinline__ void mm_pass_n(const MmTiles& T, rsrc_t rA, int a_rows, const int* srow, int nt,
                                           unsigned char* abuf, int wv, int lane, f32x4_t (&acc)[2][2]) {
   constexpr int K = NCH * kMmChunk;
@@ -470,7 +472,7 @@ __device__ __forceinline__ void mm_pass_n(const MmTiles& T, rsrc_t rA, int a_row
     for (int tt = 0; tt < 2; ++tt) acc[rt][tt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   MmRegs R[NCH];
 #pragma unroll
-  for (int u = 0; u < NCH && u < kAhead; ++u) Lay::load(T, u, R[u]);
+  for (int u = 0; u < NCH && u < AHEAD; ++u) Lay::load(T, u, R[u]);
 #pragma unroll
   for (int u = 0; u < NCH; ++u) {
     if (u % cps == 0) {  // next segment: everyone is done with the buffer, then copy
@@ -479,7 +481,7 @@ __device__ __forceinline__ void mm_pass_n(const MmTiles& T, rsrc_t rA, int a_row
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies are in
       __syncthreads();
     }
-    if (u + kAhead < NCH) Lay::load(T, u + kAhead, R[u + kAhead]);
+    if (u + AHEAD < NCH) Lay::load(T, u + AHEAD, R[u + AHEAD]);
     mm_chunk<F>(R[u], abuf, Rrows, kseg, u % cps, ntt, lane, acc);
   }
 }
@@ -554,7 +556,7 @@ __global__ __launch_bounds__(kNormThreads) void k_bnorm(float* __restrict__ h, c
 // normalised tokens up [2][B][H], and writes h = silu(gate) * up for each
 // token as three bf16 planes: hrp [3][B*k][I] by pair id (routed),
 // hsp [3][B][Is] by token (shared).
-template <bool TILED>
+template <bool TILED, int AHEAD>
 __global__ __launch_bounds__(kMmThreads, 3) void k_mm_gateup(flint_moe_layer L, int I, int Is, int k, int B,
                                                              int Umax, const uint16_t* __restrict__ up,
                                                              const int32_t* __restrict__ bk, uint16_t* __restrict__ hrp,
@@ -632,7 +634,7 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_mm_gateup(flint_moe_layer L, 
     }
     __syncthreads();
     f32x4_t acc[2][2];
-    mm_pass_n<FmtF16, kHidden / kMmChunk, typename std::conditional<TILED, MmTiled, MmRowMajor>::type>(
+    mm_pass_n<FmtF16, kHidden / kMmChunk, typename std::conditional<TILED, MmTiled, MmRowMajor>::type, AHEAD>(
         T, rA, B, srow, nt, abuf, wv, lane, acc);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
@@ -654,7 +656,7 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_mm_gateup(flint_moe_layer L, 
 // grid (H / 256, Umax + 1), 512 threads; groups as for gate/up.  Wave w takes
 // output rows r0 + 32 w .. + 31.  Routed: dr[pid][n] = w_pid * S_e * (Wd[e][n]
 // . h_pid) over K = I; shared: ds[b][n] = S * (Wsd[n] . hs_b) over K = Is.
-template <bool TILED>
+template <bool TILED, int AHEAD>
 __global__ __launch_bounds__(kMmThreads, 3) void k_mm_down(flint_moe_layer L, int I, int Is, int B, int Umax,
                                                            const uint16_t* __restrict__ hrp,
                                                            const uint16_t* __restrict__ hsp,
@@ -728,9 +730,9 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_mm_down(flint_moe_layer L, in
     }
     __syncthreads();
     f32x4_t acc[2][2];
-    if (K == 1024) mm_pass_n<FmtBF16, 4, Lay>(T, rA, a_rows, srow, nt, abuf, wv, lane, acc);
-    else if (K == 2048) mm_pass_n<FmtBF16, 8, Lay>(T, rA, a_rows, srow, nt, abuf, wv, lane, acc);
-    else mm_pass_n<FmtBF16, 2, Lay>(T, rA, a_rows, srow, nt, abuf, wv, lane, acc);
+    if (K == 1024) mm_pass_n<FmtBF16, 4, Lay, AHEAD>(T, rA, a_rows, srow, nt, abuf, wv, lane, acc);
+    else if (K == 2048) mm_pass_n<FmtBF16, 8, Lay, AHEAD>(T, rA, a_rows, srow, nt, abuf, wv, lane, acc);
+    else mm_pass_n<FmtBF16, 2, Lay, AHEAD>(T, rA, a_rows, srow, nt, abuf, wv, lane, acc);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -974,6 +976,7 @@ hipError_t launch_batch_step_tiled(const flint_moe_dims& d, const flint_moe_laye
   HeadPartial* parts = reinterpret_cast<HeadPartial*>(base + w.partials);
   const int k = d.top_k, E = d.n_experts, I = d.expert_width, Is = d.shared_width, nb = B * k;
   const int Umax = nb < E ? nb : E;
+  const bool many = nb >= 96;  // tiled weights and many (token, slot) pairs: one chunk ahead, else two
   const int gu_x = ((I > Is ? I : Is) + kMmGateUpRows - 1) / kMmGateUpRows;
   k_copy_words<<<(B * kHidden + kThreads - 1) / kThreads, kThreads, 0, s>>>(
       reinterpret_cast<const uint32_t*>(x), reinterpret_cast<uint32_t*>(h), B * kHidden);
@@ -988,18 +991,18 @@ hipError_t launch_batch_step_tiled(const flint_moe_dims& d, const flint_moe_laye
       k_copy_words<<<1, kThreads, 0, s>>>(reinterpret_cast<const uint32_t*>(idx),
                                           reinterpret_cast<uint32_t*>(routes + (size_t)l * nb), nb);
     k_bucket<<<1, kThreads, 0, s>>>(idx, nb, E, bk);
-    if (tiles)
-      k_mm_gateup<true><<<dim3(gu_x, Umax + 1), kMmThreads, 0, s>>>(
-          Ly, I, Is, k, B, Umax, up, bk, hrp, hsp, nb, tiles + (size_t)l * batch_tiles_layer_bytes(d), E);
-    else
-      k_mm_gateup<false><<<dim3(gu_x, Umax + 1), kMmThreads, 0, s>>>(Ly, I, Is, k, B, Umax, up, bk, hrp, hsp, nb,
-                                                                      nullptr, E);
-    if (tiles)
-      k_mm_down<true><<<dim3(kHidden / kMmRows, Umax + 1), kMmThreads, 0, s>>>(
-          Ly, I, Is, B, Umax, hrp, hsp, bk, wts, dr, ds, nb, tiles + (size_t)l * batch_tiles_layer_bytes(d), E);
-    else
-      k_mm_down<false><<<dim3(kHidden / kMmRows, Umax + 1), kMmThreads, 0, s>>>(Ly, I, Is, B, Umax, hrp, hsp, bk,
-                                                                               wts, dr, ds, nb, nullptr, E);
+    const uint8_t* lt = tiles ? tiles + (size_t)l * batch_tiles_layer_bytes(d) : nullptr;
+    const dim3 gg(gu_x, Umax + 1), gd(kHidden / kMmRows, Umax + 1);
+    if (tiles && many) {
+      k_mm_gateup<true, 1><<<gg, kMmThreads, 0, s>>>(Ly, I, Is, k, B, Umax, up, bk, hrp, hsp, nb, lt, E);
+      k_mm_down<true, 1><<<gd, kMmThreads, 0, s>>>(Ly, I, Is, B, Umax, hrp, hsp, bk, wts, dr, ds, nb, lt, E);
+    } else if (tiles) {
+      k_mm_gateup<true, 2><<<gg, kMmThreads, 0, s>>>(Ly, I, Is, k, B, Umax, up, bk, hrp, hsp, nb, lt, E);
+      k_mm_down<true, 2><<<gd, kMmThreads, 0, s>>>(Ly, I, Is, B, Umax, hrp, hsp, bk, wts, dr, ds, nb, lt, E);
+    } else {  // row-major weights: longer load latency, three chunks ahead
+      k_mm_gateup<false, 3><<<gg, kMmThreads, 0, s>>>(Ly, I, Is, k, B, Umax, up, bk, hrp, hsp, nb, lt, E);
+      k_mm_down<false, 3><<<gd, kMmThreads, 0, s>>>(Ly, I, Is, B, Umax, hrp, hsp, bk, wts, dr, ds, nb, lt, E);
+    }
     // the residual update and the next norm (after the last layer: the
     // final norm, the head's input)
     k_bnorm<<<B, kNormThreads, 0, s>>>(h, dr, ds, k, l + 1 < L ? u : nullptr, up, B, eps);
