@@ -428,6 +428,32 @@ __global__ __launch_bounds__(256) void k_attn_merge(const float* __restrict__ pa
   }
 }
 
+// Short contexts (nchunks <= 16): one wave per query head, every record of
+// the head requested at once, no LDS.  Same rule as k_attn_merge.
+__global__ __launch_bounds__(64) void k_attn_merge16(const float* __restrict__ part, const float* __restrict__ sinks,
+                                                     int group, int nchunks, float* __restrict__ o) {
+  const int lane = threadIdx.x, h = blockIdx.x, g = h / group, hh = h % group;
+  const float* P0 = part + ((size_t)g * kMaxGroup + hh) * kMaxChunks * kPart;
+  float2 ov[16];
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc)
+    ov[cc] = cc < nchunks ? *reinterpret_cast<const float2*>(P0 + cc * kPart + 2 + 2 * lane) : make_float2(0.f, 0.f);
+  const float mc = lane < nchunks ? P0[lane * kPart] : -INFINITY;
+  const float lc = lane < nchunks ? P0[lane * kPart + 1] : 0.0f;
+  const float sink = sinks[h];
+  const float M = wave_max(fmaxf(mc, sink));
+  const float f = lane < nchunks ? __expf(mc - M) : 0.0f;
+  const float Z = wave_sum(f * lc) + __expf(sink - M);
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) {
+    const float fc = lane_f32(f, cc);  // 0 past nchunks
+    a0 = __builtin_fmaf(fc, ov[cc].x, a0);
+    a1 = __builtin_fmaf(fc, ov[cc].y, a1);
+  }
+  *reinterpret_cast<float2*>(o + h * kD + 2 * lane) = make_float2(a0 / Z, a1 / Z);
+}
+
 // --------------------------------------------------------- host helpers --
 struct AttnWs {
   size_t qkv, o, part, total;
@@ -533,7 +559,9 @@ hipError_t flint::attn_run(const flint_attn_dims& d, const flint_attn_layer& lay
   k_attn<<<dim3(A.nchunks, d.n_kv_heads), 256, 0, s>>>(A);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (A.nchunks <= 64)
+  if (A.nchunks <= 16)
+    k_attn_merge16<<<d.n_q_heads, 64, 0, s>>>(A.part, layer.sinks, A.group, A.nchunks, o);
+  else if (A.nchunks <= 64)
     k_attn_merge<64><<<d.n_q_heads, 256, 0, s>>>(A.part, layer.sinks, A.group, A.nchunks, o);
   else
     k_attn_merge<kMaxChunks><<<d.n_q_heads, 256, 0, s>>>(A.part, layer.sinks, A.group, A.nchunks, o);
