@@ -309,6 +309,19 @@ int32_t flint_stack_error(const void* ws, size_t ws_bytes, int32_t* error /*[hos
 int32_t flint_nvfp4_quantize(const float* w, int64_t n_mats, int64_t rows, int64_t cols, uint8_t* codes,
                              uint8_t* scales, float* tscales, void* ws, size_t ws_bytes, void* stream);
 
+/* NVFP4 quantiser on the host [P3 "Checking 125 tokens a second": 4-bit
+ * values, one 8-bit scale per 16 values; P1 "Quantization with Offline
+ * Distillation": NVFP4 weights and output head]: the library's own encoder
+ * for weights prepared off the GPU, with the recipe of flint_nvfp4_quantize
+ * (bit-identical results) for one matrix w [rows][cols] (all [host]):
+ * codes uint8 [rows][cols/2], scales uint8 [rows][cols/16], *tscale = S.
+ * cols must be a multiple of 16 (>= 16), rows >= 1.  Needs no GPU and no HIP
+ * runtime; runs on up to 32 host threads (the result does not depend on
+ * their number); synchronous.  Returns FLINT_E_NULL or FLINT_E_DIMS without
+ * writing anything, else FLINT_OK.  Inputs must be finite. */
+int32_t flint_nvfp4_quantize_host(const float* w, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                                  float* tscale);
+
 /* Dequantise an NVFP4 matrix to float [rows][cols] (the exact values above). */
 int32_t flint_nvfp4_dequantize(const flint_nvfp4* w /*[host]*/, int64_t rows, int64_t cols, float* out, void* stream);
 

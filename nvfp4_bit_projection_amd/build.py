@@ -1,7 +1,7 @@
 """Build step of the HIP library (hipcc, gfx950 only).
 
-``build_library()`` compiles ``csrc/*.hip`` into ``libflint_moe.so`` next to
-this file.  All device code is built with packed FP32 instructions disabled
+``build_library()`` compiles ``csrc/*.hip`` (device and host code) and
+``csrc/*.cpp`` (host-only code) into ``libflint_moe.so`` next to this file.  All device code is built with packed FP32 instructions disabled
 (``-target-feature -packed-fp32-ops``), so the compiler emits only scalar
 FP32 FMAs.
 """
@@ -20,7 +20,7 @@ COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}
 
 
 def sources() -> list[str]:
-    return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
+    return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")) + glob.glob(os.path.join(HERE, "csrc", "*.cpp")))
 
 
 def build_library(out: str = LIB_PATH) -> str:

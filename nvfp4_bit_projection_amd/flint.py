@@ -104,6 +104,7 @@ def _load():
                                             _SZ, _P], _I32),
         "flint_nvfp4_quantize": ([_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _I32),
         "flint_nvfp4_dequantize": ([ctypes.POINTER(NVFP4), _I64, _I64, _P, _P], _I32),
+        "flint_nvfp4_quantize_host": ([_P, _I64, _I64, _P, _P, _P], _I32),
         "flint_attn_workspace_bytes": ([ctypes.POINTER(AttnDims)], _SZ),
         "flint_attn_decode": ([ctypes.POINTER(AttnDims), ctypes.POINTER(AttnLayer), _P, _I32, _P, _P, _I32, _P, _P,
                                _SZ, _P], _I32),
@@ -136,7 +137,7 @@ EXPORTED = ("flint_status_str", "flint_last_hip_error", "flint_workspace_bytes",
             "flint_stack_prepare",
             "flint_stack_decode", "flint_stack_decode_traced", "flint_stack_decode_batch", "flint_stack_error",
             "flint_stack_batch_tiles_bytes", "flint_stack_batch_tiles", "flint_stack_decode_batch_tiled",
-            "flint_nvfp4_quantize", "flint_nvfp4_dequantize",
+            "flint_nvfp4_quantize", "flint_nvfp4_dequantize", "flint_nvfp4_quantize_host",
             # include/flint_attn.h
             "flint_attn_workspace_bytes", "flint_attn_decode", "flint_dense_workspace_bytes", "flint_dense_mlp",
             # include/flint_int4.h
@@ -231,6 +232,21 @@ def quantize(w: torch.Tensor) -> NVFP4Tensor:
     if squeeze:
         return NVFP4Tensor(codes[0], scales[0], ts[:1])
     return NVFP4Tensor(codes, scales, ts)
+
+
+def quantize_host(w):
+    """w float32 numpy [rows, cols] (host) -> (codes uint8 [rows, cols/2],
+    scales uint8 [rows, cols/16], tscale float32) by the library's host
+    encoder; no GPU involved."""
+    import numpy as np
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, cols = w.shape
+    codes = np.empty((rows, cols // 2), dtype=np.uint8)
+    scales = np.empty((rows, cols // 16), dtype=np.uint8)
+    ts = np.zeros(1, dtype=np.float32)
+    _check(_lib.flint_nvfp4_quantize_host(w.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data,
+                                          ts.ctypes.data), "flint_nvfp4_quantize_host")
+    return codes, scales, ts[0]
 
 
 def quantize_into(w: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, tscales: torch.Tensor,
