@@ -7,6 +7,7 @@ launch of the persistent stack kernel.  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
   python bench.py --batch 32        # small-batch decode: B tokens per step
+  python bench.py --layer           # one MoE layer (256 experts), 8 layers in turn
   python bench.py --copy-calib      # one 1 GiB device copy (counter calibration)
 """
 from __future__ import annotations
@@ -23,6 +24,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+RUNS = 5  # timed runs of K steps each in the default bench; the median is reported
 KERNEL = "k_stack_decode"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_stack_decode_stack47_b1_traffic.md")
 KERNEL_SOURCES = ["nvfp4_bit_projection_amd/csrc/stack.hip", "nvfp4_bit_projection_amd/csrc/flint_device.h",
@@ -55,11 +57,23 @@ def measured_traffic() -> int | None:
     return int(val.group(1))
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(target_s: float = 10.0, max_reps: int = 64) -> dict:
     """The oracle (plain fp64 CPU code) on a bounded sample of the same
     workload: one token through all 47 layers and the full head, with the
     weights it touches prepared beforehand, repeated until about `target_s`
-    seconds of oracle compute have been timed."""
+    seconds of oracle compute have been timed (all oracle threads).  Also the
+    single layer (256 experts) and the head alone, median of 3 calls each, on
+    all oracle threads and on one."""
     import numpy as np
 
     import oracle
@@ -87,9 +101,52 @@ def cpu_baseline(target_s: float = 10.0, max_reps: int = 64) -> dict:
         reps += 1
         if again != first:
             raise RuntimeError("the oracle is not deterministic")
-    return {"value": reps / timed, "unit": "tok/s", "cores": oracle.default_threads(), "kind": "oracle",
+
+    def median3(fn):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return sorted(ts)[1]
+
+    u = x * oracle.rms_inv(x, 1e-6)
+    nt = oracle.default_threads()
+    per_call = {}
+    for threads in (nt, 1):
+        per_call[f"layer_e256_ms_{threads}t"] = round(1e3 * median3(lambda: moe_layer(W, 0, u, nthreads=threads)), 2)
+        per_call[f"head_v150144_ms_{threads}t"] = round(
+            1e3 * median3(lambda: oracle.nvfp4_gemv(W.head(), u, nthreads=threads)), 1)
+    return {"value": reps / timed, "unit": "tok/s", "cores": nt, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"one token through all 47 layers + full head, weights prepared beforehand, "
-                      f"timed {reps} times: {timed:.1f} s"}
+                      f"timed {reps} times: {timed:.1f} s on {nt} threads",
+            "per_call_median_of_3": per_call}
+
+
+def achievable_gbs(nbytes: int = 4 << 30, reps: int = 10) -> dict:
+    """The library's streaming-read probe (flint_stream_read: 128-bit
+    non-temporal loads, nothing else) over a buffer 16x the 256 MB last-level
+    cache: the achievable HBM read rate on this machine."""
+    import torch
+
+    from nvfp4_bit_projection_amd import flint
+
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        flint.stream_read(buf, out)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        flint.stream_read(buf, out)
+    ev1.record()
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del buf, out
+    torch.cuda.empty_cache()
+    return {"kernel": "k_stream_read", "gbs": round(gbs, 1), "bytes": nbytes, "reps": reps,
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def copy_calib() -> int:
@@ -171,6 +228,64 @@ def bench_batch(args) -> int:
                      "bytes_per_step": round(step_bytes)},
     }
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_layer(args) -> int:
+    """Config 1: one full MoE layer (256 experts, top-6, shared expert) for one
+    token.  Eight distinct layers (3.7 GB, 14x the last-level cache) are used
+    in turn, so every call streams its weights from HBM.  Timed per call with
+    HIP events: the persistent kernel's one-layer launch
+    (flint_stack_decode_layers, norm + layer + residual add) and the kernel
+    sequence (flint_moe_decode: router/top-k, gate/up, down).  Bytes per call:
+    the router, 6 routed experts and the shared expert, 16,252,928 B."""
+    import torch
+
+    import synth
+    from nvfp4_bit_projection_amd import bytes_model as bm
+    from nvfp4_bit_projection_amd import flint, workload
+
+    torch.cuda.set_device(0)
+    dims = synth.MoEDims()
+    NL = 8
+    tmp = torch.empty(dims.n_experts * dims.expert_width * dims.hidden, dtype=torch.float32, device="cuda")
+    layers = [workload.build_layer(dims, seed=l, tmp=tmp) for l in range(NL)]
+    del tmp
+    head = workload.build_head(16, dims.hidden)
+    d = flint.dims_struct(dims.hidden, dims.n_experts, dims.expert_width, dims.top_k, dims.shared_width)
+    stack = flint.Stack(d, layers, head, 16, schedule=flint.SCHEDULE_PERSISTENT)
+    n = args.warmup + args.steps
+    x = workload.tokens([synth.TOKEN_SEED0 + t for t in range(n)], dims.hidden)
+    h = torch.empty_like(x)
+    y = torch.empty((1, dims.hidden), dtype=torch.float32, device="cuda")
+    ws = flint.workspace(flint.OP_DECODE, d, 1)
+    nbytes = bm.layer_bytes(bm.LayerShape())
+    out = []
+    calls = (("persistent_one_layer", lambda i: stack.decode_layers(x[i], i % NL, 1, h_out=h[i])),
+             ("kernel_sequence", lambda i: flint.moe_decode(d, layers[i % NL], x[i:i + 1], ws=ws)))
+    for name, fn in calls:
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for j, i in enumerate(range(args.warmup, n)):
+            evs[j][0].record()
+            fn(i)
+            evs[j][1].record()
+        torch.cuda.synchronize()
+        us = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+        med = us[len(us) // 2]
+        gbs = nbytes / (med * 1e-6) / 1e9
+        log(f"layer {name}: median {med:.2f} us (min {us[0]:.2f}, max {us[-1]:.2f}), {gbs:.0f} GB/s")
+        out.append({"schedule": name, "us_median": round(med, 2), "us_min": round(us[0], 2),
+                    "us_max": round(us[-1], 2), "bytes": nbytes, "achieved_gbs": round(gbs, 1),
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    assert stack.error() == 0
+    print(json.dumps({"metric": "one MoE layer us per token (E=256, batch 1)", "unit": "us",
+                      "higher_is_better": False, "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
+                      "config": {"workload": "moe_layer_e256_b1", "hidden": 2048, "experts": 256, "top_k": 6,
+                                 "expert_width": 512, "shared_width": 1024, "distinct_layers_rotated": NL},
+                      "peak_gbs": HBM_PEAK_GBS, "schedules": out}), flush=True)
     return 0
 
 
@@ -318,19 +433,21 @@ def bench_int4(args) -> int:
     """The 150,144 x 2,048 output head as group-64 affine INT4 (BF16 scale and
     offset) against the same head as NVFP4: one GEMV + argmax per token
     (flint_int4_gemv, flint_lmhead_gemv), timed from HIP-graph replays.  Both
-    formats read 1,152 bytes per row."""
+    formats read 1,152 bytes per row (173 MB per call); four copies of each
+    head (692 MB, 2.7x the last-level cache) are used in turn, so every call
+    streams its head from HBM."""
     import torch
 
     import synth
     from nvfp4_bit_projection_amd import flint, workload
 
     torch.cuda.set_device(0)
-    V, H = 150144, 2048
+    V, H, NC = 150144, 2048, 4
     w = torch.empty(V * H, dtype=torch.float32, device="cuda")
     synth.normal_device(synth.HEAD_SEED, synth.stream_id(synth.HEAD), V * H, w, std=synth.WEIGHT_STD)
-    q4 = flint.int4_quantize(w.view(V, H))
+    q4 = [flint.int4_quantize(w.view(V, H)) for _ in range(NC)]
     del w
-    head = workload.build_head(V, H)
+    heads = [workload.build_head(V, H) for _ in range(NC)]
     x = workload.tokens([synth.TOKEN_SEED0], H)
     nbytes = V * (H // 2 + H // 16)
     ws4 = torch.zeros(flint.lib().flint_int4_gemv_workspace_bytes(1), dtype=torch.uint8, device="cuda")
@@ -341,26 +458,27 @@ def bench_int4(args) -> int:
     an = torch.empty(1, dtype=torch.int32, device="cuda")
     out = []
     for name, fn, check in (
-            ("int4_g64_head", lambda: flint.int4_gemv(q4, x, ws=ws4, y=y4, argmax=a4), lambda: y4),
-            ("int4_g64_gemv_no_argmax", lambda: flint.int4_gemv(q4, x, want_argmax=False, ws=ws4, y=y4), lambda: y4),
-            ("nvfp4_head", lambda: flint.lmhead(head, V, x, ws=wsn, logits=yn, argmax=an), lambda: yn)):
-        for _ in range(args.warmup):
-            fn()
+            ("int4_g64_head", lambda c: flint.int4_gemv(q4[c], x, ws=ws4, y=y4, argmax=a4), lambda: y4),
+            ("int4_g64_gemv_no_argmax", lambda c: flint.int4_gemv(q4[c], x, want_argmax=False, ws=ws4, y=y4),
+             lambda: y4),
+            ("nvfp4_head", lambda c: flint.lmhead(heads[c], V, x, ws=wsn, logits=yn, argmax=an), lambda: yn)):
+        for i in range(args.warmup):
+            fn(i % NC)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            fn()
+            fn(0)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        ref = check().clone() if check else None
+        ref = check().clone()
         with torch.cuda.graph(g):
-            for _ in range(16):
-                fn()
+            for i in range(16):
+                fn(i % NC)
         g.replay()
         torch.cuda.synchronize()
-        if check is not None and not torch.equal(check(), ref):
+        if not torch.equal(check(), ref):  # every copy holds the same head
             raise RuntimeError("graph replay differs from the eager call")
         reps = max(1, args.steps // 16)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -371,12 +489,13 @@ def bench_int4(args) -> int:
         torch.cuda.synchronize()
         us = ev0.elapsed_time(ev1) * 1e3 / (reps * 16)
         gbs = nbytes / (us * 1e-6) / 1e9
-        log(f"{name}: {us:.2f} us per token, {gbs:.0f} GB/s")
+        log(f"{name}: {us:.2f} us per token, {gbs:.0f} GB/s ({NC} copies in turn)")
         out.append({"kernel": name, "us": round(us, 2), "bytes": nbytes, "achieved_gbs": round(gbs, 1),
                     "frac": round(gbs / HBM_PEAK_GBS, 4)})
     print(json.dumps({"metric": "output head GEMV + argmax us per token (batch 1)", "unit": "us",
                       "higher_is_better": False, "steps": args.steps, "warmup": args.warmup, "data": "synthetic",
-                      "config": {"workload": "lmhead_v150144_int4_vs_nvfp4", "vocab": V, "hidden": H},
+                      "config": {"workload": "lmhead_v150144_int4_vs_nvfp4", "vocab": V, "hidden": H,
+                                 "head_copies_rotated": NC},
                       "peak_gbs": HBM_PEAK_GBS, "heads": out}), flush=True)
     return 0
 
@@ -547,6 +666,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--layers", type=int, default=47)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-achievable", action="store_true", help="skip the streaming-read achievable line")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--batch", type=int, default=1,
                     help="tokens per step; above 1 the batched step (experts deduplicated per layer) is timed")
@@ -556,6 +676,8 @@ def main() -> int:
                     help="time the router call alone in its four variants (fp32/BF16 router, softmax/sigmoid)")
     ap.add_argument("--attn", action="store_true",
                     help="time one attention layer (sliding and full context) and the dense MLP")
+    ap.add_argument("--layer", action="store_true",
+                    help="time one MoE layer of 256 experts (8 distinct layers in turn), both schedules")
     ap.add_argument("--int4", action="store_true",
                     help="time the output head as group-64 affine INT4 against the NVFP4 head")
     ap.add_argument("--gemm", action="store_true", help="time the prefill GEMM (A32 and A4) on model shapes")
@@ -577,6 +699,8 @@ def main() -> int:
         return bench_attn(args)
     if args.int4:
         return bench_int4(args)
+    if args.layer:
+        return bench_layer(args)
     if args.gemm:
         return bench_gemm(args)
     if args.model:
@@ -616,32 +740,44 @@ def main() -> int:
     if stack.error():
         log("the stack kernel raised its error flag")
         return 1
-    # every step is one launch of the stack kernel on torch's current stream;
-    # events around each launch give its duration, events around the whole
-    # loop the throughput
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    ev0.record()
-    for i, t in enumerate(range(args.warmup, T)):
-        starts[i].record()
-        step(t)
-        ends[i].record()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = ev0.elapsed_time(ev1)
+    # RUNS timed runs of exactly K steps each, every run bracketed by
+    # synchronisations; every step is one launch of the stack kernel on
+    # torch's current stream: events around each launch give its duration,
+    # events around the run its throughput.  The reported value is the
+    # median run; min and max are reported with it.
+    run_ms, launch_ms, walls = [], [], []
+    for run in range(RUNS):
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        ev0.record()
+        for i, t in enumerate(range(args.warmup, T)):
+            starts[i].record()
+            step(t)
+            ends[i].record()
+        ev1.record()
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - wall0)
+        run_ms.append(ev0.elapsed_time(ev1))
+        launch_ms += [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    if stack.error():
+        log("the stack kernel raised its error flag")
+        return 1
+    order = sorted(range(RUNS), key=lambda r: run_ms[r])
+    ms = run_ms[order[RUNS // 2]]
     ms_per_step = ms / args.steps
     tok_s = 1000.0 / ms_per_step
-    launch_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    tok_runs = [1000.0 * args.steps / m for m in run_ms]
+    launch_ms.sort()
     launch_avg = sum(launch_ms) / len(launch_ms)
     shape = bm.LayerShape()
     token_bytes = bm.token_bytes(shape, L, V)
     gbs = token_bytes / (launch_avg * 1e-3) / 1e9
-    log(f"{args.steps} tokens in {ms:.1f} ms (wall {wall * 1e3:.1f} ms): {tok_s:.1f} tok/s; "
-        f"{KERNEL} launch avg {launch_avg * 1e3:.1f} us (median {launch_ms[len(launch_ms) // 2] * 1e3:.1f}), "
-        f"{gbs:.1f} GB/s")
+    log(f"{RUNS} runs of {args.steps} tokens: median {ms:.2f} ms ({tok_s:.1f} tok/s), "
+        f"min {min(tok_runs):.1f} max {max(tok_runs):.1f} tok/s; {KERNEL} launch avg {launch_avg * 1e3:.1f} us "
+        f"(median {launch_ms[len(launch_ms) // 2] * 1e3:.1f}), {gbs:.1f} GB/s")
 
     traffic = measured_traffic()
     result = {
@@ -665,12 +801,18 @@ def main() -> int:
                      "traffic": (round(traffic / (launch_avg * 1e-3) / 1e9, 1) if traffic else None),
                      "kernel": KERNEL, "bytes_per_launch": token_bytes,
                      "traffic_bytes_per_launch": traffic, "launch_us": round(launch_avg * 1e3, 2)},
+        "runs": {"n": RUNS, "steps_each": args.steps, "tok_s_median": round(tok_s, 2),
+                 "tok_s_min": round(min(tok_runs), 2), "tok_s_max": round(max(tok_runs), 2),
+                 "tok_s": [round(v, 2) for v in tok_runs], "wall_s": [round(w, 4) for w in walls]},
     }
     # release device memory before the interpreter exits (keeps profilers'
     # teardown away from live allocations)
-    del stack, layers, head, x, logits, argmax, starts, ends, ev0, ev1
+    del stack, layers, head, x, logits, argmax
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    if not args.no_achievable:
+        result["achievable"] = achievable_gbs()
+        log(f"achievable (streaming read): {result['achievable']['gbs']} GB/s")
     if not args.no_cpu_baseline:
         log("timing the oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline()

@@ -252,6 +252,22 @@ int32_t flint_stack_decode_traced(const flint_stack_plan* plan /*[host]*/, const
                                   float* logits, int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes,
                                   int64_t* trace, void* stream);
 
+/* Part of the stack for one token, no head [P2 "How does Flint's
+ * architecture work?": 47 MoE layers; P3 "The shape, read from the headers"]:
+ * h_0 = x (float [H]); for l = l0 .. l0 + n - 1 of the plan's layers,
+ * h <- h + MoE_l(h / sqrt(mean(h^2) + eps)); the final h to h_out (float
+ * [H]; may be the same buffer as x).  One launch of the persistent schedule
+ * (the plan needs packed down projections; FLINT_E_UNSUPPORTED otherwise),
+ * for checking single layers against a reference and for models that put
+ * other layers between MoE layers.  routes_opt int32 [n][k] receives each
+ * layer's chosen experts (by logit descending) when non-NULL.  Workspace and
+ * watchdog flag as for flint_stack_decode (the same stack workspace may be
+ * used by both, one call after the other).  l0 >= 0, n >= 1,
+ * l0 + n <= n_layers. */
+int32_t flint_stack_decode_layers(const flint_stack_plan* plan /*[host]*/, int32_t l0, int32_t n, const float* x,
+                                  float eps, float* h_out, int32_t* routes_opt, void* ws, size_t ws_bytes,
+                                  void* stream);
+
 /* Small-batch decode step [P2 "How does Flint's architecture work?"; P3
  * "The shape, read from the headers"]: B tokens (1 <= B <= 64) through the
  * same stack and head together, each token with its own top-k routing:
@@ -324,6 +340,16 @@ int32_t flint_nvfp4_quantize_host(const float* w, int64_t rows, int64_t cols, ui
 
 /* Dequantise an NVFP4 matrix to float [rows][cols] (the exact values above). */
 int32_t flint_nvfp4_dequantize(const flint_nvfp4* w /*[host]*/, int64_t rows, int64_t cols, float* out, void* stream);
+
+/* Measurement aid, not part of the decode path: reads `bytes` bytes of src
+ * (device, 16-byte aligned, bytes a multiple of 16) once with 128-bit
+ * non-temporal loads, the access pattern of the decode kernels' weight
+ * streams, and does nothing else with them (out, one device uint32, is
+ * written only on a hash coincidence).  Timed over a buffer much larger than
+ * the 256 MB last-level cache it gives the achievable read bandwidth that the
+ * decode step's bandwidth (bytes per token x tokens per second [P3 "Checking
+ * 125 tokens a second"]) is compared with. */
+int32_t flint_stream_read(const void* src, size_t bytes, uint32_t* out, void* stream);
 
 /* Human-readable status; the last hipError_t seen by a failing call (0 if none). */
 const char* flint_status_str(int32_t status);

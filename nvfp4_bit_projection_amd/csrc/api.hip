@@ -363,6 +363,24 @@ int32_t flint_stack_decode_traced(const flint_stack_plan* plan, const float* x, 
   return stack_decode_impl(plan, x, T, eps, logits, argmax, routes_opt, ws, ws_bytes, trace, stream);
 }
 
+int32_t flint_stack_decode_layers(const flint_stack_plan* plan, int32_t l0, int32_t n, const float* x, float eps,
+                                  float* h_out, int32_t* routes_opt, void* ws, size_t ws_bytes, void* stream) {
+  int32_t st;
+  if (!plan || !x || !h_out || !ws) return FLINT_E_NULL;
+  if ((st = check_dims(&plan->dims))) return st;
+  if (!plan->layers || !plan->table) return FLINT_E_NULL;
+  if (plan->n_layers < 1 || l0 < 0 || n < 1 || l0 + n > plan->n_layers || !(eps > 0.0f)) return FLINT_E_DIMS;
+  if (!plan->packed || !stack_persistent_supported(plan->dims, plan->n_layers)) return FLINT_E_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(h_out) || !aligned16(ws) || (routes_opt && !aligned4(routes_opt)))
+    return FLINT_E_ALIGN;
+  StackWs sw(plan->dims, plan->vocab > 0 ? plan->vocab : 1);
+  if (ws_bytes < sw.total) return FLINT_E_WORKSPACE;
+  if ((st = check_device())) return st;
+  hipError_t e = launch_stack_persistent(plan->dims, n, 0, plan->table, x, 1, eps, nullptr, nullptr, routes_opt,
+                                         static_cast<char*>(ws) + sw.persist, nullptr, (hipStream_t)stream, l0, h_out);
+  return e == hipSuccess ? FLINT_OK : hip_fail(e);
+}
+
 int32_t flint_stack_decode_batch(const flint_stack_plan* plan, const float* x, int32_t B, float eps, float* logits,
                                  int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes, void* stream) {
   int32_t st;

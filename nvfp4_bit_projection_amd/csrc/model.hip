@@ -124,10 +124,14 @@ int32_t flint_model_decode(const flint_model* m, const float* x, int32_t pos, fl
       e = dense_run(dn[0], dn[1], dn[2], m->dense_width, h, m->eps, h, true, sc, s);
     } else if (m->moe_plan) {
       // one launch of the persistent kernel: layer l - n_dense of the plan's
-      // table, no head, the residual updated in place (every workgroup has
-      // read h before any can store: each needs all 256 router logits first);
-      // it also applies the next layer's q, k, v projections to the norm of
-      // the new residual, which it holds in every workgroup
+      // table, no head, the residual updated in place.  Every workgroup
+      // copies h into LDS before its first exchange store, and the
+      // workgroups that write h_out do so only after the layer's residual
+      // exchange, which needs the partial outputs of all 256 workgroups (each
+      // owns 64 of the 2,048 rows in every XCD); so no store to h can
+      // overtake a read of it, whatever the number of experts.  The launch
+      // also applies the next layer's q, k, v projections to the norm of the
+      // new residual, which it holds in every workgroup
       StackQkv nx{};
       const bool next = l + 1 < m->n_layers;
       if (next) {

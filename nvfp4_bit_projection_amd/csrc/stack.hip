@@ -93,6 +93,12 @@ struct StackParams {
   StackQkv qkv;    // k_stack_decode<false>: rows applied to the final residual's norm (out == nullptr: none)
 };
 
+// In-place use (h_out == x, one launch per layer of a longer model) relies on
+// every workgroup storing a partial output of every layer: each workgroup of
+// an XCD owns 64 rows of the 2,048-wide partial output, so the residual
+// exchange cannot finish before every workgroup has read x.
+static_assert(kGroupWGs * 64 == kHidden, "every workgroup owns 64 rows of the partial outputs");
+
 constexpr int kTracePoints = 16;
 constexpr int kTraceMaxLayers = kMaxStackLayers;
 

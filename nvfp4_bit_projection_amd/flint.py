@@ -97,6 +97,8 @@ def _load():
                                        _P], _I32),
         "flint_stack_decode_batch": ([ctypes.POINTER(StackPlan), _P, _I32, ctypes.c_float, _P, _P, _P, _P, _SZ, _P],
                                      _I32),
+        "flint_stack_decode_layers": ([ctypes.POINTER(StackPlan), _I32, _I32, _P, ctypes.c_float, _P, _P, _P, _SZ,
+                                       _P], _I32),
         "flint_stack_error": ([_P, _SZ, ctypes.POINTER(_I32)], _I32),
         "flint_stack_batch_tiles_bytes": ([ctypes.POINTER(Dims), _I32], _SZ),
         "flint_stack_batch_tiles": ([ctypes.POINTER(StackPlan), _P, _SZ, _P], _I32),
@@ -105,6 +107,7 @@ def _load():
         "flint_nvfp4_quantize": ([_P, _I64, _I64, _I64, _P, _P, _P, _P, _SZ, _P], _I32),
         "flint_nvfp4_dequantize": ([ctypes.POINTER(NVFP4), _I64, _I64, _P, _P], _I32),
         "flint_nvfp4_quantize_host": ([_P, _I64, _I64, _P, _P, _P], _I32),
+        "flint_stream_read": ([_P, _SZ, _P, _P], _I32),
         "flint_attn_workspace_bytes": ([ctypes.POINTER(AttnDims)], _SZ),
         "flint_attn_decode": ([ctypes.POINTER(AttnDims), ctypes.POINTER(AttnLayer), _P, _I32, _P, _P, _I32, _P, _P,
                                _SZ, _P], _I32),
@@ -136,8 +139,9 @@ EXPORTED = ("flint_status_str", "flint_last_hip_error", "flint_workspace_bytes",
             "flint_moe_decode", "flint_lmhead_gemv", "flint_stack_table_bytes", "flint_stack_packed_bytes",
             "flint_stack_prepare",
             "flint_stack_decode", "flint_stack_decode_traced", "flint_stack_decode_batch", "flint_stack_error",
+            "flint_stack_decode_layers",
             "flint_stack_batch_tiles_bytes", "flint_stack_batch_tiles", "flint_stack_decode_batch_tiled",
-            "flint_nvfp4_quantize", "flint_nvfp4_dequantize", "flint_nvfp4_quantize_host",
+            "flint_nvfp4_quantize", "flint_nvfp4_dequantize", "flint_nvfp4_quantize_host", "flint_stream_read",
             # include/flint_attn.h
             "flint_attn_workspace_bytes", "flint_attn_decode", "flint_dense_workspace_bytes", "flint_dense_mlp",
             # include/flint_int4.h
@@ -232,6 +236,13 @@ def quantize(w: torch.Tensor) -> NVFP4Tensor:
     if squeeze:
         return NVFP4Tensor(codes[0], scales[0], ts[:1])
     return NVFP4Tensor(codes, scales, ts)
+
+
+def stream_read(buf: torch.Tensor, out: torch.Tensor) -> None:
+    """One streaming read of buf (a device tensor, byte size a multiple of 16);
+    out: a device int32/uint32 tensor of at least one element."""
+    _check(_lib.flint_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), out.data_ptr(), _stream()),
+           "flint_stream_read")
 
 
 def quantize_host(w):
@@ -405,6 +416,16 @@ class Stack:
                                                  argmax.data_ptr(), _ptr(routes), ws.data_ptr(), ws.numel(),
                                                  _stream()), "flint_stack_decode_batch")
         return logits, argmax
+
+    def decode_layers(self, x: torch.Tensor, l0: int, n: int, eps: float = 1e-6, h_out: torch.Tensor | None = None,
+                      routes: torch.Tensor | None = None) -> torch.Tensor:
+        """x float32 [H]: one token through layers l0 .. l0+n-1 (persistent
+        schedule, no head) -> the final residual float32 [H]."""
+        h_out = torch.empty_like(x) if h_out is None else h_out
+        _check(_lib.flint_stack_decode_layers(ctypes.byref(self.plan), l0, n, x.data_ptr(), eps, h_out.data_ptr(),
+                                              _ptr(routes), self.ws.data_ptr(), self.ws.numel(), _stream()),
+               "flint_stack_decode_layers")
+        return h_out
 
     def decode(self, x: torch.Tensor, eps: float = 1e-6, logits: torch.Tensor | None = None,
                argmax: torch.Tensor | None = None, routes: torch.Tensor | None = None, want_logits: bool = True):

@@ -1,10 +1,13 @@
 """GPU parity of the attention layer and the dense MLP (through the C ABI)
 against the CPU oracle on the same seeded inputs.
 
-Bars: y within relative L2 <= 1e-4 and max-abs <= 2e-3 * max|ref|; the cache
-slot of the new token equal to the oracle's BF16 values except where fp32 and
-fp64 round a value near a BF16 midpoint apart (one rounding step, and rare);
-every other cache slot untouched.
+Bars: y within relative L2 <= 1e-4 and max-abs <= 2e-3 * max|ref|; every
+cache slot other than the new token's untouched (bit for bit); the new
+token's key and value rows equal to the oracle's BF16 values except where the
+fp32 and fp64 values round to neighbouring BF16 values: at most one BF16 step
+apart (sign-aware distance between the bit patterns), or, for values so close
+to zero that fp32 rounding alone exceeds a step, within 4e-6 of the largest
+magnitude of their head's row; and at most 4 such values per slot.
 """
 import numpy as np
 import pytest
@@ -12,6 +15,7 @@ import torch
 
 import oracle
 import synth
+from bf16_checks import bf16_steps
 
 pytestmark = pytest.mark.gpu
 
@@ -46,17 +50,25 @@ def dims_c(F, d):
     return F[0].attn_dims_struct(d.hidden, d.n_q, d.n_kv, d.head_dim, d.window, d.rope, d.theta)
 
 
-def check_caches(gk, gv, rk, rv, slot):
-    """gk/gv GPU caches (uint16 numpy), rk/rv oracle caches after the step."""
+def check_rows(g, r):
+    """g, r: uint16 BF16 rows [n_kv][D] (GPU, oracle) of one written slot."""
+    steps = bf16_steps(g, r)
+    gv, rv = oracle.bf16_decode(g), oracle.bf16_decode(r)
+    near_zero = np.abs(gv - rv) <= 4e-6 * np.abs(rv).max(axis=-1, keepdims=True)
+    assert ((steps <= 1) | near_zero).all(), np.argwhere((steps > 1) & ~near_zero)[:4].tolist()
+    assert (steps > 0).sum() <= 4, (steps > 0).sum()
+
+
+def check_caches(gk, gv, rk, rv, slots):
+    """gk/gv GPU caches (uint16 numpy [n_kv][cap][D]), rk/rv the oracle's after
+    the same steps; slots: the slots written by those steps."""
+    slots = np.atleast_1d(slots)
     for g, r in ((gk, rk), (gv, rv)):
         other = np.ones(g.shape[1], bool)
-        other[slot] = False
+        other[slots] = False
         assert np.array_equal(g[:, other], r[:, other])
-        # one BF16 rounding apart (fp32 and fp64 may round a value near a
-        # midpoint apart; near zero the step is absolute)
-        gv, rv = oracle.bf16_decode(g[:, slot]), oracle.bf16_decode(r[:, slot])
-        assert (np.abs(gv - rv) <= 2.0 ** -7 * np.abs(rv) + 1e-5).all()
-        assert (gv != rv).sum() <= 4
+        for s in slots:
+            check_rows(g[:, s], r[:, s])
 
 
 def run_case(F, d, seed, pos, cap, tok_seed=0):
@@ -118,8 +130,10 @@ def test_consecutive_tokens(F):
                                          rope=True, theta=d.theta)
         torch.cuda.synchronize()
         assert_close(y.cpu().numpy(), y_ref, f"token {i}")
-    gv, rv = oracle.bf16_decode(gk.cpu().numpy().view(np.uint16)), oracle.bf16_decode(kc)
-    assert (np.abs(gv - rv) <= 2.0 ** -7 * np.abs(rv) + 1e-5).all()
+    # both caches: the five written slots within the bar, every other slot
+    # untouched
+    check_caches(gk.cpu().numpy().view(np.uint16), gv.cpu().numpy().view(np.uint16), kc, vc,
+                 [(p0 + i) % cap for i in range(5)])
 
 
 @pytest.mark.parametrize("width,B", [(6144, 1), (6144, 3), (2048, 2), (8192, 1)])

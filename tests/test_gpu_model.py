@@ -26,6 +26,20 @@ def F():
     return flint, workload
 
 
+def check_cache(gb, ob, written, what):
+    """gb, ob: BF16 caches (uint16 [n_kv][cap][D]) of the GPU and the oracle;
+    written: bool [cap].  Unwritten slots bit for bit; a written row holds
+    keys or values computed from the layer's input, which here differs from
+    the oracle's by the fp32 error of every layer before it, so the bar is
+    the fp32 bar (max-abs <= 2e-3 * max|ref| of the head's row) plus one BF16
+    rounding step."""
+    assert np.array_equal(gb[:, ~written], ob[:, ~written]), what
+    gv, ov = oracle.bf16_decode(gb[:, written]), oracle.bf16_decode(ob[:, written])
+    scale = np.abs(ov).max(axis=2, keepdims=True)
+    bad = np.abs(gv - ov) > 2.0 ** -7 * np.abs(ov) + 2e-3 * scale
+    assert not bad.any(), (what, np.argwhere(bad)[:4].tolist(), gv[bad][:4], ov[bad][:4])
+
+
 def attn_oracle(seed, d):
     mats = [oracle.quantize(synth.attn_f32(seed, d, k)) for k in (synth.ATTN_Q, synth.ATTN_K, synth.ATTN_V,
                                                                    synth.ATTN_O)]
@@ -85,18 +99,117 @@ def test_small_model_consecutive_tokens(F, persistent_moe, pos0, window, cap_ful
         assert np.abs(got - r.logits).max() <= 2e-3 * np.abs(r.logits).max()
         assert int(am[0]) == r.argmax
         kc, vc = trial_k, trial_v
-        for l in range(nl):  # caches: the written slots within BF16 rounding, the rest untouched
+        for l in range(nl):  # caches: the written slots within the bar, the rest untouched
             for g_, o_ in ((kg[l], kc[l]), (vg[l], vc[l])):
-                gb = g_.cpu().numpy().view(np.uint16)
                 written = np.zeros(o_.shape[1], bool)
                 written[[p_ % o_.shape[1] for p_ in range(pos0, pos + 1)]] = True
-                assert np.array_equal(gb[:, ~written], o_[:, ~written])
-                # the written values: the fp32 bar (max-abs <= 2e-3 * max|ref|
-                # per written row) plus one BF16 rounding step
-                gv, ov = oracle.bf16_decode(gb[:, written]), oracle.bf16_decode(o_[:, written])
-                scale = np.abs(ov).max(axis=2, keepdims=True)
-                bad = np.abs(gv - ov) > 2.0 ** -7 * np.abs(ov) + 2e-3 * scale
-                assert not bad.any(), (l, pos, np.argwhere(bad)[:4].tolist(), gv[bad][:4], ov[bad][:4])
+                check_cache(g_.cpu().numpy().view(np.uint16), o_, written, (l, pos))
         pos += 1
         done += 1
     assert M.error() == 0
+
+
+# ------------------------------------------------------- the full-shape step --
+# The benchmarked whole step (49 layers: 2 dense of width 6,144 then 47 MoE of
+# 256 experts, 14 full-context and 35 sliding-window layers, the 150,144-row
+# head) at position 600, one screened token against the oracle.  The oracle's
+# weights are prepared in the first test and kept for the second (quantising
+# the 49 attention layers takes about a minute, the token's experts and the
+# head about 40 s more); run alone, the second test prepares them itself.
+FULL_L, FULL_ND, FULL_V, FULL_POS = 49, 2, 150144, 600
+_full = {}
+
+
+def full_layer(l):
+    """14 of 49 layers attend to the whole context (2 of every 7)."""
+    return l % 7 in (3, 6)
+
+
+def full_dims():
+    return [synth.FULL if full_layer(l) else synth.SLIDING for l in range(FULL_L)]
+
+
+def full_caps():
+    return [1024 if full_layer(l) else 513 for l in range(FULL_L)]
+
+
+def full_oracle_weights():
+    if "attn" not in _full:
+        dims = full_dims()
+        _full["attn"] = [attn_oracle(100 + l, dims[l]) for l in range(FULL_L)]
+        _full["dense"] = [tuple(oracle.quantize(synth.dense_f32(200 + l, 2048, synth.DENSE_WIDTH, k))
+                                for k in (synth.DENSE_GATE, synth.DENSE_UP, synth.DENSE_DOWN)) for l in range(FULL_ND)]
+    return _full["attn"], _full["dense"]
+
+
+def test_full_model_weights(F):
+    """Prepares the oracle's 49 attention and 2 dense layers, and checks that
+    the device-built ones carry the same codes, scales and tensor scales."""
+    flint, workload = F
+    attn_o, dense_o = full_oracle_weights()
+    dims = full_dims()
+    for l in (0, 3, 48):
+        g = workload.build_attn(dims[l], 100 + l)
+        for got, ref in ((g.q, attn_o[l].q), (g.o, attn_o[l].o), (g.k, attn_o[l].k)):
+            assert np.array_equal(got.codes.cpu().numpy(), ref.codes)
+            assert np.array_equal(got.scales.cpu().numpy(), ref.scales)
+            assert float(got.tscale[0]) == ref.tscale
+    gd = workload.build_dense(201, 2048, synth.DENSE_WIDTH)
+    assert np.array_equal(gd[2].codes.cpu().numpy(), dense_o[1][2].codes)
+
+
+@pytest.mark.parametrize("persistent_moe", [True, False])
+def test_full_model_token(F, persistent_moe):
+    """One token through the full-shape model (MoE layers as persistent
+    launches, or as the kernel sequence) against model_token: logits at the
+    fp32 bar, argmax exact, every written cache row within one BF16 step of
+    the oracle's, the rest of every cache untouched."""
+    flint, workload = F
+    H = 2048
+    md = synth.MoEDims()
+    dims, caps = full_dims(), full_caps()
+    attn_o, dense_o = full_oracle_weights()
+    if "W" not in _full:
+        W = SyntheticWeights(md, vocab=FULL_V)
+        W.head()
+        _full["W"] = W
+    W = _full["W"]
+    kc = [synth.kv_cache_bits(300 + l, dims[l], caps[l], synth.K_CACHE) for l in range(FULL_L)]
+    vc = [synth.kv_cache_bits(300 + l, dims[l], caps[l], synth.V_CACHE) for l in range(FULL_L)]
+    if "ref" not in _full:
+        seed = 40
+        while True:  # the first token seed whose oracle margins are >= 1e-5
+            tk, tv = [c.copy() for c in kc], [c.copy() for c in vc]
+            r = model_token(W, attn_o, dims, dense_o, list(range(FULL_L - FULL_ND)), W.head(),
+                            synth.token_f32(seed, H), FULL_POS, tk, tv)
+            if min(r.gaps) >= MARGIN and r.argmax_gap >= MARGIN:
+                break
+            seed += 1
+        _full["ref"] = (seed, r, tk, tv)
+    seed, r, rk, rv = _full["ref"]
+    tmp = torch.empty(md.n_experts * md.expert_width * md.hidden, dtype=torch.float32, device="cuda")
+    moe_g = [workload.build_layer(md, seed=s, tmp=tmp) for s in range(FULL_L - FULL_ND)]
+    del tmp
+    attn_g = [workload.build_attn(dims[l], 100 + l) for l in range(FULL_L)]
+    dense_g = [workload.build_dense(200 + l, H, synth.DENSE_WIDTH) for l in range(FULL_ND)]
+    head = workload.build_head(FULL_V, H)
+    kg = [torch.from_numpy(c.view(np.int16).copy()).cuda() for c in kc]
+    vg = [torch.from_numpy(c.view(np.int16).copy()).cuda() for c in vc]
+    ad = lambda d: flint.attn_dims_struct(H, d.n_q, d.n_kv, d.head_dim, d.window, d.rope, d.theta)
+    M = flint.Model(flint.dims_struct(md.hidden, md.n_experts, md.expert_width, md.top_k, md.shared_width),
+                    ad(synth.SLIDING), ad(synth.FULL), attn_g, [int(full_layer(l)) for l in range(FULL_L)], kg, vg,
+                    dense_g, moe_g, head, FULL_V, dense_width=synth.DENSE_WIDTH, persistent_moe=persistent_moe)
+    print(f"full model token seed={seed} pos={FULL_POS} persistent_moe={persistent_moe}", flush=True)
+    lg, am = M.decode(torch.from_numpy(synth.token_f32(seed, H)).cuda(), FULL_POS)
+    torch.cuda.synchronize()
+    assert M.error() == 0
+    got = lg.cpu().numpy().astype(np.float64)
+    rel = np.linalg.norm(got - r.logits) / np.linalg.norm(r.logits)
+    assert rel <= 1e-4, rel
+    assert np.abs(got - r.logits).max() <= 2e-3 * np.abs(r.logits).max()
+    assert int(am[0]) == r.argmax
+    for l in range(FULL_L):
+        written = np.zeros(caps[l], bool)
+        written[FULL_POS % caps[l]] = True
+        for g_, o_ in ((kg[l], rk[l]), (vg[l], rv[l])):
+            check_cache(g_.cpu().numpy().view(np.uint16), o_, written, l)

@@ -324,21 +324,101 @@ def test_stack_schedules_agree_and_repeat(F):
         assert_close(out["persistent"][0][t], out["kernels"][0][t], "schedules")
 
 
-def test_stack_full_size_sampled(F, full_head):
-    """The benchmarked shape: 47 layers of 256 experts and the 150,144-row
-    head, persistent schedule; one screened token against the oracle."""
-    _, q, V = full_head
-    stack_case(F, synth.MoEDims(), L=47, vocab=V, n_tokens=1, seed0=synth.TOKEN_SEED0, schedule=2, head_q=q)
+# The benchmarked shape (47 layers of 256 experts, the 150,144-row head):
+# four tokens decoded in one persistent launch, each compared with its own
+# oracle run in a test of its own (an oracle token at this size takes about
+# 35 s, most of it quantising the experts the token touches).  The seeds were
+# screened with the oracle (every routing gap and the head's top-2 gap >=
+# 1e-5); each test checks that again on its own oracle run.
+FULL_SEEDS = (synth.TOKEN_SEED0, synth.TOKEN_SEED0 + 1, synth.TOKEN_SEED0 + 2, synth.TOKEN_SEED0 + 3)
+_full_oracle = {}
+
+
+@pytest.fixture(scope="module")
+def full_stack(F, full_head):
+    flint, workload = F
+    head, q, V = full_head
+    dims = synth.MoEDims()
+    L = 47
+    tmp = torch.empty(dims.n_experts * dims.expert_width * dims.hidden, dtype=torch.float32, device="cuda")
+    layers = [workload.build_layer(dims, seed=l, tmp=tmp) for l in range(L)]
+    del tmp
+    stack = flint.Stack(dims_struct(F, dims), layers, head, V, schedule=2)
+    x = workload.tokens(FULL_SEEDS, dims.hidden)
+    routes = torch.zeros((len(FULL_SEEDS), L, dims.top_k), dtype=torch.int32, device="cuda")
+    print(f"full stack: {len(FULL_SEEDS)} tokens in one persistent launch", flush=True)
+    logits, am = stack.decode(x, routes=routes)
+    torch.cuda.synchronize()
+    assert stack.error() == 0
+    W = SyntheticWeights(dims, vocab=V)
+    W._head = q
+    return stack, W, logits.cpu().numpy(), am.cpu().numpy(), routes.cpu().numpy()
+
+
+def full_oracle(W, t):
+    if t not in _full_oracle:
+        _full_oracle[t] = stack_token(W, synth.token_f32(FULL_SEEDS[t], 2048), 47, keep_inputs=True)
+    return _full_oracle[t]
+
+
+@pytest.mark.parametrize("t", range(len(FULL_SEEDS)))
+def test_stack_full_size_tokens(F, full_stack, t):
+    """Token t of the four decoded in one launch at the full shape: every
+    layer's routes, the logits (fp32 bar) and the argmax against the oracle."""
+    _, W, logits, am, routes = full_stack
+    r = full_oracle(W, t)
+    assert min(r.gaps) >= MARGIN and r.argmax_gap >= MARGIN, "seed no longer screened"
+    for l in range(47):
+        assert sorted(routes[t, l].tolist()) == sorted(r.routes[l].tolist()), (t, l)
+    assert_close(logits[t], r.logits, f"full stack token {t}")
+    assert int(am[t]) == r.argmax
+
+
+def test_stack_full_size_per_layer(F, full_stack):
+    """Teacher-forced layer check at the full shape: each of the 47 layers run
+    alone (one launch of the persistent kernel, no head) on the oracle's own
+    input to that layer; its routes exactly and its output h_out - h_in at
+    the fp32 bar against the oracle's layer output, so each layer's error is
+    bounded on its own."""
+    stack = full_stack[0]
+    r = full_oracle(full_stack[1], 0)
+    assert min(r.gaps) >= MARGIN
+    routes = torch.zeros((1, 6), dtype=torch.int32, device="cuda")
+    for l in range(47):
+        h_in = torch.from_numpy(r.layer_inputs[l].astype(np.float32)).cuda()
+        h_out = stack.decode_layers(h_in, l, 1, routes=routes)
+        torch.cuda.synchronize()
+        assert stack.error() == 0
+        assert sorted(routes[0].cpu().numpy().tolist()) == sorted(r.routes[l].tolist()), l
+        y = h_out.cpu().numpy().astype(np.float64) - r.layer_inputs[l].astype(np.float32).astype(np.float64)
+        assert_close(y, r.layer_inputs[l + 1] - r.layer_inputs[l], f"layer {l} output")
+
+
+def test_stack_decode_layers_composes(F, full_stack):
+    """Layers 0-46 as three calls of flint_stack_decode_layers (in place) give
+    the same bits as one call over all of them."""
+    stack = full_stack[0]
+    x = F[1].tokens([FULL_SEEDS[1]], 2048)[0]
+    one = stack.decode_layers(x, 0, 47)
+    h = x.clone()
+    for l0, n in ((0, 20), (20, 1), (21, 26)):
+        stack.decode_layers(h, l0, n, h_out=h)
+    torch.cuda.synchronize()
+    assert torch.equal(one, h)
 
 
 # ------------------------------------------------------------ batched step --
-def batch_oracle_case(F, dims, L, vocab, B, seed0):
-    """B screened tokens decoded together; each against its own oracle run."""
+def batch_oracle_case(F, dims, L, vocab, B, seed0, layouts=("row-major",)):
+    """B screened tokens decoded together; each against its own oracle run.
+    layouts: the expert weights read row-major, from the tiled copy, or both
+    (one oracle run serves every layout)."""
     flint, workload = F
     layers = [workload.build_layer(dims, seed=l) for l in range(L)]
     head = workload.build_head(vocab, dims.hidden)
     W = SyntheticWeights(dims, vocab=vocab)
     stack = flint.Stack(dims_struct(F, dims), layers, head, vocab)
+    if "tiled" in layouts:
+        stack.make_batch_tiles()
     s, chosen, refs = seed0, [], []
     while len(chosen) < B:
         r = stack_token(W, synth.token_f32(s, dims.hidden), L)
@@ -347,20 +427,50 @@ def batch_oracle_case(F, dims, L, vocab, B, seed0):
             refs.append(r)
         s += 1
     x = workload.tokens(chosen, dims.hidden)
-    routes = torch.zeros((L, B, dims.top_k), dtype=torch.int32, device="cuda")
-    logits, am = stack.decode_batch(x, routes=routes)
-    torch.cuda.synchronize()
-    for t, r in enumerate(refs):
-        for l in range(L):
-            assert sorted(routes[l, t].cpu().numpy().tolist()) == sorted(r.routes[l].tolist()), (t, l)
-        assert_close(logits[t].cpu().numpy(), r.logits, f"batch token {t}")
-        assert int(am[t]) == r.argmax, t
+    for layout in layouts:
+        print(f"batch case E={dims.n_experts} L={L} V={vocab} B={B} layout={layout}", flush=True)
+        routes = torch.zeros((L, B, dims.top_k), dtype=torch.int32, device="cuda")
+        logits, am = stack.decode_batch(x, routes=routes, tiled=layout == "tiled")
+        torch.cuda.synchronize()
+        for t, r in enumerate(refs):
+            for l in range(L):
+                assert sorted(routes[l, t].cpu().numpy().tolist()) == sorted(r.routes[l].tolist()), (layout, t, l)
+            assert_close(logits[t].cpu().numpy(), r.logits, f"batch token {t} ({layout})")
+            assert int(am[t]) == r.argmax, (layout, t)
+    return refs
 
 
 @pytest.mark.parametrize("B", [1, 3, 8])
 def test_stack_batch_against_oracle(F, B):
     """Batched decode (tokens bucketed by expert) = the oracle, token by token."""
     batch_oracle_case(F, synth.MoEDims(n_experts=32), L=3, vocab=4099, B=B, seed0=40)
+
+
+@pytest.mark.parametrize("B", [17, 32])
+def test_stack_batch_two_tiles_against_oracle(F, B):
+    """B > 16: the second 16-token tile of every group (the shared expert's,
+    the head's and busy experts') holds real tokens; row-major and tiled
+    weights, every token against the oracle."""
+    batch_oracle_case(F, synth.MoEDims(n_experts=32), L=3, vocab=4099, B=B, seed0=140,
+                      layouts=("row-major", "tiled"))
+
+
+def test_stack_batch_e256_b32_against_oracle(F):
+    """The batched shape of the benchmark (256 experts, top-6, B = 32 tokens
+    per step, 16,385-row head) over two layers, row-major and tiled weights,
+    every token against the oracle (routes exact, logits at the fp32 bar,
+    argmax exact)."""
+    batch_oracle_case(F, synth.MoEDims(), L=2, vocab=16385, B=32, seed0=synth.TOKEN_SEED0 + 300,
+                      layouts=("row-major", "tiled"))
+
+
+def test_stack_batch_e8_b48_against_oracle(F):
+    """8 experts and 48 tokens: experts with more than 32 tokens (two
+    passes of two 16-token tiles), row-major and tiled, against the oracle."""
+    refs = batch_oracle_case(F, synth.MoEDims(n_experts=8), L=3, vocab=4099, B=48, seed0=500,
+                             layouts=("row-major", "tiled"))
+    counts = np.bincount(np.concatenate([r.routes[0] for r in refs]), minlength=8)
+    assert counts.max() > 32, counts
 
 
 def batch_vs_single(F, L, V, B, seed0, head=None):
