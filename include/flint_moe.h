@@ -172,6 +172,23 @@ int32_t flint_moe_decode(const flint_moe_dims* dims /*[host]*/, const flint_moe_
                          const float* x, int32_t B, float* y, int32_t* topk_idx_opt, float* topk_w_opt, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* flint_moe_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same layer, arguments and results (bit-identical), but no
+ * workspace argument.  Its scratch is a fixed 1.125 MiB device array inside
+ * the library, one per GPU, held until the process ends; the first call on a
+ * device looks up that array's address (hipGetSymbolAddress) and keeps it.
+ * The call allocates nothing (no hipMalloc, no allocating library routine).
+ * Sizes whose flint_workspace_bytes(FLINT_OP_DECODE, dims, B) exceeds the
+ * array return FLINT_E_WORKSPACE before anything is enqueued (the Flint
+ * layer, E = 256, k = 6, I = 512, Is = 1024, fits up to B = 64).  Every call
+ * on one GPU uses the same array and leaves its contents behind: calls that
+ * may overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  Nothing needs clearing between calls. */
+int32_t flint_moe_decode_noalloc(const flint_moe_dims* dims /*[host]*/, const flint_moe_layer* layer /*[host]*/,
+                                 const float* x, int32_t B, float* y, int32_t* topk_idx_opt, float* topk_w_opt,
+                                 void* stream);
+
 /* NVFP4 output head [P1 "Quantization with Offline Distillation"; P3 "Why
  * active parameters set the speed"]: logits[b][v] = sum_k Wdeq[v][k] x[b][k]
  * for head W [vocab][hidden], x float [B][hidden]; argmax[b] = first index

@@ -2,6 +2,7 @@
 // carving and kernel launches.  Every check runs on the host before anything
 // is enqueued, so a failing call leaves all buffers untouched.
 #include <atomic>
+#include <mutex>
 #include <string.h>
 
 #include "flint_common.h"
@@ -212,6 +213,63 @@ int32_t flint_moe_decode(const flint_moe_dims* dims, const flint_moe_layer* laye
   DecodeWs dw(*dims, B);
   if (ws_bytes < dw.total) return FLINT_E_WORKSPACE;
   if ((st = check_device())) return st;
+  int32_t* idx = topk_idx_opt ? topk_idx_opt : carve<int32_t>(ws, dw.idx);
+  float* w = topk_w_opt ? topk_w_opt : carve<float>(ws, dw.wts);
+  return decode_impl(*dims, *layer, x, B, -1.0f, y, false, idx, w, ws, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// Scratch of flint_moe_decode_noalloc: a fixed device array, one copy per
+// GPU, held until the process ends.  Host code never passes `scratch` itself
+// to a kernel (on the host that name is only a stand-in); it takes the
+// array's device address from hipGetSymbolAddress once per device and uses
+// that address everywhere.
+constexpr size_t kNoAllocScratchBytes = 1179648;  // 1.125 MiB
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // device address of `scratch` per device (null until set up)
+
+int32_t noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= 64) return FLINT_E_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {  // first call on this device, with it current
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (!p) return FLINT_E_INTERNAL;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FLINT_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int32_t flint_moe_decode_noalloc(const flint_moe_dims* dims, const flint_moe_layer* layer, const float* x, int32_t B,
+                                 float* y, int32_t* topk_idx_opt, float* topk_w_opt, void* stream) {
+  int32_t st;
+  if ((st = check_dims(dims))) return st;
+  if ((st = check_layer(layer))) return st;
+  if (!x || !y) return FLINT_E_NULL;
+  if (B < 1) return FLINT_E_DIMS;
+  if (!aligned16(x) || !aligned16(y) || (topk_idx_opt && !aligned4(topk_idx_opt)) ||
+      (topk_w_opt && !aligned4(topk_w_opt)))
+    return FLINT_E_ALIGN;
+  const DecodeWs dw(*dims, B);
+  if (dw.total > kNoAllocScratchBytes) return FLINT_E_WORKSPACE;
+  if ((st = check_device())) return st;
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(&ws))) return st;
+  // the same kernels as flint_moe_decode on the same scratch layout; every
+  // scratch byte a kernel reads was written earlier in this call, so nothing
+  // has to be cleared
   int32_t* idx = topk_idx_opt ? topk_idx_opt : carve<int32_t>(ws, dw.idx);
   float* w = topk_w_opt ? topk_w_opt : carve<float>(ws, dw.wts);
   return decode_impl(*dims, *layer, x, B, -1.0f, y, false, idx, w, ws, (hipStream_t)stream);

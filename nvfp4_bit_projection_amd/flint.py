@@ -88,6 +88,7 @@ def _load():
         "flint_moe_route_ex": ([ctypes.POINTER(Dims), _P, _I32, _I32, _P, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
         "flint_moe_decode": ([ctypes.POINTER(Dims), ctypes.POINTER(Layer), _P, _I32, _P, _P, _P, _P, _SZ, _P], _I32),
         "flint_lmhead_gemv": ([ctypes.POINTER(NVFP4), _I32, _I32, _P, _I32, _P, _P, _P, _SZ, _P], _I32),
+        "flint_moe_decode_noalloc": ([ctypes.POINTER(Dims), ctypes.POINTER(Layer), _P, _I32, _P, _P, _P, _P], _I32),
         "flint_stack_table_bytes": ([_I32], _SZ),
         "flint_stack_packed_bytes": ([ctypes.POINTER(Dims), _I32], _SZ),
         "flint_stack_prepare": ([ctypes.POINTER(Dims), ctypes.POINTER(Layer), _I32, ctypes.POINTER(NVFP4), _I32, _P,
@@ -136,7 +137,7 @@ _lib = _load()
 # every symbol include/flint_moe.h declares
 EXPORTED = ("flint_status_str", "flint_last_hip_error", "flint_workspace_bytes", "flint_moe_route",
             "flint_moe_route_ex",
-            "flint_moe_decode", "flint_lmhead_gemv", "flint_stack_table_bytes", "flint_stack_packed_bytes",
+            "flint_moe_decode", "flint_moe_decode_noalloc", "flint_lmhead_gemv", "flint_stack_table_bytes", "flint_stack_packed_bytes",
             "flint_stack_prepare",
             "flint_stack_decode", "flint_stack_decode_traced", "flint_stack_decode_batch", "flint_stack_error",
             "flint_stack_decode_layers",
@@ -326,6 +327,17 @@ def moe_decode(dims: Dims, layer: LayerWeights, x: torch.Tensor, ws: torch.Tenso
     _check(_lib.flint_moe_decode(ctypes.byref(dims), ctypes.byref(lc), x.data_ptr(), B, y.data_ptr(), idx.data_ptr(),
                                  w.data_ptr(), ws.data_ptr(), ws.numel(), _stream()), "flint_moe_decode")
     return y, idx, w
+
+
+def moe_decode_noalloc(dims: Dims, layer: LayerWeights, x: torch.Tensor, y: torch.Tensor, idx: torch.Tensor,
+                       w: torch.Tensor) -> None:
+    """flint_moe_decode on the library's own fixed scratch (no workspace):
+    x float32 [B][H] -> y [B][H], idx int32 [B][k], w float32 [B][k]
+    (preallocated outputs)."""
+    lc = layer.c()
+    _check(_lib.flint_moe_decode_noalloc(ctypes.byref(dims), ctypes.byref(lc), x.data_ptr(), x.shape[0],
+                                         y.data_ptr(), idx.data_ptr(), w.data_ptr(), _stream()),
+           "flint_moe_decode_noalloc")
 
 
 def lmhead(head: NVFP4Tensor, vocab: int, x: torch.Tensor, ws: torch.Tensor | None = None,
