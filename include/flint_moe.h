@@ -285,6 +285,21 @@ int32_t flint_stack_decode_layers(const flint_stack_plan* plan /*[host]*/, int32
                                   float eps, float* h_out, int32_t* routes_opt, void* ws, size_t ws_bytes,
                                   void* stream);
 
+/* Test hook for the persistent schedule's exchange protocol: the decode of
+ * flint_stack_decode (same arguments, workspace and results) by a second
+ * instantiation of the persistent kernel that, before every exchange store,
+ * sleeps for a pseudo-random time derived from `seed` (up to about 14 us, at
+ * one store in four), permutes the roles of the workgroups inside each XCD,
+ * and lets every wait give up after `spin_limit` polls (>= 1; the plain
+ * kernel's limit is 2^22).  With a generous limit the results are
+ * bit-identical to flint_stack_decode's; with a tiny one the waits give up,
+ * the watchdog flag is raised (flint_stack_error) and the call's outputs are
+ * unspecified.  Needs a plan with packed down projections
+ * (FLINT_E_UNSUPPORTED otherwise). */
+int32_t flint_stack_decode_stress(const flint_stack_plan* plan /*[host]*/, const float* x, int32_t T, float eps,
+                                  float* logits, int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes,
+                                  uint32_t seed, uint32_t spin_limit, void* stream);
+
 /* Small-batch decode step [P2 "How does Flint's architecture work?"; P3
  * "The shape, read from the headers"]: B tokens (1 <= B <= 64) through the
  * same stack and head together, each token with its own top-k routing:

@@ -439,6 +439,27 @@ int32_t flint_stack_decode_layers(const flint_stack_plan* plan, int32_t l0, int3
   return e == hipSuccess ? FLINT_OK : hip_fail(e);
 }
 
+int32_t flint_stack_decode_stress(const flint_stack_plan* plan, const float* x, int32_t T, float eps, float* logits,
+                                  int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes, uint32_t seed,
+                                  uint32_t spin_limit, void* stream) {
+  int32_t st;
+  if (!plan || !x || !argmax || !ws) return FLINT_E_NULL;
+  if ((st = check_dims(&plan->dims))) return st;
+  if (!plan->layers || !plan->table) return FLINT_E_NULL;
+  if (T < 1 || plan->n_layers < 1 || plan->vocab < 1 || !(eps > 0.0f) || spin_limit < 1) return FLINT_E_DIMS;
+  if (!plan->packed || !stack_persistent_supported(plan->dims, plan->n_layers)) return FLINT_E_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(ws) || !aligned4(argmax) || (logits && !aligned4(logits)) ||
+      (routes_opt && !aligned4(routes_opt)))
+    return FLINT_E_ALIGN;
+  StackWs sw(plan->dims, plan->vocab);
+  if (ws_bytes < sw.total) return FLINT_E_WORKSPACE;
+  if ((st = check_device())) return st;
+  hipError_t e = launch_stack_persistent(plan->dims, plan->n_layers, plan->vocab, plan->table, x, T, eps, logits,
+                                         argmax, routes_opt, static_cast<char*>(ws) + sw.persist, nullptr,
+                                         (hipStream_t)stream, 0, nullptr, nullptr, seed, spin_limit);
+  return e == hipSuccess ? FLINT_OK : hip_fail(e);
+}
+
 int32_t flint_stack_decode_batch(const flint_stack_plan* plan, const float* x, int32_t B, float eps, float* logits,
                                  int32_t* argmax, int32_t* routes_opt, void* ws, size_t ws_bytes, void* stream) {
   int32_t st;

@@ -142,10 +142,13 @@ struct StackQkv {
 };
 // vocab == 0: no head, T == 1; layers l0 .. l0 + L - 1 of the table, the
 // final residual to h_out (which may be x), and with qkv its rows.
+// spin_limit != 0 (with a head): the stress instantiation, with delays seeded
+// by stress_seed and waits that give up after spin_limit polls.
 hipError_t launch_stack_persistent(const flint_moe_dims& d, int L, int vocab, const void* table, const float* x,
                                    int T, float eps, float* logits, int32_t* argmax, int32_t* routes, void* ws,
                                    int64_t* trace, hipStream_t s, int l0 = 0, float* h_out = nullptr,
-                                   const StackQkv* qkv = nullptr);
+                                   const StackQkv* qkv = nullptr, uint32_t stress_seed = 0,
+                                   uint32_t spin_limit = 0);
 hipError_t read_stack_error(const void* ws, int32_t* out);
 
 }  // namespace flint

@@ -91,6 +91,8 @@ struct StackParams {
   int64_t* trace;  // optional [2][L+1][kTracePoints] phase timestamps of workgroups 0 and 255
   float* h_out;    // k_stack_decode<false> (one token, no head): the final residual [H]
   StackQkv qkv;    // k_stack_decode<false>: rows applied to the final residual's norm (out == nullptr: none)
+  uint32_t stress_seed;  // stress instantiation: seed of the injected delays
+  uint32_t spin_limit;   // stress instantiation: polls before a wait gives up
 };
 
 // In-place use (h_out == x, one launch per layer of a longer model) relies on
@@ -135,13 +137,14 @@ __device__ __forceinline__ void wg_barrier() {
 
 struct WaitCtx {
   uint32_t* err;
-  int* bad;  // LDS flag
+  int* bad;        // LDS flag
+  uint32_t limit;  // polls before a wait gives up
 };
 
 // Raise the error flag after a wait timed out (or another workgroup raised it).
 __device__ __forceinline__ bool poll_gave_up(uint32_t& spins, const WaitCtx& w) {
   ++spins;
-  if (spins > kSpinLimit || ((spins & 1023) == 0 && ld_dev_u32(w.err))) {
+  if (spins > w.limit || ((spins & 1023) == 0 && ld_dev_u32(w.err))) {
     atomicOr(w.err, 1u);
     *w.bad = 1;
     return true;
@@ -264,6 +267,25 @@ struct StackCoord {
   bool tracing;
 };
 
+// Stress instantiation only: before an exchange store, a wave sleeps for a
+// pseudo-random time (a hash of the seed, workgroup, wave, token, layer and
+// store site; one store in four, up to 15 x 32 x 64 clocks, about 14 us), so
+// that workgroups and waves reach every exchange in arbitrary orders and with
+// arbitrary skew.  The results must not change.
+template <bool kStress>
+__device__ __forceinline__ void stress_delay(const StackParams& P, int tok, int l, int site) {
+  if constexpr (kStress) {
+    uint32_t h = P.stress_seed * 0x9E3779B1u ^ blockIdx.x * 0x85EBCA77u ^ (uint32_t)(tok * 128 + l) * 0xC2B2AE3Du ^
+                 (uint32_t)site * 0x27D4EB2Fu ^ (threadIdx.x >> 6) * 0x165667B1u;
+    h ^= h >> 15; h *= 0x2C1B3C6Du; h ^= h >> 12; h *= 0x297A2D39u; h ^= h >> 15;
+    h = __builtin_amdgcn_readfirstlane(h);
+    if ((h & 3) == 0) {
+      const int n = (int)((h >> 2) & 15);
+      for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(32);
+    }
+  }
+}
+
 // One role's pass over all tokens.  Both roles execute the same sequence of
 // workgroup barriers (marked B1..B5 per layer, H1..H5 per token) and
 // leave at the same barrier on error; returns false then.
@@ -277,13 +299,13 @@ struct StackCoord {
 // (phase A), one routed gate/up pair and the down-projection operands
 // (phase B), the partial outputs (phase C), the residual rows (phase D), and
 // the next layer's router and shared rows, requested ahead of time.
-template <bool kComm, bool kHead>
+template <bool kComm, bool kHead, bool kStress>
 __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& C) {
   const int t = C.t, lane = C.lane, wv = C.wv, g = C.g, li = C.li;
   const int L = C.L, E = C.E, I = C.I, k = C.k, Is = C.Is, V = C.V;
   const int Ix = C.Ix, Isx = C.Isx, nroutedx = C.nroutedx;
   const int lw = wv - kCommWaves;  // loading-wave index (loading role)
-  WaitCtx wc{P.ctrl + 1, &S.bad};
+  WaitCtx wc{P.ctrl + 1, &S.bad, kStress ? P.spin_limit : kSpinLimit};
 #define FLINT_TRACE_AT(tid_, l_, i_)                                                                 \
   do {                                                                                                 \
     if (C.tracing && t == (tid_) && tok == 0) S.tr[(l_) * kTracePoints + (i_)] = wall_clock64();       \
@@ -297,7 +319,9 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
   // wave one pair qa of the shared expert and its tensor scales.
   // Unconditional loads (a wave without a row reads row 0 and ignores it), so
   // that no branch join forces an early wait on the data.
-  const int rrow = blockIdx.x;  // router row of this workgroup (if < E)
+  // router row of this workgroup (if < E); the stress instantiation permutes
+  // the roles inside each XCD, and with them the rows
+  const int rrow = kStress ? g + kGroups * li : (int)blockIdx.x;
   const int qa = li + kGroupWGs * lw;
   float4 wr[kHidden / 256];
   uint4 cgs = make_uint4(0, 0, 0, 0), cus = make_uint4(0, 0, 0, 0);
@@ -393,13 +417,15 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       FLINT_TRACE(l, 1);
       float xv[32];  // this lane's 32 normalised activations (phases A and B)
       lds_x32(S.u + kRowPad * lane, xv);
-      // router logit blockIdx.x, stored into the logit exchange of every group
+      // router logit rrow, stored into the logit exchange of every group
+      stress_delay<kStress>(P, tok, l, 0);
       if (!kComm && lw == 0 && rrow < E) {
         const float acc = router_dot();
         if (lane < kGroups) put_pair<Scope::kDevice>(&P.s2[((size_t)par * kGroups + lane) * kMaxExperts + rrow], acc, ep0);
       }
       if constexpr (!kComm) {
         FLINT_TRACE_LOAD(l, 8);
+        stress_delay<kStress>(P, tok, l, 1);
         if (qa < Isx) {
           const float gv = wave_sum(nvfp4_lane_dot32(cgs, sgs, xv)) * tgs;
           const float av = wave_sum(nvfp4_lane_dot32(cus, sus, xv)) * tus;
@@ -420,7 +446,7 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       auto wait_picks = [&](int need) {
         uint32_t spins = 0;
         while (__hip_atomic_load(&S.nk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < nk0 + need) {
-          if (++spins > kSpinLimit) {
+          if (++spins > wc.limit) {
             S.bad = 1;
             break;
           }
@@ -569,6 +595,7 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
         load_down_shared();
         load_down_routed();
       }
+      stress_delay<kStress>(P, tok, l, 2);
 #pragma unroll
       for (int pp = 0; pp < kNq; ++pp) {
         if (pq[pp] < nroutedx) {
@@ -587,6 +614,7 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       FLINT_TRACE(l, 5);
 
       // ---------------------------------------------------------- phase C
+      stress_delay<kStress>(P, tok, l, 3);
       {
         float hv[32];
         lds_x32(S.hs + kRowPad * j, hv);
@@ -637,6 +665,7 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       if constexpr (kComm) {
         poll_pairs<Scope::kXcd>(s4b, kHidden, ep0 + 3, S.h, wc);
       } else {
+        stress_delay<kStress>(P, tok, l, 4);
         if (lw == 0) {
           float y = 0.0f;
 #pragma unroll
@@ -732,6 +761,7 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       if (lane == 0) { S.bv[wv] = best; S.bi[wv] = besti; }
       wg_barrier();  // H3
       FLINT_TRACE(L, 1);
+      stress_delay<kStress>(P, tok, L, 5);
       if (!kComm && t == kCommThreads) {
         float bv = S.bv[0];
         int bi = S.bi[0];
@@ -766,8 +796,10 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
 #undef FLINT_TRACE_AT
 }
 
-// kHead false: one token, no head, the final residual to P.h_out
-template <bool kHead>
+// kHead false: one token, no head, the final residual to P.h_out.  kStress:
+// injected delays, roles permuted inside each XCD, the caller's wait limit
+// (a test of the exchange protocol; the results equal the plain kernel's).
+template <bool kHead, bool kStress = false>
 __global__ __launch_bounds__(kStackThreads, 1) void k_stack_decode(StackParams P,
                                                                   const StackTable* __restrict__ table) {
   __shared__ StackLds S;
@@ -778,7 +810,7 @@ __global__ __launch_bounds__(kStackThreads, 1) void k_stack_decode(StackParams P
   // and everything derived from it stay scalar
   C.wv = __builtin_amdgcn_readfirstlane(C.t >> 6);
   C.g = blockIdx.x % kGroups;
-  C.li = blockIdx.x / kGroups;
+  C.li = kStress ? kGroupWGs - 1 - (int)blockIdx.x / kGroups : (int)blockIdx.x / kGroups;
   C.L = P.L; C.E = P.E; C.I = P.I; C.k = P.k; C.Is = P.Is; C.V = P.V;
   C.Ix = C.I / kGroups;
   C.Isx = C.Is / kGroups;
@@ -804,7 +836,8 @@ __global__ __launch_bounds__(kStackThreads, 1) void k_stack_decode(StackParams P
   }
   C.base = ld_dev_u32(P.ctrl);
   if (C.tracing && C.t == 0) S.tr[C.L * kTracePoints + 4] = wall_clock64();  // set-up done
-  const bool ok = C.wv < kCommWaves ? stack_role<true, kHead>(P, S, C) : stack_role<false, kHead>(P, S, C);
+  const bool ok =
+      C.wv < kCommWaves ? stack_role<true, kHead, kStress>(P, S, C) : stack_role<false, kHead, kStress>(P, S, C);
   if (!ok) return;
   if (C.tracing) {
     const int L = C.L, t = C.t;
@@ -838,8 +871,12 @@ size_t stack_persistent_ws_bytes() {
 
 hipError_t launch_stack_persistent(const flint_moe_dims& d, int L, int vocab, const void* table, const float* x,
                                    int T, float eps, float* logits, int32_t* argmax, int32_t* routes, void* ws,
-                                   int64_t* trace, hipStream_t s, int l0, float* h_out, const StackQkv* qkv) {
+                                   int64_t* trace, hipStream_t s, int l0, float* h_out, const StackQkv* qkv,
+                                   uint32_t stress_seed, uint32_t spin_limit) {
   StackParams P;
+  P.stress_seed = stress_seed;
+  P.spin_limit = spin_limit;
+  const bool stress = spin_limit != 0 && vocab > 0;
   P.trace = trace;
   P.qkv = qkv ? *qkv : StackQkv{};
   P.table = static_cast<const StackTable*>(table);
@@ -871,17 +908,23 @@ hipError_t launch_stack_persistent(const flint_moe_dims& d, int L, int vocab, co
   if (r == 0) {
     int per_cu = 0, cus = 0;
     int per_cu2 = 0;
+    int per_cu3 = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stack_decode<true>, kStackThreads, 0);
     if (e == hipSuccess)
       e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu2, k_stack_decode<false>, kStackThreads, 0);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu3, k_stack_decode<true, true>, kStackThreads, 0);
     per_cu = per_cu < per_cu2 ? per_cu : per_cu2;
+    per_cu = per_cu < per_cu3 ? per_cu : per_cu3;
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     r = per_cu * cus >= kStackWGs ? 1 : -1;
     resident[dev].store(r);
   }
   if (r != 1) return hipErrorCooperativeLaunchTooLarge;
-  if (vocab > 0)
+  if (stress)
+    k_stack_decode<true, true><<<dim3(kStackWGs), dim3(kStackThreads), 0, s>>>(P, tab);
+  else if (vocab > 0)
     k_stack_decode<true><<<dim3(kStackWGs), dim3(kStackThreads), 0, s>>>(P, tab);
   else
     k_stack_decode<false><<<dim3(kStackWGs), dim3(kStackThreads), 0, s>>>(P, tab);

@@ -100,6 +100,8 @@ def _load():
                                      _I32),
         "flint_stack_decode_layers": ([ctypes.POINTER(StackPlan), _I32, _I32, _P, ctypes.c_float, _P, _P, _P, _SZ,
                                        _P], _I32),
+        "flint_stack_decode_stress": ([ctypes.POINTER(StackPlan), _P, _I32, ctypes.c_float, _P, _P, _P, _P, _SZ,
+                                       ctypes.c_uint32, ctypes.c_uint32, _P], _I32),
         "flint_stack_error": ([_P, _SZ, ctypes.POINTER(_I32)], _I32),
         "flint_stack_batch_tiles_bytes": ([ctypes.POINTER(Dims), _I32], _SZ),
         "flint_stack_batch_tiles": ([ctypes.POINTER(StackPlan), _P, _SZ, _P], _I32),
@@ -140,7 +142,7 @@ EXPORTED = ("flint_status_str", "flint_last_hip_error", "flint_workspace_bytes",
             "flint_moe_decode", "flint_moe_decode_noalloc", "flint_lmhead_gemv", "flint_stack_table_bytes", "flint_stack_packed_bytes",
             "flint_stack_prepare",
             "flint_stack_decode", "flint_stack_decode_traced", "flint_stack_decode_batch", "flint_stack_error",
-            "flint_stack_decode_layers",
+            "flint_stack_decode_layers", "flint_stack_decode_stress",
             "flint_stack_batch_tiles_bytes", "flint_stack_batch_tiles", "flint_stack_decode_batch_tiled",
             "flint_nvfp4_quantize", "flint_nvfp4_dequantize", "flint_nvfp4_quantize_host", "flint_stream_read",
             # include/flint_attn.h
@@ -427,6 +429,18 @@ class Stack:
             _check(_lib.flint_stack_decode_batch(ctypes.byref(self.plan), x.data_ptr(), B, eps, _ptr(logits),
                                                  argmax.data_ptr(), _ptr(routes), ws.data_ptr(), ws.numel(),
                                                  _stream()), "flint_stack_decode_batch")
+        return logits, argmax
+
+    def decode_stress(self, x: torch.Tensor, seed: int, spin_limit: int, eps: float = 1e-6,
+                      routes: torch.Tensor | None = None):
+        """The persistent decode with injected delays, permuted roles and the
+        given wait limit (a test of the exchange protocol) -> (logits, argmax)."""
+        T = x.shape[0]
+        logits = torch.empty((T, self.vocab), dtype=torch.float32, device=x.device)
+        argmax = torch.empty(T, dtype=torch.int32, device=x.device)
+        _check(_lib.flint_stack_decode_stress(ctypes.byref(self.plan), x.data_ptr(), T, eps, logits.data_ptr(),
+                                              argmax.data_ptr(), _ptr(routes), self.ws.data_ptr(), self.ws.numel(),
+                                              seed, spin_limit, _stream()), "flint_stack_decode_stress")
         return logits, argmax
 
     def decode_layers(self, x: torch.Tensor, l0: int, n: int, eps: float = 1e-6, h_out: torch.Tensor | None = None,
