@@ -549,9 +549,9 @@ __global__ __launch_bounds__(kNormThreads) void k_bnorm(float* __restrict__ h, c
 }
 
 // ------------------------------------------------------------ gate / up --
-// grid (max(I, Is) / 128, Umax + 1), 512 threads.  Group ub < U: the rank-ub
-// chosen expert and its (token, slot) pairs; group Umax: the shared expert
-// and all B tokens.  Wave w takes gate rows and up rows r0 + 16 w .. + 15 of
+// grid (max(I, Is) / 64, Umax + 1), 256 threads.  Grid row 0: the shared
+// expert and all B tokens; row 1 + ub (ub < U): the rank-ub chosen expert and
+// its (token, slot) pairs.  Wave w takes gate rows and up rows r0 + 16 w .. + 15 of
 // its group (two tiles with the same rows) from the fp16 planes of the
 // normalised tokens up [2][B][H], and writes h = silu(gate) * up for each
 // token as three bf16 planes: hrp [3][B*k][I] by pair id (routed),
@@ -565,8 +565,10 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_mm_gateup(flint_moe_layer L, 
   __shared__ __align__(16) unsigned char abuf[mm_buf_bytes<FmtF16>()];
   __shared__ int srow[kMmTok], orow[kMmTok];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, m = lane & 15, q = lane >> 4;
-  const int ub = blockIdx.y;
-  const bool sh = ub == Umax;
+  // grid row 0 is the shared expert (all B tokens, the longest workgroups:
+  // dispatched first, they overlap the routed experts' rows 1 .. U)
+  const bool sh = blockIdx.y == 0;
+  const int ub = (int)blockIdx.y - 1;
   if (!sh && ub >= bk[0]) return;
   const int rows = sh ? Is : I, r0 = blockIdx.x * kMmGateUpRows;
   if (r0 >= rows) return;
@@ -653,7 +655,7 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_mm_gateup(flint_moe_layer L, 
 }
 
 // ----------------------------------------------------------------- down --
-// grid (H / 256, Umax + 1), 512 threads; groups as for gate/up.  Wave w takes
+// grid (H / 128, Umax + 1), 256 threads; groups as for gate/up.  Wave w takes
 // output rows r0 + 32 w .. + 31.  Routed: dr[pid][n] = w_pid * S_e * (Wd[e][n]
 // . h_pid) over K = I; shared: ds[b][n] = S * (Wsd[n] . hs_b) over K = Is.
 template <bool TILED, int AHEAD>
@@ -668,8 +670,10 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_mm_down(flint_moe_layer L, in
   __shared__ int srow[kMmTok];
   __shared__ float coef[kMmTok];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, m = lane & 15, q = lane >> 4;
-  const int ub = blockIdx.y;
-  const bool sh = ub == Umax;
+  // grid row 0 is the shared expert (all B tokens, the longest workgroups:
+  // dispatched first, they overlap the routed experts' rows 1 .. U)
+  const bool sh = blockIdx.y == 0;
+  const int ub = (int)blockIdx.y - 1;
   if (!sh && ub >= bk[0]) return;
   int e = 0, p0 = 0, ntok = B;
   if (!sh) {
