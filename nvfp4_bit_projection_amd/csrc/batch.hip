@@ -549,9 +549,10 @@ __global__ __launch_bounds__(kNormThreads) void k_bnorm(float* __restrict__ h, c
 }
 
 // ------------------------------------------------------------ gate / up --
-// grid (max(I, Is) / 64, Umax + 1), 256 threads.  Grid row 0: the shared
-// expert and all B tokens; row 1 + ub (ub < U): the rank-ub chosen expert and
-// its (token, slot) pairs.  Wave w takes gate rows and up rows r0 + 16 w .. + 15 of
+// grid (I / 64, nsh + Umax), 256 threads, nsh = ceil(Is / I).  Grid rows
+// 0 .. nsh - 1: the shared expert and all B tokens (workgroup (x, y) takes
+// rows 64 (y I/64 + x) ..); row nsh + ub (ub < U): the rank-ub chosen expert
+// and its (token, slot) pairs.  Wave w takes gate rows and up rows r0 + 16 w .. + 15 of
 // its group (two tiles with the same rows) from the fp16 planes of the
 // normalised tokens up [2][B][H], and writes h = silu(gate) * up for each
 // token as three bf16 planes: hrp [3][B*k][I] by pair id (routed),
@@ -565,12 +566,13 @@ __global__ __launch_bounds__(kMmThreads, 3) void k_mm_gateup(flint_moe_layer L, 
   __shared__ __align__(16) unsigned char abuf[mm_buf_bytes<FmtF16>()];
   __shared__ int srow[kMmTok], orow[kMmTok];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6, m = lane & 15, q = lane >> 4;
-  // grid row 0 is the shared expert (all B tokens, the longest workgroups:
-  // dispatched first, they overlap the routed experts' rows 1 .. U)
-  const bool sh = blockIdx.y == 0;
-  const int ub = (int)blockIdx.y - 1;
+  // the first nsh grid rows are the shared expert (all B tokens, the longest
+  // workgroups: dispatched first, they overlap the routed experts' rows)
+  const int nsh = (Is + I - 1) / I;
+  const bool sh = (int)blockIdx.y < nsh;
+  const int ub = (int)blockIdx.y - nsh;
   if (!sh && ub >= bk[0]) return;
-  const int rows = sh ? Is : I, r0 = blockIdx.x * kMmGateUpRows;
+  const int rows = sh ? Is : I, r0 = ((sh ? (int)blockIdx.y * (int)gridDim.x : 0) + (int)blockIdx.x) * kMmGateUpRows;
   if (r0 >= rows) return;
   int e = 0, p0 = 0, ntok = B;
   if (!sh) {
@@ -981,7 +983,8 @@ hipError_t launch_batch_step_tiled(const flint_moe_dims& d, const flint_moe_laye
   const int k = d.top_k, E = d.n_experts, I = d.expert_width, Is = d.shared_width, nb = B * k;
   const int Umax = nb < E ? nb : E;
   const bool many = nb >= 96;  // tiled weights and many (token, slot) pairs: one chunk ahead, else two
-  const int gu_x = ((I > Is ? I : Is) + kMmGateUpRows - 1) / kMmGateUpRows;
+  const int gu_x = (I + kMmGateUpRows - 1) / kMmGateUpRows;  // a routed expert's rows; the shared one spans
+  const int gu_sh = (Is + I - 1) / I;                        // gu_sh grid rows
   k_copy_words<<<(B * kHidden + kThreads - 1) / kThreads, kThreads, 0, s>>>(
       reinterpret_cast<const uint32_t*>(x), reinterpret_cast<uint32_t*>(h), B * kHidden);
   hipError_t e = hipGetLastError();
@@ -996,7 +999,7 @@ hipError_t launch_batch_step_tiled(const flint_moe_dims& d, const flint_moe_laye
                                           reinterpret_cast<uint32_t*>(routes + (size_t)l * nb), nb);
     k_bucket<<<1, kThreads, 0, s>>>(idx, nb, E, bk);
     const uint8_t* lt = tiles ? tiles + (size_t)l * batch_tiles_layer_bytes(d) : nullptr;
-    const dim3 gg(gu_x, Umax + 1), gd(kHidden / kMmRows, Umax + 1);
+    const dim3 gg(gu_x, gu_sh + Umax), gd(kHidden / kMmRows, Umax + 1);
     if (tiles && many) {
       k_mm_gateup<true, 1><<<gg, kMmThreads, 0, s>>>(Ly, I, Is, k, B, Umax, up, bk, hrp, hsp, nb, lt, E);
       k_mm_down<true, 1><<<gd, kMmThreads, 0, s>>>(Ly, I, Is, B, Umax, hrp, hsp, bk, wts, dr, ds, nb, lt, E);
