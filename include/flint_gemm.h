@@ -37,11 +37,15 @@ size_t flint_nvfp4_gemm_workspace_bytes(int32_t T, int32_t K, int32_t mode);
  *     flint_nvfp4_quantize as one [T][K] tensor (one fp32 tensor scale over
  *     all of X, E4M3 scales per 16 values along K), then
  *     Y = deq(Xq) . deq(W)^T, one fp16 part per operand.
- * Sizes: N >= 1, T >= 1, K a multiple of 256 (FLINT_E_UNSUPPORTED otherwise).
+ * Sizes: N >= 1, T >= 1, K a multiple of 256 and at most 2^20
+ * (FLINT_E_UNSUPPORTED otherwise).
  * Workspace: flint_nvfp4_gemm_workspace_bytes(T, K, mode), zero-filled before
  * first use; every completed call leaves its counter zero.  A4 keeps the
  * quantised activations there: codes [T][K/2] from byte 512, then the E4M3
- * scales [T][K/16] at the next 256-byte boundary. */
+ * scales [T][K/16] at the next 256-byte boundary.  After them (both modes)
+ * come the activations as fp16 planes for the matrix cores, [2][T][K]
+ * (A32: hi, lo) or [T][K] (A4: code x block scale), written by calls whose
+ * grid is large enough for the 256 x 256 tiles. */
 int32_t flint_nvfp4_gemm(const flint_nvfp4* W /*[host]*/, int32_t N, int32_t K, const float* X, int32_t T,
                          int32_t mode, float* Y, void* ws, size_t ws_bytes, void* stream);
 

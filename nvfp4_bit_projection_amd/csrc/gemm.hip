@@ -30,6 +30,8 @@
 // requested before the current chunk is multiplied.
 #include <float.h>
 
+#include <algorithm>
+
 #include "../../include/flint_gemm.h"
 #include "flint_common.h"
 #include "flint_device.h"
@@ -232,20 +234,245 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
   }
 }
 
-// A4 workspace: the quantiser's amax counter first (at a fixed offset, so
-// calls with different T on one workspace find it zero), then the tensor
-// scale, the codes and the block scales of the quantised activations.
+// ------------------------------------------------------------ wide tiles --
+// Many tokens: a workgroup of 8 waves owns 256 weight rows x 256 tokens;
+// wave w takes rows 128 (w & 1) .. + 127 and tokens 64 (w >> 1) .. + 63, as
+// 8 x 4 tiles of 16 x 16 (128 fp32 accumulators a lane).  The activations
+// arrive as fp16 planes written once by a pre-pass (A32: hi and lo; A4: the
+// decoded NVFP4 value, exact in fp16, the tensor scale applied at the end),
+// so a K stage of the token tile is a plain buffer-to-LDS copy; the stage's
+// weight rows are decoded once per workgroup into LDS by all 512 threads.
+// Every product then takes both operands from LDS: a decoded weight serves
+// 256 tokens, a staged activation 256 rows, against 32 tokens a decode in
+// the narrow kernel above.
+// Stages of BK K values are double-buffered: the next stage's weight bytes
+// and activation copies are requested before the current stage's products,
+// its weights decoded into the other buffer after them; one barrier a stage.
+// Matrix-core operands: A = weight rows (C rows), B = tokens (C columns), so
+// a lane's four accumulators are four consecutive weight rows of one token:
+// one 16-byte store of Y.
+// LDS rows hold BK fp16 values; granule g (8 values) of row r sits in slot
+// g ^ wswz(r): the 8 rows that a 128-bit read serves in one cycle, and the 8
+// granules of one decode store, fall in distinct banks.
+constexpr int kWRows = 256, kWTok = 256, kWThreads = 512;
+
+template <int BK>
+__device__ __forceinline__ int wswz(int r) {
+  constexpr int G = BK / 8;  // granules a row
+  return (r / (8 / G)) & (G - 1);
+}
+
+struct WideArgs {
+  const uint8_t* wc;    // W codes [N][K/2]
+  const uint8_t* ws;    // W scales [N][K/16]
+  const float* wS;      // W tensor scale
+  const uint16_t* xp;   // activation planes [P][T][K] fp16
+  const float* xS;      // A4: X tensor scale (else null)
+  float* y;             // Y [T][N]
+  int N, K, T;
+};
+
+// One workgroup's stage traffic: the decoding thread's weight bytes (row
+// drow, values BK/2 dh .. + BK/2 of a stage) and the activation copies (1 KB
+// buffer-to-LDS loads dealt round-robin to the waves).  Rows and tokens past
+// the ends of W and X read as zero (buffer bounds).
+template <int P, int BK>
+struct WideStage {
+  static constexpr int RB = 2 * BK, TB = kWTok * RB;
+  static constexpr int NW = BK / 16;     // code words a decoding thread holds
+  static constexpr int CPP = TB / 1024;  // 1 KB copies a plane
+  static_assert(CPP % 8 == 0, "a plane's copies are dealt to the 8 waves evenly");
+  rsrc_t rc, rs, rx[P];
+  uint32_t c_off, s_off, wcw[NW], wsb;
+  int drow, dh, K;
+  __device__ __forceinline__ void init(const WideArgs& A, int n0, int t0, int tid) {
+    const int rows_here = A.N - n0 < kWRows ? A.N - n0 : kWRows;
+    const int toks_here = A.T - t0 < kWTok ? A.T - t0 : kWTok;
+    rc = make_rsrc(A.wc + (size_t)n0 * (A.K / 2), (uint64_t)rows_here * (A.K / 2));
+    rs = make_rsrc(A.ws + (size_t)n0 * (A.K / 16), (uint64_t)rows_here * (A.K / 16));
+#pragma unroll
+    for (int p = 0; p < P; ++p) rx[p] = make_rsrc(A.xp + ((size_t)p * A.T + t0) * A.K, (uint64_t)toks_here * A.K * 2);
+    K = A.K;
+    drow = tid >> 1;
+    dh = tid & 1;
+    c_off = (uint32_t)drow * (K / 2) + dh * (BK / 4);
+    s_off = (uint32_t)drow * (K / 16) + dh * (BK / 32);
+  }
+  __device__ __forceinline__ void wload(int k0) {
+    if constexpr (NW == 4) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rc, c_off + k0 / 2, 0, kAuxNT);
+      wcw[0] = v[0]; wcw[1] = v[1]; wcw[2] = v[2]; wcw[3] = v[3];
+      wsb = (uint32_t)(unsigned short)__builtin_amdgcn_raw_buffer_load_b16(rs, s_off + k0 / 16, 0, kAuxNT);
+    } else {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(rc, c_off + k0 / 2, 0, kAuxNT);
+      wcw[0] = v[0]; wcw[1] = v[1];
+      wsb = (uint32_t)(unsigned char)__builtin_amdgcn_raw_buffer_load_b8(rs, s_off + k0 / 16, 0, kAuxNT);
+    }
+  }
+  __device__ __forceinline__ void wstore(unsigned char* wbuf) const {
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const int g = dh * NW + j;
+      *reinterpret_cast<h8_t*>(wbuf + drow * RB + ((g ^ wswz<BK>(drow)) << 4)) =
+          h16_decode(wcw[j], h16_scale((wsb >> (8 * (j >> 1))) & 0xFF));
+    }
+  }
+  __device__ __forceinline__ void tcopy(int k0, unsigned char* tbuf, int wv, int lane) const {
+#pragma unroll
+    for (int i = 0; i < P * CPP / 8; ++i) {
+      const int p = 8 * i / CPP, cc = 8 * i % CPP + wv;  // copy wv + 8 i (CPP is a multiple of 8)
+      const int pos = cc * 1024 + 16 * lane, r = pos / RB, g = ((pos % RB) >> 4) ^ wswz<BK>(r);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx[p],
+                                               (__attribute__((address_space(3))) void*)(tbuf + p * TB + cc * 1024),
+                                               16, (uint32_t)((r * K + k0 + 8 * g) * 2), 0, 0, 0);
+    }
+  }
+};
+
+template <int P, int BK>
+__global__ __launch_bounds__(kWThreads) void k_gemm_wide(WideArgs A) {
+  constexpr int RB = 2 * BK;          // bytes a LDS row
+  constexpr int WB = kWRows * RB;     // weight tile bytes a stage
+  constexpr int TB = kWTok * RB;      // one plane's token tile bytes a stage
+  constexpr int SB = WB + P * TB;
+  __shared__ __align__(16) unsigned char lds[2][SB];
+
+  // tile: workgroups L, L + 8, ... run on one XCD and take consecutive tiles
+  // (the token blocks of one row block first), so a weight block is read
+  // from memory once per XCD and served from its L2 to the other token blocks
+  const int nrb = (A.N + kWRows - 1) / kWRows, ntb = (A.T + kWTok - 1) / kWTok;
+  const int per = (int)gridDim.x / 8, L = (int)blockIdx.x;
+  const int lt = (L % 8) * per + L / 8;
+  if (lt >= nrb * ntb) return;
+  const int n0 = (lt / ntb) * kWRows, t0 = (lt % ntb) * kWTok;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, m = lane & 15, q = lane >> 4;
+  const int wr = wv & 1, wt = wv >> 1;
+
+  WideStage<P, BK> S;
+  S.init(A, n0, t0, tid);
+  f4_t acc[8][4];
+#pragma unroll
+  for (int rt = 0; rt < 8; ++rt)
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) acc[rt][tt] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int nst = A.K / BK;
+  S.wload(0);
+  S.tcopy(0, lds[0] + WB, wv, lane);
+  S.wstore(lds[0]);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies are in
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    unsigned char* cur = lds[st & 1];
+    unsigned char* nxt = lds[(st + 1) & 1];
+    const bool more = st + 1 < nst;
+    if (more) {
+      S.wload((st + 1) * BK);
+      S.tcopy((st + 1) * BK, nxt + WB, wv, lane);
+    }
+#pragma unroll
+    for (int s = 0; s < BK / 32; ++s) {
+      h8_t a[8];
+#pragma unroll
+      for (int rt = 0; rt < 8; ++rt) {
+        const int r = 128 * wr + 16 * rt + m;
+        a[rt] = *reinterpret_cast<const h8_t*>(cur + r * RB + (((4 * s + q) ^ wswz<BK>(r)) << 4));
+      }
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) {
+        const int r = 64 * wt + 16 * tt + m;
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const h8_t b = *reinterpret_cast<const h8_t*>(cur + WB + p * TB + r * RB + (((4 * s + q) ^ wswz<BK>(r)) << 4));
+#pragma unroll
+          for (int rt = 0; rt < 8; ++rt)
+            acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[rt], b, acc[rt][tt], 0, 0, 0);
+        }
+      }
+    }
+    if (more) S.wstore(nxt);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+  }
+
+  // lane (m, q) of tile (rt, tt): weight rows 4q .. 4q+3 of the tile, token m
+  const float sc = *A.wS * (P == 1 && A.xS ? *A.xS : 1.0f);
+  const bool vec = (A.N & 3) == 0;
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const int t = t0 + 64 * wt + 16 * tt + m;
+    if (t >= A.T) continue;
+    float* yrow = A.y + (size_t)t * A.N;
+#pragma unroll
+    for (int rt = 0; rt < 8; ++rt) {
+      const int n = n0 + 128 * wr + 16 * rt + 4 * q;
+      const f4_t v = acc[rt][tt] * sc;
+      if (vec) {
+        if (n < A.N) __builtin_nontemporal_store(v, reinterpret_cast<f4_t*>(yrow + n));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (n + i < A.N) yrow[n + i] = v[i];
+      }
+    }
+  }
+}
+
+// Activation planes for the wide kernel.  A32: x = hi + lo, [2][T][K] fp16;
+// each thread 8 values a step.
+__global__ __launch_bounds__(256) void k_gemm_split(const float* __restrict__ x, size_t n,
+                                                    uint16_t* __restrict__ planes) {
+  for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8; i < n; i += (size_t)gridDim.x * 256 * 8) {
+    const float4 u = *reinterpret_cast<const float4*>(x + i), v = *reinterpret_cast<const float4*>(x + i + 4);
+    const float f[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+    h8_t hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      hi[e] = (_Float16)f[e];
+      lo[e] = (_Float16)(f[e] - (float)hi[e]);
+    }
+    *reinterpret_cast<h8_t*>(planes + i) = hi;
+    *reinterpret_cast<h8_t*>(planes + n + i) = lo;
+  }
+}
+// A4: the quantised activations decoded (code x block scale, exact in fp16),
+// [T][K]; each thread one 16-value block a step.
+__global__ __launch_bounds__(256) void k_gemm_deq(const uint8_t* __restrict__ codes,
+                                                  const uint8_t* __restrict__ scales, size_t n,
+                                                  uint16_t* __restrict__ plane) {
+  for (size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 16; i < n; i += (size_t)gridDim.x * 256 * 16) {
+    const uint2 c = *reinterpret_cast<const uint2*>(codes + i / 2);
+    const H16Scale s = h16_scale(scales[i / 16]);
+    *reinterpret_cast<h8_t*>(plane + i) = h16_decode(c.x, s);
+    *reinterpret_cast<h8_t*>(plane + i + 8) = h16_decode(c.y, s);
+  }
+}
+
+// Workspace: the quantiser's amax counter first (at a fixed offset, so calls
+// with different T on one workspace find it zero), then the tensor scale, the
+// codes and the block scales of the quantised activations (A4), then the fp16
+// activation planes of the wide kernel ([2][T][K] for A32, [T][K] for A4).
 struct GemmWs {
-  size_t amax, tscale, codes, scales, total;
-  GemmWs(int T, int K) {
+  size_t amax, tscale, codes, scales, planes, total;
+  GemmWs(int T, int K, int mode) {
+    const bool a4 = mode == FLINT_GEMM_A4;
     size_t o = 0;
     amax = o; o = align_up(o + 4, 256);
     tscale = o; o = align_up(o + 4, 256);
-    codes = o; o = align_up(o + (size_t)T * K / 2, 256);
-    scales = o; o = align_up(o + (size_t)T * K / 16, 256);
+    codes = o; o = align_up(o + (a4 ? (size_t)T * K / 2 : 0), 256);
+    scales = o; o = align_up(o + (a4 ? (size_t)T * K / 16 : 0), 256);
+    planes = o; o = align_up(o + (a4 ? 1 : 2) * (size_t)T * K * 2, 256);
     total = o;
   }
 };
+
+// The wide kernel takes calls with at least this many 256 x 256 tiles (half
+// a grid of one workgroup per compute unit: a tile of K = 2,048 takes about
+// 93 us with A4 and 160 us with A32, about the narrow kernel's time for a
+// 6,144 x 2,048 x 2,048 call); below it the narrow kernel (256 rows x 32
+// tokens a workgroup) fills more of the chip.
+constexpr int kWideMinTiles = 128;
 
 bool a16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool a4b(const void* p) { return ((uintptr_t)p & 3u) == 0; }
@@ -259,42 +486,68 @@ extern "C" {
 
 size_t flint_nvfp4_gemm_workspace_bytes(int32_t T, int32_t K, int32_t mode) {
   if (T < 1 || K < kGChunk || K % kGChunk || (mode != FLINT_GEMM_A32 && mode != FLINT_GEMM_A4)) return 0;
-  return mode == FLINT_GEMM_A4 ? GemmWs(T, K).total : 256;
+  return GemmWs(T, K, mode).total;
 }
 
 int32_t flint_nvfp4_gemm(const flint_nvfp4* W, int32_t N, int32_t K, const float* X, int32_t T, int32_t mode,
                          float* Y, void* ws, size_t ws_bytes, void* stream) {
   if (!W || !W->codes || !W->scales || !W->tscale || !X || !Y || !ws) return FLINT_E_NULL;
   if (N < 1 || K < 1 || T < 1 || (mode != FLINT_GEMM_A32 && mode != FLINT_GEMM_A4)) return FLINT_E_DIMS;
-  if (K % kGChunk || (int64_t)T * K > (1ll << 40)) return FLINT_E_UNSUPPORTED;
+  if (K % kGChunk || (int64_t)T * K > (1ll << 40) || K > (1 << 20)) return FLINT_E_UNSUPPORTED;
   if (!a16(W->codes) || !a4b(W->scales) || !a4b(W->tscale) || !a16(X) || !a16(Y) || !a16(ws)) return FLINT_E_ALIGN;
   if (ws_bytes < flint_nvfp4_gemm_workspace_bytes(T, K, mode)) return FLINT_E_WORKSPACE;
   int32_t st;
   if ((st = api_check_device())) return st;
   hipStream_t s = (hipStream_t)stream;
-  GemmArgs A{};
-  A.wc = W->codes;
-  A.ws = W->scales;
-  A.wS = W->tscale;
-  A.x = X;
-  A.y = Y;
-  A.N = N;
-  A.K = K;
-  A.T = T;
-  const dim3 grid((N + kGRows - 1) / kGRows, (T + kGTok - 1) / kGTok);
-  hipError_t e;
+  const GemmWs w(T, K, mode);
+  char* base = static_cast<char*>(ws);
+  hipError_t e = hipSuccess;
+  const uint8_t* xc = reinterpret_cast<uint8_t*>(base + w.codes);
+  const uint8_t* xs = reinterpret_cast<uint8_t*>(base + w.scales);
+  const float* xS = reinterpret_cast<float*>(base + w.tscale);
   if (mode == FLINT_GEMM_A4) {
-    const GemmWs w(T, K);
-    char* base = static_cast<char*>(ws);
-    A.xc = reinterpret_cast<uint8_t*>(base + w.codes);
-    A.xs = reinterpret_cast<uint8_t*>(base + w.scales);
-    A.xS = reinterpret_cast<float*>(base + w.tscale);
-    e = launch_quantize(X, 1, T, K, const_cast<uint8_t*>(A.xc), const_cast<uint8_t*>(A.xs),
-                        const_cast<float*>(A.xS), reinterpret_cast<uint32_t*>(base + w.amax), s);
+    e = launch_quantize(X, 1, T, K, const_cast<uint8_t*>(xc), const_cast<uint8_t*>(xs), const_cast<float*>(xS),
+                        reinterpret_cast<uint32_t*>(base + w.amax), s);
     if (e != hipSuccess) return api_hip_fail(e);
-    k_gemm<1><<<grid, 256, 0, s>>>(A);
+  }
+  const int64_t tiles = (int64_t)((N + kWRows - 1) / kWRows) * ((T + kWTok - 1) / kWTok);
+  if (tiles >= kWideMinTiles) {
+    WideArgs A{};
+    A.wc = W->codes;
+    A.ws = W->scales;
+    A.wS = W->tscale;
+    A.xp = reinterpret_cast<uint16_t*>(base + w.planes);
+    A.y = Y;
+    A.N = N;
+    A.K = K;
+    A.T = T;
+    const size_t n = (size_t)T * K;
+    const int pg = (int)std::min<size_t>((n + 256 * 16 - 1) / (256 * 16), 4096);
+    const int grid = (int)((tiles + 7) / 8 * 8);
+    if (mode == FLINT_GEMM_A4) {
+      A.xS = xS;
+      k_gemm_deq<<<pg, 256, 0, s>>>(xc, xs, n, const_cast<uint16_t*>(A.xp));
+      k_gemm_wide<1, 64><<<grid, kWThreads, 0, s>>>(A);
+    } else {
+      k_gemm_split<<<pg, 256, 0, s>>>(X, n, const_cast<uint16_t*>(A.xp));
+      k_gemm_wide<2, 32><<<grid, kWThreads, 0, s>>>(A);
+    }
   } else {
-    k_gemm<2><<<grid, 256, 0, s>>>(A);
+    GemmArgs A{};
+    A.wc = W->codes;
+    A.ws = W->scales;
+    A.wS = W->tscale;
+    A.x = X;
+    A.y = Y;
+    A.N = N;
+    A.K = K;
+    A.T = T;
+    A.xc = xc;
+    A.xs = xs;
+    A.xS = xS;
+    const dim3 grid((N + kGRows - 1) / kGRows, (T + kGTok - 1) / kGTok);
+    if (mode == FLINT_GEMM_A4) k_gemm<1><<<grid, 256, 0, s>>>(A);
+    else k_gemm<2><<<grid, 256, 0, s>>>(A);
   }
   e = hipGetLastError();
   return e == hipSuccess ? FLINT_OK : api_hip_fail(e);

@@ -58,3 +58,52 @@ def test_gemm_repeat_calls_same_workspace(F):
         Y = F.nvfp4_gemm(q, torch.from_numpy(X).cuda(), 1, ws=ws)
         torch.cuda.synchronize()
         assert_close(Y.cpu().numpy(), oracle.nvfp4_gemm(ref_q, X, a4=True), f"T={T}")
+
+
+def wide_tiles(N, T):
+    """256 x 256 tiles of a call: at 128 or more the library takes the wide
+    kernel (weights decoded once per workgroup into LDS, fp16 activation
+    planes), below it the narrow one."""
+    return -(-N // 256) * -(-T // 256)
+
+
+@pytest.mark.parametrize("N,K,T", [(16456, 2048, 1000), (16385, 1024, 1024), (8200, 1024, 2000)])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_gemm_wide_against_oracle(F, N, K, T, mode):
+    """Shapes on the wide kernel, every output against the oracle: ragged last
+    row block (72, 1 and 8 rows; N % 4 = 1 takes the scalar stores) and
+    ragged last token block."""
+    assert wide_tiles(N, T) >= 128
+    w = synth.head_f32(1010, N, K)
+    ref_q = oracle.quantize(w)
+    q = F.quantize(torch.from_numpy(w).cuda())
+    X = synth.normal(1011, synth.stream_id(synth.TOKEN), T * K, std=1.0).reshape(T, K)
+    print(f"gemm wide N={N} K={K} T={T} mode={mode}", flush=True)
+    Y = F.nvfp4_gemm(q, torch.from_numpy(X).cuda(), mode)
+    torch.cuda.synchronize()
+    assert_close(Y.cpu().numpy(), oracle.nvfp4_gemm(ref_q, X, a4=bool(mode)), f"N={N} K={K} T={T}")
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_gemm_head_full_size_sampled(F, mode):
+    """The 150,144 x 2,048 head and 2,048 tokens, the call the prefill bench
+    times: the weights quantised on the device (bit-exact with the oracle's
+    quantiser, checked in the codec tests), all 2,048 tokens on 80 sampled
+    weight rows (the first and last row blocks among them) against the oracle
+    applied to those rows of the oracle's own quantised head."""
+    V, H, T = 150144, 2048, 2048
+    w = torch.empty(V * H, dtype=torch.float32, device="cuda")
+    synth.normal_device(synth.HEAD_SEED, synth.stream_id(synth.HEAD), V * H, w, std=synth.WEIGHT_STD)
+    q = F.quantize(w.view(V, H))
+    del w
+    ref = oracle.quantize(synth.head_f32(synth.HEAD_SEED, V, H))
+    X = synth.normal(1020, synth.stream_id(synth.TOKEN), T * H, std=1.0).reshape(T, H)
+    print(f"gemm head full size mode={mode}", flush=True)
+    Y = F.nvfp4_gemm(q, torch.from_numpy(X).cuda(), mode)
+    rng = np.random.default_rng(5)
+    sel = np.unique(np.concatenate([[0, 1, 255, 256, V - 256, V - 2, V - 1], rng.integers(0, V, 73)]))
+    got = Y[:, torch.from_numpy(sel).cuda()].cpu().numpy()
+    torch.cuda.synchronize()
+    del Y
+    sub = oracle.NVFP4(ref.codes[sel], ref.scales[sel], ref.tscale, len(sel), H)
+    assert_close(got, oracle.nvfp4_gemm(sub, X, a4=bool(mode)), f"head sampled mode={mode}")

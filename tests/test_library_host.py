@@ -205,7 +205,10 @@ def test_int4_rejections(F):
 def test_gemm_rejections(F):
     L = F.lib()
     assert L.flint_nvfp4_gemm_workspace_bytes(8, 2048, 0) > 0
-    assert L.flint_nvfp4_gemm_workspace_bytes(8, 2048, 1) > L.flint_nvfp4_gemm_workspace_bytes(8, 2048, 0)
+    # room for the layout the header gives: A4 codes from byte 512, the block
+    # scales, then the fp16 planes ([2][T][K] for A32, [T][K] for A4)
+    assert L.flint_nvfp4_gemm_workspace_bytes(8, 2048, 1) >= 512 + 8 * 2048 // 2 + 8 * 2048 // 16 + 8 * 2048 * 2
+    assert L.flint_nvfp4_gemm_workspace_bytes(8, 2048, 0) >= 2 * 8 * 2048 * 2
     assert L.flint_nvfp4_gemm_workspace_bytes(8, 100, 0) == 0
     assert L.flint_nvfp4_gemm_workspace_bytes(8, 2048, 2) == 0
     m = F.NVFP4(FAKE, FAKE, FAKE)
@@ -216,6 +219,7 @@ def test_gemm_rejections(F):
     assert g(0, 2048, 8, 1) == -2
     assert g(10, 2048, 8, 3) == -2
     assert g(10, 2000, 8, 0) == -8
+    assert g(10, (1 << 20) + 256, 1, 0) == -8  # K above 2^20
     assert g(10, 2048, 8, 1, wsb=need - 1) == -4
     assert g(10, 2048, 8, 1, x=FAKE + 4) == -3
 
