@@ -289,6 +289,16 @@ def bench_layer(args) -> int:
     return 0
 
 
+ROTATE_BYTES = 384 * 2**20  # 1.5x the 256 MB last-level cache
+
+
+def rotation(nbytes: int, cap: int = 512) -> int:
+    """Distinct copies of a call's working set (nbytes each) used in turn so
+    that together they exceed the last-level cache and every call reads its
+    bytes from HBM (at least 2)."""
+    return max(2, min(cap, -(-ROTATE_BYTES // max(1, nbytes))))
+
+
 def bench_router(args) -> int:
     """The router call alone (flint_moe_route_ex at E = 256) in its four
     variants: fp32 or BF16 router, softmax or sigmoid weights.  One step = one
@@ -306,27 +316,31 @@ def bench_router(args) -> int:
     r32 = torch.empty((dims.n_experts, dims.hidden), dtype=torch.float32, device="cuda")
     synth.normal_device(0, synth.stream_id(synth.ROUTER), r32.numel(), r32, std=synth.WEIGHT_STD)
     r16 = r32.to(torch.bfloat16)
+    # copies of each router used in turn (together 1.5x the last-level cache)
+    routers = {"f32": [r32] + [r32.clone() for _ in range(rotation(r32.numel() * 4) - 1)],
+               "bf16": [r16] + [r16.clone() for _ in range(rotation(r16.numel() * 2) - 1)]}
     x = workload.tokens([synth.TOKEN_SEED0 + t for t in range(B)], dims.hidden)
     ws = flint.workspace(flint.OP_ROUTE, d, B)
     out = []
-    for name, router, scoring in (("f32_softmax", r32, flint.SCORE_SOFTMAX), ("f32_sigmoid", r32, flint.SCORE_SIGMOID),
-                                  ("bf16_softmax", r16, flint.SCORE_SOFTMAX),
-                                  ("bf16_sigmoid", r16, flint.SCORE_SIGMOID)):
-        for _ in range(args.warmup):
-            flint.route_ex(d, router, x, scoring=scoring, ws=ws)
+    for name, kind, scoring in (("f32_softmax", "f32", flint.SCORE_SOFTMAX), ("f32_sigmoid", "f32", flint.SCORE_SIGMOID),
+                                ("bf16_softmax", "bf16", flint.SCORE_SOFTMAX),
+                                ("bf16_sigmoid", "bf16", flint.SCORE_SIGMOID)):
+        rs = routers[kind]
+        for i in range(args.warmup):
+            flint.route_ex(d, rs[i % len(rs)], x, scoring=scoring, ws=ws)
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record()
-        for _ in range(args.steps):
-            flint.route_ex(d, router, x, scoring=scoring, ws=ws)
+        for i in range(args.steps):
+            flint.route_ex(d, rs[i % len(rs)], x, scoring=scoring, ws=ws)
         ev1.record()
         torch.cuda.synchronize()
         us = ev0.elapsed_time(ev1) * 1e3 / args.steps
-        nbytes = router.numel() * router.element_size() * B
+        nbytes = rs[0].numel() * rs[0].element_size() * B
         gbs = nbytes / (us * 1e-6) / 1e9
-        log(f"router {name} B={B}: {us:.2f} us/call, {gbs:.1f} GB/s")
+        log(f"router {name} B={B}: {us:.2f} us/call, {gbs:.1f} GB/s ({len(rs)} copies in turn)")
         out.append({"variant": name, "us_per_call": round(us, 3), "bytes": nbytes, "achieved_gbs": round(gbs, 1),
-                    "frac": round(gbs / HBM_PEAK_GBS, 4)})
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "copies_rotated": len(rs)})
     print(json.dumps({"metric": "router call us (E=256)", "unit": "us", "batch": B, "steps": args.steps,
                       "warmup": args.warmup, "higher_is_better": False, "data": "synthetic",
                       "config": {"workload": f"router_e256_b{B}"}, "peak_gbs": HBM_PEAK_GBS, "variants": out}),
@@ -352,15 +366,20 @@ def bench_attn(args) -> int:
     steps, warm = args.steps, args.warmup
     out = []
 
-    def timed(fn, check):
-        for _ in range(warm):
-            fn()
+    def timed(fns, check):
+        """fns: one call per copy of the working set, used in turn; the
+        graph holds a whole number of rounds, ending on the last copy."""
+        nc = len(fns)
+        for i in range(max(warm, nc)):
+            fns[i % nc]()
+        torch.cuda.synchronize()
+        fns[-1]()
         torch.cuda.synchronize()
         ref = check().clone()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ev0.record()
-        for _ in range(steps):
-            fn()
+        for i in range(steps):
+            fns[i % nc]()
         ev1.record()
         torch.cuda.synchronize()
         eager_us = ev0.elapsed_time(ev1) * 1e3 / steps
@@ -368,34 +387,36 @@ def bench_attn(args) -> int:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            fn()
+            fns[0]()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
+        per = nc * max(1, 16 // nc)
         with torch.cuda.graph(g):
-            for _ in range(16):
-                fn()
+            for i in range(per):
+                fns[i % nc]()
         for _ in range(3):  # replays agree with the eager result
             g.replay()
             torch.cuda.synchronize()
             if not torch.equal(check(), ref):
                 raise RuntimeError("graph replay differs from the eager call")
-        reps = max(1, steps // 16)
+        reps = max(1, steps // per)
         ev0.record()
         for _ in range(reps):
             g.replay()
         ev1.record()
         torch.cuda.synchronize()
-        return eager_us, ev0.elapsed_time(ev1) * 1e3 / (reps * 16)
+        return eager_us, ev0.elapsed_time(ev1) * 1e3 / (reps * per)
 
     nq, nk = 32 * 128, 4 * 128
     w_bytes = (nq + 2 * nk) * H * 9 // 16 + H * nq * 9 // 16
     for name, d, ctx in (("sliding513", synth.SLIDING, 4096), ("full_1k", synth.FULL, 1024),
                          ("full_8k", synth.FULL, 8192), ("full_32k", synth.FULL, 32768),
                          ("full_128k", synth.FULL, 131072)):
-        W = workload.build_attn(d, 0)
         cap = 513 if d.window else ctx
-        kc = workload.kv_cache(d, 1, cap, synth.K_CACHE)
-        vc = workload.kv_cache(d, 1, cap, synth.V_CACHE)
+        nc = rotation(w_bytes + cap * d.n_kv * d.head_dim * 2 * 2, cap=48)  # layers + caches in turn
+        Ws = [workload.build_attn(d, c) for c in range(nc)]
+        kcs = [workload.kv_cache(d, 1 + c, cap, synth.K_CACHE) for c in range(nc)]
+        vcs = [workload.kv_cache(d, 1 + c, cap, synth.V_CACHE) for c in range(nc)]
         x = workload.tokens([synth.TOKEN_SEED0], H)[0]
         dc = flint.attn_dims_struct(H, d.n_q, d.n_kv, d.head_dim, d.window, d.rope, d.theta)
         ws = flint.attn_workspace(dc)
@@ -403,23 +424,28 @@ def bench_attn(args) -> int:
         pos = ctx - 1
         n = min(pos + 1, d.window) if d.window else pos + 1
         nbytes = w_bytes + n * d.n_kv * d.head_dim * 2 * 2
-        eager_us, graph_us = timed(lambda: flint.attn_decode(dc, W, x, pos, kc, vc, ws=ws, y=y), lambda: y)
+        fns = [(lambda c=c: flint.attn_decode(dc, Ws[c], x, pos, kcs[c], vcs[c], ws=ws, y=y)) for c in range(nc)]
+        eager_us, graph_us = timed(fns, lambda: y)
         gbs = nbytes / (graph_us * 1e-6) / 1e9
-        log(f"attention {name}: {n} positions, {eager_us:.2f} us eager, {graph_us:.2f} us graph, {gbs:.0f} GB/s")
+        log(f"attention {name}: {n} positions, {eager_us:.2f} us eager, {graph_us:.2f} us graph, {gbs:.0f} GB/s "
+            f"({nc} layers in turn)")
         out.append({"layer": name, "positions": n, "bytes": nbytes, "us_eager": round(eager_us, 2),
                     "us_graph": round(graph_us, 2), "achieved_gbs": round(gbs, 1),
-                    "frac": round(gbs / HBM_PEAK_GBS, 4)})
-        del W, kc, vc, ws
-    g, u, dn = workload.build_dense(0, H, synth.DENSE_WIDTH)
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "copies_rotated": nc})
+        del Ws, kcs, vcs, ws, fns
+    nbytes = 3 * synth.DENSE_WIDTH * H * 9 // 16
+    nc = rotation(nbytes, cap=48)
+    mlps = [workload.build_dense(c, H, synth.DENSE_WIDTH) for c in range(nc)]
     x = workload.tokens([synth.TOKEN_SEED0], H)
     yd = torch.empty((1, H), dtype=torch.float32, device="cuda")
     wsd = torch.empty(4 * synth.DENSE_WIDTH, dtype=torch.uint8, device="cuda")
-    nbytes = 3 * synth.DENSE_WIDTH * H * 9 // 16
-    eager_us, graph_us = timed(lambda: flint.dense_mlp(g, u, dn, x, ws=wsd, y=yd), lambda: yd)
+    fns = [(lambda c=c: flint.dense_mlp(*mlps[c], x, ws=wsd, y=yd)) for c in range(nc)]
+    eager_us, graph_us = timed(fns, lambda: yd)
     gbs = nbytes / (graph_us * 1e-6) / 1e9
-    log(f"dense MLP 6144: {eager_us:.2f} us eager, {graph_us:.2f} us graph, {gbs:.0f} GB/s")
+    log(f"dense MLP 6144: {eager_us:.2f} us eager, {graph_us:.2f} us graph, {gbs:.0f} GB/s ({nc} copies in turn)")
     out.append({"layer": "dense_6144", "bytes": nbytes, "us_eager": round(eager_us, 2),
-                "us_graph": round(graph_us, 2), "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)})
+                "us_graph": round(graph_us, 2), "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "copies_rotated": nc})
     print(json.dumps({"metric": "attention and dense layer us per token (batch 1)", "unit": "us",
                       "higher_is_better": False, "steps": steps, "warmup": warm, "data": "synthetic",
                       "config": {"workload": "flint_attn_dense_b1", "q_heads": 32, "kv_heads": 4, "head_dim": 128,
@@ -536,6 +562,10 @@ def bench_gemm(args) -> int:
         synth.normal_device(7, synth.stream_id(synth.HEAD), N * K, w, std=synth.WEIGHT_STD)
         q = flint.quantize(w.view(N, K))
         del w
+        # weight copies used in turn (together 1.5x the last-level cache), so
+        # each call starts with its weights in HBM
+        nc = rotation(N * K * 9 // 16)
+        qs = [q] + [flint.NVFP4Tensor(q.codes.clone(), q.scales.clone(), q.tscale.clone()) for _ in range(nc - 1)]
         for T in (512, 2048):
             X = torch.empty(T * K, dtype=torch.float32, device="cuda")
             synth.normal_device(8, synth.stream_id(synth.TOKEN), T * K, X)
@@ -543,40 +573,42 @@ def bench_gemm(args) -> int:
             for mode, mname in ((flint.GEMM_A32, "a32"), (flint.GEMM_A4, "a4")):
                 ws = flint.gemm_workspace(T, K, mode)
                 Y = torch.empty((T, N), dtype=torch.float32, device="cuda")
-                fn = lambda: flint.nvfp4_gemm(q, X, mode, ws=ws, Y=Y)
-                for _ in range(2):
-                    fn()
+                fns = [(lambda c=c: flint.nvfp4_gemm(qs[c], X, mode, ws=ws, Y=Y)) for c in range(nc)]
+                for f in fns:
+                    f()
                 torch.cuda.synchronize()
-                ref = Y.clone()
+                ref = Y.clone()  # the last copy's result (all copies hold the same weights)
                 g = torch.cuda.CUDAGraph()
                 side = torch.cuda.Stream()
                 side.wait_stream(torch.cuda.current_stream())
                 with torch.cuda.stream(side):
-                    fn()
+                    fns[0]()
                 torch.cuda.current_stream().wait_stream(side)
                 torch.cuda.synchronize()
+                per = nc * max(1, 4 // nc)
                 with torch.cuda.graph(g):
-                    for _ in range(4):
-                        fn()
+                    for i in range(per):
+                        fns[i % nc]()
                 g.replay()
                 torch.cuda.synchronize()
                 if not torch.equal(Y, ref):
                     raise RuntimeError("graph replay differs from the eager call")
-                reps = max(1, min(args.steps, 64) // 4)
+                reps = max(1, min(args.steps, 64) // per)
                 ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 ev0.record()
                 for _ in range(reps):
                     g.replay()
                 ev1.record()
                 torch.cuda.synchronize()
-                us = ev0.elapsed_time(ev1) * 1e3 / (reps * 4)
+                us = ev0.elapsed_time(ev1) * 1e3 / (reps * per)
                 tf = 2.0 * T * N * K / (us * 1e-6) / 1e12
-                log(f"gemm {name} T={T} {mname}: {us:.1f} us, {tf:.1f} TFLOP/s ({100 * tf / peak:.1f}% of fp16 peak)")
+                log(f"gemm {name} T={T} {mname}: {us:.1f} us, {tf:.1f} TFLOP/s ({100 * tf / peak:.1f}% of fp16 peak, "
+                    f"{nc} weight copies in turn)")
                 out.append({"shape": name, "T": T, "mode": mname, "us": round(us, 2), "tflops": round(tf, 1),
-                            "frac_fp16_peak": round(tf / peak, 4)})
-                del ws, Y
+                            "frac_fp16_peak": round(tf / peak, 4), "weight_copies_rotated": nc})
+                del ws, Y, fns
             del X
-        del q
+        del q, qs
     print(json.dumps({"metric": "prefill GEMM TFLOP/s (NVFP4 weights)", "unit": "TFLOP/s", "higher_is_better": True,
                       "data": "synthetic", "config": {"workload": "nvfp4_prefill_gemm"}, "peak_tflops": peak,
                       "results": out}), flush=True)
