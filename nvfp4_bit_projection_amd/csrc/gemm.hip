@@ -384,7 +384,9 @@ __device__ __forceinline__ void wide_mma(const h8_t (&a)[8], const unsigned char
 // st + 2, the products of stage st in two halves, and between them the
 // decode of stage st + 1 (its VALU work overlaps the first half's matrix
 // operations) followed by the request of stage st + 3's weight bytes into
-// the set just decoded.  Every iteration makes the same requests (stages
+// the set just decoded.  A wave raises its issue priority while it issues a
+// half's matrix operations, so the other wave of its SIMD decodes in the
+// gaps rather than delaying them (0.6-3% faster with A4).  Every iteration makes the same requests (stages
 // past the end re-read the last one: cache hits, never used), so each ends
 // with the same wait and the compiler's own waits stay exact.
 template <int P, int BK, int R>
@@ -398,15 +400,21 @@ __device__ __forceinline__ void wide_iter(WideStage<P, BK>& S, int st, int nst, 
   S.tcopy(min((st + 2) * BK, last), tbuf + ((st + 2) % 3) * P * TB, wv, lane);
   h8_t a[8];
   wide_afrag<BK>(cw, 0, wr, m, q, a);
+  __builtin_amdgcn_s_setprio(1);
   if constexpr (BK == 64) wide_mma<P, BK, 0, 4>(a, ct, 0, wt, m, q, acc);
   else wide_mma<P, BK, 0, 2>(a, ct, 0, wt, m, q, acc);
+  __builtin_amdgcn_s_setprio(0);
   S.template wstore<R>(wbuf + ((st + 1) & 1) * WB);  // past the end: a buffer no one reads again
   S.template wload<R>(min((st + 3) * BK, last));
   if constexpr (BK == 64) {
     wide_afrag<BK>(cw, 1, wr, m, q, a);
+    __builtin_amdgcn_s_setprio(1);
     wide_mma<P, BK, 0, 4>(a, ct, 1, wt, m, q, acc);
+    __builtin_amdgcn_s_setprio(0);
   } else {
+    __builtin_amdgcn_s_setprio(1);
     wide_mma<P, BK, 2, 4>(a, ct, 0, wt, m, q, acc);
+    __builtin_amdgcn_s_setprio(0);
   }
   stage_barrier<WideStage<P, BK>::OPS_W + WideStage<P, BK>::OPS_T>();  // stage st + 1 is in
 }
