@@ -67,12 +67,15 @@ def wide_tiles(N, T):
     return -(-N // 256) * -(-T // 256)
 
 
-@pytest.mark.parametrize("N,K,T", [(16456, 2048, 1000), (16385, 1024, 1024), (8200, 1024, 2000)])
+@pytest.mark.parametrize("N,K,T", [(16456, 2048, 1000), (16385, 1024, 1024), (8200, 1024, 2000),
+                                   (8448, 256, 1024), (8448, 6144, 1000), (32800, 512, 100)])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_gemm_wide_against_oracle(F, N, K, T, mode):
     """Shapes on the wide kernel, every output against the oracle: ragged last
-    row block (72, 1 and 8 rows; N % 4 = 1 takes the scalar stores) and
-    ragged last token block."""
+    row block (72, 1 and 8 rows; N % 4 = 1 takes the scalar stores), ragged
+    last token block, K = 256 (the shortest pipeline: 4 or 8 stages, every
+    request past the end clamped), K = 6,144, and one token block of 100
+    tokens under 129 row blocks."""
     assert wide_tiles(N, T) >= 128
     w = synth.head_f32(1010, N, K)
     ref_q = oracle.quantize(w)
