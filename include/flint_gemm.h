@@ -44,8 +44,7 @@ size_t flint_nvfp4_gemm_workspace_bytes(int32_t T, int32_t K, int32_t mode);
  * quantised activations there: codes [T][K/2] from byte 512, then the E4M3
  * scales [T][K/16] at the next 256-byte boundary.  After them (both modes)
  * come the activations as fp16 planes for the matrix cores, [2][T][K]
- * (A32: hi, lo) or [T][K] (A4: code x block scale), written by calls whose
- * grid is large enough for the 256 x 256 tiles. */
+ * (A32: hi, lo) or [T][K] (A4: code x block scale), written by every call. */
 int32_t flint_nvfp4_gemm(const flint_nvfp4* W /*[host]*/, int32_t N, int32_t K, const float* X, int32_t T,
                          int32_t mode, float* Y, void* ws, size_t ws_bytes, void* stream);
 

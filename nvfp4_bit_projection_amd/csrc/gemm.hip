@@ -18,16 +18,20 @@
 //    through the matrix cores, products are exact in fp32;
 //  - A4: the activations are NVFP4 too (one tensor scale over X, quantised
 //    on the device by the same codec) and decode like the weights: one part.
+// A pre-pass writes the activations once per call as fp16 planes in the
+// workspace (A32: hi and lo; A4: code x block scale), which both kernels
+// below copy into LDS with buffer-to-LDS loads.
 // gfx950's scaled-FP4 MFMA takes one power-of-two scale per 32 values, so it
 // cannot carry NVFP4's E4M3 scale per 16 exactly; it is not used.
 //
-// Tiling: a workgroup (4 waves) owns 256 weight rows x 32 tokens; each wave
-// 64 rows (four 16-row tiles) x the 32 tokens (two 16-token tiles), so every
-// activation fragment read from LDS feeds four products.  K runs in
-// chunks of 256: the chunk's activations are staged in LDS as fp16 parts
-// (double-buffered; the next chunk's global loads are issued before the
-// current chunk's products), each lane's weight bytes for the next chunk are
-// requested before the current chunk is multiplied.
+// Narrow kernel (calls with few 256 x 256 tiles): a workgroup (4 waves) owns
+// 256 weight rows x 32 tokens; each wave 64 rows (four 16-row tiles) x the
+// 32 tokens (two 16-token tiles), so every activation fragment read from LDS
+// feeds four products.  K runs in chunks of 256: the chunk's planes are
+// copied into LDS (double-buffered; the next chunk's copies are issued
+// before the current chunk's products), each lane's weight bytes for the
+// next chunk are requested before the current chunk is multiplied and
+// decoded in registers.
 #include <float.h>
 
 #include <algorithm>
@@ -75,14 +79,12 @@ __device__ __forceinline__ h8_t h16_decode(uint32_t w, H16Scale s) {
 }
 
 struct GemmArgs {
-  const uint8_t* wc;  // W codes [N][K/2]
-  const uint8_t* ws;  // W scales [N][K/16]
-  const float* wS;    // W tensor scale
-  const float* x;     // A32: X [T][K]
-  const uint8_t* xc;  // A4: X codes [T][K/2]
-  const uint8_t* xs;  // A4: X scales [T][K/16]
-  const float* xS;    // A4: X tensor scale
-  float* y;           // Y [T][N]
+  const uint8_t* wc;   // W codes [N][K/2]
+  const uint8_t* ws;   // W scales [N][K/16]
+  const float* wS;     // W tensor scale
+  const uint16_t* xp;  // activation planes [P][T][K] fp16 (A32: hi, lo; A4: code x block scale)
+  const float* xS;     // A4: X tensor scale (else null)
+  float* y;            // Y [T][N]
   int N, K, T;
 };
 
@@ -91,61 +93,25 @@ struct GemmArgs {
 // a wave reads for one product fall on different banks
 __device__ __forceinline__ int stage_off(int r, int g) { return r * kGRowBytes + ((g ^ (r & 15)) << 4); }
 
-// Activation staging, thread t: token row t >> 3, values 32 (t & 7) .. +32 of
-// the chunk (groups 4 (t & 7) .. +3).
+// Activation staging: a chunk's P planes (32 token rows x 512 bytes each)
+// are copied buffer-to-LDS, 1 KB (two rows) per wave instruction, into the
+// swizzled layout above: lane L of copy c writes row 2c + L/32, slot L % 32,
+// which holds granule (L % 32) ^ (row % 16).  Rows past T read as zero.
 template <int P>
-struct Stage {
-  float4 v[8];     // A32
-  uint4 c;         // A4 codes
-  uint32_t s;      // A4 scale bytes
+struct PlaneRsrc {  // the activation planes of a token block, one buffer resource each
+  rsrc_t r[P];
+  __device__ __forceinline__ void copy(int K, int kc, unsigned char* buf, int wv, int lane) const {
+    constexpr int kCopies = kGPartBytes / 1024;  // per plane
+#pragma unroll
+    for (int i = 0; i < P * kCopies / 4; ++i) {
+      const int p = 4 * i / kCopies, c = 4 * i % kCopies + wv;  // copy wv + 4 i (kCopies is a multiple of 4)
+      const int row = 2 * c + (lane >> 5), g = (lane & 31) ^ (row & 15);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r[p],
+                                               (__attribute__((address_space(3))) void*)(buf + p * kGPartBytes + c * 1024),
+                                               16, (uint32_t)((row * K + kc + 8 * g) * 2), 0, 0, 0);
+    }
+  }
 };
-
-template <int P>
-__device__ __forceinline__ void stage_load(const GemmArgs& A, int t0, int kc, int tid, Stage<P>& st) {
-  const int r = tid >> 3, seg = tid & 7, tok = t0 + r;
-  if constexpr (P == 2) {
-    if (tok < A.T) {
-      const float4* src = reinterpret_cast<const float4*>(A.x + (size_t)tok * A.K + kc + 32 * seg);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) st.v[i] = src[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) st.v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  } else {
-    if (tok < A.T) {
-      st.c = *reinterpret_cast<const uint4*>(A.xc + (size_t)tok * (A.K / 2) + kc / 2 + 16 * seg);
-      st.s = *reinterpret_cast<const uint16_t*>(A.xs + (size_t)tok * (A.K / 16) + kc / 16 + 2 * seg);
-    } else {
-      st.c = make_uint4(0, 0, 0, 0);
-      st.s = 0;
-    }
-  }
-}
-
-template <int P>
-__device__ __forceinline__ void stage_store(const Stage<P>& st, unsigned char* buf, int tid) {
-  const int r = tid >> 3, seg = tid & 7;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int off = stage_off(r, 4 * seg + u);
-    if constexpr (P == 2) {
-      const float f[8] = {st.v[2 * u].x, st.v[2 * u].y, st.v[2 * u].z, st.v[2 * u].w,
-                          st.v[2 * u + 1].x, st.v[2 * u + 1].y, st.v[2 * u + 1].z, st.v[2 * u + 1].w};
-      h8_t hi, lo;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        hi[e] = (_Float16)f[e];
-        lo[e] = (_Float16)(f[e] - (float)hi[e]);
-      }
-      *reinterpret_cast<h8_t*>(buf + off) = hi;
-      *reinterpret_cast<h8_t*>(buf + kGPartBytes + off) = lo;
-    } else {
-      const uint32_t w = (&st.c.x)[u];
-      *reinterpret_cast<h8_t*>(buf + off) = h16_decode(w, h16_scale((st.s >> (8 * (u >> 1))) & 0xFF));
-    }
-  }
-}
 
 // a lane's weight bytes of one chunk for its row tiles: 64 values
 // (K = kc + 64 q .. +64) of row m of each tile
@@ -163,6 +129,52 @@ __device__ __forceinline__ void wfrag_load(const GemmArgs& A, const int* rows, i
   }
 }
 
+// The products of one 256-wide chunk from its staged planes (buf) and this
+// lane's weight bytes (f).
+template <int P>
+__device__ __forceinline__ void narrow_chunk(const WFrag& f, const unsigned char* buf, int m, int q,
+                                             f4_t (&acc)[kRT][2]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    h8_t b[kRT];
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt)
+      b[rt] = h16_decode((&f.c[rt][j >> 2].x)[j & 3], h16_scale((f.s[rt] >> (8 * (j >> 1))) & 0xFF));
+    const int g = 8 * q + j;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int r = 16 * tt + m;
+      const unsigned char* ap = buf + stage_off(r, g);
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const h8_t a = *reinterpret_cast<const h8_t*>(ap + p * kGPartBytes);
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt)
+          acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[rt], acc[rt][tt], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Iteration c (R = c % 2): chunk c's planes are in sbuf[R] and its weight
+// bytes in f[R]; the next chunk's copies and bytes go to sbuf[1 - R] and
+// f[1 - R] first.  The requests are made unconditionally (past the end the
+// last chunk again, into buffers no one reads any more) and the register
+// sets are not copied, so the compiler's waits before this chunk's products
+// never include the requests just made.  When the chunk count is odd, the
+// second half of the last pair of iterations only makes its requests.
+template <int P, int R>
+__device__ __forceinline__ void narrow_iter(const GemmArgs& A, const PlaneRsrc<P>& rx, const int (&rows)[kRT], int c,
+                                            int nch, unsigned char (&sbuf)[2][P * kGPartBytes], WFrag (&f)[2],
+                                            int wv, int lane, f4_t (&acc)[kRT][2]) {
+  const int m = lane & 15, q = lane >> 4;
+  const int cn = c + 1 < nch ? c + 1 : nch - 1;
+  rx.copy(A.K, cn * kGChunk, sbuf[1 - R], wv, lane);
+  wfrag_load(A, rows, cn * kGChunk, q, f[1 - R]);
+  if (c < nch) narrow_chunk<P>(f[R], sbuf[R], m, q, acc);
+  __syncthreads();  // every wave's copies of the next chunk are in (after the last, every copy has landed)
+}
+
 template <int P>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
   __shared__ __align__(16) unsigned char sbuf[2][P * kGPartBytes];
@@ -178,48 +190,21 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs A) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) acc[rt][tt] = f4_t{0.f, 0.f, 0.f, 0.f};
 
-  Stage<P> st;
-  stage_load<P>(A, t0, 0, tid, st);
-  WFrag cur;
-  wfrag_load(A, rows, 0, q, cur);
-  stage_store<P>(st, sbuf[0], tid);
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const bool more = c + 1 < nch;
-    WFrag nxt;
-    if (more) {
-      stage_load<P>(A, t0, (c + 1) * kGChunk, tid, st);
-      wfrag_load(A, rows, (c + 1) * kGChunk, q, nxt);
-    }
-    const unsigned char* buf = sbuf[c & 1];
+  const int toks_here = A.T - t0 < kGTok ? A.T - t0 : kGTok;
+  PlaneRsrc<P> rx;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      h8_t b[kRT];
-#pragma unroll
-      for (int rt = 0; rt < kRT; ++rt)
-        b[rt] = h16_decode((&cur.c[rt][j >> 2].x)[j & 3], h16_scale((cur.s[rt] >> (8 * (j >> 1))) & 0xFF));
-      const int g = 8 * q + j;
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-        const int r = 16 * tt + m;
-        const unsigned char* ap = buf + stage_off(r, g);
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-          const h8_t a = *reinterpret_cast<const h8_t*>(ap + p * kGPartBytes);
-#pragma unroll
-          for (int rt = 0; rt < kRT; ++rt)
-            acc[rt][tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[rt], acc[rt][tt], 0, 0, 0);
-        }
-      }
-    }
-    if (more) {
-      stage_store<P>(st, sbuf[(c + 1) & 1], tid);
-      cur = nxt;
-    }
-    __syncthreads();
+  for (int p = 0; p < P; ++p) rx.r[p] = make_rsrc(A.xp + ((size_t)p * A.T + t0) * A.K, (uint64_t)toks_here * A.K * 2);
+  WFrag f[2];
+  rx.copy(A.K, 0, sbuf[0], wv, lane);
+  wfrag_load(A, rows, 0, q, f[0]);
+  __syncthreads();  // waits for this wave's copies as well
+  for (int c = 0; c < nch; c += 2) {
+    narrow_iter<P, 0>(A, rx, rows, c, nch, sbuf, f, wv, lane, acc);
+    narrow_iter<P, 1>(A, rx, rows, c + 1, nch, sbuf, f, wv, lane, acc);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the last (unused) requests are in before the workgroup ends
   // lane (m, q) holds tokens 4q .. 4q+3 of each token tile for weight row m
-  const float S = *A.wS * (P == 1 ? *A.xS : 1.0f);
+  const float S = *A.wS * (P == 1 && A.xS ? *A.xS : 1.0f);
 #pragma unroll
   for (int rt = 0; rt < kRT; ++rt) {
     const int n = n0 + 16 * rt + m;
@@ -588,41 +573,39 @@ int32_t flint_nvfp4_gemm(const flint_nvfp4* W, int32_t N, int32_t K, const float
                         reinterpret_cast<uint32_t*>(base + w.amax), s);
     if (e != hipSuccess) return api_hip_fail(e);
   }
+  // the activations as fp16 planes (both kernels stage them with
+  // buffer-to-LDS copies)
+  uint16_t* xp = reinterpret_cast<uint16_t*>(base + w.planes);
+  const size_t n = (size_t)T * K;
+  const int pg = (int)std::min<size_t>((n + 256 * 16 - 1) / (256 * 16), 4096);
+  if (mode == FLINT_GEMM_A4) k_gemm_deq<<<pg, 256, 0, s>>>(xc, xs, n, xp);
+  else k_gemm_split<<<pg, 256, 0, s>>>(X, n, xp);
   const int64_t tiles = (int64_t)((N + kWRows - 1) / kWRows) * ((T + kWTok - 1) / kWTok);
   if (tiles >= kWideMinTiles) {
     WideArgs A{};
     A.wc = W->codes;
     A.ws = W->scales;
     A.wS = W->tscale;
-    A.xp = reinterpret_cast<uint16_t*>(base + w.planes);
+    A.xp = xp;
+    A.xS = mode == FLINT_GEMM_A4 ? xS : nullptr;
     A.y = Y;
     A.N = N;
     A.K = K;
     A.T = T;
-    const size_t n = (size_t)T * K;
-    const int pg = (int)std::min<size_t>((n + 256 * 16 - 1) / (256 * 16), 4096);
     const int grid = (int)((tiles + 7) / 8 * 8);
-    if (mode == FLINT_GEMM_A4) {
-      A.xS = xS;
-      k_gemm_deq<<<pg, 256, 0, s>>>(xc, xs, n, const_cast<uint16_t*>(A.xp));
-      k_gemm_wide<1, 64><<<grid, kWThreads, 0, s>>>(A);
-    } else {
-      k_gemm_split<<<pg, 256, 0, s>>>(X, n, const_cast<uint16_t*>(A.xp));
-      k_gemm_wide<2, 32><<<grid, kWThreads, 0, s>>>(A);
-    }
+    if (mode == FLINT_GEMM_A4) k_gemm_wide<1, 64><<<grid, kWThreads, 0, s>>>(A);
+    else k_gemm_wide<2, 32><<<grid, kWThreads, 0, s>>>(A);
   } else {
     GemmArgs A{};
     A.wc = W->codes;
     A.ws = W->scales;
     A.wS = W->tscale;
-    A.x = X;
+    A.xp = xp;
+    A.xS = mode == FLINT_GEMM_A4 ? xS : nullptr;
     A.y = Y;
     A.N = N;
     A.K = K;
     A.T = T;
-    A.xc = xc;
-    A.xs = xs;
-    A.xS = xS;
     const dim3 grid((N + kGRows - 1) / kGRows, (T + kGTok - 1) / kGTok);
     if (mode == FLINT_GEMM_A4) k_gemm<1><<<grid, 256, 0, s>>>(A);
     else k_gemm<2><<<grid, 256, 0, s>>>(A);
