@@ -191,6 +191,30 @@ struct AttnArgs {
   float* part;  // [n_kv][kMaxGroup][kMaxChunks][kPart]
 };
 
+// The cache rows of sub-chunk s for key/value head g: thread tid loads 16
+// bytes (segment tid & 15) of rows (tid >> 4) + 16 j of the keys and of the
+// values; rows at or past pos are zero.  Positions fit in 32 bits (pos and
+// cap are int32 at the boundary), so the ring slot is a 32-bit remainder;
+// every load is issued whatever the row (a masked row reads slot 0) and the
+// eight are independent, so they are in flight together.
+__device__ __forceinline__ void attn_load_sub(const AttnArgs& A, int g, int tid, int s, uint4 (&kk)[4],
+                                              uint4 (&vv)[4]) {
+  const uint32_t cap = (uint32_t)A.cap, pos = (uint32_t)A.pos;
+  const uint32_t p0 = (uint32_t)A.first + (uint32_t)s * kSub;
+  const size_t head = (size_t)g * (size_t)cap;
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t t = p0 + (uint32_t)(tid >> 4) + 16u * (uint32_t)j;
+    const bool ok = t < pos;
+    const size_t off = (head + (ok ? t : 0u) % cap) * kD + (size_t)(tid & 15) * 8;
+    const uint4 kr = *reinterpret_cast<const uint4*>(A.kc + off);
+    const uint4 vr = *reinterpret_cast<const uint4*>(A.vc + off);
+    kk[j] = ok ? kr : zero;
+    vv[j] = ok ? vr : zero;
+  }
+}
+
 // grid (nchunks, n_kv), 256 threads.  Chunk c covers sub-chunks
 // [c*per, min((c+1)*per, n_sub)) of 64 positions from `first`; the last chunk
 // holds `pos`.  Wave w owns query heads 2w and 2w+1 of the group (a second
@@ -212,22 +236,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs A) {
   // cache rows of one sub-chunk: thread tid loads 16 bytes (segment tid & 15)
   // of rows (tid >> 4) + 16 j; rows at or past pos are zero here
   uint4 kk[4], vv[4];
-  auto load_sub = [&](int s) {
-    const long long p0 = A.first + (long long)s * kSub;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const long long t = p0 + (tid >> 4) + 16 * j;
-      if (t < A.pos) {
-        const long long off = ((long long)g * A.cap + t % A.cap) * kD + (tid & 15) * 8;
-        kk[j] = *reinterpret_cast<const uint4*>(A.kc + off);
-        vv[j] = *reinterpret_cast<const uint4*>(A.vc + off);
-      } else {
-        kk[j] = make_uint4(0, 0, 0, 0);
-        vv[j] = make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  load_sub(s_begin);
+  attn_load_sub(A, g, tid, s_begin, kk, vv);
 
   const float cs = A.rope ? A.rope_cos[lane] : 1.0f, sn = A.rope ? A.rope_sin[lane] : 0.0f;
   const float qscale = 0.08838834764831845f;  // 1 / sqrt(128)
@@ -294,7 +303,7 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs A) {
       sK[r * kKRow + seg * 4 + 2] = kw.z;
       sK[r * kKRow + seg * 4 + 3] = kw.w;
     }
-    if (s + 1 < s_end) load_sub(s + 1);
+    if (s + 1 < s_end) attn_load_sub(A, g, tid, s + 1, kk, vv);
     __syncthreads();
     if (act) {
       // scores of both heads at position t = lane: four independent chains
