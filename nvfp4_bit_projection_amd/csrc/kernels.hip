@@ -355,9 +355,11 @@ __device__ __forceinline__ uint32_t e2m1_rne_code(double v) {
   return c | (signbit(v) ? 8u : 0u);
 }
 
-// amax: four independent 16-byte loads a thread in flight (per_mat is a
-// multiple of 16 and every matrix 64-byte aligned); the maximum does not
-// depend on the order.
+// amax: each thread keeps four independent 16-byte loads in flight per step
+// (per_mat is a multiple of 16 and every matrix 64-byte aligned); the
+// workgroup's maximum is reduced in LDS and published with one atomic, so a
+// matrix sees one atomic per workgroup (one per wave made the atomics on the
+// single word the bottleneck).  The maximum does not depend on the order.
 __global__ __launch_bounds__(256) void k_quant_amax(const float* __restrict__ w, int64_t per_mat,
                                                     uint32_t* __restrict__ amax_bits) {
   const int m = blockIdx.y;
@@ -378,7 +380,11 @@ __global__ __launch_bounds__(256) void k_quant_amax(const float* __restrict__ w,
     mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
   }
   mx = wave_max(mx);
-  if ((threadIdx.x & 63) == 0) atomicMax(&amax_bits[m], __float_as_uint(mx));
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax(&amax_bits[m], __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
 }
 
 __global__ __launch_bounds__(256) void k_quant_pack(const float* __restrict__ w, int64_t rows, int64_t cols,
@@ -500,8 +506,8 @@ hipError_t launch_lmhead(const flint_nvfp4& head, int vocab, const float* x, int
 hipError_t launch_quantize(const float* w, int64_t n_mats, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, float* tscales, uint32_t* amax_bits, hipStream_t s) {
   const int64_t per_mat = rows * cols;
-  int gx = (int)((per_mat + 256 * 16 - 1) / (256 * 16));
-  if (gx > 4096) gx = 4096;
+  int gx = (int)((per_mat + 256 * 64 - 1) / (256 * 64));  // 64 values a thread: fewer workgroups, fewer atomics
+  if (gx > 1024) gx = 1024;
   if (gx < 1) gx = 1;
   for (int64_t m0 = 0; m0 < n_mats; m0 += 65535) {
     const int nm = (int)((n_mats - m0) < 65535 ? (n_mats - m0) : 65535);
