@@ -137,10 +137,16 @@ __global__ __launch_bounds__(64) void k_btopk(const float* __restrict__ logits, 
                                               int32_t* __restrict__ idx, float* __restrict__ wts) {
   const int b = blockIdx.x, lane = threadIdx.x;
   int key[4], id[4];
+  float lv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // all four loads in flight (an index past E reads expert E - 1)
+    const int e = lane + 64 * j;
+    lv[j] = logits[(size_t)b * E + (e < E ? e : E - 1)];
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     id[j] = lane + 64 * j;
-    key[j] = id[j] < E ? ord_key(logits[(size_t)b * E + id[j]]) : INT_MIN;
+    key[j] = id[j] < E ? ord_key(lv[j]) : INT_MIN;
   }
   auto cswap = [&](int a, int c) {
     const bool sw = key[c] > key[a] || (key[c] == key[a] && id[c] < id[a]);
@@ -512,7 +518,10 @@ __global__ __launch_bounds__(kNormThreads) void k_bnorm(float* __restrict__ h, c
     for (int i = 0; i < kHidden / kNormThreads; ++i) {
       const int n = t + i * kNormThreads;
 #pragma unroll
-      for (int sl = 0; sl < kMaxTopK; ++sl) y[i][sl] = sl < k ? dr[((size_t)b * k + sl) * kHidden + n] : 0.0f;
+      for (int sl = 0; sl < kMaxTopK; ++sl) {  // unconditional loads (slot k - 1 again past k), all in flight
+        const float v = dr[((size_t)b * k + (sl < k ? sl : k - 1)) * kHidden + n];
+        y[i][sl] = sl < k ? v : 0.0f;
+      }
       y[i][kMaxTopK] = ds[(size_t)b * kHidden + n];
     }
 #pragma unroll

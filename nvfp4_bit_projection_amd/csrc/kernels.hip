@@ -105,10 +105,17 @@ __global__ __launch_bounds__(64) void k_topk(const float* __restrict__ logits, i
   float v[4];
   int id[4];
 #pragma unroll
+  for (int j = 0; j < 4; ++j) {  // all four loads in flight (an index past E reads expert E - 1)
+    const int e = lane + 64 * j;
+    v[j] = logits[(size_t)b * E + (e < E ? e : E - 1)];
+  }
+#pragma unroll
   for (int j = 0; j < 4; ++j) {
     id[j] = lane + 64 * j;
-    v[j] = (id[j] < E) ? logits[(size_t)b * E + id[j]] : -FLT_MAX;
-    if (id[j] >= E) id[j] = INT_MAX;
+    if (id[j] >= E) {
+      v[j] = -FLT_MAX;
+      id[j] = INT_MAX;
+    }
   }
   float top_v[kMaxTopK];
   int top_i[kMaxTopK];
