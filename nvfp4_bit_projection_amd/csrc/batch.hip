@@ -461,10 +461,10 @@ __device__ __forceinline__ void mm_chunk(const MmRegs& R, const unsigned char* b
 // NCH.  The caller has published srow with a barrier.  The activations are
 // staged segment by segment (a barrier pair each); a lane's weight bytes are
 // requested AHEAD chunks before they are multiplied (the chunk loop is
-// unrolled, so every chunk has its own registers).  From the tiled copy, two
-// chunks ahead suit small grids and one suits many (token, slot) pairs, and
-// so many workgroups (three was slower at B = 8 and 32); from row-major
-// weights three are best at B = 8 and as good at B = 32.
+// unrolled, so every chunk has its own registers).  From the tiled copy two
+// chunks ahead (with the grids sized to each group's rows, better than one
+// at B = 32 and than three at B = 8); from row-major weights three are best
+// at B = 8 and as good at B = 32.
 template <class F, int NCH, class Lay = MmRowMajor, int AHEAD = 2>
 __device__ __forceinline__ void mm_pass_n(const MmTiles& T, rsrc_t rA, int a_rows, const int* srow, int nt,
                                           unsigned char* abuf, int wv, int lane, f32x4_t (&acc)[2][2]) {
@@ -991,7 +991,6 @@ hipError_t launch_batch_step_tiled(const flint_moe_dims& d, const flint_moe_laye
   HeadPartial* parts = reinterpret_cast<HeadPartial*>(base + w.partials);
   const int k = d.top_k, E = d.n_experts, I = d.expert_width, Is = d.shared_width, nb = B * k;
   const int Umax = nb < E ? nb : E;
-  const bool many = nb >= 96;  // tiled weights and many (token, slot) pairs: one chunk ahead, else two
   const int gu_x = (I + kMmGateUpRows - 1) / kMmGateUpRows;  // a routed expert's rows; the shared one spans
   const int gu_sh = (Is + I - 1) / I;                        // gu_sh grid rows
   k_copy_words<<<(B * kHidden + kThreads - 1) / kThreads, kThreads, 0, s>>>(
@@ -1009,10 +1008,7 @@ hipError_t launch_batch_step_tiled(const flint_moe_dims& d, const flint_moe_laye
     k_bucket<<<1, kThreads, 0, s>>>(idx, nb, E, bk);
     const uint8_t* lt = tiles ? tiles + (size_t)l * batch_tiles_layer_bytes(d) : nullptr;
     const dim3 gg(gu_x, gu_sh + Umax), gd(kHidden / kMmRows, Umax + 1);
-    if (tiles && many) {
-      k_mm_gateup<true, 1><<<gg, kMmThreads, 0, s>>>(Ly, I, Is, k, B, Umax, up, bk, hrp, hsp, nb, lt, E);
-      k_mm_down<true, 1><<<gd, kMmThreads, 0, s>>>(Ly, I, Is, B, Umax, hrp, hsp, bk, wts, dr, ds, nb, lt, E);
-    } else if (tiles) {
+    if (tiles) {  // tiled weights: two chunks ahead (with the current grids at every B; three is slower at B = 8)
       k_mm_gateup<true, 2><<<gg, kMmThreads, 0, s>>>(Ly, I, Is, k, B, Umax, up, bk, hrp, hsp, nb, lt, E);
       k_mm_down<true, 2><<<gd, kMmThreads, 0, s>>>(Ly, I, Is, B, Umax, hrp, hsp, bk, wts, dr, ds, nb, lt, E);
     } else {  // row-major weights: longer load latency, three chunks ahead
