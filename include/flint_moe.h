@@ -337,8 +337,12 @@ int32_t flint_stack_decode_batch_tiled(const flint_stack_plan* plan /*[host]*/, 
                                        void* ws, size_t ws_bytes, void* stream);
 
 /* Stack workspace contract: zero-filled before the first call; afterwards it
- * carries the persistent schedule's epoch counter and must not be changed
- * between calls.  Every wait inside the persistent kernel is bounded; if one
+ * carries the persistent schedule's epoch counter and the placement phase of
+ * its logit exchange, and must not be changed between calls.  The first call
+ * on a zeroed workspace measures that phase (a few microseconds: one
+ * workgroup times device-scope stores to blocks of the exchange area, which
+ * the chip serves from its nearer or farther half depending on the address);
+ * the phase affects speed only, never results.  Every wait inside the persistent kernel is bounded; if one
  * gives up (a fault elsewhere), the kernel raises a flag in the workspace and
  * returns, and later calls on that workspace do nothing until it is zeroed
  * again.  flint_stack_error synchronously copies that flag to *error [host]

@@ -324,6 +324,38 @@ def test_stack_schedules_agree_and_repeat(F):
         assert_close(out["persistent"][0][t], out["kernels"][0][t], "schedules")
 
 
+def test_stack_exchange_phase_placement_only(F):
+    """The first persistent call on a zeroed workspace measures the placement
+    phase of its logit exchange and keeps it in the third control word (1 or
+    2).  The phase only decides where the logit copies live: forcing the
+    other phase, or clearing the word so that the next call measures it
+    again, gives bit-identical logits, routes and argmax."""
+    flint, workload = F
+    dims = synth.MoEDims()
+    L, V, T = 3, 4099, 3
+    layers = [workload.build_layer(dims, seed=40 + l) for l in range(L)]
+    head = workload.build_head(V, dims.hidden)
+    x = workload.tokens(range(700, 700 + T), dims.hidden)
+    st = flint.Stack(dims_struct(F, dims), layers, head, V, schedule=2)
+    ctrl = st.ws[:16].view(torch.int32)
+
+    def run():
+        r = torch.zeros((T, L, dims.top_k), dtype=torch.int32, device="cuda")
+        lg, am = st.decode(x, routes=r)
+        torch.cuda.synchronize()
+        assert st.error() == 0
+        return lg.cpu(), am.cpu(), r.cpu()
+
+    ref = run()
+    phase = int(ctrl[2])
+    assert phase in (1, 2)
+    for forced in (3 - phase, 0):
+        ctrl[2] = forced
+        got = run()
+        assert all(torch.equal(a, b) for a, b in zip(got, ref)), forced
+        assert int(ctrl[2]) in ((forced,) if forced else (1, 2))
+
+
 # The benchmarked shape (47 layers of 256 experts, the 150,144-row head):
 # four tokens decoded in one persistent launch, each compared with its own
 # oracle run in a test of its own (an oracle token at this size takes about
