@@ -621,3 +621,17 @@ def test_stack_error_flag_stops_calls(F):
     stack.decode(x, argmax=am, want_logits=False)
     torch.cuda.synchronize()
     assert stack.error() == 0 and torch.equal(am, good)
+
+
+@pytest.mark.parametrize("nbytes", [16, 8192 + 48, 256 * 8 * 8192 + 8192 * 3 + 16])
+def test_stream_read_sizes(F, nbytes):
+    """The streaming-read probe on sizes below one 8 KB piece, with a partial
+    piece, and past whole rounds of eight pieces a workgroup: it returns
+    without error and writes nothing on zero data (its fold of every word is
+    zero, never the key)."""
+    flint, _ = F
+    buf = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+    out = torch.full((2,), 7, dtype=torch.int32, device="cuda")
+    flint.stream_read(buf, out)
+    torch.cuda.synchronize()
+    assert out.tolist() == [7, 7]
