@@ -252,16 +252,20 @@ int32_t flint_stack_decode(const flint_stack_plan* plan /*[host]*/, const float*
 /* Profiling variant of flint_stack_decode for the persistent schedule: also
  * writes, for the first token, device wall-clock stamps (100 MHz ticks) of
  * the phase boundaries of two workgroups (one on the first XCD, one on the
- * last) into trace, int64 [2][L+1][16], followed by the stamps of layer 1 of
- * all 256 workgroups, int64 [256][16].  Per layer l, seen by the first
- * polling wave: 0 layer start, 1 norm done, 2 logits arrived, 3 every pick
- * of the top k published, 4 its routed pairs stored, 5 hidden slice arrived,
- * 6 partial outputs arrived, 7 new residual arrived, 15 routing weights
- * computed; seen by the
- * first loading wave: 8 router logit stored, 9 shared pair stored, 11 routed
- * phase started, 12 its routed pair stored, 13 partial outputs stored and
- * the next layer's rows requested, 14 residual rows stored; 10 is unused
- * (0).  Row L holds the head start, the head rows done, the head partials
+ * last) into trace, int64 [2][L+1][32], followed by the stamps of layer 1 of
+ * all 256 workgroups, int64 [256][32].  Per layer l, seen by the first
+ * polling wave: 0 layer start, 1 norm done, 2 logits arrived, 16 its keys
+ * sorted, 17 first pick published, 18 last round done, 3 every pick of the
+ * top k published, 4 its routed pairs stored, 5 hidden slice arrived,
+ * 28 its partial outputs stored, 6 partial outputs arrived, 7 new residual
+ * arrived, 15 routing weights computed; seen by the second polling wave: 23 / 25 the pick of its first /
+ * second pair known, 24 / 26 that pair requested, 27 its pairs stored; seen
+ * by the first loading wave: 8 router logit stored, 9 shared pair stored, 11
+ * routed phase started, 19 the pick of its pair known, 20 its pair
+ * requested, 21 every pick known, 22 down-projection operands requested, 12
+ * its routed pair stored, 29 its partial outputs stored, 13 the next layer's
+ * rows requested, 14 residual rows stored; 10, 30 and 31 are unused (0).
+ * Row L holds the head start, the head rows done, the head partials
  * arrived, the kernel entry and the end of the kernel's set-up.  Returns
  * FLINT_E_UNSUPPORTED for the kernel-sequence schedule and for more than 64
  * layers. */

@@ -122,7 +122,7 @@ struct StackParams {
 // exchange cannot finish before every workgroup has read x.
 static_assert(kGroupWGs * 64 == kHidden, "every workgroup owns 64 rows of the partial outputs");
 
-constexpr int kTracePoints = 16;
+constexpr int kTracePoints = 32;
 constexpr int kTraceMaxLayers = kMaxStackLayers;
 
 // Exchange scopes.  Values that cross XCDs are stored with device-scope
@@ -274,11 +274,10 @@ struct StackLds {
   float hp[2 * kStackWGs];                           // head partials (max, index)
   float red[kStackWaves];
   float w[kMaxTopK];
-  int32_t idx[kMaxTopK];
+  int32_t pk[kMaxTopK];                              // picks of phase B: (layer tag << 8) | expert
   float bv[kStackWaves];
   int32_t bi[kStackWaves];
   int32_t bad;
-  int32_t nk;                                        // top-k picks published (phase B)
   uint32_t ctl[3];                                   // control words read at the start
   uint64_t tab[kMaxStackLayers * kLayerWords + 3];   // layer table, then the head
   int64_t tr[(kTraceMaxLayers + 1) * kTracePoints];  // phase stamps of the first token
@@ -404,20 +403,32 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
     uint32_t sg, su;
     float Sg, Su;
   };
-  auto load_pair = [&](int w0, int p) {
-    const int p_ = p < nroutedx ? p : 0;
-    const int slot = p_ / Ix, rl = p_ % Ix;
-    const int e = S.idx[slot];
-    const uint32_t row = (uint32_t)(e * I + g * Ix + rl);
+  // The layer's routed gate/up buffers, set up before the picks are known so
+  // that a pick is followed by its loads at once.
+  struct PairRs {
+    rsrc_t gc, uc, gs, us, ts;
+  };
+  auto pair_rs = [&](int w0) {
     const uint64_t nc = (uint64_t)E * I * kHidden / 2, ns = (uint64_t)E * I * kHidden / 16;
-    const rsrc_t rts = make_rsrc(tab_ptr<const float>(S, w0 + kWExpTs), (uint64_t)E * 3 * 4);
+    PairRs r;
+    r.gc = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWGateC), nc);
+    r.uc = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWUpC), nc);
+    r.gs = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWGateS), ns);
+    r.us = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWUpS), ns);
+    r.ts = make_rsrc(tab_ptr<const float>(S, w0 + kWExpTs), (uint64_t)E * 3 * 4);
+    return r;
+  };
+  // pair p of this group's slice of expert e (the pick of slot p / Ix)
+  auto load_pair = [&](const PairRs& R, int p, int e) {
+    const int rl = (p < nroutedx ? p : 0) % Ix;
+    const uint32_t row = (uint32_t)(e * I + g * Ix + rl);
     PairOps o;
-    o.cg = bload_u4_nt(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWGateC), nc), row * (kHidden / 2) + 16 * lane);
-    o.cu = bload_u4_nt(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWUpC), nc), row * (kHidden / 2) + 16 * lane);
-    o.sg = bload_u16_nt(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWGateS), ns), row * (kHidden / 16) + 2 * lane);
-    o.su = bload_u16_nt(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWUpS), ns), row * (kHidden / 16) + 2 * lane);
-    o.Sg = bload_f32(rts, (uint32_t)(3 * e + 0) * 4);
-    o.Su = bload_f32(rts, (uint32_t)(3 * e + 1) * 4);
+    o.cg = bload_u4_nt(R.gc, row * (kHidden / 2) + 16 * lane);
+    o.cu = bload_u4_nt(R.uc, row * (kHidden / 2) + 16 * lane);
+    o.sg = bload_u16_nt(R.gs, row * (kHidden / 16) + 2 * lane);
+    o.su = bload_u16_nt(R.us, row * (kHidden / 16) + 2 * lane);
+    o.Sg = bload_f32(R.ts, (uint32_t)(3 * e + 0) * 4);
+    o.Su = bload_f32(R.ts, (uint32_t)(3 * e + 1) * 4);
     return o;
   };
   // ... and the SwiGLU value g(x) * u(x) with g = silu(gate . x)
@@ -471,29 +482,34 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       }
       // ---------------------------------------------------------- phase B
       // The first communication wave gathers the E logits and takes the top
-      // k.  It publishes each pick in LDS as soon as its round ends (S.idx[r],
-      // then the count S.nk), and every other wave requests the gate/up rows
-      // of its pairs as soon as their expert is known, so the routed loads
-      // overlap the remaining rounds; the first wave takes the pairs of the
-      // last pick.  Routed gate/up pairs p = li + 32 q of this group's slice:
-      // q = 2 (wv - 1) + {0, 1} for communication waves 1-3, q = 6 + lw for a
-      // loading wave, q = 10 + {0, 1} for the first wave.
-      const int nk0 = (tok * L + l) * kMaxTopK;  // S.nk = nk0 + picks published in this layer
-      auto wait_picks = [&](int need) {
+      // k.  It publishes each pick in LDS as soon as its round ends (S.pk[r]:
+      // this layer's tag and the expert in one word, written by the lane that
+      // held the pick), and every other wave requests the gate/up rows of its
+      // pairs as soon as their expert is known, so the routed loads overlap
+      // the remaining rounds; the first wave takes the pairs of the last pick.
+      // Routed gate/up pairs p = li + 32 q of this group's slice: q = 2 (wv -
+      // 1) + {0, 1} for communication waves 1-3, q = 6 + lw for a loading
+      // wave, q = 10 + {0, 1} for the first wave.
+      // 24-bit tag of this (token, layer), never 0 (0 marks no layer); a slot
+      // is rewritten every layer, so a stale word never carries this tag
+      const uint32_t tag = ((uint32_t)(tok * L + l) % 0xFFFFFFu) + 1u;
+      // expert of pick r once it is published (S.bad and expert 0 on time-out)
+      auto wait_pick = [&](int r) {
         uint32_t spins = 0;
-        while (__hip_atomic_load(&S.nk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < nk0 + need) {
+        uint32_t v;
+        while (((v = (uint32_t)__hip_atomic_load(&S.pk[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) >> 8) !=
+               tag) {
           if (++spins > wc.limit) {
             S.bad = 1;
+            v = 0;
             break;
           }
           __builtin_amdgcn_s_sleep(1);
         }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        return __builtin_amdgcn_readfirstlane((int)(v & 0xFFu));
       };
-      auto publish_picks = [&](int n) {
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (lane == 0) __hip_atomic_store(&S.nk, nk0 + n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      };
+      const PairRs prs = pair_rs(w0);
       constexpr int kNq = kComm ? kGateUpComm : 1;
       int pq[kNq];
 #pragma unroll
@@ -534,7 +550,7 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
         const rsrc_t rdc = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWDownC), (uint64_t)E * kHidden * I / 2);
         const rsrc_t rds = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWDownS), (uint64_t)E * kHidden * I / 16);
         const int doff = routed ? (32 * j) % Ix : 0;  // column in the expert's slice
-        const int de = S.idx[dslot];
+        const int de = S.pk[dslot] & 0xFF;
         const uint32_t rslice = (uint32_t)((de * kGroups + g) * kHidden);
         const uint32_t oob_c = (uint32_t)((uint64_t)E * kHidden * I / 2);
 #pragma unroll
@@ -582,37 +598,43 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
           c4[i0] = hi; c4[i1] = lo;
         };
         cx(0, 1); cx(2, 3); cx(0, 2); cx(1, 3); cx(1, 2);
+        FLINT_TRACE(l, 16);
         // k rounds: the wave maximum of the lanes' first keys (upper halves)
         // and, by a ballot, the lowest lane holding it; lanes cover the
         // experts in increasing order and each lane's first key is its lowest
         // index among equal logits, so that lane holds the lowest index.  The
-        // winning lane drops its first key.  Lane r keeps the r-th key.
+        // winning lane publishes its expert (all but the last pick) and drops
+        // its first key.  Lane r keeps the r-th key.
         int my_key = INT_MIN;
+        int popped = 0;  // expert of the key this lane dropped last
+        int lwin = 0;    // winning lane of the last round
         for (int r = 0; r < k; ++r) {
           const int head = (int)(c4[0] >> 32);
           const int m = wave_max_i32_s(head);
-          const int lmax = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(head == m));
-          const int low = __builtin_amdgcn_readlane((int)(uint32_t)c4[0], lmax);
+          lwin = (int)__builtin_ctzll(__builtin_amdgcn_ballot_w64(head == m));
           my_key = lane == r ? m : my_key;
-          const bool win = lane == lmax;
+          const bool win = lane == lwin;
+          const int e = kMaxExperts - 1 - (int)(uint32_t)c4[0];
+          if (win && r + 1 < k)
+            __hip_atomic_store(&S.pk[r], (int)((tag << 8) | (uint32_t)e), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+          popped = win ? e : popped;
           c4[0] = win ? c4[1] : c4[0];
           c4[1] = win ? c4[2] : c4[1];
           c4[2] = win ? c4[3] : c4[2];
           c4[3] = win ? (int64_t)((uint64_t)(uint32_t)INT_MIN << 32) : c4[3];
-          // pick r, then the count of picks published (the last pick is
-          // counted only after this wave has requested its own pairs)
-          const int np = r + 1 < k ? r + 1 : r;
-          if (lane == 0) {
-            S.idx[r] = kMaxExperts - 1 - low;
-            __atomic_signal_fence(__ATOMIC_SEQ_CST);
-            __hip_atomic_store(&S.nk, nk0 + np, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          }
+          if (r == 0) FLINT_TRACE(l, 17);
         }
-        // this wave's own pairs (the last pick is in S.idx), then every pick
-        // is published
+        FLINT_TRACE(l, 18);
+        // this wave's own pairs (of the last pick), then the last pick is
+        // published: the other waves' down-projection requests follow them
+        const int elast = __builtin_amdgcn_readlane(popped, lwin);
 #pragma unroll
-        for (int pp = 0; pp < kNq; ++pp) o[pp] = load_pair(w0, pq[pp]);
-        publish_picks(k);
+        for (int pp = 0; pp < kNq; ++pp) o[pp] = load_pair(prs, pq[pp], elast);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0)
+          __hip_atomic_store(&S.pk[k - 1], (int)((tag << 8) | (uint32_t)elast), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_WORKGROUP);
         FLINT_TRACE(l, 3);
         load_down_shared();
         load_down_routed();
@@ -628,16 +650,22 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
         if constexpr (!kComm) FLINT_TRACE_LOAD(l, 11);
 #pragma unroll
         for (int pp = 0; pp < kNq; ++pp) {
-          wait_picks((pq[pp] < nroutedx ? pq[pp] / Ix : 0) + 1);
-          o[pp] = load_pair(w0, pq[pp]);
+          const int e = wait_pick(pq[pp] < nroutedx ? pq[pp] / Ix : 0);
+          FLINT_TRACE_AT(64, l, 23 + 2 * pp);
+          FLINT_TRACE_LOAD(l, 19);
+          o[pp] = load_pair(prs, pq[pp], e);
+          FLINT_TRACE_AT(64, l, 24 + 2 * pp);
+          FLINT_TRACE_LOAD(l, 20);
         }
-        wait_picks(k);
+        wait_pick(k - 1);
+        FLINT_TRACE_LOAD(l, 21);
         if constexpr (!kComm) {
           if (P.routes && blockIdx.x == 0 && t - kCommThreads < k)
-            P.routes[((size_t)tok * L + l) * k + (t - kCommThreads)] = S.idx[t - kCommThreads];
+            P.routes[((size_t)tok * L + l) * k + (t - kCommThreads)] = S.pk[t - kCommThreads] & 0xFF;
         }
         load_down_shared();
         load_down_routed();
+        FLINT_TRACE_LOAD(l, 22);
       }
       stress_delay<kStress>(P, tok, l, 2);
 #pragma unroll
@@ -647,6 +675,7 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
           if (lane == 0) put_pair<Scope::kXcd>(&s3[pq[pp]], hval, ep0 + 1);
         }
       }
+      FLINT_TRACE_AT(64, l, 27);
       if constexpr (kComm) {
         FLINT_TRACE(l, 4);
         poll_pairs<Scope::kXcd>(s3, kSliceK, ep0 + 1, S.hs, wc, true);
@@ -672,6 +701,8 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
           if (j == 0) put_pair<Scope::kDevice>(&s4a[(size_t)g * kHidden + n], acc, ep0 + 2);
         }
       }
+      FLINT_TRACE(l, 28);
+      FLINT_TRACE_LOAD(l, 29);
       if constexpr (kComm) {
         // rows 64 li .. 64 li + 63 of every group's partial output
         __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(s4a, 0, kGroups * kHidden * 8, 0x00020000);
@@ -920,9 +951,9 @@ __global__ __launch_bounds__(kStackThreads, 1) void k_stack_decode(StackParams P
     const uint64_t* hsrc = reinterpret_cast<const uint64_t*>(&table->head);
     if (C.t < 3) S.tab[kMaxStackLayers * kLayerWords + C.t] = hsrc[C.t];
   }
+  if (C.t < kMaxTopK) S.pk[C.t] = 0;  // tag 0: no layer
   if (C.t == 0) {
     S.bad = 0;
-    S.nk = 0;
     // control words [0] epoch base, [1] error flag, [2] logit-area phase, in
     // one device-scope load
     const auto cw = __builtin_amdgcn_raw_buffer_load_b128(__builtin_amdgcn_make_buffer_rsrc(P.ctrl, 0, 16, 0x00020000),

@@ -72,7 +72,7 @@ class INT4(ctypes.Structure):
     _fields_ = [("codes", _P), ("scales", _P), ("biases", _P)]
 
 
-TRACE_POINTS = 16  # stamps per layer of flint_stack_decode_traced
+TRACE_POINTS = 32  # stamps per layer of flint_stack_decode_traced
 SCHEDULE_AUTO, SCHEDULE_KERNELS, SCHEDULE_PERSISTENT = 0, 1, 2
 
 
