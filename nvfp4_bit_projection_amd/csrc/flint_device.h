@@ -42,6 +42,15 @@ __device__ __forceinline__ float4 bload_f4(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ float bload_f32(rsrc_t r, uint32_t off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
+// Scalar load of read-only data at a wave-uniform address (through the
+// constant address space, so the compiler emits a scalar-memory load): for
+// per-matrix values such as tensor scales, which then take no slot of the
+// vector-memory pipeline.  The data must not be written while a kernel that
+// reads it runs (the scalar cache is not kept coherent with vector stores).
+typedef __attribute__((address_space(4))) const float const_f32;
+__device__ __forceinline__ float sload_f32(const float* p, uint32_t i) {
+  return ((const_f32*)p)[i];
+}
 // Streaming variants (non-temporal: the weights are read once per token and
 // not kept in the caches), about 10% more HBM bandwidth on long streams.
 constexpr int kAuxNT = 2;

@@ -56,6 +56,7 @@ constexpr int kSliceK = 512;            // k * (I/8) + Is/8: one group's slice o
 constexpr int kHeadRowsPerWave = 8;
 constexpr int kCommWaves = 4;                      // waves that poll the exchanges
 constexpr int kCommThreads = kCommWaves * 64;
+static_assert(kStackWaves - kCommWaves == 4, "the router logit sums four partial dot products, one per loading wave");
 constexpr int kGateUpComm = 2;                     // routed gate/up pairs per communication wave
 constexpr int kDownPasses = 2;                     // 4-row down-projection passes of every wave
 constexpr uint32_t kSpinLimit = 1u << 22;
@@ -234,8 +235,11 @@ __device__ __forceinline__ void lds_x32(const float* src, float* xv) {
   }
 }
 
-// RMSNorm scale of h (kHidden values) -> u = s * h (padded rows); two barriers
-__device__ __forceinline__ void rms_to_u(const float* h, float* u, float* red, float eps) {
+// RMSNorm scale s of h (kHidden values) -> u = s * h (padded rows); two
+// barriers.  on_scale(s) runs in every wave as soon as s is known, before u
+// is written.
+template <class F>
+__device__ __forceinline__ void rms_to_u(const float* h, float* u, float* red, float eps, F&& on_scale) {
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   float v[kHidden / kStackThreads];
   float ss = 0.0f;
@@ -251,9 +255,13 @@ __device__ __forceinline__ void rms_to_u(const float* h, float* u, float* red, f
 #pragma unroll
   for (int i = 0; i < kStackWaves; ++i) tot += red[i];
   const float s = 1.0f / sqrtf(tot * (1.0f / kHidden) + eps);
+  on_scale(s);
 #pragma unroll
   for (int i = 0; i < kHidden / kStackThreads; ++i) u[padded(t + i * kStackThreads)] = v[i] * s;
   wg_barrier();
+}
+__device__ __forceinline__ void rms_to_u(const float* h, float* u, float* red, float eps) {
+  rms_to_u(h, u, red, eps, [](float) {});
 }
 
 // The layer table (device pointers) is copied to LDS at the start, so that a
@@ -273,6 +281,7 @@ struct StackLds {
   float part[kGroups * 64];                          // the 8 partial outputs of this workgroup's rows
   float hp[2 * kStackWGs];                           // head partials (max, index)
   float red[kStackWaves];
+  float rp[kStackWaves - kCommWaves];                // router logit: one partial dot per loading wave
   float w[kMaxTopK];
   int32_t pk[kMaxTopK];                              // picks of phase B: (layer tag << 8) | expert
   float bv[kStackWaves];
@@ -358,37 +367,48 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
   // the roles inside each XCD, and with them the rows
   const int rrow = kStress ? g + kGroups * li : (int)blockIdx.x;
   const int qa = li + kGroupWGs * lw;
-  float4 wr[kHidden / 256];
+  // the loading waves split the router row: wave lw holds columns
+  // 512 lw .. 512 lw + 511
+  constexpr int kRouterCols = kHidden / (kStackWaves - kCommWaves);
+  float4 wr[kRouterCols / 256];
   uint4 cgs = make_uint4(0, 0, 0, 0), cus = make_uint4(0, 0, 0, 0);
   uint32_t sgs = 0, sus = 0;
   float tgs = 0.0f, tus = 0.0f;
   bool have_a = false;  // this layer's phase-A operands were requested earlier
-  auto load_phase_a = [&](int lx) {
+  // Every loading wave issues the same loads, with no branch around them, so
+  // that the wait counts for data requested before them are exact (a branch
+  // join makes the compiler wait as if the longer path had been taken).
+  // live false (no next layer in this call): the buffers get a size of 0, so
+  // the loads return zeros and touch no memory.
+  auto load_phase_a = [&](int lx, bool live) {
     const int w0 = lx * kLayerWords;
-    if (lw == 0) {
-      const rsrc_t rr = make_rsrc(tab_ptr<const float>(S, w0 + kWRouter), (uint64_t)E * kHidden * 4);
-      const uint32_t r0 = rrow < E ? (uint32_t)rrow : 0u;
+    const rsrc_t rr =
+        make_rsrc(tab_ptr<const float>(S, w0 + kWRouter), live && rrow < E ? (uint64_t)E * kHidden * 4 : 0);
+    const uint32_t r0 = rrow < E ? (uint32_t)rrow : 0u;
 #pragma unroll
-      for (int i = 0; i < kHidden / 256; ++i) wr[i] = bload_f4_nt(rr, (r0 * kHidden + 256 * i) * 4 + 16 * lane);
-    }
+    for (int i = 0; i < kRouterCols / 256; ++i)
+      wr[i] = bload_f4_nt(rr, (r0 * kHidden + kRouterCols * lw + 256 * i) * 4 + 16 * lane);
     const uint32_t row = (uint32_t)(g * Isx + (qa < Isx ? qa : 0));
-    const uint64_t nc = (uint64_t)Is * kHidden / 2, ns = (uint64_t)Is * kHidden / 16;
+    const uint64_t nc = live ? (uint64_t)Is * kHidden / 2 : 0, ns = live ? (uint64_t)Is * kHidden / 16 : 0;
     cgs = bload_u4_nt(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSgC), nc), row * (kHidden / 2) + 16 * lane);
     sgs = bload_u16_nt(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSgS), ns), row * (kHidden / 16) + 2 * lane);
     cus = bload_u4_nt(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSuC), nc), row * (kHidden / 2) + 16 * lane);
     sus = bload_u16_nt(make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSuS), ns), row * (kHidden / 16) + 2 * lane);
-    tgs = bload_f32(make_rsrc(tab_ptr<const float>(S, w0 + kWSgT), 4), 0);
-    tus = bload_f32(make_rsrc(tab_ptr<const float>(S, w0 + kWSuT), 4), 0);
+    tgs = sload_f32(tab_ptr<const float>(S, w0 + kWSgT), 0);
+    tus = sload_f32(tab_ptr<const float>(S, w0 + kWSuT), 0);
   };
-  // router row (registers) . normalised activations: lane i takes columns
-  // 256 c + 4 i .. 256 c + 4 i + 3, c = 0..7
+  // this wave's part of router row . residual (before the norm; the logit
+  // is the sum of the parts times the norm's scale, since the norm scales
+  // every value alike): lane i takes columns 512 lw + 256 c + 4 i ..
+  // 512 lw + 256 c + 4 i + 3, c = 0, 1
   auto router_dot = [&]() {
-    float4 u[kHidden / 256];
+    float4 u[kRouterCols / 256];
 #pragma unroll
-    for (int c = 0; c < kHidden / 256; ++c) u[c] = *reinterpret_cast<const float4*>(S.u + padded(256 * c + 4 * lane));
+    for (int c = 0; c < kRouterCols / 256; ++c)
+      u[c] = *reinterpret_cast<const float4*>(S.h + kRouterCols * lw + 256 * c + 4 * lane);
     float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;  // four chains for latency
 #pragma unroll
-    for (int c = 0; c < kHidden / 256; ++c) {
+    for (int c = 0; c < kRouterCols / 256; ++c) {
       a0 = __builtin_fmaf(wr[c].x, u[c].x, a0);
       a1 = __builtin_fmaf(wr[c].y, u[c].y, a1);
       a2 = __builtin_fmaf(wr[c].z, u[c].z, a2);
@@ -406,7 +426,8 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
   // The layer's routed gate/up buffers, set up before the picks are known so
   // that a pick is followed by its loads at once.
   struct PairRs {
-    rsrc_t gc, uc, gs, us, ts;
+    rsrc_t gc, uc, gs, us;
+    const float* ts;  // expert tensor scales [E][3] (gate, up, down)
   };
   auto pair_rs = [&](int w0) {
     const uint64_t nc = (uint64_t)E * I * kHidden / 2, ns = (uint64_t)E * I * kHidden / 16;
@@ -415,7 +436,7 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
     r.uc = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWUpC), nc);
     r.gs = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWGateS), ns);
     r.us = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWUpS), ns);
-    r.ts = make_rsrc(tab_ptr<const float>(S, w0 + kWExpTs), (uint64_t)E * 3 * 4);
+    r.ts = tab_ptr<const float>(S, w0 + kWExpTs);
     return r;
   };
   // pair p of this group's slice of expert e (the pick of slot p / Ix)
@@ -427,8 +448,10 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
     o.cu = bload_u4_nt(R.uc, row * (kHidden / 2) + 16 * lane);
     o.sg = bload_u16_nt(R.gs, row * (kHidden / 16) + 2 * lane);
     o.su = bload_u16_nt(R.us, row * (kHidden / 16) + 2 * lane);
-    o.Sg = bload_f32(R.ts, (uint32_t)(3 * e + 0) * 4);
-    o.Su = bload_f32(R.ts, (uint32_t)(3 * e + 1) * 4);
+    // (vector loads: a scalar load here would make the wave's next LDS wait
+    // also wait for it)
+    o.Sg = sload_f32(R.ts, (uint32_t)(3 * e + 0));
+    o.Su = sload_f32(R.ts, (uint32_t)(3 * e + 1));
     return o;
   };
   // ... and the SwiGLU value g(x) * u(x) with g = silu(gate . x)
@@ -457,21 +480,32 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       // ---------------------------------------------------------- phase A
       FLINT_TRACE(l, 0);
       if (!kComm && !have_a) {
-        load_phase_a(l);
+        load_phase_a(l, true);
       }
-      rms_to_u(S.h, S.u, S.red, P.eps);  // B1, B2
+      // router logit rrow = (router row . residual) * the norm's scale: the
+      // loading waves' partial dot products go to LDS before the norm's
+      // first barrier, and the first loading wave stores their sum times the
+      // scale into the logit exchange of every group as soon as the scale is
+      // known
+      if constexpr (!kComm) {
+        const float part = router_dot();
+        if (lane == 0) S.rp[lw] = part;
+      }
+      const bool rwave = !kComm && lw == 0 && rrow < E;  // uniform
+      rms_to_u(S.h, S.u, S.red, P.eps, [&](float sc) {  // B1, B2
+        if (rwave) {
+          stress_delay<kStress>(P, tok, l, 0);
+          const float racc = (S.rp[0] + S.rp[1]) + (S.rp[2] + S.rp[3]);
+          if (lane < kGroups)
+            put_pair<Scope::kDevice>(reinterpret_cast<uint64_t*>(P.s2 + s2_off(par, lane, rrow, C.phase)), racc * sc,
+                                     ep0);
+          FLINT_TRACE_LOAD(l, 8);
+        }
+      });
       FLINT_TRACE(l, 1);
       float xv[32];  // this lane's 32 normalised activations (phases A and B)
       lds_x32(S.u + kRowPad * lane, xv);
-      // router logit rrow, stored into the logit exchange of every group
-      stress_delay<kStress>(P, tok, l, 0);
-      if (!kComm && lw == 0 && rrow < E) {
-        const float acc = router_dot();
-        if (lane < kGroups)
-          put_pair<Scope::kDevice>(reinterpret_cast<uint64_t*>(P.s2 + s2_off(par, lane, rrow, C.phase)), acc, ep0);
-      }
       if constexpr (!kComm) {
-        FLINT_TRACE_LOAD(l, 8);
         stress_delay<kStress>(P, tok, l, 1);
         if (qa < Isx) {
           const float gv = wave_sum(nvfp4_lane_dot32(cgs, sgs, xv)) * tgs;
@@ -524,43 +558,36 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       const int j = lane & 15;
       const bool routed = 32 * j < nroutedx;
       const int dslot = routed ? (32 * j) / Ix : 0;
-      uint4 cdr[kDownPasses], cds[kDownPasses];
-      uint32_t sdr[kDownPasses], sds[kDownPasses];
-      float dts = 0.0f, sts = 0.0f;
-      // column-sliced layouts (packed at prepare time): routed [E][8][H][Ix],
-      // shared [8][H][Isx], codes 2 per byte, one scale byte per 16 columns.
-      // Every lane issues both kinds of loads; the one that is not its own
-      // reads past the end of its buffer, which returns zeros and touches no
-      // memory, so the two combine with an OR and no branch is needed.
-      auto load_down_shared = [&]() {
-        const rsrc_t rsdc = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSdC), (uint64_t)kHidden * Is / 2);
-        const rsrc_t rsds = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWSdS), (uint64_t)kHidden * Is / 16);
-        const int scol = routed ? 0 : 32 * j - nroutedx;  // column in the shared slice
-        const uint32_t sslice = (uint32_t)(g * kHidden);
-        const uint32_t oob_s = (uint32_t)((uint64_t)kHidden * Is / 2);
-#pragma unroll
-        for (int pc = 0; pc < kDownPasses; ++pc) {
-          const uint32_t sr = sslice + (uint32_t)(64 * li + 8 * wv + 4 * pc + (lane >> 4));
-          cds[pc] = bload_u4_nt(rsdc, routed ? oob_s : sr * (Isx / 2) + scol / 2);
-          sds[pc] = bload_u16_nt(rsds, routed ? oob_s / 8 : sr * (Isx / 16) + scol / 16);
-        }
-        sts = bload_f32(make_rsrc(tab_ptr<const float>(S, w0 + kWSdT), 4), 0);
-      };
-      auto load_down_routed = [&]() {
-        const rsrc_t rdc = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWDownC), (uint64_t)E * kHidden * I / 2);
-        const rsrc_t rds = make_rsrc(tab_ptr<const uint8_t>(S, w0 + kWDownS), (uint64_t)E * kHidden * I / 16);
-        const int doff = routed ? (32 * j) % Ix : 0;  // column in the expert's slice
+      uint4 cd[kDownPasses];
+      uint32_t sd[kDownPasses];
+      float sts = 0.0f;
+      // Column-sliced layouts (packed at prepare time, one block per layer in
+      // the order routed codes, routed scales, shared codes, shared scales):
+      // routed [E][8][H][Ix], shared [8][H][Isx], codes 2 per byte, one scale
+      // byte per 16 columns.  One buffer covers the block, so a lane takes
+      // its routed or shared chunk with the same two loads per pass.  The
+      // routed columns' tensor scale is folded into the routing weights (by
+      // the first wave); the shared one is a scalar load.
+      auto load_down = [&]() {
+        const uint8_t* blk = tab_ptr<const uint8_t>(S, w0 + kWDownC);
+        const uint8_t* ss = tab_ptr<const uint8_t>(S, w0 + kWSdS);
+        const uint32_t o_rs = (uint32_t)(tab_ptr<const uint8_t>(S, w0 + kWDownS) - blk);
+        const uint32_t o_sc = (uint32_t)(tab_ptr<const uint8_t>(S, w0 + kWSdC) - blk);
+        const uint32_t o_ss = (uint32_t)(ss - blk);
+        const rsrc_t rd = make_rsrc(blk, (uint64_t)o_ss + (uint64_t)kHidden * Is / 16);
         const int de = S.pk[dslot] & 0xFF;
+        const int doff = routed ? (32 * j) % Ix : 0;          // column in the expert's slice
+        const int scol = routed ? 0 : 32 * j - nroutedx;      // column in the shared slice
         const uint32_t rslice = (uint32_t)((de * kGroups + g) * kHidden);
-        const uint32_t oob_c = (uint32_t)((uint64_t)E * kHidden * I / 2);
+        const uint32_t sslice = (uint32_t)(g * kHidden);
 #pragma unroll
         for (int pc = 0; pc < kDownPasses; ++pc) {
-          const uint32_t rr = rslice + (uint32_t)(64 * li + 8 * wv + 4 * pc + (lane >> 4));
-          cdr[pc] = bload_u4_nt(rdc, routed ? rr * (Ix / 2) + doff / 2 : oob_c);
-          sdr[pc] = bload_u16_nt(rds, routed ? rr * (Ix / 16) + doff / 16 : oob_c / 8);
+          const uint32_t n = (uint32_t)(64 * li + 8 * wv + 4 * pc + (lane >> 4));
+          const uint32_t rr = rslice + n, sr = sslice + n;
+          cd[pc] = bload_u4_nt(rd, routed ? rr * (Ix / 2) + doff / 2 : o_sc + sr * (Isx / 2) + scol / 2);
+          sd[pc] = bload_u16_nt(rd, routed ? o_rs + rr * (Ix / 16) + doff / 16 : o_ss + sr * (Isx / 16) + scol / 16);
         }
-        dts = bload_f32(make_rsrc(tab_ptr<const float>(S, w0 + kWExpTs), (uint64_t)E * 3 * 4),
-                        (uint32_t)(3 * de + 2) * 4);
+        sts = sload_f32(tab_ptr<const float>(S, w0 + kWSdT), 0);
       };
       PairOps o[kNq];
       if (kComm && wv == 0) {
@@ -635,16 +662,20 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
         if (lane == 0)
           __hip_atomic_store(&S.pk[k - 1], (int)((tag << 8) | (uint32_t)elast), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_WORKGROUP);
+        // the down tensor scale of the expert of pick r (lane r), requested
+        // before the down operands so that it arrives with this wave's pairs
+        const float dts = bload_f32(make_rsrc(prs.ts, (uint64_t)E * 3 * 4),
+                                    (uint32_t)(3 * (lane < k ? S.pk[lane] & 0xFF : 0) + 2) * 4);
         FLINT_TRACE(l, 3);
-        load_down_shared();
-        load_down_routed();
+        load_down();
         // softmax over the k chosen logits (lane r holds the r-th; the first
-        // is the largest); the weights are read in phase C
+        // is the largest), times the down tensor scale of its expert; the
+        // weights are read in phase C
         const float my_v = ord_key_value(my_key);
         const float first = lane_f32(my_v, 0);
         const float ex = lane < k ? __expf(my_v - first) : 0.0f;
         const float z = lane_f32(row16_sum(ex), 0);
-        if (lane < k) S.w[lane] = ex / z;
+        if (lane < k) S.w[lane] = ex / z * dts;
         FLINT_TRACE(l, 15);
       } else {
         if constexpr (!kComm) FLINT_TRACE_LOAD(l, 11);
@@ -663,9 +694,18 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
           if (P.routes && blockIdx.x == 0 && t - kCommThreads < k)
             P.routes[((size_t)tok * L + l) * k + (t - kCommThreads)] = S.pk[t - kCommThreads] & 0xFF;
         }
-        load_down_shared();
-        load_down_routed();
+        load_down();
         FLINT_TRACE_LOAD(l, 22);
+        if constexpr (!kComm) {
+          // the next layer's router and shared rows (the next token's first
+          // layer after the last one) do not depend on this token: request
+          // them behind this layer's down-projection operands, so that they
+          // stream in with the routed weights rather than during the
+          // exchanges at the end of the layer (whose polls they would slow)
+          have_a = l + 1 < L || tok + 1 < P.T;
+          load_phase_a(l + 1 < L ? l + 1 : 0, have_a);
+          FLINT_TRACE_LOAD(l, 13);
+        }
       }
       stress_delay<kStress>(P, tok, l, 2);
 #pragma unroll
@@ -691,12 +731,10 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       {
         float hv[32];
         lds_x32(S.hs + kRowPad * j, hv);
-        const float coef = routed ? S.w[dslot] * dts : sts;
+        const float coef = routed ? S.w[dslot] : sts;
 #pragma unroll
         for (int pc = 0; pc < kDownPasses; ++pc) {
-          const uint4 c = make_uint4(cdr[pc].x | cds[pc].x, cdr[pc].y | cds[pc].y, cdr[pc].z | cds[pc].z,
-                                     cdr[pc].w | cds[pc].w);
-          const float acc = row16_sum(coef * nvfp4_lane_dot32(c, sdr[pc] | sds[pc], hv));
+          const float acc = row16_sum(coef * nvfp4_lane_dot32(cd[pc], sd[pc], hv));
           const int n = 64 * li + 8 * wv + 4 * pc + (lane >> 4);
           if (j == 0) put_pair<Scope::kDevice>(&s4a[(size_t)g * kHidden + n], acc, ep0 + 2);
         }
@@ -718,15 +756,6 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
           }
           if (poll_gave_up(spins, wc)) break;
         }
-      } else {
-        // the next layer's router and shared rows (the next token's first
-        // layer after the last one) do not depend on this token: request them
-        // now, while the partial outputs and the residual are exchanged
-        const int next = l + 1 < L ? l + 1 : (tok + 1 < P.T ? 0 : -1);
-        __builtin_amdgcn_sched_barrier(0);
-        have_a = next >= 0;
-        if (have_a) load_phase_a(next);
-        FLINT_TRACE_LOAD(l, 13);
       }
       wg_barrier();  // B4: partial outputs of this workgroup's rows in LDS
       if (S.bad) return false;
