@@ -61,10 +61,11 @@ constexpr int kGateUpComm = 2;                     // routed gate/up pairs per c
 constexpr int kDownPasses = 2;                     // 4-row down-projection passes of every wave
 constexpr uint32_t kSpinLimit = 1u << 22;
 #ifndef FLINT_POLL_SLEEP
-#define FLINT_POLL_SLEEP 2
+#define FLINT_POLL_SLEEP 0
 #endif
-// back-off between polls of data that has not arrived (units of 64 clocks):
-// keeps waiting workgroups from flooding the coherence point
+// back-off between polls of data that has not arrived (units of 64 clocks).
+// None by default: with the current exchanges every back-off measured
+// (1, 2 and 4 sleeps of 64 clocks) made the stack slower
 __device__ __forceinline__ void poll_backoff() {
   if (FLINT_POLL_SLEEP > 0) __builtin_amdgcn_s_sleep(FLINT_POLL_SLEEP);
 }
