@@ -56,7 +56,8 @@ constexpr int kSliceK = 512;            // k * (I/8) + Is/8: one group's slice o
 constexpr int kHeadRowsPerWave = 8;
 constexpr int kCommWaves = 4;                      // waves that poll the exchanges
 constexpr int kCommThreads = kCommWaves * 64;
-static_assert(kStackWaves - kCommWaves == 4, "the router logit sums four partial dot products, one per loading wave");
+static_assert(kStackWaves - kCommWaves == 4 && kCommWaves == 4,
+              "four loading waves hold the router row; four polling waves sum its dot product and the norm");
 constexpr int kGateUpComm = 2;                     // routed gate/up pairs per communication wave
 constexpr int kDownPasses = 2;                     // 4-row down-projection passes of every wave
 constexpr uint32_t kSpinLimit = 1u << 22;
@@ -193,9 +194,22 @@ __device__ __forceinline__ bool poll_gave_up(uint32_t& spins, const WaitCtx& w) 
 // ep; values -> dst (pair i to dst[i], or to its padded row position).  Called
 // by the communication waves only; each thread owns up to four 128-bit
 // chunks and keeps all of its outstanding chunks in flight at once.
-template <Scope sc>
+// Router partial dot product and sum of squares of one (value, value) pair of
+// rows 2c, 2c + 1, and the fixed order in which a polling thread adds its
+// four pairs' parts; the same arithmetic whether the values come from an
+// exchange or from LDS, so that a layer gives the same bits either way.
+__device__ __forceinline__ float pair_dot(float2 w, float v0, float v1) { return __builtin_fmaf(w.y, v1, w.x * v0); }
+__device__ __forceinline__ float pair_sq(float v0, float v1) { return __builtin_fmaf(v1, v1, v0 * v0); }
+__device__ __forceinline__ float sum4(const float* p) { return (p[0] + p[1]) + (p[2] + p[3]); }
+
+// With kDot, each of the thread's pairs (rows 2c, 2c + 1) also gives
+// pair_dot(wrow[2c], wrow[2c + 1]; v0, v1) and pair_sq(v0, v1) (wrow in LDS,
+// read before the first poll); the thread's parts are added in a fixed order
+// once all have arrived (whatever the order of arrival), into dacc and sacc.
+template <Scope sc, bool kDot = false>
 __device__ __forceinline__ void poll_pairs(const uint64_t* buf, int n, uint32_t ep, float* dst, const WaitCtx& w,
-                                           bool pad = false) {
+                                           bool pad = false, const float* wrow = nullptr, float* dacc = nullptr,
+                                           float* sacc = nullptr) {
   constexpr int kMaxPer = 4;
   __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint64_t*>(buf), 0, n * 8, 0x00020000);
   const int t = threadIdx.x;
@@ -204,6 +218,17 @@ __device__ __forceinline__ void poll_pairs(const uint64_t* buf, int n, uint32_t 
   for (int i = 0; i < kMaxPer; ++i)
     if (t + i * kCommThreads < n / 2) pending |= 1u << i;
   uint32_t spins = 0;
+  float2 ww[kMaxPer];
+  float dp[kMaxPer], sp[kMaxPer];
+  if constexpr (kDot) {
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      const int c = t + i * kCommThreads;
+      ww[i] = (pending & (1u << i)) ? *reinterpret_cast<const float2*>(wrow + 2 * c) : make_float2(0.0f, 0.0f);
+      dp[i] = 0.0f;
+      sp[i] = 0.0f;
+    }
+  }
   while (pending) {
     uint32_t v[kMaxPer][4];
 #pragma unroll
@@ -218,12 +243,22 @@ __device__ __forceinline__ void poll_pairs(const uint64_t* buf, int n, uint32_t 
       if ((pending & (1u << i)) && v[i][1] == ep && v[i][3] == ep) {
         const int c = t + i * kCommThreads;
         const int d = pad ? padded(2 * c) : 2 * c;  // 2c, 2c+1 share a row
-        dst[d] = __uint_as_float(v[i][0]);
-        dst[d + 1] = __uint_as_float(v[i][2]);
+        const float v0 = __uint_as_float(v[i][0]), v1 = __uint_as_float(v[i][2]);
+        dst[d] = v0;
+        dst[d + 1] = v1;
+        if constexpr (kDot) {
+          dp[i] = pair_dot(ww[i], v0, v1);
+          sp[i] = pair_sq(v0, v1);
+        }
         pending &= ~(1u << i);
       }
     }
     if (!pending || poll_gave_up(spins, w)) break;
+  }
+  if constexpr (kDot) {
+    static_assert(kMaxPer == 4, "four parts per thread");
+    *dacc = sum4(dp);
+    *sacc = sum4(sp);
   }
 }
 
@@ -282,7 +317,9 @@ struct StackLds {
   float part[kGroups * 64];                          // the 8 partial outputs of this workgroup's rows
   float hp[2 * kStackWGs];                           // head partials (max, index)
   float red[kStackWaves];
-  float rp[kStackWaves - kCommWaves];                // router logit: one partial dot per loading wave
+  float rp[kCommWaves];                              // router logit: one partial dot per polling wave
+  float rq[kCommWaves];                              // sum of squares of the residual: one part per polling wave
+  float wr[kHidden];                                 // router row of this workgroup for the next layer
   float w[kMaxTopK];
   int32_t pk[kMaxTopK];                              // picks of phase B: (layer tag << 8) | expert
   float bv[kStackWaves];
@@ -398,26 +435,6 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
     tgs = sload_f32(tab_ptr<const float>(S, w0 + kWSgT), 0);
     tus = sload_f32(tab_ptr<const float>(S, w0 + kWSuT), 0);
   };
-  // this wave's part of router row . residual (before the norm; the logit
-  // is the sum of the parts times the norm's scale, since the norm scales
-  // every value alike): lane i takes columns 512 lw + 256 c + 4 i ..
-  // 512 lw + 256 c + 4 i + 3, c = 0, 1
-  auto router_dot = [&]() {
-    float4 u[kRouterCols / 256];
-#pragma unroll
-    for (int c = 0; c < kRouterCols / 256; ++c)
-      u[c] = *reinterpret_cast<const float4*>(S.h + kRouterCols * lw + 256 * c + 4 * lane);
-    float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;  // four chains for latency
-#pragma unroll
-    for (int c = 0; c < kRouterCols / 256; ++c) {
-      a0 = __builtin_fmaf(wr[c].x, u[c].x, a0);
-      a1 = __builtin_fmaf(wr[c].y, u[c].y, a1);
-      a2 = __builtin_fmaf(wr[c].z, u[c].z, a2);
-      a3 = __builtin_fmaf(wr[c].w, u[c].w, a3);
-    }
-    return wave_sum((a0 + a1) + (a2 + a3));
-  };
-
   // SwiGLU of routed gate/up pair p of this group's slice: loads ...
   struct PairOps {
     uint4 cg, cu;
@@ -483,26 +500,60 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       if (!kComm && !have_a) {
         load_phase_a(l, true);
       }
-      // router logit rrow = (router row . residual) * the norm's scale: the
-      // loading waves' partial dot products go to LDS before the norm's
-      // first barrier, and the first loading wave stores their sum times the
-      // scale into the logit exchange of every group as soon as the scale is
-      // known
-      if constexpr (!kComm) {
-        const float part = router_dot();
-        if (lane == 0) S.rp[lw] = part;
-      }
+      // router logit rrow = (router row . residual) * the norm's scale,
+      // stored into the logit exchange of every group by the first loading
+      // wave as soon as the scale is known.
       const bool rwave = !kComm && lw == 0 && rrow < E;  // uniform
-      rms_to_u(S.h, S.u, S.red, P.eps, [&](float sc) {  // B1, B2
+      auto publish_logit = [&](float sc) {
         if (rwave) {
           stress_delay<kStress>(P, tok, l, 0);
-          const float racc = (S.rp[0] + S.rp[1]) + (S.rp[2] + S.rp[3]);
+          const float racc = sum4(S.rp);
           if (lane < kGroups)
             put_pair<Scope::kDevice>(reinterpret_cast<uint64_t*>(P.s2 + s2_off(par, lane, rrow, C.phase)), racc * sc,
                                      ep0);
           FLINT_TRACE_LOAD(l, 8);
         }
-      });
+      };
+      if (l == 0) {
+        // a call's or token's first layer: the residual did not come through
+        // the exchange, so the polling waves take the same parts of it from
+        // LDS (the router row goes there from the loading waves' registers)
+        if constexpr (!kComm) {
+#pragma unroll
+          for (int i = 0; i < kRouterCols / 256; ++i)
+            *reinterpret_cast<float4*>(S.wr + kRouterCols * lw + 256 * i + 4 * lane) = wr[i];
+        }
+        wg_barrier();  // B0: router row in LDS
+        if constexpr (kComm) {
+          float dp[4], sp[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = t + i * kCommThreads;
+            const float2 ww = *reinterpret_cast<const float2*>(S.wr + 2 * c);
+            const float2 hv = *reinterpret_cast<const float2*>(S.h + 2 * c);
+            dp[i] = pair_dot(ww, hv.x, hv.y);
+            sp[i] = pair_sq(hv.x, hv.y);
+          }
+          const float d = wave_sum(sum4(dp)), q = wave_sum(sum4(sp));
+          if (lane == 0) {
+            S.rp[wv] = d;
+            S.rq[wv] = q;
+          }
+        }
+        wg_barrier();  // B0'
+      }
+      // The polling waves have the parts of the router dot product and of the
+      // sum of squares (summed while the residual arrived, in phase D of the
+      // previous layer, or just above): the logit goes out at once, and u =
+      // s h needs one barrier.
+      {
+        const float sc = 1.0f / sqrtf(sum4(S.rq) * (1.0f / kHidden) + P.eps);
+        publish_logit(sc);
+#pragma unroll
+        for (int i = 0; i < kHidden / kStackThreads; ++i)
+          S.u[padded(t + i * kStackThreads)] = S.h[t + i * kStackThreads] * sc;
+        wg_barrier();  // B1
+      }
       FLINT_TRACE(l, 1);
       float xv[32];  // this lane's 32 normalised activations (phases A and B)
       lds_x32(S.u + kRowPad * lane, xv);
@@ -742,6 +793,15 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       }
       FLINT_TRACE(l, 28);
       FLINT_TRACE_LOAD(l, 29);
+      if constexpr (!kComm) {
+        // the next layer's router row (requested in phase B) to LDS, where
+        // the polling waves apply it to the residual as it arrives
+        if (l + 1 < L) {
+#pragma unroll
+          for (int i = 0; i < kRouterCols / 256; ++i)
+            *reinterpret_cast<float4*>(S.wr + kRouterCols * lw + 256 * i + 4 * lane) = wr[i];
+        }
+      }
       if constexpr (kComm) {
         // rows 64 li .. 64 li + 63 of every group's partial output
         __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(s4a, 0, kGroups * kHidden * 8, 0x00020000);
@@ -768,7 +828,18 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
       // group's new residual (the rows this workgroup owns arrive only after
       // they were read here)
       if constexpr (kComm) {
-        poll_pairs<Scope::kXcd>(s4b, kHidden, ep0 + 3, S.h, wc);
+        if (l + 1 < L) {
+          float dacc, sacc;
+          poll_pairs<Scope::kXcd, true>(s4b, kHidden, ep0 + 3, S.h, wc, false, S.wr, &dacc, &sacc);
+          dacc = wave_sum(dacc);
+          sacc = wave_sum(sacc);
+          if (lane == 0) {
+            S.rp[wv] = dacc;
+            S.rq[wv] = sacc;
+          }
+        } else {
+          poll_pairs<Scope::kXcd>(s4b, kHidden, ep0 + 3, S.h, wc);
+        }
       } else {
         stress_delay<kStress>(P, tok, l, 4);
         if (lw == 0) {
