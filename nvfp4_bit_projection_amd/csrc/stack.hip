@@ -202,10 +202,9 @@ __device__ __forceinline__ float pair_dot(float2 w, float v0, float v1) { return
 __device__ __forceinline__ float pair_sq(float v0, float v1) { return __builtin_fmaf(v1, v1, v0 * v0); }
 __device__ __forceinline__ float sum4(const float* p) { return (p[0] + p[1]) + (p[2] + p[3]); }
 
-// With kDot, each of the thread's pairs (rows 2c, 2c + 1) also gives
-// pair_dot(wrow[2c], wrow[2c + 1]; v0, v1) and pair_sq(v0, v1) (wrow in LDS,
-// read before the first poll); the thread's parts are added in a fixed order
-// once all have arrived (whatever the order of arrival), into dacc and sacc.
+// With kDot, once all of the thread's pairs have arrived, each (rows 2c,
+// 2c + 1) gives pair_dot(wrow[2c], wrow[2c + 1]; v0, v1) and pair_sq(v0, v1)
+// (wrow in LDS), added in a fixed order into dacc and sacc.
 template <Scope sc, bool kDot = false>
 __device__ __forceinline__ void poll_pairs(const uint64_t* buf, int n, uint32_t ep, float* dst, const WaitCtx& w,
                                            bool pad = false, const float* wrow = nullptr, float* dacc = nullptr,
@@ -218,17 +217,9 @@ __device__ __forceinline__ void poll_pairs(const uint64_t* buf, int n, uint32_t 
   for (int i = 0; i < kMaxPer; ++i)
     if (t + i * kCommThreads < n / 2) pending |= 1u << i;
   uint32_t spins = 0;
-  float2 ww[kMaxPer];
-  float dp[kMaxPer], sp[kMaxPer];
-  if constexpr (kDot) {
+  float2 got[kMaxPer];  // kDot: the thread's pairs, kept for the sums after the loop
 #pragma unroll
-    for (int i = 0; i < kMaxPer; ++i) {
-      const int c = t + i * kCommThreads;
-      ww[i] = (pending & (1u << i)) ? *reinterpret_cast<const float2*>(wrow + 2 * c) : make_float2(0.0f, 0.0f);
-      dp[i] = 0.0f;
-      sp[i] = 0.0f;
-    }
-  }
+  for (int i = 0; i < kMaxPer; ++i) got[i] = make_float2(0.0f, 0.0f);
   while (pending) {
     uint32_t v[kMaxPer][4];
 #pragma unroll
@@ -246,10 +237,7 @@ __device__ __forceinline__ void poll_pairs(const uint64_t* buf, int n, uint32_t 
         const float v0 = __uint_as_float(v[i][0]), v1 = __uint_as_float(v[i][2]);
         dst[d] = v0;
         dst[d + 1] = v1;
-        if constexpr (kDot) {
-          dp[i] = pair_dot(ww[i], v0, v1);
-          sp[i] = pair_sq(v0, v1);
-        }
+        if constexpr (kDot) got[i] = make_float2(v0, v1);
         pending &= ~(1u << i);
       }
     }
@@ -257,6 +245,15 @@ __device__ __forceinline__ void poll_pairs(const uint64_t* buf, int n, uint32_t 
   }
   if constexpr (kDot) {
     static_assert(kMaxPer == 4, "four parts per thread");
+    float dp[kMaxPer], sp[kMaxPer];
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i) {
+      const int c = t + i * kCommThreads;
+      const float2 ww = (t + i * kCommThreads < n / 2) ? *reinterpret_cast<const float2*>(wrow + 2 * c)
+                                                        : make_float2(0.0f, 0.0f);
+      dp[i] = pair_dot(ww, got[i].x, got[i].y);
+      sp[i] = pair_sq(got[i].x, got[i].y);
+    }
     *dacc = sum4(dp);
     *sacc = sum4(sp);
   }
