@@ -465,8 +465,11 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
     o.su = bload_u16_nt(R.us, row * (kHidden / 16) + 2 * lane);
     // (vector loads: a scalar load here would make the wave's next LDS wait
     // also wait for it)
-    o.Sg = sload_f32(R.ts, (uint32_t)(3 * e + 0));
-    o.Su = sload_f32(R.ts, (uint32_t)(3 * e + 1));
+    // (vector loads: a scalar load here would make the wave's next LDS wait,
+    // such as the next pick or the down operands' expert, wait for it too)
+    const rsrc_t rts = make_rsrc(R.ts, (uint64_t)E * 3 * 4);
+    o.Sg = bload_f32(rts, (uint32_t)(3 * e + 0) * 4);
+    o.Su = bload_f32(rts, (uint32_t)(3 * e + 1) * 4);
     return o;
   };
   // ... and the SwiGLU value g(x) * u(x) with g = silu(gate . x)
