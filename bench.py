@@ -35,11 +35,20 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def kernel_code(text: str) -> str:
+    """The code of a C++/HIP source without its comments and with runs of
+    whitespace collapsed, so that an edit to comments alone keeps the hash
+    (the sources hashed here hold no comment markers inside string literals)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(kernel_code(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -17,10 +17,12 @@
 // workgroups of one XCD, and li = b / 8 is the index inside the group.
 //
 // Work split of one layer (E experts, top-k, width I, shared width Is):
-//  A  RMSNorm of the residual; workgroup b computes router row b (the fp32
-//     router is read once per layer) and stores its logit into the logit
-//     exchange of every group; each group computes the SwiGLU of its 1/8
-//     slice of the shared expert's rows;
+//  A  workgroup b owns router row b (the fp32 router is read once per
+//     layer): its logit is (row . h) * s, s the RMSNorm scale of the
+//     residual h, both sums formed while h arrived (phase D of the layer
+//     before), and goes into the logit exchange of every group; u = s h;
+//     each group computes the SwiGLU of its 1/8 slice of the shared
+//     expert's rows;
 //  B  the first wave of every workgroup gathers the E logits and takes the
 //     top k, then the group computes the SwiGLU of its 1/8 slice (I/8 rows)
 //     of each chosen expert; the down-projection weights of phase C are
@@ -29,7 +31,8 @@
 //     matching 1/8 column slice of every down matrix (routed, weighted by the
 //     routing weights, and shared): a partial output for all H rows;
 //  D  the 8 partial outputs are summed (fixed order) and added to the
-//     residual.
+//     residual; the polling threads form the next layer's router and norm
+//     sums from the new residual they receive.
 // Exchanges.  A -> B logits (across XCDs), B -> C hidden slice (inside a
 // group), C -> D partial outputs (across groups) and D -> A the new residual
 // (inside a group).  Values travel as 64-bit (value, epoch) pairs; a
@@ -370,14 +373,15 @@ __device__ __forceinline__ void stress_delay(const StackParams& P, int tok, int 
 // leave at the same barrier on error; returns false then.
 //
 // Communication role (waves 0-3): polls every exchange (the first wave alone
-// gathers the logits and takes the top k), and computes 2 of the 12 routed
-// gate/up pairs per wave and workgroup.  A wave's
-// loads complete in issue order, so a wave that polls must not have weight
-// loads in flight.
-// Loading role (waves 4-7): router rows and the shared expert's gate/up
-// (phase A), one routed gate/up pair and the down-projection operands
-// (phase B), the partial outputs (phase C), the residual rows (phase D), and
-// the next layer's router and shared rows, requested ahead of time.
+// gathers the logits and takes the top k), computes 2 of the 12 routed
+// gate/up pairs per wave and workgroup, and forms the router and norm sums
+// from the residual it receives.  A wave's loads complete in issue order, so
+// a wave that polls must not have weight loads in flight.
+// Loading role (waves 4-7): the shared expert's gate/up (phase A), one
+// routed gate/up pair and the down-projection operands (phase B), the
+// partial outputs (phase C), the residual rows (phase D), and the next
+// layer's router row (a quarter per wave, to LDS in phase C) and shared
+// rows, requested behind the down operands.
 template <bool kComm, bool kHead, bool kStress>
 __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& C) {
   const int t = C.t, lane = C.lane, wv = C.wv, g = C.g, li = C.li;
