@@ -426,6 +426,20 @@ def test_stack_full_size_per_layer(F, full_stack):
         assert_close(y, r.layer_inputs[l + 1] - r.layer_inputs[l], f"layer {l} output")
 
 
+def test_stack_tokens_one_launch_equal_separate_launches(F, full_stack):
+    """Three tokens in one launch give the same bits as one launch per token:
+    every token's first layer forms its router and norm sums from LDS with the
+    same arithmetic as the later layers do from the exchange."""
+    stack = full_stack[0]
+    x = F[1].tokens(FULL_SEEDS[:3], 2048)
+    lg, am = stack.decode(x)
+    sep = [stack.decode(x[t:t + 1]) for t in range(3)]
+    torch.cuda.synchronize()
+    assert stack.error() == 0
+    for t, (l1, a1) in enumerate(sep):
+        assert torch.equal(lg[t:t + 1], l1) and torch.equal(am[t:t + 1], a1), t
+
+
 def test_stack_decode_layers_composes(F, full_stack):
     """Layers 0-46 as three calls of flint_stack_decode_layers (in place) give
     the same bits as one call over all of them."""
