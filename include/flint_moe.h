@@ -257,14 +257,16 @@ int32_t flint_stack_decode(const flint_stack_plan* plan /*[host]*/, const float*
  * polling wave: 0 layer start, 1 norm done, 2 logits arrived, 16 its keys
  * sorted, 17 first pick published, 18 last round done, 3 every pick of the
  * top k published, 4 its routed pairs stored, 5 hidden slice arrived,
- * 28 its partial outputs stored, 6 partial outputs arrived, 7 new residual
- * arrived, 15 routing weights computed; seen by the second polling wave: 23 / 25 the pick of its first /
+ * 28 its partial outputs stored, 14 its residual rows stored (partial
+ * outputs arrived and summed), 6 the barrier after them passed, 7 new
+ * residual arrived, 15 routing weights computed; seen by the second polling
+ * wave: 23 / 25 the pick of its first /
  * second pair known, 24 / 26 that pair requested, 27 its pairs stored; seen
  * by the first loading wave: 8 router logit stored, 9 shared pair stored, 11
  * routed phase started, 19 the pick of its pair known, 20 its pair
  * requested, 21 every pick known, 22 down-projection operands requested, 13
  * the next layer's rows requested, 12 its routed pair stored, 29 its partial
- * outputs stored, 14 residual rows stored; 10, 30 and 31 are unused (0).
+ * outputs stored; 10, 30 and 31 are unused (0).
  * Row L holds the head start, the head rows done, the head partials
  * arrived, the kernel entry and the end of the kernel's set-up.  Returns
  * FLINT_E_UNSUPPORTED for the kernel-sequence schedule and for more than 64

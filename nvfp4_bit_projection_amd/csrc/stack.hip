@@ -30,9 +30,10 @@
 //  C  the group multiplies its slice of the hidden activations by the
 //     matching 1/8 column slice of every down matrix (routed, weighted by the
 //     routing weights, and shared): a partial output for all H rows;
-//  D  the 8 partial outputs are summed (fixed order) and added to the
-//     residual; the polling threads form the next layer's router and norm
-//     sums from the new residual they receive.
+//  D  the 8 partial outputs are summed (fixed order, across 8 lanes of
+//     the polling waves) and added to the residual; the polling threads form
+//     the next layer's router and norm sums from the new residual they
+//     receive.
 // Exchanges.  A -> B logits (across XCDs), B -> C hidden slice (inside a
 // group), C -> D partial outputs (across groups) and D -> A the new residual
 // (inside a group).  Values travel as 64-bit (value, epoch) pairs; a
@@ -314,7 +315,6 @@ struct StackLds {
   float h[kHidden];                                  // residual stream
   float u[kHidden / 32 * kRowPad];                   // normalised residual, padded rows
   float hs[kSliceK / 32 * kRowPad];                  // this group's hidden slice, padded rows
-  float part[kGroups * 64];                          // the 8 partial outputs of this workgroup's rows
   float hp[2 * kStackWGs];                           // head partials (max, index)
   float red[kStackWaves];
   float rp[kCommWaves];                              // router logit: one partial dot per polling wave
@@ -379,9 +379,10 @@ __device__ __forceinline__ void stress_delay(const StackParams& P, int tok, int 
 // a wave that polls must not have weight loads in flight.
 // Loading role (waves 4-7): the shared expert's gate/up (phase A), one
 // routed gate/up pair and the down-projection operands (phase B), the
-// partial outputs (phase C), the residual rows (phase D), and the next
-// layer's router row (a quarter per wave, to LDS in phase C) and shared
-// rows, requested behind the down operands.
+// partial outputs (phase C), and the next layer's router row (a quarter per
+// wave, to LDS in phase C) and shared rows, requested behind the down
+// operands.  The polling waves also sum the partial outputs of the
+// workgroup's residual rows and publish them (end of phase C).
 template <bool kComm, bool kHead, bool kStress>
 __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& C) {
   const int t = C.t, lane = C.lane, wv = C.wv, g = C.g, li = C.li;
@@ -807,30 +808,45 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
         }
       }
       if constexpr (kComm) {
-        // rows 64 li .. 64 li + 63 of every group's partial output
+        // rows 64 li .. 64 li + 63: thread t takes group t % 8's partial
+        // outputs of rows 64 li + 2 (t / 8) and the next one; the 8 groups'
+        // values are summed over 8 neighbouring lanes (fixed butterfly
+        // order), added to the residual and published by the group-0 lane
         __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(s4a, 0, kGroups * kHidden * 8, 0x00020000);
-        const int gg = t >> 5, cc = t & 31;  // kCommThreads == kGroups * 32 chunks
-        const int off = (gg * kHidden + 64 * li + 2 * cc) * 8;
+        const int gg = t & 7, rp = t >> 3;  // kCommThreads == kGroups * 32 pairs of rows
+        const int off = (gg * kHidden + 64 * li + 2 * rp) * 8;
+        float y0 = 0.0f, y1 = 0.0f;
         uint32_t spins = 0;
         while (true) {
           auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 16);
           if (v[1] == ep0 + 2 && v[3] == ep0 + 2) {
-            S.part[gg * 64 + 2 * cc] = __uint_as_float(v[0]);
-            S.part[gg * 64 + 2 * cc + 1] = __uint_as_float(v[2]);
+            y0 = __uint_as_float(v[0]);
+            y1 = __uint_as_float(v[2]);
             break;
           }
           if (poll_gave_up(spins, wc)) break;
         }
+        y0 += dpp_f32<kDppXor1>(y0);
+        y1 += dpp_f32<kDppXor1>(y1);
+        y0 += dpp_f32<kDppXor2>(y0);
+        y1 += dpp_f32<kDppXor2>(y1);
+        y0 += dpp_f32<kDppHalfMirror>(y0);
+        y1 += dpp_f32<kDppHalfMirror>(y1);
+        stress_delay<kStress>(P, tok, l, 4);
+        if (gg == 0) {
+          const int n = 64 * li + 2 * rp;
+          put_pair<Scope::kXcd>(&s4b[n], S.h[n] + y0, ep0 + 3);
+          put_pair<Scope::kXcd>(&s4b[n + 1], S.h[n + 1] + y1, ep0 + 3);
+        }
+        FLINT_TRACE(l, 14);
       }
-      wg_barrier();  // B4: partial outputs of this workgroup's rows in LDS
+      wg_barrier();  // B4: the next layer's router row in LDS (phase D reads it)
       if (S.bad) return false;
       FLINT_TRACE(l, 6);
 
       // ---------------------------------------------------------- phase D
-      // the first loading wave adds the partials (fixed order) to its rows of
-      // the residual and publishes them; the communication waves collect the
-      // group's new residual (the rows this workgroup owns arrive only after
-      // they were read here)
+      // the communication waves collect the group's new residual (the rows
+      // this workgroup owns arrive only after they were read above)
       if constexpr (kComm) {
         if (l + 1 < L) {
           float dacc, sacc;
@@ -843,15 +859,6 @@ __device__ bool stack_role(const StackParams& P, StackLds& S, const StackCoord& 
           }
         } else {
           poll_pairs<Scope::kXcd>(s4b, kHidden, ep0 + 3, S.h, wc);
-        }
-      } else {
-        stress_delay<kStress>(P, tok, l, 4);
-        if (lw == 0) {
-          float y = 0.0f;
-#pragma unroll
-          for (int gg = 0; gg < kGroups; ++gg) y += S.part[gg * 64 + lane];
-          put_pair<Scope::kXcd>(&s4b[64 * li + lane], S.h[64 * li + lane] + y, ep0 + 3);
-          FLINT_TRACE_LOAD(l, 14);
         }
       }
       wg_barrier();  // B5: new residual in LDS
