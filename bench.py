@@ -782,27 +782,44 @@ def main() -> int:
         log("the stack kernel raised its error flag")
         return 1
     # RUNS timed runs of exactly K steps each, every run bracketed by
-    # synchronisations; every step is one launch of the stack kernel on
-    # torch's current stream: events around each launch give its duration,
-    # events around the run its throughput.  The reported value is the
-    # median run; min and max are reported with it.
-    run_ms, launch_ms, walls = [], [], []
-    for run in range(RUNS):
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # synchronisations and one event pair on torch's current stream, the
+    # stream every launch goes to: their throughput is the reported value
+    # (the median run; min and max are reported with it).  Then RUNS more runs
+    # of the same K steps with an event pair around every launch: these give
+    # the kernel's launch duration for the roofline.  An event between two
+    # launches adds a marker to the queue and widens the gap between them, so
+    # the throughput runs carry none; the instrumented runs' own throughput is
+    # reported beside it.
+    def timed_run(per_launch):
+        n = args.steps if per_launch else 0
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
         ev0.record()
-        for i, t in enumerate(range(args.warmup, T)):
-            starts[i].record()
-            step(t)
-            ends[i].record()
+        if per_launch:
+            for i, t in enumerate(range(args.warmup, T)):
+                starts[i].record()
+                step(t)
+                ends[i].record()
+        else:
+            for t in range(args.warmup, T):
+                step(t)
         ev1.record()
         torch.cuda.synchronize()
-        walls.append(time.perf_counter() - wall0)
-        run_ms.append(ev0.elapsed_time(ev1))
-        launch_ms += [a.elapsed_time(b) for a, b in zip(starts, ends)]
+        wall = time.perf_counter() - wall0
+        return ev0.elapsed_time(ev1), [a.elapsed_time(b) for a, b in zip(starts, ends)], wall
+
+    run_ms, launch_ms, walls, inst_ms = [], [], [], []
+    for run in range(RUNS):
+        ms_run, _, wall = timed_run(False)
+        run_ms.append(ms_run)
+        walls.append(wall)
+    for run in range(RUNS):
+        ms_run, per_launch, _ = timed_run(True)
+        inst_ms.append(ms_run)
+        launch_ms += per_launch
     if stack.error():
         log("the stack kernel raised its error flag")
         return 1
@@ -818,7 +835,8 @@ def main() -> int:
     gbs = token_bytes / (launch_avg * 1e-3) / 1e9
     log(f"{RUNS} runs of {args.steps} tokens: median {ms:.2f} ms ({tok_s:.1f} tok/s), "
         f"min {min(tok_runs):.1f} max {max(tok_runs):.1f} tok/s; {KERNEL} launch avg {launch_avg * 1e3:.1f} us "
-        f"(median {launch_ms[len(launch_ms) // 2] * 1e3:.1f}), {gbs:.1f} GB/s")
+        f"(median {launch_ms[len(launch_ms) // 2] * 1e3:.1f}), {gbs:.1f} GB/s; runs with an event pair around "
+        f"every launch: median {1000.0 * args.steps / sorted(inst_ms)[RUNS // 2]:.1f} tok/s")
 
     traffic = measured_traffic()
     result = {
@@ -844,7 +862,8 @@ def main() -> int:
                      "traffic_bytes_per_launch": traffic, "launch_us": round(launch_avg * 1e3, 2)},
         "runs": {"n": RUNS, "steps_each": args.steps, "tok_s_median": round(tok_s, 2),
                  "tok_s_min": round(min(tok_runs), 2), "tok_s_max": round(max(tok_runs), 2),
-                 "tok_s": [round(v, 2) for v in tok_runs], "wall_s": [round(w, 4) for w in walls]},
+                 "tok_s": [round(v, 2) for v in tok_runs], "wall_s": [round(w, 4) for w in walls],
+                 "instrumented_tok_s_median": round(1000.0 * args.steps / sorted(inst_ms)[RUNS // 2], 2)},
     }
     # release device memory before the interpreter exits (keeps profilers'
     # teardown away from live allocations)
